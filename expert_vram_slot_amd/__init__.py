@@ -1,0 +1,179 @@
+"""Python binding of libmoeslot.so, the gfx950 expert-slot MoE layer.
+
+Argument marshalling only: every function here has the name and argument
+order of its C entry point in include/moe_slot.h, takes torch tensors (or
+raw integer addresses) for pointers and defaults the stream to torch's
+current stream.  All arithmetic runs in the library's HIP kernels (and, for
+``moe_ffn_host_misses``, its C++ host pass).  If the library is missing the
+import of any function fails loudly; there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "lib", "libmoeslot.so")
+
+MOE_OK = 0
+MOE_E_ARG, MOE_E_ALIGN, MOE_E_DTYPE, MOE_E_SHAPE, MOE_E_HIP, MOE_E_NOMEM = -1, -2, -3, -4, -5, -6
+MOE_X_F32, MOE_X_BF16 = 0, 1
+MOE_W_F32, MOE_W_BF16, MOE_W_W8A8, MOE_W_Q4B32 = 0, 1, 2, 3
+MOE_STATIC, MOE_LRU, MOE_LFU = 0, 1, 2
+MOE_MAX_E, MOE_MAX_S, MOE_MAX_K = 4096, 1024, 32
+POLICIES = {"static": MOE_STATIC, "lru": MOE_LRU, "lfu": MOE_LFU}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, code: int, reason: str):
+        super().__init__(f"{fn} failed ({code}): {reason}")
+        self.code = code
+
+
+class CacheState(ctypes.Structure):
+    _fields_ = [("e2s", ctypes.c_void_p), ("s2e", ctypes.c_void_p), ("last", ctypes.c_void_p),
+                ("freq", ctypes.c_void_p), ("step", ctypes.c_void_p), ("E", ctypes.c_int32), ("S", ctypes.c_int32)]
+
+
+class SlabLayout(ctypes.Structure):
+    _fields_ = [("w", ctypes.c_int64 * 3), ("s", ctypes.c_int64 * 3), ("total", ctypes.c_int64)]
+
+
+_lib = None
+
+
+def lib():
+    """Load the library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: run __graft_entry__.build() (hipcc for gfx950) first")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+        sig = {
+            "moe_abi_version": (i32, []),
+            "moe_last_error": (ctypes.c_char_p, []),
+            "moe_slab_layout": (i32, [i32, i32, i32, ctypes.POINTER(SlabLayout)]),
+            "moe_bias_table": (i32, [vp, i32, i32, f32, vp, vp]),
+            "moe_route": (i32, [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "cache_init": (i32, [ctypes.POINTER(CacheState), vp, vp]),
+            "cache_pick_static": (i32, [vp, i32, i32, i32, vp, vp]),
+            "cache_manage": (i32, [ctypes.POINTER(CacheState), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
+            "cache_gather": (i32, [vp, vp, i32, vp, vp, sz, vp]),
+            "moe_ffn_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
+            "moe_ffn_slots": (i32, [vp, i32, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, vp, sz, vp]),
+            "moe_ffn_host_misses": (i32, [vp, i32, vp, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, i32]),
+            "moe_combine": (i32, [vp, vp, i32, i32, vp]),
+            "moe_host_alloc": (vp, [sz]),
+            "moe_host_free": (i32, [vp]),
+        }
+        for name, (res, args) in sig.items():
+            f = getattr(L, name)
+            f.restype, f.argtypes = res, args
+        _lib = L
+    return _lib
+
+
+def _p(a):
+    """Pointer of a tensor / numpy array / int / None."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if hasattr(a, "data_ptr"):
+        return a.data_ptr()
+    if hasattr(a, "ctypes"):
+        return a.ctypes.data
+    raise TypeError(f"cannot take a pointer of {type(a)!r}")
+
+
+def _stream(s):
+    if s is not None:
+        return s.cuda_stream if hasattr(s, "cuda_stream") else int(s)
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _check(name, rc):
+    if rc != MOE_OK:
+        raise MoeError(name, rc, (lib().moe_last_error() or b"").decode())
+    return rc
+
+
+def moe_abi_version() -> int:
+    return lib().moe_abi_version()
+
+
+def moe_last_error() -> str:
+    return (lib().moe_last_error() or b"").decode()
+
+
+def moe_slab_layout(w_type, H, I) -> SlabLayout:
+    out = SlabLayout()
+    _check("moe_slab_layout", lib().moe_slab_layout(w_type, H, I, ctypes.byref(out)))
+    return out
+
+
+def moe_bias_table(b, E, n_hot, cap, bias, stream=None):
+    return _check("moe_bias_table", lib().moe_bias_table(_p(b), E, n_hot, cap, _p(bias), _stream(stream)))
+
+
+def moe_route(x, x_dtype, G, bias, ids_in, T, H, E, k, ids, w, logits, stream=None):
+    return _check("moe_route", lib().moe_route(_p(x), x_dtype, _p(G), _p(bias), _p(ids_in), T, H, E, k, _p(ids),
+                                               _p(w), _p(logits), _stream(stream)))
+
+
+def cache_state(e2s, s2e, last, freq, step, E, S) -> CacheState:
+    return CacheState(_p(e2s), _p(s2e), _p(last), _p(freq), _p(step), E, S)
+
+
+def cache_init(st, resident, stream=None):
+    return _check("cache_init", lib().cache_init(ctypes.byref(st), _p(resident), _stream(stream)))
+
+
+def cache_pick_static(ids, n_ids, E, S, resident, stream=None):
+    return _check("cache_pick_static", lib().cache_pick_static(_p(ids), n_ids, E, S, _p(resident), _stream(stream)))
+
+
+def cache_manage(st, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_host, stats=None, stream=None):
+    return _check("cache_manage", lib().cache_manage(ctypes.byref(st), policy, _p(ids), n_ids, _p(slot_ids), _p(miss),
+                                                     _p(n_miss), _p(host_miss), _p(n_host), _p(stats),
+                                                     _stream(stream)))
+
+
+def cache_gather(miss, n_miss, max_miss, host_store, slot_store, slab_bytes, stream=None):
+    return _check("cache_gather", lib().cache_gather(_p(miss), _p(n_miss), max_miss, _p(host_store), _p(slot_store),
+                                                     slab_bytes, _stream(stream)))
+
+
+def moe_ffn_workspace_bytes(T, k, S, w_type, H, I) -> int:
+    return int(lib().moe_ffn_workspace_bytes(T, k, S, w_type, H, I))
+
+
+def moe_ffn_slots(x, x_dtype, slot_ids, w, T, k, slot_store, slab_bytes, S, w_type, H, I, y, ws, ws_bytes,
+                  stream=None):
+    return _check("moe_ffn_slots", lib().moe_ffn_slots(_p(x), x_dtype, _p(slot_ids), _p(w), T, k, _p(slot_store),
+                                                       slab_bytes, S, w_type, H, I, _p(y), _p(ws), ws_bytes,
+                                                       _stream(stream)))
+
+
+def moe_ffn_host_misses(x_h, x_dtype, ids_h, slot_ids_h, w_h, T, k, host_store, slab_bytes, E, w_type, H, I, y_h,
+                        n_threads):
+    return _check("moe_ffn_host_misses", lib().moe_ffn_host_misses(_p(x_h), x_dtype, _p(ids_h), _p(slot_ids_h),
+                                                                   _p(w_h), T, k, _p(host_store), slab_bytes, E,
+                                                                   w_type, H, I, _p(y_h), n_threads))
+
+
+def moe_combine(y, y_add, T, H, stream=None):
+    return _check("moe_combine", lib().moe_combine(_p(y), _p(y_add), T, H, _stream(stream)))
+
+
+def moe_host_alloc(nbytes: int) -> int:
+    p = lib().moe_host_alloc(nbytes)
+    if not p:
+        raise MoeError("moe_host_alloc", MOE_E_NOMEM, moe_last_error())
+    return p
+
+
+def moe_host_free(p: int):
+    return _check("moe_host_free", lib().moe_host_free(p))

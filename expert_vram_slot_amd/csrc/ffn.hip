@@ -1,0 +1,647 @@
+// Grouped SwiGLU expert FFN over resident slots (decode-sized token groups),
+// with zero-return for picks whose expert is not resident.
+//
+// sozai.app transcript "rtx-3060-run-35b-llamacpp", "What the video covers" /
+// "Full Transcript": the GPU expert step returns zeros for an expert that is
+// not on the GPU, so a separate pass over the remaining experts can be added
+// in.  Here a pick with slot -1 is simply never scheduled; the output row of a
+// token with no resident pick is written as +0.0.
+//
+// Pipeline (all on the caller's stream, deterministic):
+//   k_group      stable counting sort of the T*k picks by slot (one workgroup,
+//                ballot-matched ranks, no atomics) -> per-slot pick lists and
+//                the list of slots with work
+//   k_quant_rows (W8A8) int8 codes + scale per token
+//   k_gu         gate and up rows of a slot against the slot's tokens, SwiGLU
+//                epilogue -> h[pick][I]
+//   k_quant_rows (W8A8) int8 codes + scale per pick of h
+//   k_down       down rows against h -> part[pick][H] = w * o
+//   k_reduce     y[t] = sum over resident picks in top-k order
+//
+// Weight streaming: each workgroup owns a tile of rows of one slot; the four
+// waves split the rows, the 64 lanes of a wave read consecutive 16-byte
+// granules of a row (coalesced 1 KiB per wave load), the slot's tokens sit in
+// LDS, and the per-lane partial sums of all rows and tokens are reduced across
+// the wave in one multi-value butterfly.
+#include <math.h>
+
+#include "common.hpp"
+
+namespace {
+
+using v4u = uint32_t __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int FFN_THREADS = 256;
+constexpr int NTMAX = 8;       // tokens of one slot handled per pass
+constexpr int RPW_GU = 4;      // gate rows (and as many up rows) per wave
+constexpr int RPW_DN = 8;      // down rows per wave
+constexpr int GROUP_THREADS = 1024;
+
+// ------------------------------------------------------------ formats
+
+template <int F>
+struct Fmt;
+template <>
+struct Fmt<MOE_W_F32> {
+    static constexpr int EPG = 4;       // weights per 16-byte granule
+    static constexpr int ABYTES = 4;    // bytes per activation element in LDS
+    using Acc = float;
+};
+template <>
+struct Fmt<MOE_W_BF16> {
+    static constexpr int EPG = 8;
+    static constexpr int ABYTES = 2;
+    using Acc = float;
+};
+template <>
+struct Fmt<MOE_W_W8A8> {
+    static constexpr int EPG = 16;
+    static constexpr int ABYTES = 1;
+    using Acc = int;
+};
+template <>
+struct Fmt<MOE_W_Q4B32> {
+    static constexpr int EPG = 32;
+    static constexpr int ABYTES = 2;
+    using Acc = float;
+};
+
+__device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
+}
+
+// Accumulate one 16-byte weight granule against the matching activation
+// granule `xa` (16 bytes for fp32/bf16/int8; 64 bytes of bf16 for 4-bit).
+template <int F>
+__device__ __forceinline__ void granule_dot(const v4u& w, const unsigned char* xa, float qscale, float qxsum,
+                                            typename Fmt<F>::Acc& acc) {
+    if constexpr (F == MOE_W_F32) {
+        const float4 xv = *reinterpret_cast<const float4*>(xa);
+        acc = fmaf(__uint_as_float(w.x), xv.x, acc);
+        acc = fmaf(__uint_as_float(w.y), xv.y, acc);
+        acc = fmaf(__uint_as_float(w.z), xv.z, acc);
+        acc = fmaf(__uint_as_float(w.w), xv.w, acc);
+    } else if constexpr (F == MOE_W_BF16) {
+        const v4u xv = *reinterpret_cast<const v4u*>(xa);
+        acc = dot2bf(w.x, xv.x, acc);
+        acc = dot2bf(w.y, xv.y, acc);
+        acc = dot2bf(w.z, xv.z, acc);
+        acc = dot2bf(w.w, xv.w, acc);
+    } else if constexpr (F == MOE_W_W8A8) {
+        const v4u xv = *reinterpret_cast<const v4u*>(xa);
+        acc = __builtin_amdgcn_sdot4((int)w.x, (int)xv.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.y, (int)xv.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.z, (int)xv.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.w, (int)xv.w, acc, false);
+    } else {
+        // 32 nibbles of one block.  Each code q becomes the bf16 value 128 + q
+        // (bits 0x4300 | q, exact), so a bf16 dot gives sum (q + 128) x; the
+        // block's sum of x (qxsum) removes the offset: sum (q - 8) x =
+        // sum (q + 128) x - 136 sum x.  Input j of the block is the low nibble
+        // of byte j (j < 16) or the high nibble of byte j - 16.
+        const v4u x0 = *reinterpret_cast<const v4u*>(xa);        // inputs 0..7
+        const v4u x1 = *reinterpret_cast<const v4u*>(xa + 16);   // inputs 8..15
+        const v4u x2 = *reinterpret_cast<const v4u*>(xa + 32);   // inputs 16..23
+        const v4u x3 = *reinterpret_cast<const v4u*>(xa + 48);   // inputs 24..31
+        const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+        const uint32_t xl[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+        const uint32_t xh[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+        float d = 0.0f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t lo = wv[i] & 0x0F0F0F0Fu;          // inputs 4i .. 4i+3
+            const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;   // inputs 16+4i .. 16+4i+3
+            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u), xl[2 * i], d);
+            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u), xl[2 * i + 1], d);
+            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u), xh[2 * i], d);
+            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u), xh[2 * i + 1], d);
+        }
+        acc = fmaf(qscale, fmaf(-136.0f, qxsum, d), acc);
+    }
+}
+
+__device__ __forceinline__ float half_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
+
+__device__ __forceinline__ int pow2_ceil_small(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
+
+// ---------------------------------------------------------- workspace
+
+struct WsLayout {
+    size_t slot_off, pair_list, active, n_active, h, hq, hs, xq, xs, part, total;
+};
+
+WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
+    WsLayout L{};
+    const size_t P = (size_t)T * k;
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        size_t r = o;
+        o = (o + bytes + 255) & ~(size_t)255;
+        return r;
+    };
+    L.slot_off = take(4 * ((size_t)S + 1));
+    L.pair_list = take(4 * (P ? P : 1));
+    L.active = take(4 * (size_t)S);
+    L.n_active = take(16);
+    const size_t hb = (w_type == MOE_W_BF16 || w_type == MOE_W_Q4B32) ? 2 : 4;
+    L.h = take(hb * P * I);
+    if (w_type == MOE_W_W8A8) {
+        L.hq = take(P * I);
+        L.hs = take(4 * P);
+        L.xq = take((size_t)T * H);
+        L.xs = take(4 * (size_t)T);
+    }
+    L.part = take(4 * P * H);
+    L.total = o;
+    return L;
+}
+
+// ---------------------------------------------------------- grouping
+
+// Stable counting sort of the P picks by slot.  Picks are taken 1024 at a
+// time; inside a wave the picks with the same slot are found with one ballot
+// per slot-id bit, their order is the lane order; per-wave counts are
+// prefix-summed per slot across the 16 waves.  Pass 0 counts, pass 1 places.
+__global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restrict__ slot_ids, int P, int S,
+                                                         int32_t* __restrict__ slot_off, int32_t* __restrict__ pair_list,
+                                                         int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+    __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
+    __shared__ int base[MOE_MAX_S];
+    __shared__ int ctot[MOE_MAX_S];
+    __shared__ int scratch[GROUP_THREADS / 64 + 1];
+    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int nbits = 0;
+    while ((1 << nbits) < S) ++nbits;
+
+    for (int s = tid; s < S; s += GROUP_THREADS) base[s] = 0;
+    __syncthreads();
+    for (int pass = 0; pass < 2; ++pass) {
+        for (int c0 = 0; c0 < P; c0 += GROUP_THREADS) {
+            for (int i = tid; i < (GROUP_THREADS / 64) * S; i += GROUP_THREADS) wtab[i / S][i % S] = 0;
+            __syncthreads();
+            const int p = c0 + tid;
+            int s = p < P ? slot_ids[p] : -1;
+            if (s >= S) s = -1;
+            const bool valid = s >= 0;
+            uint64_t mask = __ballot(valid);
+            for (int b = 0; b < nbits; ++b) {
+                const bool bit = valid && ((s >> b) & 1);
+                const uint64_t bm = __ballot(bit);
+                mask &= bit ? bm : ~bm;
+            }
+            const int rank = __popcll(mask & lt);
+            if (valid && rank == 0) wtab[wid][s] = (uint16_t)__popcll(mask);
+            __syncthreads();
+            for (int s2 = tid; s2 < S; s2 += GROUP_THREADS) {
+                int acc = 0;
+                for (int w = 0; w < GROUP_THREADS / 64; ++w) {
+                    const int c = wtab[w][s2];
+                    wtab[w][s2] = (uint16_t)acc;
+                    acc += c;
+                }
+                ctot[s2] = acc;
+            }
+            __syncthreads();
+            if (pass == 1 && valid) pair_list[base[s] + wtab[wid][s] + rank] = p;
+            __syncthreads();
+            for (int s2 = tid; s2 < S; s2 += GROUP_THREADS) base[s2] += ctot[s2];
+            __syncthreads();
+        }
+        if (pass == 0) {
+            // counts -> offsets; slots with work, ascending
+            const int cnt = tid < S ? base[tid] : 0;
+            int tot;
+            const int off = moe::block_exclusive_scan(cnt, scratch, &tot);
+            if (tid < S) {
+                slot_off[tid] = off;
+                base[tid] = off;
+            }
+            if (tid == 0) slot_off[S] = tot;
+            const int flag = (tid < S && cnt > 0) ? 1 : 0;
+            int na;
+            const int apos = moe::block_exclusive_scan(flag, scratch, &na);
+            if (flag) active[apos] = tid;
+            if (tid == 0) *n_active = na;
+            __syncthreads();
+        }
+    }
+}
+
+// ------------------------------------------------------- W8A8 quantiser
+
+// Per row: scale = absmax / 127 (1 if the row is all zero), code =
+// clamp(rint(v / scale), -127, 127), in fp32.  Rows whose `valid` entry is
+// negative (picks not resident) are skipped.
+template <bool SRC_BF16>
+__global__ void __launch_bounds__(256) k_quant_rows(const void* __restrict__ src, int len,
+                                                    const int32_t* __restrict__ valid, int8_t* __restrict__ q,
+                                                    float* __restrict__ scale) {
+    __shared__ float red[4];
+    const int row = blockIdx.x;
+    if (valid && valid[row] < 0) return;
+    auto val = [&](int i) -> float {
+        if constexpr (SRC_BF16) return moe::bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[(int64_t)row * len + i]);
+        else return reinterpret_cast<const float*>(src)[(int64_t)row * len + i];
+    };
+    float m = 0.0f;
+    for (int i = threadIdx.x; i < len; i += 256) m = fmaxf(m, fabsf(val(i)));
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+    __syncthreads();
+    const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float sc = amax > 0.0f ? amax / 127.0f : 1.0f;
+    for (int i = threadIdx.x; i < len; i += 256) {
+        float c = rintf(val(i) / sc);
+        c = fminf(fmaxf(c, -127.0f), 127.0f);
+        q[(int64_t)row * len + i] = (int8_t)c;
+    }
+    if (threadIdx.x == 0) scale[row] = sc;
+}
+
+// ------------------------------------------------------ GEMV kernels
+
+struct SlabView {
+    const unsigned char* slots;
+    size_t slab_bytes;
+    int64_t w0, w1, s0, s1;  // weight and scale plane offsets used by the kernel
+};
+
+// Stage the activations of up to NTMAX tokens of this slot into LDS, rows of
+// `len` elements.  For 4-bit weights also the per-block sums of x.
+template <int F>
+__device__ __forceinline__ void stage_rows(unsigned char* xs, float* bsum, int32_t* pick_ids, const void* src,
+                                           const int32_t* __restrict__ pair_list, int p0, int c0, int nt, int k,
+                                           int len, bool by_token) {
+    constexpr int AB = Fmt<F>::ABYTES;
+    const int row_bytes = len * AB;
+    const int g16 = row_bytes / 16;
+    if (threadIdx.x < NTMAX) pick_ids[threadIdx.x] = threadIdx.x < nt ? pair_list[p0 + c0 + threadIdx.x] : -1;
+    __syncthreads();
+    for (int i = threadIdx.x; i < NTMAX * g16; i += FFN_THREADS) {
+        const int j = i / g16, g = i % g16;
+        v4u v = {0u, 0u, 0u, 0u};
+        const int pick = pick_ids[j];
+        if (pick >= 0) {
+            const int64_t r = by_token ? pick / k : pick;
+            v = *reinterpret_cast<const v4u*>(reinterpret_cast<const unsigned char*>(src) + r * row_bytes + (int64_t)g * 16);
+        }
+        *reinterpret_cast<v4u*>(xs + (size_t)j * row_bytes + (size_t)g * 16) = v;
+    }
+    if constexpr (F == MOE_W_Q4B32) {
+        __syncthreads();
+        const int nb = len / 32;
+        for (int i = threadIdx.x; i < NTMAX * nb; i += FFN_THREADS) {
+            const int j = i / nb, b = i % nb;
+            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs + (size_t)j * row_bytes) + 32 * b;
+            float s = 0.0f;
+            for (int e = 0; e < 32; ++e) s += moe::bf16_to_f32(xr[e]);
+            bsum[j * nb + b] = s;
+        }
+    }
+}
+
+template <int F, int NT>
+__device__ __forceinline__ void gu_body(const SlabView& sv, const unsigned char* slab, const unsigned char* xs,
+                                        const float* bsum, const int32_t* pick_ids, int nt, int H, int I, int k,
+                                        int r_base, const float* __restrict__ xscale, void* __restrict__ hbuf) {
+    using Acc = typename Fmt<F>::Acc;
+    constexpr int AB = Fmt<F>::ABYTES;
+    constexpr int EPG = Fmt<F>::EPG;
+    constexpr int V = 2 * RPW_GU * NT;
+    const int lane = threadIdx.x & 63;
+    const int KG = H / EPG;  // 16-byte granules per weight row
+    const int64_t row_bytes = (int64_t)KG * 16;
+    Acc acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0;
+    for (int c = 0; c < KG; c += 64) {
+        const int g = c + lane;
+        if (g < KG) {
+#pragma unroll
+            for (int pj = 0; pj < 2; ++pj) {
+                const int64_t woff = pj == 0 ? sv.w0 : sv.w1;
+#pragma unroll
+                for (int r = 0; r < RPW_GU; ++r) {
+                    const int row = r_base + r;
+                    if (row < I) {
+                        const v4u w = *reinterpret_cast<const v4u*>(slab + woff + row * row_bytes + (int64_t)g * 16);
+                        float qs = 0.0f;
+                        if constexpr (F == MOE_W_Q4B32) {
+                            const int64_t soff = pj == 0 ? sv.s0 : sv.s1;
+                            qs = half_bits_to_f32(
+                                *reinterpret_cast<const uint16_t*>(slab + soff + ((int64_t)row * KG + g) * 2));
+                        }
+#pragma unroll
+                        for (int t = 0; t < NT; ++t) {
+                            const unsigned char* xa = xs + (size_t)t * H * AB + (size_t)g * EPG * AB;
+                            const float xsum = F == MOE_W_Q4B32 ? bsum[t * KG + g] : 0.0f;
+                            granule_dot<F>(w, xa, qs, xsum, acc[(pj * RPW_GU + r) * NT + t]);
+                        }
+                    }
+                }
+            }
+        }
+    }
+    int idx;
+    Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
+    const Acc up = __shfl_xor(v, 32, 64);
+    if (moe::multi_sum_holder<V>(lane) && !(lane & 32)) {
+        const int r = (idx / NT) % RPW_GU, t = idx % NT;
+        const int row = r_base + r;
+        if (row < I && t < nt) {
+            const int pick = pick_ids[t];
+            if constexpr (F == MOE_W_W8A8) {
+                const float sx = xscale[pick / k];
+                const float sg = reinterpret_cast<const float*>(slab + sv.s0)[row];
+                const float su = reinterpret_cast<const float*>(slab + sv.s1)[row];
+                const float g = ((float)v * sx) * sg;
+                const float u = ((float)up * sx) * su;
+                const double hd = ((double)g / (1.0 + exp(-(double)g))) * (double)u;
+                reinterpret_cast<float*>(hbuf)[(int64_t)pick * I + row] = (float)hd;
+            } else {
+                const float g = (float)v, u = (float)up;
+                const float h = g / (1.0f + expf(-g)) * u;
+                if constexpr (F == MOE_W_F32) reinterpret_cast<float*>(hbuf)[(int64_t)pick * I + row] = h;
+                else reinterpret_cast<uint16_t*>(hbuf)[(int64_t)pick * I + row] = moe::f32_to_bf16(h);
+            }
+        }
+    }
+}
+
+template <int F>
+__global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __restrict__ act,
+                                                    const float* __restrict__ xscale, int H, int I, int k,
+                                                    const int32_t* __restrict__ slot_off,
+                                                    const int32_t* __restrict__ pair_list,
+                                                    const int32_t* __restrict__ active,
+                                                    const int32_t* __restrict__ n_active, void* __restrict__ hbuf,
+                                                    int tiles) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int AB = Fmt<F>::ABYTES;
+    unsigned char* xs = smem;
+    float* bsum = reinterpret_cast<float*>(smem + (size_t)NTMAX * H * AB);
+    __shared__ int32_t pick_ids[NTMAX];
+
+    const int a = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    if (a >= *n_active) return;
+    const int s = active[a];
+    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
+    const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
+    const int r_base = tile * (4 * RPW_GU) + (threadIdx.x >> 6) * RPW_GU;
+    for (int c0 = 0; c0 < ns; c0 += NTMAX) {
+        const int nt = min(NTMAX, ns - c0);
+        __syncthreads();
+        stage_rows<F>(xs, bsum, pick_ids, act, pair_list, p0, c0, nt, k, H, true);
+        __syncthreads();
+        switch (pow2_ceil_small(nt)) {
+            case 1: gu_body<F, 1>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
+            case 2: gu_body<F, 2>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
+            case 4: gu_body<F, 4>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
+            default: gu_body<F, 8>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
+        }
+    }
+}
+
+template <int F, int NT>
+__device__ __forceinline__ void down_body(const SlabView& sv, const unsigned char* slab, const unsigned char* hs,
+                                          const float* bsum, const int32_t* pick_ids, int nt, int H, int I,
+                                          int r_base, const float* __restrict__ hscale, const float* __restrict__ wts,
+                                          float* __restrict__ part) {
+    using Acc = typename Fmt<F>::Acc;
+    constexpr int AB = Fmt<F>::ABYTES;
+    constexpr int EPG = Fmt<F>::EPG;
+    constexpr int V = RPW_DN * NT;
+    const int lane = threadIdx.x & 63;
+    const int KG = I / EPG;
+    const int64_t row_bytes = (int64_t)KG * 16;
+    Acc acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0;
+    for (int c = 0; c < KG; c += 64) {
+        const int g = c + lane;
+        if (g < KG) {
+#pragma unroll
+            for (int r = 0; r < RPW_DN; ++r) {
+                const int row = r_base + r;
+                if (row < H) {
+                    const v4u w = *reinterpret_cast<const v4u*>(slab + sv.w0 + row * row_bytes + (int64_t)g * 16);
+                    float qs = 0.0f;
+                    if constexpr (F == MOE_W_Q4B32)
+                        qs = half_bits_to_f32(
+                            *reinterpret_cast<const uint16_t*>(slab + sv.s0 + ((int64_t)row * KG + g) * 2));
+#pragma unroll
+                    for (int t = 0; t < NT; ++t) {
+                        const unsigned char* xa = hs + (size_t)t * I * AB + (size_t)g * EPG * AB;
+                        const float xsum = F == MOE_W_Q4B32 ? bsum[t * KG + g] : 0.0f;
+                        granule_dot<F>(w, xa, qs, xsum, acc[r * NT + t]);
+                    }
+                }
+            }
+        }
+    }
+    int idx;
+    Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
+    if (moe::multi_sum_holder<V>(lane)) {
+        const int r = idx / NT, t = idx % NT;
+        const int row = r_base + r;
+        if (row < H && t < nt) {
+            const int pick = pick_ids[t];
+            float o;
+            if constexpr (F == MOE_W_W8A8)
+                o = ((float)v * hscale[pick]) * reinterpret_cast<const float*>(slab + sv.s0)[row];
+            else
+                o = (float)v;
+            part[(int64_t)pick * H + row] = wts[pick] * o;
+        }
+    }
+}
+
+template <int F>
+__global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* __restrict__ hact,
+                                                      const float* __restrict__ hscale, const float* __restrict__ wts,
+                                                      int H, int I, const int32_t* __restrict__ slot_off,
+                                                      const int32_t* __restrict__ pair_list,
+                                                      const int32_t* __restrict__ active,
+                                                      const int32_t* __restrict__ n_active, float* __restrict__ part,
+                                                      int tiles) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int AB = Fmt<F>::ABYTES;
+    unsigned char* hs = smem;
+    float* bsum = reinterpret_cast<float*>(smem + (size_t)NTMAX * I * AB);
+    __shared__ int32_t pick_ids[NTMAX];
+
+    const int a = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    if (a >= *n_active) return;
+    const int s = active[a];
+    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
+    const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
+    const int r_base = tile * (4 * RPW_DN) + (threadIdx.x >> 6) * RPW_DN;
+    for (int c0 = 0; c0 < ns; c0 += NTMAX) {
+        const int nt = min(NTMAX, ns - c0);
+        __syncthreads();
+        stage_rows<F>(hs, bsum, pick_ids, hact, pair_list, p0, c0, nt, 1, I, false);
+        __syncthreads();
+        switch (pow2_ceil_small(nt)) {
+            case 1: down_body<F, 1>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
+            case 2: down_body<F, 2>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
+            case 4: down_body<F, 4>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
+            default: down_body<F, 8>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
+        }
+    }
+}
+
+// y[t][m] = sum_j part[t*k+j][m] over resident picks, j ascending; +0.0 if none.
+__global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ part, const int32_t* __restrict__ slot_ids,
+                                                int T, int k, int S, int H, float* __restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
+    const int h4 = H / 4;
+    if (i >= (int64_t)T * h4) return;
+    const int t = (int)(i / h4), m4 = (int)(i % h4);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+        const int sl = slot_ids[t * k + j];
+        if (sl < 0 || sl >= S) continue;
+        const float4 v = reinterpret_cast<const float4*>(part + (int64_t)(t * k + j) * H)[m4];
+        acc.x += v.x;
+        acc.y += v.y;
+        acc.z += v.z;
+        acc.w += v.w;
+    }
+    reinterpret_cast<float4*>(y + (int64_t)t * H)[m4] = acc;
+}
+
+__global__ void __launch_bounds__(256) k_combine(float* __restrict__ y, const float* __restrict__ y_add, int64_t n) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i < n) y[i] = y[i] + y_add[i];
+}
+
+// Kernels whose dynamic LDS exceeds 64 KiB must say so before the launch.
+int allow_lds(const void* fn, size_t lds) {
+    if (lds <= 64 * 1024) return MOE_OK;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) {
+            (void)hipGetLastError();
+            return moe_fail(MOE_E_HIP, "moe_ffn_slots: LDS attribute: %s", hipGetErrorString(e));
+        }
+    return MOE_OK;
+}
+
+template <int F>
+int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k, const void* slot_store,
+            size_t slab_bytes, int S, int H, int I, float* y, unsigned char* ws, const WsLayout& L,
+            const moe_slab_layout_t& lay, hipStream_t st) {
+    constexpr int AB = Fmt<F>::ABYTES;
+    const int P = T * k;
+    int32_t* slot_off = reinterpret_cast<int32_t*>(ws + L.slot_off);
+    int32_t* pair_list = reinterpret_cast<int32_t*>(ws + L.pair_list);
+    int32_t* active = reinterpret_cast<int32_t*>(ws + L.active);
+    int32_t* n_active = reinterpret_cast<int32_t*>(ws + L.n_active);
+    void* hbuf = ws + L.h;
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    int rc;
+
+    hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
+                       n_active);
+    if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
+
+    const void* gu_act = x;
+    const float* xscale = nullptr;
+    if constexpr (F == MOE_W_W8A8) {
+        int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
+        float* xs = reinterpret_cast<float*>(ws + L.xs);
+        hipLaunchKernelGGL((k_quant_rows<true>), dim3(T), dim3(256), 0, st, x, H, (const int32_t*)nullptr, xq, xs);
+        if ((rc = moe_check_launch("moe_ffn_slots/quant_x"))) return rc;
+        gu_act = xq;
+        xscale = xs;
+    }
+
+    SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
+    const int tiles_gu = (I + 4 * RPW_GU - 1) / (4 * RPW_GU);
+    size_t lds = (size_t)NTMAX * H * AB + (F == MOE_W_Q4B32 ? (size_t)NTMAX * (H / 32) * 4 : 0);
+    if (lds > 150 * 1024) return moe_fail(MOE_E_SHAPE, "moe_ffn_slots: H=%d too large for the LDS token tile", H);
+    if ((rc = allow_lds(reinterpret_cast<const void*>(&k_gu<F>), lds))) return rc;
+    hipLaunchKernelGGL((k_gu<F>), dim3(S * tiles_gu), dim3(FFN_THREADS), lds, st, gv, gu_act, xscale, H, I, k,
+                       slot_off, pair_list, active, n_active, hbuf, tiles_gu);
+    if ((rc = moe_check_launch("moe_ffn_slots/gate_up"))) return rc;
+
+    const void* dn_act = hbuf;
+    const float* hscale = nullptr;
+    if constexpr (F == MOE_W_W8A8) {
+        int8_t* hq = reinterpret_cast<int8_t*>(ws + L.hq);
+        float* hsc = reinterpret_cast<float*>(ws + L.hs);
+        hipLaunchKernelGGL((k_quant_rows<false>), dim3(P), dim3(256), 0, st, hbuf, I, slot_ids, hq, hsc);
+        if ((rc = moe_check_launch("moe_ffn_slots/quant_h"))) return rc;
+        dn_act = hq;
+        hscale = hsc;
+    }
+    SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
+    const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
+    lds = (size_t)NTMAX * I * AB + (F == MOE_W_Q4B32 ? (size_t)NTMAX * (I / 32) * 4 : 0);
+    if (lds > 150 * 1024) return moe_fail(MOE_E_SHAPE, "moe_ffn_slots: I=%d too large for the LDS tile", I);
+    if ((rc = allow_lds(reinterpret_cast<const void*>(&k_down<F>), lds))) return rc;
+    hipLaunchKernelGGL((k_down<F>), dim3(S * tiles_dn), dim3(FFN_THREADS), lds, st, dv, dn_act, hscale, w, H, I,
+                       slot_off, pair_list, active, n_active, part, tiles_dn);
+    if ((rc = moe_check_launch("moe_ffn_slots/down"))) return rc;
+
+    const int64_t n4 = (int64_t)T * (H / 4);
+    hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, slot_ids, T, k, S, H, y);
+    return moe_check_launch("moe_ffn_slots/reduce");
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_ffn_workspace_bytes(int T, int k, int S, int w_type, int H, int I) {
+    if (T < 0 || k < 1 || S < 1 || H < 1 || I < 1) return 0;
+    return ws_layout(T, k, S, w_type, H, I).total;
+}
+
+int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
+                  const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    MOE_REQUIRE(T >= 0 && k >= 1 && k <= MOE_MAX_K && S >= 1 && H >= 1 && I >= 1, MOE_E_ARG,
+                "moe_ffn_slots: T=%d k=%d S=%d H=%d I=%d out of range", T, k, S, H, I);
+    MOE_REQUIRE(S <= MOE_MAX_S, MOE_E_SHAPE, "moe_ffn_slots: S=%d exceeds %d", S, MOE_MAX_S);
+    if (T == 0) return moe_ok();
+    MOE_REQUIRE(x && slot_ids && w && slot_store && y && ws, MOE_E_ARG,
+                "moe_ffn_slots: x, slot_ids, w, slot_store, y and ws must be non-NULL");
+    moe_slab_layout_t lay;
+    int rc = moe_layout(w_type, H, I, &lay);
+    if (rc) return rc;
+    MOE_REQUIRE(slab_bytes >= (size_t)lay.total && slab_bytes % 16 == 0, MOE_E_ALIGN,
+                "moe_ffn_slots: slab_bytes=%zu must be a 16-byte multiple >= %lld", slab_bytes, (long long)lay.total);
+    MOE_REQUIRE(moe_aligned16(slot_store) && moe_aligned16(x) && moe_aligned16(ws) && moe_aligned16(y), MOE_E_ALIGN,
+                "moe_ffn_slots: x, slot_store, y and ws must be 16-byte aligned");
+    const int want_x = w_type == MOE_W_F32 ? MOE_X_F32 : MOE_X_BF16;
+    MOE_REQUIRE(x_dtype == want_x, MOE_E_DTYPE, "moe_ffn_slots: weight format %d needs activation format %d, got %d",
+                w_type, want_x, x_dtype);
+    const WsLayout L = ws_layout(T, k, S, w_type, H, I);
+    MOE_REQUIRE(ws_bytes >= L.total, MOE_E_ARG, "moe_ffn_slots: workspace of %zu bytes, need %zu", ws_bytes, L.total);
+    unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
+    switch (w_type) {
+        case MOE_W_F32:
+            return run_ffn<MOE_W_F32>(x, slot_ids, w, T, k, slot_store, slab_bytes, S, H, I, y, wsb, L, lay, stream);
+        case MOE_W_BF16:
+            return run_ffn<MOE_W_BF16>(x, slot_ids, w, T, k, slot_store, slab_bytes, S, H, I, y, wsb, L, lay, stream);
+        case MOE_W_W8A8:
+            return run_ffn<MOE_W_W8A8>(x, slot_ids, w, T, k, slot_store, slab_bytes, S, H, I, y, wsb, L, lay, stream);
+        case MOE_W_Q4B32:
+            return run_ffn<MOE_W_Q4B32>(x, slot_ids, w, T, k, slot_store, slab_bytes, S, H, I, y, wsb, L, lay, stream);
+        default:
+            return moe_fail(MOE_E_DTYPE, "moe_ffn_slots: unknown weight format %d", w_type);
+    }
+}
+
+int moe_combine(float* y, const float* y_add, int T, int H, hipStream_t stream) {
+    MOE_REQUIRE(y && y_add && T >= 0 && H >= 1, MOE_E_ARG, "moe_combine: bad arguments");
+    const int64_t n = (int64_t)T * H;
+    if (n == 0) return moe_ok();
+    hipLaunchKernelGGL(k_combine, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, stream, y, y_add, n);
+    return moe_check_launch("moe_combine");
+}
+
+}  // extern "C"

@@ -1,0 +1,375 @@
+// Host pass of the expert-slot layer: the SwiGLU FFN of the picks whose
+// expert is not resident, on CPU threads, reading the host expert store.
+//
+// sozai.app transcript "rtx-3060-run-35b-llamacpp", "What the video covers"
+// and "Full Transcript": the experts that stay in RAM are run by the CPU in a
+// pass of their own, concurrently with the GPU pass, and one add joins the
+// two results.  The arithmetic per weight format is the GPU kernels' (see
+// moe_slot.h); every output element is produced by one work item in a fixed
+// order, so the result does not depend on the thread count.
+#include <immintrin.h>
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <atomic>
+#include <condition_variable>
+#include <functional>
+#include <mutex>
+#include <thread>
+#include <vector>
+
+#include "../../include/moe_slot.h"
+
+int moe_fail(int code, const char* fmt, ...);
+int moe_ok();
+int moe_layout(int w_type, int H, int I, moe_slab_layout_t* out);
+
+namespace {
+
+// ----------------------------------------------------------- thread pool
+
+class Pool {
+   public:
+    // Run fn(item) for item in [0, n) on `threads` threads (the caller
+    // included).  Items are handed out dynamically; each runs exactly once.
+    void run(int threads, int n, const std::function<void(int)>& fn) {
+        if (n <= 0) return;
+        threads = std::max(1, std::min({threads, n, 64}));
+        if (threads == 1) {
+            for (int i = 0; i < n; ++i) fn(i);
+            return;
+        }
+        std::lock_guard<std::mutex> serial(call_mu_);  // one call at a time
+        while ((int)workers_.size() < threads - 1) {
+            const int id = (int)workers_.size();
+            workers_.emplace_back([this, id] { loop(id); });
+        }
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            fn_ = &fn;
+            n_ = n;
+            next_.store(0);
+            enlisted_ = threads - 1;  // workers 0 .. threads-2 take part
+            pending_ = threads - 1;
+            ++gen_;
+        }
+        cv_.notify_all();
+        work();
+        std::unique_lock<std::mutex> lk(mu_);
+        done_cv_.wait(lk, [&] { return pending_ == 0; });
+        fn_ = nullptr;
+    }
+
+    ~Pool() {
+        {
+            std::lock_guard<std::mutex> lk(mu_);
+            stop_ = true;
+            ++gen_;
+        }
+        cv_.notify_all();
+        for (auto& t : workers_) t.join();
+    }
+
+   private:
+    void work() {
+        for (;;) {
+            const int i = next_.fetch_add(1);
+            if (i >= n_) break;
+            (*fn_)(i);
+        }
+    }
+    void loop(int id) {
+        uint64_t seen = 0;
+        for (;;) {
+            {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
+                if (stop_) return;
+                seen = gen_;
+                if (id >= enlisted_) continue;
+            }
+            work();
+            std::lock_guard<std::mutex> lk(mu_);
+            if (--pending_ == 0) done_cv_.notify_all();
+        }
+    }
+
+    std::mutex call_mu_, mu_;
+    std::condition_variable cv_, done_cv_;
+    std::vector<std::thread> workers_;
+    const std::function<void(int)>* fn_ = nullptr;
+    std::atomic<int> next_{0};
+    int n_ = 0, enlisted_ = 0, pending_ = 0;
+    uint64_t gen_ = 0;
+    bool stop_ = false;
+};
+
+Pool& pool() {
+    static Pool p;
+    return p;
+}
+
+void parallel(int threads, int n, const std::function<void(int)>& fn) { pool().run(threads, n, fn); }
+
+// ---------------------------------------------------------- formats
+
+inline float bf16f(uint16_t h) {
+    uint32_t b = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &b, 4);
+    return f;
+}
+
+inline uint16_t f2bf(float f) {
+    uint32_t b;
+    memcpy(&b, &f, 4);
+    b += 0x7FFFu + ((b >> 16) & 1u);
+    return (uint16_t)(b >> 16);
+}
+
+inline float half_to_float(uint16_t h) { return _cvtsh_ss(h); }
+
+// dot of a bf16 weight row with a bf16 activation row, n a multiple of 32
+__attribute__((target("avx512f,avx512bf16"))) float dot_bf16_avx512(const uint16_t* w, const uint16_t* x, int n) {
+    __m512 acc = _mm512_setzero_ps();
+    for (int i = 0; i < n; i += 32) {
+        const __m512i wv = _mm512_loadu_si512(reinterpret_cast<const void*>(w + i));
+        const __m512i xv = _mm512_loadu_si512(reinterpret_cast<const void*>(x + i));
+        acc = _mm512_dpbf16_ps(acc, (__m512bh)wv, (__m512bh)xv);
+    }
+    return _mm512_reduce_add_ps(acc);
+}
+
+float dot_bf16_plain(const uint16_t* w, const uint16_t* x, int n) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int i = 0; i < n; i += 8)
+        for (int j = 0; j < 8; ++j) acc[j] += bf16f(w[i + j]) * bf16f(x[i + j]);
+    return ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+}
+
+bool have_avx512bf16() {
+    static const bool v = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bf16");
+    return v;
+}
+
+float dot_f32(const float* w, const float* x, int n) {
+    float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+    int i = 0;
+    for (; i + 8 <= n; i += 8)
+        for (int j = 0; j < 8; ++j) acc[j] += w[i + j] * x[i + j];
+    float s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
+    for (; i < n; ++i) s += w[i] * x[i];
+    return s;
+}
+
+int32_t dot_i8(const int8_t* w, const int8_t* x, int n) {
+    int32_t acc = 0;
+    for (int i = 0; i < n; ++i) acc += (int32_t)w[i] * (int32_t)x[i];
+    return acc;
+}
+
+// 4-bit row (nibble plane row + fp16 scales) against fp32 activations
+float dot_q4(const uint8_t* q, const uint16_t* sc, const float* x, int n) {
+    float acc = 0.0f;
+    for (int b = 0; b < n / 32; ++b) {
+        const uint8_t* blk = q + 16 * b;
+        const float* xb = x + 32 * b;
+        float d = 0.0f;
+        for (int j = 0; j < 16; ++j) {
+            d += (float)((int)(blk[j] & 0xF) - 8) * xb[j];
+            d += (float)((int)(blk[j] >> 4) - 8) * xb[j + 16];
+        }
+        acc += half_to_float(sc[b]) * d;
+    }
+    return acc;
+}
+
+// symmetric int8 quantisation, fp32 decisions (as on the GPU)
+float quant_row(const float* v, int n, int8_t* q) {
+    float amax = 0.0f;
+    for (int i = 0; i < n; ++i) amax = std::max(amax, fabsf(v[i]));
+    const float s = amax > 0.0f ? amax / 127.0f : 1.0f;
+    for (int i = 0; i < n; ++i) {
+        float c = rintf(v[i] / s);
+        c = std::min(std::max(c, -127.0f), 127.0f);
+        q[i] = (int8_t)c;
+    }
+    return s;
+}
+
+}  // namespace
+
+extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* ids_h, const int32_t* slot_ids_h,
+                                   const float* w_h, int T, int k, const void* host_store, size_t slab_bytes, int E,
+                                   int w_type, int H, int I, float* y_h, int n_threads) {
+    if (T < 0 || k < 1 || E < 1 || H < 1 || I < 1) return moe_fail(MOE_E_ARG, "moe_ffn_host_misses: bad sizes");
+    if (T == 0) return moe_ok();
+    if (!x_h || !ids_h || !slot_ids_h || !w_h || !host_store || !y_h)
+        return moe_fail(MOE_E_ARG, "moe_ffn_host_misses: NULL argument");
+    moe_slab_layout_t lay;
+    int rc = moe_layout(w_type, H, I, &lay);
+    if (rc) return rc;
+    if (slab_bytes < (size_t)lay.total)
+        return moe_fail(MOE_E_ALIGN, "moe_ffn_host_misses: slab_bytes=%zu < %lld", slab_bytes, (long long)lay.total);
+    const int want_x = w_type == MOE_W_F32 ? MOE_X_F32 : MOE_X_BF16;
+    if (x_dtype != want_x)
+        return moe_fail(MOE_E_DTYPE, "moe_ffn_host_misses: weight format %d needs activation format %d", w_type, want_x);
+    if (n_threads < 1) n_threads = 1;
+
+    const int P = T * k;
+    // picks served here: slot < 0 with a valid expert, grouped by expert (pick order kept)
+    std::vector<int> cnt(E + 1, 0);
+    for (int p = 0; p < P; ++p)
+        if (slot_ids_h[p] < 0 && ids_h[p] >= 0 && ids_h[p] < E) cnt[ids_h[p] + 1]++;
+    for (int e = 0; e < E; ++e) cnt[e + 1] += cnt[e];
+    std::vector<int> order(cnt[E]);
+    {
+        std::vector<int> fill(cnt.begin(), cnt.end() - 1);
+        for (int p = 0; p < P; ++p)
+            if (slot_ids_h[p] < 0 && ids_h[p] >= 0 && ids_h[p] < E) order[fill[ids_h[p]]++] = p;
+    }
+    std::vector<int> experts;
+    for (int e = 0; e < E; ++e)
+        if (cnt[e + 1] > cnt[e]) experts.push_back(e);
+    const int NE = (int)experts.size();
+    const unsigned char* store = reinterpret_cast<const unsigned char*>(host_store);
+
+    // activations as fp32 (fp32 / 4-bit), bf16 bits (bf16) or int8 (W8A8)
+    std::vector<float> xf;
+    std::vector<int8_t> xq;
+    std::vector<float> xs;
+    const uint16_t* xb = reinterpret_cast<const uint16_t*>(x_h);
+    if (w_type == MOE_W_F32) {
+        xf.assign(reinterpret_cast<const float*>(x_h), reinterpret_cast<const float*>(x_h) + (size_t)T * H);
+    } else if (w_type == MOE_W_Q4B32 || w_type == MOE_W_W8A8) {
+        xf.resize((size_t)T * H);
+        for (size_t i = 0; i < (size_t)T * H; ++i) xf[i] = bf16f(xb[i]);
+        if (w_type == MOE_W_W8A8) {
+            xq.resize((size_t)T * H);
+            xs.resize(T);
+            for (int t = 0; t < T; ++t) xs[t] = quant_row(&xf[(size_t)t * H], H, &xq[(size_t)t * H]);
+        }
+    }
+
+    // phase 1: gate/up rows, blocks of RB rows per work item
+    const int RB = 32;
+    const int nrb = (I + RB - 1) / RB;
+    std::vector<float> hf((size_t)P * I);  // h per pick (fp32; bf16-rounded where the format says so)
+    const bool bf16_fast = w_type == MOE_W_BF16 && have_avx512bf16() && H % 32 == 0 && I % 32 == 0;
+    parallel(n_threads, NE * nrb, [&](int item) {
+        const int e = experts[item / nrb], r0 = (item % nrb) * RB, r1 = std::min(I, r0 + RB);
+        const unsigned char* slab = store + (size_t)e * slab_bytes;
+        for (int r = r0; r < r1; ++r) {
+            for (int q = cnt[e]; q < cnt[e + 1]; ++q) {
+                const int p = order[q], t = p / k;
+                float g, u;
+                switch (w_type) {
+                    case MOE_W_F32: {
+                        const float* wg = reinterpret_cast<const float*>(slab + lay.w[0]) + (size_t)r * H;
+                        const float* wu = reinterpret_cast<const float*>(slab + lay.w[1]) + (size_t)r * H;
+                        g = dot_f32(wg, &xf[(size_t)t * H], H);
+                        u = dot_f32(wu, &xf[(size_t)t * H], H);
+                    } break;
+                    case MOE_W_BF16: {
+                        const uint16_t* wg = reinterpret_cast<const uint16_t*>(slab + lay.w[0]) + (size_t)r * H;
+                        const uint16_t* wu = reinterpret_cast<const uint16_t*>(slab + lay.w[1]) + (size_t)r * H;
+                        const uint16_t* xr = xb + (size_t)t * H;
+                        g = bf16_fast ? dot_bf16_avx512(wg, xr, H) : dot_bf16_plain(wg, xr, H);
+                        u = bf16_fast ? dot_bf16_avx512(wu, xr, H) : dot_bf16_plain(wu, xr, H);
+                    } break;
+                    case MOE_W_W8A8: {
+                        const int8_t* wg = reinterpret_cast<const int8_t*>(slab + lay.w[0]) + (size_t)r * H;
+                        const int8_t* wu = reinterpret_cast<const int8_t*>(slab + lay.w[1]) + (size_t)r * H;
+                        const float sg = reinterpret_cast<const float*>(slab + lay.s[0])[r];
+                        const float su = reinterpret_cast<const float*>(slab + lay.s[1])[r];
+                        g = ((float)dot_i8(wg, &xq[(size_t)t * H], H) * xs[t]) * sg;
+                        u = ((float)dot_i8(wu, &xq[(size_t)t * H], H) * xs[t]) * su;
+                    } break;
+                    default: {
+                        const uint8_t* qg = slab + lay.w[0] + (size_t)r * (H / 2);
+                        const uint8_t* qu = slab + lay.w[1] + (size_t)r * (H / 2);
+                        const uint16_t* sg = reinterpret_cast<const uint16_t*>(slab + lay.s[0]) + (size_t)r * (H / 32);
+                        const uint16_t* su = reinterpret_cast<const uint16_t*>(slab + lay.s[1]) + (size_t)r * (H / 32);
+                        g = dot_q4(qg, sg, &xf[(size_t)t * H], H);
+                        u = dot_q4(qu, su, &xf[(size_t)t * H], H);
+                    } break;
+                }
+                float h;
+                if (w_type == MOE_W_W8A8) h = (float)(((double)g / (1.0 + exp(-(double)g))) * (double)u);
+                else h = g / (1.0f + expf(-g)) * u;
+                if (w_type == MOE_W_BF16 || w_type == MOE_W_Q4B32) h = bf16f(f2bf(h));
+                hf[(size_t)p * I + r] = h;
+            }
+        }
+    });
+
+    // W8A8: h quantised per pick
+    std::vector<int8_t> hq;
+    std::vector<float> hs;
+    if (w_type == MOE_W_W8A8) {
+        hq.resize((size_t)P * I);
+        hs.resize(P);
+        for (int p : order) hs[p] = quant_row(&hf[(size_t)p * I], I, &hq[(size_t)p * I]);
+    }
+    std::vector<uint16_t> hb;
+    if (w_type == MOE_W_BF16 && bf16_fast) {
+        hb.resize((size_t)P * I);
+        for (int p : order)
+            for (int i = 0; i < I; ++i) hb[(size_t)p * I + i] = f2bf(hf[(size_t)p * I + i]);
+    }
+
+    // phase 2: down rows -> part[p][m] = w * o
+    const int RD = 64;
+    const int nrd = (H + RD - 1) / RD;
+    std::vector<float> part((size_t)P * H);
+    parallel(n_threads, NE * nrd, [&](int item) {
+        const int e = experts[item / nrd], m0 = (item % nrd) * RD, m1 = std::min(H, m0 + RD);
+        const unsigned char* slab = store + (size_t)e * slab_bytes;
+        for (int m = m0; m < m1; ++m) {
+            for (int q = cnt[e]; q < cnt[e + 1]; ++q) {
+                const int p = order[q];
+                float o;
+                switch (w_type) {
+                    case MOE_W_F32:
+                        o = dot_f32(reinterpret_cast<const float*>(slab + lay.w[2]) + (size_t)m * I, &hf[(size_t)p * I], I);
+                        break;
+                    case MOE_W_BF16: {
+                        const uint16_t* wd = reinterpret_cast<const uint16_t*>(slab + lay.w[2]) + (size_t)m * I;
+                        if (bf16_fast) {
+                            o = dot_bf16_avx512(wd, &hb[(size_t)p * I], I);
+                        } else {
+                            float a = 0.0f;
+                            for (int i = 0; i < I; ++i) a += bf16f(wd[i]) * hf[(size_t)p * I + i];
+                            o = a;
+                        }
+                    } break;
+                    case MOE_W_W8A8: {
+                        const int8_t* wd = reinterpret_cast<const int8_t*>(slab + lay.w[2]) + (size_t)m * I;
+                        const float sd = reinterpret_cast<const float*>(slab + lay.s[2])[m];
+                        o = ((float)dot_i8(wd, &hq[(size_t)p * I], I) * hs[p]) * sd;
+                    } break;
+                    default: {
+                        const uint8_t* qd = slab + lay.w[2] + (size_t)m * (I / 2);
+                        const uint16_t* sd = reinterpret_cast<const uint16_t*>(slab + lay.s[2]) + (size_t)m * (I / 32);
+                        o = dot_q4(qd, sd, &hf[(size_t)p * I], I);
+                    } break;
+                }
+                part[(size_t)p * H + m] = w_h[p] * o;
+            }
+        }
+    });
+
+    // phase 3: y[t] = sum over non-resident picks, j ascending
+    parallel(n_threads, T, [&](int t) {
+        float* yr = y_h + (size_t)t * H;
+        for (int m = 0; m < H; ++m) yr[m] = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int p = t * k + j;
+            if (slot_ids_h[p] >= 0 || ids_h[p] < 0 || ids_h[p] >= E) continue;
+            const float* pr = &part[(size_t)p * H];
+            for (int m = 0; m < H; ++m) yr[m] += pr[m];
+        }
+    });
+    return moe_ok();
+}

@@ -1,0 +1,126 @@
+"""Call order of one expert-slot MoE layer step over the C ABI.
+
+Holds the device and pinned-host buffers of one layer and issues the entry
+points in the order the method needs them; it computes nothing itself.
+
+Order of a step (sozai.app transcript "rtx-3060-run-35b-llamacpp": all GPU
+work in one unbroken run, all CPU work in another, one add at the end;
+"Porting vllm-expert-cache to NVIDIA GPUs": manage, gather, remap, expert
+FFN over slot space):
+
+  compute stream  moe_route -> cache_manage -> moe_ffn_slots -> moe_combine
+  side stream                    `-> cache_gather --^ (event)
+  copy stream     x, ids, slot_ids, w -> pinned host      (event)
+  CPU thread                       `-> moe_ffn_host_misses -> y_host
+"""
+from __future__ import annotations
+
+import concurrent.futures as cf
+import os
+
+import torch
+
+from . import (MOE_W_F32, MOE_X_BF16, MOE_X_F32, POLICIES, cache_gather, cache_init, cache_manage, cache_state,
+               moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_route, moe_slab_layout)
+
+
+def host_threads() -> int:
+    return max(1, min(16, os.cpu_count() or 1))
+
+
+class SlotLayer:
+    def __init__(self, *, E, k, H, I, S, w_type, T_max, policy, host_store, slot_store, G, bias=None,
+                 n_threads=None, device="cuda"):
+        dev = torch.device(device)
+        self.E, self.k, self.H, self.I, self.S = E, k, H, I, S
+        self.w_type = w_type
+        self.x_dtype = MOE_X_F32 if w_type == MOE_W_F32 else MOE_X_BF16
+        self.policy = POLICIES.get(policy, policy)
+        self.T_max = T_max
+        self.slab = int(host_store.shape[1])
+        assert moe_slab_layout(w_type, H, I).total <= self.slab
+        self.host_store = host_store      # pinned [E][slab] uint8
+        self.slot_store = slot_store      # device [S][slab] uint8
+        self.G, self.bias = G, bias
+        self.n_threads = n_threads or host_threads()
+        P = T_max * k
+        i32 = dict(dtype=torch.int32, device=dev)
+        self.ids = torch.empty(P, **i32)
+        self.slot_ids = torch.empty(P, **i32)
+        self.w = torch.empty(P, dtype=torch.float32, device=dev)
+        self.miss = torch.empty(2 * max(S, 1), **i32)
+        self.n_miss = torch.zeros(1, **i32)
+        self.host_miss = torch.empty(E, **i32)
+        self.n_host = torch.zeros(1, **i32)
+        self.stats = torch.zeros(4, **i32)
+        self.e2s = torch.empty(E, **i32)
+        self.s2e = torch.empty(max(S, 1), **i32)
+        self.last = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+        self.freq = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+        self.step_ctr = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.st = cache_state(self.e2s, self.s2e, self.last, self.freq, self.step_ctr, E, S)
+        self.ws_bytes = moe_ffn_workspace_bytes(T_max, k, max(S, 1), w_type, H, I)
+        self.ws = torch.empty(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(T_max * H, dtype=torch.float32, device=dev)
+        self.y_host_dev = torch.empty(T_max * H, dtype=torch.float32, device=dev)
+        xb = 4 if self.x_dtype == MOE_X_F32 else 2
+        pin = dict(pin_memory=True)
+        self.h_x = torch.empty(T_max * H * xb, dtype=torch.uint8, **pin)
+        self.h_ids = torch.empty(P, dtype=torch.int32, **pin)
+        self.h_slot = torch.empty(P, dtype=torch.int32, **pin)
+        self.h_w = torch.empty(P, dtype=torch.float32, **pin)
+        self.h_y = torch.empty(T_max * H, dtype=torch.float32, **pin)
+        self.side = torch.cuda.Stream(device=dev)
+        self.copy = torch.cuda.Stream(device=dev)
+        self.pool = cf.ThreadPoolExecutor(max_workers=1)
+
+    def init_cache(self, resident=None):
+        cache_init(self.st, resident)
+
+    def _host_pass(self, ev, T):
+        ev.synchronize()
+        moe_ffn_host_misses(self.h_x, self.x_dtype, self.h_ids, self.h_slot, self.h_w, T, self.k, self.host_store,
+                            self.slab, self.E, self.w_type, self.H, self.I, self.h_y, self.n_threads)
+
+    def step(self, x, T, ids_in=None, host_pass=True):
+        """One layer step for T tokens of x (device, [T][H]); returns y [T][H] fp32 (device)."""
+        assert T <= self.T_max
+        cur = torch.cuda.current_stream()
+        P = T * self.k
+        # 1. router (picks, or weights of given picks)
+        moe_route(x, self.x_dtype, self.G, self.bias, ids_in, T, self.H, self.E, self.k, self.ids, self.w, None, cur)
+        ids = self.ids if ids_in is None else ids_in
+        # 2. cache step: victims, miss list, remap
+        cache_manage(self.st, self.policy, ids, P, self.slot_ids, self.miss, self.n_miss, self.host_miss,
+                     self.n_host, self.stats, cur)
+        ev_manage = torch.cuda.Event()
+        ev_manage.record(cur)
+        fut = None
+        if host_pass:
+            # 3a. inputs of the host pass to pinned memory on the copy stream
+            self.copy.wait_event(ev_manage)
+            with torch.cuda.stream(self.copy):
+                nx = x.numel() * x.element_size()
+                self.h_x[:nx].copy_(x.reshape(-1).view(torch.uint8), non_blocking=True)
+                self.h_ids[:P].copy_(ids.reshape(-1)[:P], non_blocking=True)
+                self.h_slot[:P].copy_(self.slot_ids[:P], non_blocking=True)
+                self.h_w[:P].copy_(self.w[:P], non_blocking=True)
+                ev_copy = torch.cuda.Event()
+                ev_copy.record(self.copy)
+            fut = self.pool.submit(self._host_pass, ev_copy, T)
+        # 3b. gather on the side stream (no-op when nothing missed)
+        if self.policy != 0 and self.S > 0:
+            self.side.wait_event(ev_manage)
+            cache_gather(self.miss, self.n_miss, self.S, self.host_store, self.slot_store, self.slab, self.side)
+            ev_g = torch.cuda.Event()
+            ev_g.record(self.side)
+            cur.wait_event(ev_g)
+        # 4. expert FFN over resident slots (zero for the rest)
+        moe_ffn_slots(x, self.x_dtype, self.slot_ids, self.w, T, self.k, self.slot_store, self.slab, max(self.S, 1),
+                      self.w_type, self.H, self.I, self.y, self.ws, self.ws_bytes, cur)
+        # 5. the single add joining the two passes
+        if fut is not None:
+            fut.result()
+            self.y_host_dev[:T * self.H].copy_(self.h_y[:T * self.H], non_blocking=True)
+            moe_combine(self.y, self.y_host_dev, T, self.H, cur)
+        return self.y[:T * self.H].view(T, self.H)

@@ -1,0 +1,261 @@
+/*
+ * moe_slot.h -- C ABI of the MI355X (gfx950) expert-slot MoE layer.
+ *
+ * One Mixture-of-Experts layer whose experts live in a fixed number of VRAM
+ * "slots" in front of a pinned host copy of every expert:
+ *
+ *   moe_route            router logits, optional graded selection bias, top-k,
+ *                        softmax of the raw logits over the picked k
+ *   cache_manage         victims among slots this step does not need + miss list,
+ *                        fused with the expert-id -> slot remap
+ *   cache_gather         missing experts copied from pinned host memory to slots
+ *   moe_ffn_slots        grouped SwiGLU FFN over resident slots; picks whose slot
+ *                        is -1 contribute exactly zero
+ *   moe_ffn_host_misses  the same FFN on CPU threads for the picks that are not
+ *                        resident; summed in with moe_combine
+ *
+ * Sources (web pages, by title and section):
+ *   [RTX] sozai.app transcript "rtx-3060-run-35b-llamacpp" -- "What the video
+ *         covers", "Full Transcript": a fixed slot set chosen at load, missing
+ *         experts return zeros on the GPU, a CPU pass over the RAM experts, one
+ *         add to join them.
+ *   [VEC] "Porting vllm-expert-cache to NVIDIA GPUs" -- "What this package does"
+ *         (expert_cache_manage, expert_cache_gather, remap to slot space),
+ *         "The port" (16-byte copy unit, build-time export check, binding by
+ *         exported name), "Prove it is correct before measuring" (determinism:
+ *         no atomics, no order-dependent reduction; the device reads pinned host
+ *         memory; per-expert slabs in 16-byte multiples), "Measuring, without
+ *         fooling yourself" (a step is served from slots alone only when it fits),
+ *         "What we know, and what we are guessing" (refuse loudly, with a reason;
+ *         read source tensors fresh on every call; weights and scales are both
+ *         slot-indexed).
+ *   [PGO] "Nudge, don't cut" -- "The method in five lines": bias[l][e] =
+ *         max(cap, ln(b[l][e] / b_edge[l])), top-k by logit + bias, weights from
+ *         the router's own softmax over the picked k; static table; opt-in.
+ *
+ * Conventions for every entry point
+ *   - Return 0 on success or a negative MOE_E_* code; moe_last_error() then
+ *     holds a one-line reason (thread-local).  Nothing aborts or exits.
+ *   - "device" pointers are HIP device memory (or device-visible pinned host
+ *     memory where stated); "host" pointers are CPU memory.  The caller owns
+ *     every buffer.  The library allocates nothing per call and keeps no
+ *     pointer between calls.
+ *   - Device calls enqueue on the given stream and never synchronise with the
+ *     host.  Counts produced on the device (n_miss, n_host) stay there.
+ *   - Identical inputs give bit-identical outputs (fixed reduction orders, no
+ *     floating-point atomics).
+ *   - Weights are row-major [out][in]: gate Wg[I][H], up Wu[I][H], down
+ *     Wd[H][I]; router gate G[H][E].
+ */
+#ifndef MOE_SLOT_H
+#define MOE_SLOT_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+/* status codes */
+#define MOE_OK 0
+#define MOE_E_ARG (-1)    /* null pointer, negative or out-of-range size */
+#define MOE_E_ALIGN (-2)  /* pointer or slab not 16-byte aligned / a 16-byte multiple */
+#define MOE_E_DTYPE (-3)  /* unsupported activation / weight format pair */
+#define MOE_E_SHAPE (-4)  /* inconsistent or unsupported shape (k > E, S > E, limits) */
+#define MOE_E_HIP (-5)    /* a HIP runtime call or kernel launch failed */
+#define MOE_E_NOMEM (-6)  /* pinned host allocation failed */
+
+/* activation formats (x and the router gate G) */
+#define MOE_X_F32 0
+#define MOE_X_BF16 1
+
+/* expert weight formats (one slab per expert, see moe_slab_layout) */
+#define MOE_W_F32 0    /* fp32 weights, fp32 activations, h kept in fp32 */
+#define MOE_W_BF16 1   /* bf16 weights and activations; h rounded to bf16 (RNE) */
+#define MOE_W_W8A8 2   /* int8 weights + fp32 per-output-row scales; x and h
+                          quantised per token / per pick to int8 with scale
+                          absmax/127 (1 if all zero), code = clamp(rint(v/scale),
+                          -127, 127), both in fp32; int32 dots; dequant
+                          ((float)acc * s_act) * s_row */
+#define MOE_W_Q4B32 3  /* 4-bit blocks of 32 inputs, fp16 scale per block:
+                          w = scale * (nibble - 8); x bf16; h rounded to bf16 */
+
+/* cache policies */
+#define MOE_STATIC 0   /* resident set fixed at load, never evicted */
+#define MOE_LRU 1
+#define MOE_LFU 2
+
+/* limits */
+#define MOE_MAX_E 4096     /* experts per layer */
+#define MOE_MAX_S 1024     /* slots per layer */
+#define MOE_MAX_K 32       /* top-k */
+
+/* Cache state of one layer, all device arrays owned by the caller and
+ * mutated only by cache_manage / cache_init, in stream order.
+ *   e2s[E]   slot of expert e, -1 if not resident
+ *   s2e[S]   expert in slot s, -1 if empty
+ *   last[S]  step of the slot's last use        (LRU / LFU priority)
+ *   freq[S]  uses since the expert entered      (LFU priority)
+ *   step[1]  step counter, +1 per cache_manage call */
+typedef struct {
+    int32_t* e2s;
+    int32_t* s2e;
+    uint32_t* last;
+    uint32_t* freq;
+    uint32_t* step;
+    int32_t E;
+    int32_t S;
+} moe_cache_state;
+
+/* Byte offsets inside one expert's slab.  w[p] / s[p] are the weight plane
+ * and scale plane of projection p (0 gate, 1 up, 2 down); s[p] = -1 where the
+ * format has no scales.
+ *   F32 / BF16: Wg | Wu | Wd
+ *   W8A8:       Wg | Wu | Wd (int8) | sg[I] | su[I] | sd[H] (fp32)
+ *   Q4B32:      per projection, a nibble plane [out][in/2] then an fp16 scale
+ *               plane [out][in/32]; order gate, up, down.  Block b of a row
+ *               covers inputs 32b..32b+31; byte j of the block holds input
+ *               32b+j in its low nibble and 32b+j+16 in its high nibble. */
+typedef struct {
+    int64_t w[3];
+    int64_t s[3];
+    int64_t total;
+} moe_slab_layout_t;
+
+int moe_abi_version(void);
+const char* moe_last_error(void);
+
+/* Slab layout of one expert.  Requires H, I multiples of 16 (32 for Q4B32)
+ * so that every plane starts on a 16-byte boundary ([VEC] "Prove it is
+ * correct before measuring": per-expert slabs stay 16-byte multiples). */
+int moe_slab_layout(int w_type, int H, int I, moe_slab_layout_t* out);
+
+/* Graded selection bias of one layer, [PGO] "The method in five lines".
+ *   b      device double[E]: brightness (share of router mass) per expert
+ *   n_hot  size of the hot set = the n_hot brightest experts (ties: lower id)
+ *   cap    floor of the penalty (e.g. -1)
+ *   bias   device float[E] out: 0 for hot experts, else
+ *          max(cap, ln(b[e] / b_edge)) with b_edge the weakest hot expert's
+ *          brightness, computed in double (b = 0 gives cap).
+ * Errors: ARG (null, E < 1, n_hot < 1), SHAPE (E > MOE_MAX_E). */
+int moe_bias_table(const double* b, int E, int n_hot, float cap, float* bias, hipStream_t stream);
+
+/* Router, [PGO] "The method in five lines".
+ *   x       device [T][H] in x_dtype
+ *   G       device [H][E] in x_dtype
+ *   bias    device float[E] or NULL.  NULL gives exactly the plain top-k of
+ *           the logits (the bias is opt-in).
+ *   ids_in  device int32[T][k] or NULL.  If given, the picks are taken as is
+ *           (externally sampled routing) and only w (and logits) are produced.
+ *   ids     device int32[T][k] out: picks by score s = fl32(z + bias), highest
+ *           first, ties to the lower expert id (ignored if ids_in != NULL)
+ *   w       device float[T][k] out: softmax of the raw logits z over the k
+ *           picks (selection-only bias), computed in double
+ *   logits  device float[T][E] out, or NULL: z = x G, accumulated in double
+ *           and rounded once to fp32
+ * Errors: ARG, DTYPE, SHAPE (k > E, k > MOE_MAX_K, E > MOE_MAX_E), HIP. */
+int moe_route(const void* x, int x_dtype, const void* G, const float* bias, const int32_t* ids_in, int T, int H,
+              int E, int k, int32_t* ids, float* w, float* logits, hipStream_t stream);
+
+/* Initialise a cache state.  resident: device int32[S] (slot s holds expert
+ * resident[s]) or NULL for an empty cache.  Clears last/freq and step.
+ * Errors: ARG, SHAPE (S > E, S > MOE_MAX_S, E > MOE_MAX_E). */
+int cache_init(const moe_cache_state* st, const int32_t* resident, hipStream_t stream);
+
+/* Static resident set from a profile batch ([RTX] transcript: the set is
+ * chosen once, before the run, from what the router picks): the S most-picked
+ * experts among ids[n_ids], ties to the lower id, most-picked first.
+ *   ids device int32[n_ids]; resident device int32[S] out. */
+int cache_pick_static(const int32_t* ids, int n_ids, int E, int S, int32_t* resident, hipStream_t stream);
+
+/* One cache step, [VEC] "What this package does" (expert_cache_manage plus
+ * the remap to slot space).  One workgroup, deterministic, no atomics.
+ *   st        cache state (mutated)
+ *   policy    MOE_STATIC / MOE_LRU / MOE_LFU
+ *   ids       device int32[n_ids] routing ids of this step (T*k)
+ *   slot_ids  device int32[n_ids] out: slot of ids[i] after the step, -1 if
+ *             the expert is not resident (its pick is left to the host pass)
+ *   miss      device int32[2*S] out: (expert, slot) pairs to gather, experts
+ *             in ascending id; the i-th miss takes the i-th victim
+ *   n_miss    device int32[1] out
+ *   host_miss device int32[E] out: needed experts left non-resident
+ *             (ascending id): all misses under STATIC, the overflow beyond
+ *             the victims otherwise
+ *   n_host    device int32[1] out
+ *   stats     device int32[4] out or NULL: routing ids resident at entry,
+ *             distinct experts needed, gathered, host misses
+ * Victims are the slots that hold no expert needed this step: empty slots
+ * first (lower slot first), then LRU by last use / LFU by use count then last
+ * use, ties to the lower slot.  A hit refreshes last (LFU: count + 1 per
+ * step); an inserted expert starts at last = step, freq = 1.  STATIC never
+ * changes the maps.  Overflow (more misses than victims) is not an error.
+ * Errors: ARG, SHAPE (n_ids > 65536 or limits), HIP. */
+int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int n_ids, int32_t* slot_ids,
+                 int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host, int32_t* stats,
+                 hipStream_t stream);
+
+/* Copy each missing expert's slab from pinned host memory into its slot,
+ * [VEC] "What this package does" / "The port": the device itself reads the
+ * host memory, in 16-byte units.  Launch it on a side stream and order the
+ * FFN after it with an event.
+ *   miss        device int32[2*max_miss] (from cache_manage)
+ *   n_miss      device int32[1] (read on the device; no host sync)
+ *   host_store  pinned host memory [E][slab_bytes] (hipHostMalloc /
+ *               moe_host_alloc / torch pinned tensor); its device address is
+ *               looked up on every call
+ *   slot_store  device [S][slab_bytes]
+ * Errors: ARG (host_store not pinned), ALIGN (pointers or slab_bytes not
+ * 16-byte multiples), HIP. */
+int cache_gather(const int32_t* miss, const int32_t* n_miss, int max_miss, const void* host_store, void* slot_store,
+                 size_t slab_bytes, hipStream_t stream);
+
+/* Workspace bytes moe_ffn_slots needs for these sizes (device memory the
+ * caller allocates once and passes in). */
+size_t moe_ffn_workspace_bytes(int T, int k, int S, int w_type, int H, int I);
+
+/* Grouped SwiGLU FFN over the resident slots ([RTX] transcript: the expert
+ * step returns zeros for an expert that is not on the GPU).
+ *   x         device [T][H] in x_dtype (MOE_X_F32 for MOE_W_F32, else bf16)
+ *   slot_ids  device int32[T][k]; -1 = not resident: that pick adds exactly 0
+ *   w         device float[T][k] routing weights
+ *   slot_store device [S][slab_bytes] (16-byte aligned; slab_bytes >= layout)
+ *   y         device float[T][H] out (overwritten):
+ *             y[t] = sum over j with slot_ids[t][j] >= 0 of w[t][j] * FFN_slot(x[t]),
+ *             summed in j order; +0.0 where token t has no resident pick
+ *   ws        device workspace of >= moe_ffn_workspace_bytes(...) bytes
+ * Errors: ARG, ALIGN, DTYPE, SHAPE, HIP. */
+int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
+                  const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream);
+
+/* Host pass over the picks that are not resident, [RTX] "What the video
+ * covers" / transcript (a CPU pass over the experts still in RAM).  Runs
+ * synchronously on the calling thread plus n_threads - 1 workers; safe to
+ * run while the GPU calls are in flight.
+ *   x_h, ids_h, slot_ids_h, w_h  host copies of x [T][H], ids [T][k],
+ *                                slot_ids [T][k], w [T][k]
+ *   host_store                   host [E][slab_bytes] (pinned or not)
+ *   y_h                          host float[T][H] out (overwritten):
+ *                                sum over j with slot_ids[t][j] < 0 of
+ *                                w[t][j] * FFN_ids[t][j](x[t]), in j order
+ * Same per-format arithmetic as moe_ffn_slots.  Errors: ARG, DTYPE, SHAPE. */
+int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* ids_h, const int32_t* slot_ids_h,
+                        const float* w_h, int T, int k, const void* host_store, size_t slab_bytes, int E, int w_type,
+                        int H, int I, float* y_h, int n_threads);
+
+/* y[i] = fl32(y[i] + y_add[i]) for T*H floats on the device: the single add
+ * that joins the two passes ([RTX] transcript). */
+int moe_combine(float* y, const float* y_add, int T, int H, hipStream_t stream);
+
+/* Pinned, device-mapped host memory for the host expert store. */
+void* moe_host_alloc(size_t bytes);
+int moe_host_free(void* p);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

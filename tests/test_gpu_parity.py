@@ -1,0 +1,386 @@
+"""GPU parity: every entry point of libmoeslot.so against the CPU oracle.
+
+Bars: routing ids, slot maps, miss and host lists, cache state and gathered
+bytes bit-exact; outputs within |d| <= rtol*|ref| + atol, with (rtol, atol)
+= (1e-5, 1e-5*rms) for fp32, (2e-2, 1e-2) for bf16 and (3e-2, 3e-2*rms) for
+int8 and 4-bit weights.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+
+
+@pytest.fixture(scope="module")
+def m():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import expert_vram_slot_amd as mod
+    mod.lib()
+    return mod
+
+
+def dev(a, dtype=None):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if dtype is not None:
+        t = t.to(dtype)
+    return t.cuda()
+
+
+def host(t):
+    torch.cuda.synchronize()
+    return t.cpu().numpy()
+
+
+TOL = {0: (1e-5, None), 1: (2e-2, 1e-2), 2: (3e-2, None), 3: (3e-2, None)}
+
+
+def assert_close(got, ref, w_type, what=""):
+    rtol, atol = TOL[w_type]
+    ref = ref.astype(np.float64)
+    rms = float(np.sqrt(np.mean(ref ** 2))) or 1.0
+    if atol is None:
+        atol = rtol * rms
+    excess = np.abs(got.astype(np.float64) - ref) - (rtol * np.abs(ref) + atol)
+    assert np.all(excess <= 0), f"{what}: max excess {excess.max():.3e} at {np.unravel_index(excess.argmax(), excess.shape)} (rms {rms:.3e})"
+
+
+def x_torch_dtype(x_dtype):
+    return torch.float32 if x_dtype == 0 else torch.int16
+
+
+# ------------------------------------------------------------------ router
+
+
+def gpu_route(m, li, bias=None, ids_in=None):
+    T, H, E, k = li.T, li.H, li.E, li.k
+    x = dev(li.x.view(np.int16) if li.x_dtype else li.x)
+    G = dev(li.G.view(np.int16) if li.x_dtype else li.G)
+    ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
+    w = torch.empty((T, k), dtype=torch.float32, device="cuda")
+    z = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    b = None if bias is None else dev(bias)
+    ii = None if ids_in is None else dev(ids_in)
+    m.moe_route(x, li.x_dtype, G, b, ii, T, H, E, k, ids, w, z)
+    return host(ids), host(w), host(z)
+
+
+def check_route(m, li, bias=None):
+    ids, w, z = gpu_route(m, li, bias)
+    zo = oracle.logits(li.x, li.x_dtype, li.G)
+    # logits: one rounding of a double sum on both sides
+    ulp = np.spacing(np.abs(zo))
+    assert np.all(np.abs(z - zo) <= ulp)
+    assert np.mean(z == zo) > 0.999
+    # picks on the GPU's own logits: bit-exact
+    np.testing.assert_array_equal(ids, oracle.topk(z, li.k, bias))
+    # end-to-end picks at this seed: bit-exact
+    np.testing.assert_array_equal(ids, oracle.topk(zo, li.k, bias))
+    np.testing.assert_allclose(w, oracle.route_weights(z, ids), rtol=2e-6, atol=1e-9)
+    return ids, w, z
+
+
+@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 1), ("c2", 8), ("c2", 64), ("c3", 16), ("c4", 1),
+                                   ("c4", 32), ("c2", 300)])
+def test_route_matches_oracle(m, cfg, T):
+    li = synth.LayerInputs(cfg, T=T, with_store=False)
+    check_route(m, li)
+
+
+def test_route_prefill_shape(m):
+    li = synth.LayerInputs("c5", T=2048, with_store=False)
+    check_route(m, li)
+
+
+def test_route_with_graded_bias(m):
+    li = synth.LayerInputs("c4", T=32, with_store=False, layer=3)
+    b = synth.dirichlet(synth.key(li.base, synth.TAG_B, 3), li.E, 0.3)
+    bias_o = oracle.bias_table(b, 192, -1.0)
+    bias_g = torch.empty(li.E, dtype=torch.float32, device="cuda")
+    m.moe_bias_table(dev(b), li.E, 192, -1.0, bias_g)
+    bias_g = host(bias_g)
+    assert np.all(np.abs(bias_g - bias_o) <= np.spacing(np.abs(bias_o)))
+    np.testing.assert_array_equal(bias_g == 0, bias_o == 0)
+    ids, w, z = check_route(m, li, bias_o)
+    # the bias moved some picks, and the weights stayed the raw-logit softmax
+    assert np.any(ids != oracle.topk(z, li.k))
+
+
+def test_route_given_ids_only_weights(m):
+    li = synth.LayerInputs("c3", T=16, with_store=False)
+    ids_in = synth.zipf_ids(synth.key(li.base, synth.TAG_ZIPF_PERM), synth.key(li.base, synth.TAG_ZIPF_DRAW), 16,
+                            li.E, li.k, 0.8)
+    ids, w, z = gpu_route(m, li, ids_in=ids_in)
+    np.testing.assert_allclose(w, oracle.route_weights(z, ids_in), rtol=2e-6, atol=1e-9)
+
+
+def test_route_ties_go_to_lower_id(m):
+    # integer-valued logits with many ties: G picks one column pattern
+    T, H, E, k = 8, 16, 64, 6
+    x = np.ones((T, H), np.float32)
+    G = np.zeros((H, E), np.float32)
+    G[0, :] = np.arange(E) % 5  # five distinct logit values, many ties
+    li = type("L", (), dict(T=T, H=H, E=E, k=k, x=x, G=G, x_dtype=0))
+    ids, w, z = gpu_route(m, li)
+    np.testing.assert_array_equal(ids, oracle.topk(z, k))
+    assert list(ids[0]) == [4, 9, 14, 19, 24, 29]
+
+
+# ------------------------------------------------------------------ cache
+
+
+class GpuCache:
+    def __init__(self, m, E, S, resident=None):
+        self.m, self.E, self.S = m, E, S
+        i32 = dict(dtype=torch.int32, device="cuda")
+        self.e2s = torch.empty(E, **i32)
+        self.s2e = torch.empty(max(S, 1), **i32)
+        self.last = torch.empty(max(S, 1), **i32)
+        self.freq = torch.empty(max(S, 1), **i32)
+        self.step = torch.empty(1, **i32)
+        self.st = m.cache_state(self.e2s, self.s2e, self.last, self.freq, self.step, E, S)
+        m.cache_init(self.st, None if resident is None else dev(np.asarray(resident, np.int32)))
+        self.miss = torch.empty(2 * max(S, 1), **i32)
+        self.n_miss = torch.empty(1, **i32)
+        self.host_miss = torch.empty(E, **i32)
+        self.n_host = torch.empty(1, **i32)
+        self.stats = torch.empty(4, **i32)
+
+    def manage(self, policy, ids):
+        ids = dev(np.asarray(ids, np.int32).reshape(-1))
+        n = ids.numel()
+        slot_ids = torch.full((max(n, 1),), -9, dtype=torch.int32, device="cuda")
+        self.m.cache_manage(self.st, oracle.POLICIES[policy], ids, n, slot_ids, self.miss, self.n_miss,
+                            self.host_miss, self.n_host, self.stats)
+        nm, nh = int(host(self.n_miss)[0]), int(host(self.n_host)[0])
+        return dict(slot_ids=host(slot_ids)[:n], miss=host(self.miss)[:2 * nm].reshape(nm, 2),
+                    host_miss=host(self.host_miss)[:nh], stats=host(self.stats))
+
+
+def compare_state(g, o):
+    np.testing.assert_array_equal(host(g.e2s), o.e2s)
+    if o.S:
+        np.testing.assert_array_equal(host(g.s2e)[:o.S], o.s2e)
+        np.testing.assert_array_equal(host(g.last)[:o.S].view(np.uint32), o.last)
+        np.testing.assert_array_equal(host(g.freq)[:o.S].view(np.uint32), o.freq)
+    assert int(host(g.step)[0]) == int(o.step[0])
+
+
+@pytest.mark.parametrize("policy", ["lru", "lfu", "static"])
+@pytest.mark.parametrize("E,S,T,k,dist", [(128, 32, 16, 8, "zipf"), (128, 32, 16, 8, "uniform"),
+                                          (512, 192, 32, 10, "zipf"), (12, 1, 1, 1, "uniform"),
+                                          (64, 64, 4, 8, "zipf"), (1000, 300, 40, 8, "zipf")])
+def test_manage_matches_oracle_every_step(m, policy, E, S, T, k, dist):
+    rng = np.random.default_rng(E * 31 + S)
+    if dist == "zipf":
+        seq = synth.zipf_ids(synth.key(E, 7, S), synth.key(E, 8, S), 30 * T, E, k, 0.8).reshape(30, T, k)
+    else:
+        seq = np.stack([np.stack([rng.choice(E, k, replace=False) for _ in range(T)]) for _ in range(30)])
+    resident = list(rng.choice(E, S, replace=False)) if policy == "static" else None
+    g = GpuCache(m, E, S, resident)
+    o = oracle.Cache(E, S, policy, resident=resident)
+    compare_state(g, o)
+    for step in range(seq.shape[0]):
+        rg = g.manage(policy, seq[step])
+        ro = o.manage(seq[step])
+        for key in ("slot_ids", "miss", "host_miss", "stats"):
+            np.testing.assert_array_equal(rg[key], ro[key], err_msg=f"{key} at step {step}")
+        compare_state(g, o)
+
+
+def test_manage_empty_step_and_invalid_ids(m):
+    g = GpuCache(m, 16, 4)
+    o = oracle.Cache(16, 4, "lru")
+    r = g.manage("lru", np.zeros(0, np.int32))
+    ro = o.manage(np.zeros(0, np.int32))
+    assert r["miss"].shape[0] == 0 and r["host_miss"].shape[0] == 0
+    compare_state(g, o)
+
+
+def test_pick_static_matches_oracle(m):
+    li = synth.LayerInputs("c2", T=1024, with_store=False, step=10_000)
+    zo = oracle.logits(li.x, 1, li.G)
+    ids = oracle.topk(zo, 8)
+    res = torch.empty(64, dtype=torch.int32, device="cuda")
+    m.cache_pick_static(dev(ids.reshape(-1)), ids.size, 128, 64, res)
+    np.testing.assert_array_equal(host(res), oracle.pick_static(ids, 128, 64))
+
+
+def test_gather_copies_slabs_byte_exact(m):
+    E, S, slab = 24, 6, 4096 + 256
+    rng = np.random.default_rng(5)
+    store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
+    store.copy_(torch.from_numpy(rng.integers(0, 256, (E, slab), dtype=np.uint8)))
+    slots = torch.zeros((S, slab), dtype=torch.uint8, device="cuda")
+    g = GpuCache(m, E, S)
+    o = oracle.Cache(E, S, "lru")
+    o_slots = np.zeros((S, slab), np.uint8)
+    for step in range(12):
+        ids = rng.choice(E, 4, replace=False)
+        rg = g.manage("lru", ids)
+        ro = o.manage(ids)
+        np.testing.assert_array_equal(rg["miss"], ro["miss"])
+        m.cache_gather(g.miss, g.n_miss, S, store, slots, slab)
+        oracle.gather(ro["miss"], store.numpy(), o_slots)
+        np.testing.assert_array_equal(host(slots), o_slots)
+    for s in range(S):
+        e = int(o.s2e[s])
+        if e >= 0:
+            assert bytes(host(slots)[s]) == bytes(store.numpy()[e])
+
+
+def test_gather_refuses_unpinned_host_memory(m):
+    slab = 256
+    store = torch.zeros((4, slab), dtype=torch.uint8)  # pageable
+    slots = torch.zeros((2, slab), dtype=torch.uint8, device="cuda")
+    miss = torch.zeros(4, dtype=torch.int32, device="cuda")
+    n = torch.zeros(1, dtype=torch.int32, device="cuda")
+    with pytest.raises(m.MoeError) as e:
+        m.cache_gather(miss, n, 2, store, slots, slab)
+    assert e.value.code == m.MOE_E_ARG and "pinned" in str(e.value)
+    # the refusal leaves no pending HIP error behind for the next caller
+    assert float(torch.ones(4, device="cuda").sum()) == 4.0
+
+
+# ------------------------------------------------------------------ FFN
+
+
+def run_ffn(m, li, slot_ids, w, slot_store, S):
+    T, k, H, I = li.T, li.k, li.H, li.I
+    x = dev(li.x.view(np.int16) if li.x_dtype else li.x)
+    ws_bytes = m.moe_ffn_workspace_bytes(T, k, S, li.w_type, H, I)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    y = torch.full((T, H), np.nan, dtype=torch.float32, device="cuda")
+    m.moe_ffn_slots(x, li.x_dtype, dev(slot_ids.astype(np.int32)), dev(w), T, k, slot_store, li.slab, S, li.w_type,
+                    H, I, y, ws, ws_bytes)
+    return host(y)
+
+
+def ffn_case(m, cfg, T, S=None, E=None, step=0, layer=0):
+    li = synth.LayerInputs(cfg, T=T, E=E, step=step, layer=layer)
+    z = oracle.logits(li.x, li.x_dtype, li.G)
+    ids = oracle.topk(z, li.k)
+    w = oracle.route_weights(z, ids)
+    S = S if S is not None else li.c["S"]
+    resident = li.c.get("resident") or oracle.pick_static(ids, li.E, S)
+    c = oracle.Cache(li.E, S, "static", resident=resident)
+    sl = c.manage(ids)["slot_ids"].reshape(ids.shape)
+    slots = dev(li.store[np.asarray(resident)])
+    _, yg, yh = oracle.layer(li.w_type, li.store, li.E, li.H, li.I, li.x, li.x_dtype, ids, w, sl)
+    y = run_ffn(m, li, sl, w, slots, S)
+    return li, ids, w, sl, y, yg, yh, slots
+
+
+@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 1), ("c2", 8), ("c2", 64), ("c3", 16), ("c4", 1), ("c4", 32)])
+def test_ffn_slots_matches_oracle(m, cfg, T):
+    li, ids, w, sl, y, yg, yh, _ = ffn_case(m, cfg, T)
+    assert_close(y, yg, li.w_type, f"{cfg} T={T}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+
+
+@pytest.mark.parametrize("w_type,H,I", [(1, 112, 144), (1, 1040, 784), (0, 80, 48), (2, 1040, 784),
+                                        (3, 1056, 544)])
+def test_ffn_ragged_shapes(m, w_type, H, I):
+    """Row tiles with a ragged tail and rows whose granules do not fill the waves."""
+    E, k, T, S = 12, 3, 11, 7
+    rng = np.random.default_rng(H + I)
+    x_dtype = 0 if w_type == 0 else 1
+    x = synth.normal(synth.key(H, 1, I), (T, H), 1.0, x_dtype)
+    store = synth.slabs(w_type, 1234 + w_type, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=x_dtype, w_type=w_type,
+                            slab=store.shape[1]))
+    _, yg, _ = oracle.layer(w_type, store, E, H, I, x, x_dtype, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, w_type, f"w{w_type} H={H} I={I}")
+
+
+def test_ffn_many_tokens_on_one_slot(m):
+    """More tokens on a slot than one pass holds (token chunks of 8)."""
+    li = synth.LayerInputs("c2", T=37)
+    k = li.k
+    rng = np.random.default_rng(3)
+    ids = np.stack([np.concatenate([[5], rng.choice(np.setdiff1d(np.arange(128), [5]), k - 1, replace=False)])
+                    for _ in range(li.T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), li.T).astype(np.float32)
+    S = 16
+    resident = np.arange(0, 32, 2)
+    resident[2] = 5
+    e2s = np.full(128, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    _, yg, _ = oracle.layer(1, li.store, 128, li.H, li.I, li.x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(li.store[resident]), S)
+    assert_close(y, yg, 1, "37 tokens on one slot")
+
+
+def test_zero_return_is_exact(m):
+    li = synth.LayerInputs("c2", T=8)
+    w = np.full((8, 8), 0.125, np.float32)
+    sl = np.full((8, 8), -1, np.int32)
+    y = run_ffn(m, li, sl, w, dev(li.store[:4]), 4)
+    assert np.all(y == 0) and not np.any(np.signbit(y))
+
+
+def test_all_resident_any_permutation_bitwise(m):
+    li = synth.LayerInputs("c1")
+    z = oracle.logits(li.x, 0, li.G)
+    ids = oracle.topk(z, 2)
+    w = oracle.route_weights(z, ids)
+    ident = run_ffn(m, li, ids, w, dev(li.store), 8)
+    perm = np.random.default_rng(1).permutation(8)
+    inv = np.argsort(perm)  # slot s holds expert perm[s]
+    y = run_ffn(m, li, inv[ids], w, dev(li.store[perm]), 8)
+    np.testing.assert_array_equal(y, ident)
+    yf, _, _ = oracle.layer(0, li.store, 8, 64, 128, li.x, 0, ids, w)
+    assert_close(ident, yf, 0, "all resident vs no cache")
+
+
+def test_ffn_deterministic(m):
+    li, ids, w, sl, y, yg, yh, slots = ffn_case(m, "c2", 64)
+    y2 = run_ffn(m, li, sl, w, slots, 64)
+    np.testing.assert_array_equal(y, y2)
+
+
+# ---------------------------------------------------------- whole layer
+
+
+@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 8), ("c2", 64)])
+def test_layer_step_two_passes_sum_to_oracle(m, cfg, T):
+    from expert_vram_slot_amd.layer import SlotLayer
+    li = synth.LayerInputs(cfg, T=T)
+    c = li.c
+    S = c["S"]
+    zo = oracle.logits(li.x, li.x_dtype, li.G)
+    ids_o = oracle.topk(zo, li.k)
+    w_o = oracle.route_weights(zo, ids_o)
+    yf, _, _ = oracle.layer(li.w_type, li.store, li.E, li.H, li.I, li.x, li.x_dtype, ids_o, w_o)
+    if cfg == "c1":
+        resident = np.array(c["resident"], np.int32)
+    else:
+        warm = synth.LayerInputs(cfg, T=1024, step=10_000, with_store=False)
+        resident = oracle.pick_static(oracle.topk(oracle.logits(warm.x, 1, warm.G), li.k), li.E, S)
+    host_store = torch.empty(li.store.shape, dtype=torch.uint8, pin_memory=True)
+    host_store.copy_(torch.from_numpy(li.store))
+    slots = dev(li.store[resident])
+    G = dev(li.G.view(np.int16) if li.x_dtype else li.G)
+    L = SlotLayer(E=li.E, k=li.k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, policy="static",
+                  host_store=host_store, slot_store=slots, G=G, n_threads=8)
+    L.init_cache(dev(resident))
+    x = dev(li.x.view(np.int16) if li.x_dtype else li.x)
+    y = host(L.step(x, T))
+    np.testing.assert_array_equal(host(L.ids)[:T * li.k].reshape(T, li.k), ids_o)
+    assert_close(y, yf, li.w_type, f"{cfg} layer")
+    st = host(L.stats)
+    assert st[3] == len(set(ids_o.reshape(-1).tolist()) - set(resident.tolist()))
