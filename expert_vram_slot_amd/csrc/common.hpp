@@ -52,6 +52,31 @@ __device__ __forceinline__ T wave_sum(T v) {
     return v;
 }
 
+// One butterfly level at lane stride S with LIVE values still live: pairs of
+// lanes (l, l ^ S) swap halves, so the live count halves while each value
+// gathers the partner's partial sum.  Recurses down to stride 1 at compile
+// time (every index is a constant, so the values stay in registers).
+template <int LIVE, int S, int N, typename T>
+__device__ __forceinline__ void multi_sum_level(T (&v)[N], int lane, int& id) {
+    if constexpr (S >= 1) {
+        if constexpr (LIVE > 1) {
+            constexpr int n = LIVE / 2;
+            const bool up = (lane & S) != 0;
+#pragma unroll
+            for (int i = 0; i < n; ++i) {
+                const T send = up ? v[i] : v[i + n];
+                const T keep = up ? v[i + n] : v[i];
+                v[i] = keep + __shfl_xor(send, S, WAVE);
+            }
+            if (up) id += n;
+            multi_sum_level<n, S / 2>(v, lane, id);
+        } else {
+            v[0] += __shfl_xor(v[0], S, WAVE);
+            multi_sum_level<1, S / 2>(v, lane, id);
+        }
+    }
+}
+
 // Reduce N per-lane values over the 64 lanes at once (N a power of two,
 // N <= 64).  Each butterfly level halves the number of live values, so the
 // whole reduction costs about N exchanges instead of 6N.  On return v[0] of
@@ -61,23 +86,7 @@ template <int N, typename T>
 __device__ __forceinline__ T wave_multi_sum(T (&v)[N], int lane, int& idx) {
     static_assert(N >= 1 && N <= 64 && (N & (N - 1)) == 0, "N must be a power of two <= 64");
     int id = 0;
-    int n = N;
-#pragma unroll
-    for (int s = 32; s >= 1; s >>= 1) {
-        if (n > 1) {
-            n >>= 1;
-            const bool up = (lane & s) != 0;
-#pragma unroll
-            for (int i = 0; i < n; ++i) {
-                T send = up ? v[i] : v[i + n];
-                T keep = up ? v[i + n] : v[i];
-                v[i] = keep + __shfl_xor(send, s, WAVE);
-            }
-            if (up) id += n;
-        } else {
-            v[0] += __shfl_xor(v[0], s, WAVE);
-        }
-    }
+    multi_sum_level<N, 32>(v, lane, id);
     idx = id;
     return v[0];
 }

@@ -34,8 +34,8 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int FFN_THREADS = 256;
 constexpr int NTMAX = 8;       // tokens of one slot handled per pass
-constexpr int RPW_GU = 4;      // gate rows (and as many up rows) per wave
-constexpr int RPW_DN = 8;      // down rows per wave
+constexpr int RPW_GU = 1;      // gate rows (and as many up rows) per wave
+constexpr int RPW_DN = 4;      // down rows per wave
 constexpr int GROUP_THREADS = 1024;
 
 // ------------------------------------------------------------ formats
@@ -123,12 +123,11 @@ __device__ __forceinline__ void granule_dot(const v4u& w, const unsigned char* x
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
-__device__ __forceinline__ int pow2_ceil_small(int n) { return n <= 1 ? 1 : n <= 2 ? 2 : n <= 4 ? 4 : 8; }
 
 // ---------------------------------------------------------- workspace
 
 struct WsLayout {
-    size_t slot_off, pair_list, active, n_active, h, hq, hs, xq, xs, part, total;
+    size_t slot_off, pair_list, active, n_active, h, hq, hs, xq, xs, xbs, hbs, part, total;
 };
 
 WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
@@ -151,6 +150,10 @@ WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
         L.hs = take(4 * P);
         L.xq = take((size_t)T * H);
         L.xs = take(4 * (size_t)T);
+    }
+    if (w_type == MOE_W_Q4B32) {
+        L.xbs = take(4 * (size_t)T * (H / 32));
+        L.hbs = take(4 * P * (I / 32));
     }
     L.part = take(4 * P * H);
     L.total = o;
@@ -269,228 +272,269 @@ struct SlabView {
     int64_t w0, w1, s0, s1;  // weight and scale plane offsets used by the kernel
 };
 
-// Stage the activations of up to NTMAX tokens of this slot into LDS, rows of
-// `len` elements.  For 4-bit weights also the per-block sums of x.
-template <int F>
-__device__ __forceinline__ void stage_rows(unsigned char* xs, float* bsum, int32_t* pick_ids, const void* src,
-                                           const int32_t* __restrict__ pair_list, int p0, int c0, int nt, int k,
-                                           int len, bool by_token) {
-    constexpr int AB = Fmt<F>::ABYTES;
-    const int row_bytes = len * AB;
-    const int g16 = row_bytes / 16;
-    if (threadIdx.x < NTMAX) pick_ids[threadIdx.x] = threadIdx.x < nt ? pair_list[p0 + c0 + threadIdx.x] : -1;
-    __syncthreads();
-    for (int i = threadIdx.x; i < NTMAX * g16; i += FFN_THREADS) {
-        const int j = i / g16, g = i % g16;
-        v4u v = {0u, 0u, 0u, 0u};
-        const int pick = pick_ids[j];
-        if (pick >= 0) {
-            const int64_t r = by_token ? pick / k : pick;
-            v = *reinterpret_cast<const v4u*>(reinterpret_cast<const unsigned char*>(src) + r * row_bytes + (int64_t)g * 16);
+// Expert weights are streamed once per step: non-temporal loads keep them
+// from displacing the small, reused data (tokens, pick lists) in the caches.
+__device__ __forceinline__ v4u load_weights(const v4u* p) { return __builtin_nontemporal_load(p); }
+
+// One wave's ROWS weight rows (row r at rowp[r]; 4-bit scale rows at scp[r]).
+// Rows past the end are clamped to the last row (computed, then dropped) so
+// every load stays in bounds.
+template <int ROWS>
+struct RowPtrs {
+    const unsigned char* w[ROWS];
+    const unsigned char* s[ROWS];
+};
+
+// Activations of one pass: up to NT rows of a row-major [rows][len] array
+// (x for gate/up, h for down), read directly from global memory (they are
+// small and shared by every tile of the slot, so they stay in L2).  4-bit
+// weights also need the per-block sums of those rows.
+struct ActRows {
+    const unsigned char* base;  // row r at base + r * row_bytes
+    size_t row_bytes;
+    const float* bsum;          // [rows][len / 32] (4-bit only)
+};
+
+// Dot products of ROWS weight rows with NT activation rows over KG 16-byte
+// granules.  Lane l takes granules l, l + 64, ...: a chunk is 64 granules of
+// every row.  Chunks go in groups of NCHG whose weight loads are all issued
+// before the first is used; granules past the end read a clamped, in-bounds
+// granule with zero weights.  acc[r * NT + t].
+template <int F, int ROWS, int NT, int NCHG>
+__device__ __forceinline__ void gemv_rows(const RowPtrs<ROWS>& rp, const ActRows& ar, const int (&arow)[NT], int KG,
+                                          int lane, typename Fmt<F>::Acc (&acc)[ROWS * NT]) {
+    constexpr int XG = Fmt<F>::EPG * Fmt<F>::ABYTES;  // activation bytes per weight granule
+    for (int g0 = 0; g0 < KG; g0 += 64 * NCHG) {
+        v4u w[NCHG][ROWS];
+        float qs[NCHG][ROWS];
+        int gj[NCHG];
+        bool on[NCHG];
+#pragma unroll
+        for (int j = 0; j < NCHG; ++j) {
+            const int g = g0 + 64 * j + lane;
+            on[j] = g < KG;
+            gj[j] = on[j] ? g : KG - 1;
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                w[j][r] = load_weights(reinterpret_cast<const v4u*>(rp.w[r] + (size_t)gj[j] * 16));
+                qs[j][r] = 0.0f;
+                if constexpr (F == MOE_W_Q4B32)
+                    qs[j][r] = half_bits_to_f32(reinterpret_cast<const uint16_t*>(rp.s[r])[gj[j]]);
+            }
         }
-        *reinterpret_cast<v4u*>(xs + (size_t)j * row_bytes + (size_t)g * 16) = v;
-    }
-    if constexpr (F == MOE_W_Q4B32) {
-        __syncthreads();
-        const int nb = len / 32;
-        for (int i = threadIdx.x; i < NTMAX * nb; i += FFN_THREADS) {
-            const int j = i / nb, b = i % nb;
-            const uint16_t* xr = reinterpret_cast<const uint16_t*>(xs + (size_t)j * row_bytes) + 32 * b;
-            float s = 0.0f;
-            for (int e = 0; e < 32; ++e) s += moe::bf16_to_f32(xr[e]);
-            bsum[j * nb + b] = s;
+#pragma unroll
+        for (int j = 0; j < NCHG; ++j) {
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                if (!on[j]) {
+                    w[j][r] = v4u{0u, 0u, 0u, 0u};
+                    qs[j][r] = 0.0f;
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const unsigned char* xa = ar.base + (size_t)arow[t] * ar.row_bytes + (size_t)gj[j] * XG;
+                float xsum = 0.0f;
+                if constexpr (F == MOE_W_Q4B32) xsum = ar.bsum[(size_t)arow[t] * KG + gj[j]];
+#pragma unroll
+                for (int r = 0; r < ROWS; ++r) granule_dot<F>(w[j][r], xa, qs[j][r], xsum, acc[r * NT + t]);
+            }
         }
     }
 }
 
-template <int F, int NT>
-__device__ __forceinline__ void gu_body(const SlabView& sv, const unsigned char* slab, const unsigned char* xs,
-                                        const float* bsum, const int32_t* pick_ids, int nt, int H, int I, int k,
-                                        int r_base, const float* __restrict__ xscale, void* __restrict__ hbuf) {
+// Chunk-group size for a row of KG granules: the whole row when it has at
+// most 4 chunks, else groups of 4.
+__host__ __device__ constexpr int chunk_group(int KG) { return KG <= 64 ? 1 : KG <= 128 ? 2 : KG <= 192 ? 3 : 4; }
+
+#define MOE_NCHG_DISPATCH(KG, BODY)              \
+    do {                                         \
+        switch (chunk_group(KG)) {               \
+            case 1: BODY(1); break;              \
+            case 2: BODY(2); break;              \
+            case 3: BODY(3); break;              \
+            default: BODY(4); break;             \
+        }                                        \
+    } while (0)
+
+// Picks of one pass (uniform across the wave): pick[t] for t < nt, the last
+// valid pick repeated above (its results are dropped).
+template <int NT>
+__device__ __forceinline__ void pass_picks(const int32_t* __restrict__ pair_list, int p, int nt, int (&pick)[NT]) {
+#pragma unroll
+    for (int t = 0; t < NT; ++t) pick[t] = pair_list[p + min(t, nt - 1)];
+}
+
+template <int F, int NT, int NCHG>
+__device__ __forceinline__ void gu_pass(const RowPtrs<2 * RPW_GU>& rp, const SlabView& sv, const unsigned char* slab,
+                                        const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
+                                        int H, int I, int k, int r_base, const float* __restrict__ xscale,
+                                        void* __restrict__ hbuf) {
     using Acc = typename Fmt<F>::Acc;
-    constexpr int AB = Fmt<F>::ABYTES;
-    constexpr int EPG = Fmt<F>::EPG;
-    constexpr int V = 2 * RPW_GU * NT;
+    constexpr int ROWS = 2 * RPW_GU;  // gate rows, then the same up rows
+    constexpr int V = ROWS * NT;
     const int lane = threadIdx.x & 63;
-    const int KG = H / EPG;  // 16-byte granules per weight row
-    const int64_t row_bytes = (int64_t)KG * 16;
+    int pick[NT], tok[NT];
+    pass_picks<NT>(pair_list, p, nt, pick);
+#pragma unroll
+    for (int t = 0; t < NT; ++t) tok[t] = pick[t] / k;
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    for (int c = 0; c < KG; c += 64) {
-        const int g = c + lane;
-        if (g < KG) {
-#pragma unroll
-            for (int pj = 0; pj < 2; ++pj) {
-                const int64_t woff = pj == 0 ? sv.w0 : sv.w1;
-#pragma unroll
-                for (int r = 0; r < RPW_GU; ++r) {
-                    const int row = r_base + r;
-                    if (row < I) {
-                        const v4u w = *reinterpret_cast<const v4u*>(slab + woff + row * row_bytes + (int64_t)g * 16);
-                        float qs = 0.0f;
-                        if constexpr (F == MOE_W_Q4B32) {
-                            const int64_t soff = pj == 0 ? sv.s0 : sv.s1;
-                            qs = half_bits_to_f32(
-                                *reinterpret_cast<const uint16_t*>(slab + soff + ((int64_t)row * KG + g) * 2));
-                        }
-#pragma unroll
-                        for (int t = 0; t < NT; ++t) {
-                            const unsigned char* xa = xs + (size_t)t * H * AB + (size_t)g * EPG * AB;
-                            const float xsum = F == MOE_W_Q4B32 ? bsum[t * KG + g] : 0.0f;
-                            granule_dot<F>(w, xa, qs, xsum, acc[(pj * RPW_GU + r) * NT + t]);
-                        }
-                    }
-                }
-            }
-        }
-    }
+    gemv_rows<F, ROWS, NT, NCHG>(rp, ar, tok, H / Fmt<F>::EPG, lane, acc);
     int idx;
     Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
     const Acc up = __shfl_xor(v, 32, 64);
     if (moe::multi_sum_holder<V>(lane) && !(lane & 32)) {
-        const int r = (idx / NT) % RPW_GU, t = idx % NT;
+        const int r = idx / NT, t = idx % NT;
         const int row = r_base + r;
         if (row < I && t < nt) {
-            const int pick = pick_ids[t];
+            const int pk = pick[t];
             if constexpr (F == MOE_W_W8A8) {
-                const float sx = xscale[pick / k];
+                const float sx = xscale[tok[t]];
                 const float sg = reinterpret_cast<const float*>(slab + sv.s0)[row];
                 const float su = reinterpret_cast<const float*>(slab + sv.s1)[row];
                 const float g = ((float)v * sx) * sg;
                 const float u = ((float)up * sx) * su;
                 const double hd = ((double)g / (1.0 + exp(-(double)g))) * (double)u;
-                reinterpret_cast<float*>(hbuf)[(int64_t)pick * I + row] = (float)hd;
+                reinterpret_cast<float*>(hbuf)[(int64_t)pk * I + row] = (float)hd;
             } else {
                 const float g = (float)v, u = (float)up;
                 const float h = g / (1.0f + expf(-g)) * u;
-                if constexpr (F == MOE_W_F32) reinterpret_cast<float*>(hbuf)[(int64_t)pick * I + row] = h;
-                else reinterpret_cast<uint16_t*>(hbuf)[(int64_t)pick * I + row] = moe::f32_to_bf16(h);
+                if constexpr (F == MOE_W_F32) reinterpret_cast<float*>(hbuf)[(int64_t)pk * I + row] = h;
+                else reinterpret_cast<uint16_t*>(hbuf)[(int64_t)pk * I + row] = moe::f32_to_bf16(h);
             }
         }
     }
 }
 
-template <int F>
+// Token passes of up to NTMAX tokens; the body is instantiated for the
+// smallest power of two that holds the pass's tokens.
+constexpr int NT_TOP = NTMAX > 4 ? NTMAX : 4;
+#define MOE_NT_DISPATCH(nt, BODY)              \
+    do {                                       \
+        if ((nt) <= 1) { BODY(1); }            \
+        else if ((nt) <= 2) { BODY(2); }       \
+        else if ((nt) <= 4 || NTMAX <= 4) { BODY(4); } \
+        else { BODY(NT_TOP); }                 \
+    } while (0)
+
+// One workgroup per (slot with work, tile of 4 * RPW_GU gate rows and the
+// same up rows); each wave owns RPW_GU gate and RPW_GU up rows.  Waves are
+// independent: no LDS, no barrier.
+template <int F, int NCHG>
 __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __restrict__ act,
-                                                    const float* __restrict__ xscale, int H, int I, int k,
-                                                    const int32_t* __restrict__ slot_off,
+                                                    const float* __restrict__ xscale, const float* __restrict__ xbsum,
+                                                    int H, int I, int k, const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ pair_list,
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, void* __restrict__ hbuf,
                                                     int tiles) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int AB = Fmt<F>::ABYTES;
-    unsigned char* xs = smem;
-    float* bsum = reinterpret_cast<float*>(smem + (size_t)NTMAX * H * AB);
-    __shared__ int32_t pick_ids[NTMAX];
-
+    constexpr int ROWS = 2 * RPW_GU;
     const int a = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     if (a >= *n_active) return;
     const int s = active[a];
-    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
     const int r_base = tile * (4 * RPW_GU) + (threadIdx.x >> 6) * RPW_GU;
+    const int KG = H / Fmt<F>::EPG;
+    const size_t row_bytes = (size_t)KG * 16;
+    RowPtrs<ROWS> rp;
+#pragma unroll
+    for (int r = 0; r < RPW_GU; ++r) {
+        const int row = min(r_base + r, I - 1);
+        rp.w[r] = slab + sv.w0 + row * row_bytes;
+        rp.w[RPW_GU + r] = slab + sv.w1 + row * row_bytes;
+        rp.s[r] = slab + sv.s0 + (size_t)row * KG * 2;
+        rp.s[RPW_GU + r] = slab + sv.s1 + (size_t)row * KG * 2;
+    }
+    const ActRows ar{reinterpret_cast<const unsigned char*>(act), (size_t)H * Fmt<F>::ABYTES, xbsum};
+    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
+    // passes of up to NTMAX tokens (a slot with more tokens re-reads its rows)
     for (int c0 = 0; c0 < ns; c0 += NTMAX) {
         const int nt = min(NTMAX, ns - c0);
-        __syncthreads();
-        stage_rows<F>(xs, bsum, pick_ids, act, pair_list, p0, c0, nt, k, H, true);
-        __syncthreads();
-        switch (pow2_ceil_small(nt)) {
-            case 1: gu_body<F, 1>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
-            case 2: gu_body<F, 2>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
-            case 4: gu_body<F, 4>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
-            default: gu_body<F, 8>(sv, slab, xs, bsum, pick_ids, nt, H, I, k, r_base, xscale, hbuf); break;
-        }
+#define MOE_GU(N) gu_pass<F, N, NCHG>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, k, r_base, xscale, hbuf)
+        MOE_NT_DISPATCH(nt, MOE_GU);
+#undef MOE_GU
     }
 }
 
-template <int F, int NT>
-__device__ __forceinline__ void down_body(const SlabView& sv, const unsigned char* slab, const unsigned char* hs,
-                                          const float* bsum, const int32_t* pick_ids, int nt, int H, int I,
-                                          int r_base, const float* __restrict__ hscale, const float* __restrict__ wts,
-                                          float* __restrict__ part) {
+template <int F, int NT, int NCHG>
+__device__ __forceinline__ void down_pass(const RowPtrs<RPW_DN>& rp, const SlabView& sv, const unsigned char* slab,
+                                          const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
+                                          int H, int I, int r_base, const float* __restrict__ hscale,
+                                          const float* __restrict__ wts, float* __restrict__ part) {
     using Acc = typename Fmt<F>::Acc;
-    constexpr int AB = Fmt<F>::ABYTES;
-    constexpr int EPG = Fmt<F>::EPG;
     constexpr int V = RPW_DN * NT;
     const int lane = threadIdx.x & 63;
-    const int KG = I / EPG;
-    const int64_t row_bytes = (int64_t)KG * 16;
+    int pick[NT];
+    pass_picks<NT>(pair_list, p, nt, pick);
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    for (int c = 0; c < KG; c += 64) {
-        const int g = c + lane;
-        if (g < KG) {
-#pragma unroll
-            for (int r = 0; r < RPW_DN; ++r) {
-                const int row = r_base + r;
-                if (row < H) {
-                    const v4u w = *reinterpret_cast<const v4u*>(slab + sv.w0 + row * row_bytes + (int64_t)g * 16);
-                    float qs = 0.0f;
-                    if constexpr (F == MOE_W_Q4B32)
-                        qs = half_bits_to_f32(
-                            *reinterpret_cast<const uint16_t*>(slab + sv.s0 + ((int64_t)row * KG + g) * 2));
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) {
-                        const unsigned char* xa = hs + (size_t)t * I * AB + (size_t)g * EPG * AB;
-                        const float xsum = F == MOE_W_Q4B32 ? bsum[t * KG + g] : 0.0f;
-                        granule_dot<F>(w, xa, qs, xsum, acc[r * NT + t]);
-                    }
-                }
-            }
-        }
-    }
+    gemv_rows<F, RPW_DN, NT, NCHG>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
     int idx;
     Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
     if (moe::multi_sum_holder<V>(lane)) {
         const int r = idx / NT, t = idx % NT;
         const int row = r_base + r;
         if (row < H && t < nt) {
-            const int pick = pick_ids[t];
+            const int pk = pick[t];
             float o;
             if constexpr (F == MOE_W_W8A8)
-                o = ((float)v * hscale[pick]) * reinterpret_cast<const float*>(slab + sv.s0)[row];
+                o = ((float)v * hscale[pk]) * reinterpret_cast<const float*>(slab + sv.s0)[row];
             else
                 o = (float)v;
-            part[(int64_t)pick * H + row] = wts[pick] * o;
+            part[(int64_t)pk * H + row] = wts[pk] * o;
         }
     }
 }
 
-template <int F>
+template <int F, int NCHG>
 __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* __restrict__ hact,
-                                                      const float* __restrict__ hscale, const float* __restrict__ wts,
+                                                      const float* __restrict__ hscale,
+                                                      const float* __restrict__ hbsum, const float* __restrict__ wts,
                                                       int H, int I, const int32_t* __restrict__ slot_off,
                                                       const int32_t* __restrict__ pair_list,
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, float* __restrict__ part,
                                                       int tiles) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    constexpr int AB = Fmt<F>::ABYTES;
-    unsigned char* hs = smem;
-    float* bsum = reinterpret_cast<float*>(smem + (size_t)NTMAX * I * AB);
-    __shared__ int32_t pick_ids[NTMAX];
-
     const int a = blockIdx.x / tiles, tile = blockIdx.x % tiles;
     if (a >= *n_active) return;
     const int s = active[a];
-    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
     const int r_base = tile * (4 * RPW_DN) + (threadIdx.x >> 6) * RPW_DN;
+    const int KG = I / Fmt<F>::EPG;
+    const size_t row_bytes = (size_t)KG * 16;
+    RowPtrs<RPW_DN> rp;
+#pragma unroll
+    for (int r = 0; r < RPW_DN; ++r) {
+        const int row = min(r_base + r, H - 1);
+        rp.w[r] = slab + sv.w0 + row * row_bytes;
+        rp.s[r] = slab + sv.s0 + (size_t)row * KG * 2;
+    }
+    const ActRows ar{reinterpret_cast<const unsigned char*>(hact), (size_t)I * Fmt<F>::ABYTES, hbsum};
+    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
     for (int c0 = 0; c0 < ns; c0 += NTMAX) {
         const int nt = min(NTMAX, ns - c0);
-        __syncthreads();
-        stage_rows<F>(hs, bsum, pick_ids, hact, pair_list, p0, c0, nt, 1, I, false);
-        __syncthreads();
-        switch (pow2_ceil_small(nt)) {
-            case 1: down_body<F, 1>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
-            case 2: down_body<F, 2>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
-            case 4: down_body<F, 4>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
-            default: down_body<F, 8>(sv, slab, hs, bsum, pick_ids, nt, H, I, r_base, hscale, wts, part); break;
-        }
+#define MOE_DN(N) down_pass<F, N, NCHG>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
+        MOE_NT_DISPATCH(nt, MOE_DN);
+#undef MOE_DN
     }
+}
+
+// Per-block sums of rows of bf16 activations, for 4-bit weights: out[r][b] =
+// sum of row r's inputs 32b .. 32b+31 (fp32, in input order).
+__global__ void __launch_bounds__(256) k_block_sums(const uint16_t* __restrict__ src, int rows, int len,
+                                                    const int32_t* __restrict__ valid, float* __restrict__ out) {
+    const int nb = len / 32;
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (i >= (int64_t)rows * nb) return;
+    const int r = (int)(i / nb), b = (int)(i % nb);
+    if (valid && valid[r] < 0) return;
+    const uint16_t* p = src + (int64_t)r * len + 32 * b;
+    float sum = 0.0f;
+    for (int e = 0; e < 32; ++e) sum += moe::bf16_to_f32(p[e]);
+    out[i] = sum;
 }
 
 // y[t][m] = sum_j part[t*k+j][m] over resident picks, j ascending; +0.0 if none.
@@ -518,22 +562,10 @@ __global__ void __launch_bounds__(256) k_combine(float* __restrict__ y, const fl
     if (i < n) y[i] = y[i] + y_add[i];
 }
 
-// Kernels whose dynamic LDS exceeds 64 KiB must say so before the launch.
-int allow_lds(const void* fn, size_t lds) {
-    if (lds <= 64 * 1024) return MOE_OK;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) {
-            (void)hipGetLastError();
-            return moe_fail(MOE_E_HIP, "moe_ffn_slots: LDS attribute: %s", hipGetErrorString(e));
-        }
-    return MOE_OK;
-}
-
 template <int F>
 int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k, const void* slot_store,
             size_t slab_bytes, int S, int H, int I, float* y, unsigned char* ws, const WsLayout& L,
             const moe_slab_layout_t& lay, hipStream_t st) {
-    constexpr int AB = Fmt<F>::ABYTES;
     const int P = T * k;
     int32_t* slot_off = reinterpret_cast<int32_t*>(ws + L.slot_off);
     int32_t* pair_list = reinterpret_cast<int32_t*>(ws + L.pair_list);
@@ -549,6 +581,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
 
     const void* gu_act = x;
     const float* xscale = nullptr;
+    const float* xbsum = nullptr;
     if constexpr (F == MOE_W_W8A8) {
         int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
         float* xs = reinterpret_cast<float*>(ws + L.xs);
@@ -557,18 +590,27 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         gu_act = xq;
         xscale = xs;
     }
+    if constexpr (F == MOE_W_Q4B32) {
+        float* xbs = reinterpret_cast<float*>(ws + L.xbs);
+        const int64_t n = (int64_t)T * (H / 32);
+        hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           reinterpret_cast<const uint16_t*>(x), T, H, (const int32_t*)nullptr, xbs);
+        if ((rc = moe_check_launch("moe_ffn_slots/block_sums_x"))) return rc;
+        xbsum = xbs;
+    }
 
     SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
     const int tiles_gu = (I + 4 * RPW_GU - 1) / (4 * RPW_GU);
-    size_t lds = (size_t)NTMAX * H * AB + (F == MOE_W_Q4B32 ? (size_t)NTMAX * (H / 32) * 4 : 0);
-    if (lds > 150 * 1024) return moe_fail(MOE_E_SHAPE, "moe_ffn_slots: H=%d too large for the LDS token tile", H);
-    if ((rc = allow_lds(reinterpret_cast<const void*>(&k_gu<F>), lds))) return rc;
-    hipLaunchKernelGGL((k_gu<F>), dim3(S * tiles_gu), dim3(FFN_THREADS), lds, st, gv, gu_act, xscale, H, I, k,
-                       slot_off, pair_list, active, n_active, hbuf, tiles_gu);
+#define MOE_LAUNCH_GU(G)                                                                                       \
+    hipLaunchKernelGGL((k_gu<F, G>), dim3(S * tiles_gu), dim3(FFN_THREADS), 0, st, gv, gu_act, xscale, xbsum, H, \
+                       I, k, slot_off, pair_list, active, n_active, hbuf, tiles_gu)
+    MOE_NCHG_DISPATCH(H / Fmt<F>::EPG, MOE_LAUNCH_GU);
+#undef MOE_LAUNCH_GU
     if ((rc = moe_check_launch("moe_ffn_slots/gate_up"))) return rc;
 
     const void* dn_act = hbuf;
     const float* hscale = nullptr;
+    const float* hbsum = nullptr;
     if constexpr (F == MOE_W_W8A8) {
         int8_t* hq = reinterpret_cast<int8_t*>(ws + L.hq);
         float* hsc = reinterpret_cast<float*>(ws + L.hs);
@@ -577,13 +619,21 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         dn_act = hq;
         hscale = hsc;
     }
+    if constexpr (F == MOE_W_Q4B32) {
+        float* hbs = reinterpret_cast<float*>(ws + L.hbs);
+        const int64_t n = (int64_t)P * (I / 32);
+        hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                           reinterpret_cast<const uint16_t*>(hbuf), P, I, slot_ids, hbs);
+        if ((rc = moe_check_launch("moe_ffn_slots/block_sums_h"))) return rc;
+        hbsum = hbs;
+    }
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
     const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
-    lds = (size_t)NTMAX * I * AB + (F == MOE_W_Q4B32 ? (size_t)NTMAX * (I / 32) * 4 : 0);
-    if (lds > 150 * 1024) return moe_fail(MOE_E_SHAPE, "moe_ffn_slots: I=%d too large for the LDS tile", I);
-    if ((rc = allow_lds(reinterpret_cast<const void*>(&k_down<F>), lds))) return rc;
-    hipLaunchKernelGGL((k_down<F>), dim3(S * tiles_dn), dim3(FFN_THREADS), lds, st, dv, dn_act, hscale, w, H, I,
-                       slot_off, pair_list, active, n_active, part, tiles_dn);
+#define MOE_LAUNCH_DN(G)                                                                                          \
+    hipLaunchKernelGGL((k_down<F, G>), dim3(S * tiles_dn), dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, w, \
+                       H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
+    MOE_NCHG_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
+#undef MOE_LAUNCH_DN
     if ((rc = moe_check_launch("moe_ffn_slots/down"))) return rc;
 
     const int64_t n4 = (int64_t)T * (H / 4);

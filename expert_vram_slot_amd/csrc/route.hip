@@ -14,10 +14,8 @@
 
 namespace {
 
-constexpr int ROUTE_THREADS = 256;           // 4 waves: split over the hidden dimension
+constexpr int ROUTE_THREADS = 256;  // 4 waves
 constexpr int ROUTE_KSPLIT = ROUTE_THREADS / 64;
-constexpr int ROUTE_EJ = 8;                  // experts per lane per chunk (chunk = 512 experts)
-constexpr int ROUTE_ECHUNK = 64 * ROUTE_EJ;
 
 template <int XD>
 __device__ __forceinline__ float load_act(const void* p, int64_t i) {
@@ -61,10 +59,37 @@ __global__ void __launch_bounds__(1024) k_bias_table(const double* __restrict__ 
 
 // ----------------------------------------------------------------- router
 
-// One workgroup routes TB consecutive tokens.  Logits: the 4 waves split the
-// hidden dimension, each lane owns experts lane + 64 j of a 512-expert chunk,
-// fp64 partial sums are combined wave 0 + 1 + 2 + 3 in that order.  Top-k:
-// one wave per token, k rounds of a wave arg-max on (score desc, id asc).
+using v4u = uint32_t __attribute__((ext_vector_type(4)));
+
+// router rows (experts) per wave per pass: fewer when several tokens share a pass
+template <int TB>
+constexpr int route_rows() { return TB >= 4 ? 8 : 16; }
+
+// Widen one 16-byte granule of the gate row to doubles (exact).
+template <int XD>
+__device__ __forceinline__ void widen(const v4u& g, double (&d)[XD == MOE_X_F32 ? 4 : 8]) {
+    if constexpr (XD == MOE_X_F32) {
+        d[0] = __uint_as_float(g.x);
+        d[1] = __uint_as_float(g.y);
+        d[2] = __uint_as_float(g.z);
+        d[3] = __uint_as_float(g.w);
+    } else {
+        const uint32_t u[4] = {g.x, g.y, g.z, g.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            d[2 * i] = moe::bf16_lo(u[i]);
+            d[2 * i + 1] = moe::bf16_hi(u[i]);
+        }
+    }
+}
+
+// One workgroup routes TB consecutive tokens.  Logits: G is [E][H]; each wave
+// takes ROUTE_RW expert rows per pass, its lanes read consecutive 16-byte
+// granules of a row, the tokens sit in LDS widened to double, partial sums
+// are fp64 FMAs reduced across the wave in one multi-value butterfly (fixed
+// order), then rounded once to fp32.  Top-k: one wave per token, k rounds of
+// a wave arg-max on (score desc, id asc).  Softmax of the raw logits over the
+// picks in double.
 template <int XD, int TB>
 __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict__ x, const void* __restrict__ G,
                                                          const float* __restrict__ bias,
@@ -72,75 +97,71 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
                                                          int k, int32_t* __restrict__ ids, float* __restrict__ w,
                                                          float* __restrict__ logits) {
     extern __shared__ __align__(16) unsigned char smem[];
-    const int xbytes = XD == MOE_X_F32 ? 4 : 2;
-    // x tile, transposed [H][TB]; partial sums [TB][512] double; logits [TB][E] float
-    unsigned char* xs = smem;
-    double* part = reinterpret_cast<double*>(smem + (((size_t)H * TB * xbytes + 15) & ~(size_t)15));
-    float* zl = reinterpret_cast<float*>(part + TB * ROUTE_ECHUNK);
+    constexpr int EPG = XD == MOE_X_F32 ? 4 : 8;  // elements per 16-byte granule
+    constexpr int ROUTE_RW = route_rows<TB>();
+    constexpr int V = ROUTE_RW * TB;
+    double* xd = reinterpret_cast<double*>(smem);               // [TB][H]
+    float* zl = reinterpret_cast<float*>(xd + (size_t)TB * H);  // [TB][E]
 
     const int t0 = blockIdx.x * TB;
     const int nt = min(TB, T - t0);
     const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
 
-    for (int i = threadIdx.x; i < H * TB; i += ROUTE_THREADS) {
-        const int h = i / TB, t = i % TB;
-        if constexpr (XD == MOE_X_F32) {
-            reinterpret_cast<float*>(xs)[i] = t < nt ? reinterpret_cast<const float*>(x)[(int64_t)(t0 + t) * H + h] : 0.f;
-        } else {
-            reinterpret_cast<uint16_t*>(xs)[i] =
-                t < nt ? reinterpret_cast<const uint16_t*>(x)[(int64_t)(t0 + t) * H + h] : (uint16_t)0;
+    for (int i = threadIdx.x; i < TB * H; i += ROUTE_THREADS) {
+        const int t = i / H, h = i % H;
+        xd[i] = t < nt ? (double)load_act<XD>(x, (int64_t)(t0 + t) * H + h) : 0.0;
+    }
+    __syncthreads();
+
+    const int KG = H / EPG;
+    const int nfull = KG >> 6, tail = KG & 63;
+    const size_t row_bytes = (size_t)KG * 16;
+    const unsigned char* Gb = reinterpret_cast<const unsigned char*>(G);
+    for (int e0 = 0; e0 < E; e0 += ROUTE_KSPLIT * ROUTE_RW) {
+        const int ebase = e0 + wv * ROUTE_RW;
+        double acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0.0;
+        for (int c = 0; c <= nfull; ++c) {
+            if (c == nfull && tail == 0) break;
+            const bool last = c == nfull;
+            const int g = (c << 6) + (last ? min(lane, tail - 1) : lane);
+            const bool on = !last || lane < tail;
+            v4u gr[ROUTE_RW];
+#pragma unroll
+            for (int r = 0; r < ROUTE_RW; ++r) {
+                const int e = min(ebase + r, E - 1);  // rows past E are computed on a valid row and dropped
+                gr[r] = *reinterpret_cast<const v4u*>(Gb + e * row_bytes + (size_t)g * 16);
+                if (!on) gr[r] = v4u{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                double xv[EPG];
+#pragma unroll
+                for (int i = 0; i < EPG; ++i) xv[i] = xd[(size_t)t * H + (size_t)g * EPG + i];
+#pragma unroll
+                for (int r = 0; r < ROUTE_RW; ++r) {
+                    double gd[EPG];
+                    widen<XD>(gr[r], gd);
+                    double a = acc[r * TB + t];
+#pragma unroll
+                    for (int i = 0; i < EPG; ++i) a = fma(xv[i], gd[i], a);
+                    acc[r * TB + t] = a;
+                }
+            }
+        }
+        int idx;
+        const double v = moe::wave_multi_sum<V>(acc, lane, idx);
+        if (moe::multi_sum_holder<V>(lane)) {
+            const int r = idx / TB, t = idx % TB;
+            const int e = ebase + r;
+            if (e < E && t < nt) zl[t * E + e] = (float)v;
         }
     }
     __syncthreads();
 
-    const int hper = (H + ROUTE_KSPLIT - 1) / ROUTE_KSPLIT;
-    const int h0 = wv * hper, h1 = min(H, h0 + hper);
-    for (int ec = 0; ec < E; ec += ROUTE_ECHUNK) {
-        double acc[TB][ROUTE_EJ];
-#pragma unroll
-        for (int t = 0; t < TB; ++t)
-#pragma unroll
-            for (int j = 0; j < ROUTE_EJ; ++j) acc[t][j] = 0.0;
-        for (int h = h0; h < h1; ++h) {
-            double xv[TB];
-#pragma unroll
-            for (int t = 0; t < TB; ++t) {
-                if constexpr (XD == MOE_X_F32) xv[t] = reinterpret_cast<const float*>(xs)[h * TB + t];
-                else xv[t] = moe::bf16_to_f32(reinterpret_cast<const uint16_t*>(xs)[h * TB + t]);
-            }
-#pragma unroll
-            for (int j = 0; j < ROUTE_EJ; ++j) {
-                const int e = ec + lane + 64 * j;
-                if (e < E) {
-                    const double g = load_act<XD>(G, (int64_t)h * E + e);
-#pragma unroll
-                    for (int t = 0; t < TB; ++t) acc[t][j] = fma(xv[t], g, acc[t][j]);
-                }
-            }
-        }
-        // fixed-order combination of the 4 partial sums
-        for (int ww = 0; ww < ROUTE_KSPLIT; ++ww) {
-            if (wv == ww) {
-#pragma unroll
-                for (int t = 0; t < TB; ++t)
-#pragma unroll
-                    for (int j = 0; j < ROUTE_EJ; ++j) {
-                        double* p = &part[t * ROUTE_ECHUNK + lane + 64 * j];
-                        *p = ww == 0 ? acc[t][j] : *p + acc[t][j];
-                    }
-            }
-            __syncthreads();
-        }
-        for (int i = threadIdx.x; i < TB * ROUTE_ECHUNK; i += ROUTE_THREADS) {
-            const int t = i / ROUTE_ECHUNK, e = ec + i % ROUTE_ECHUNK;
-            if (e < E) zl[t * E + e] = (float)part[i];
-        }
-        __syncthreads();
-    }
-
     if (logits) {
-        for (int i = threadIdx.x; i < nt * E; i += ROUTE_THREADS)
-            logits[(int64_t)t0 * E + i] = zl[i];
+        for (int i = threadIdx.x; i < nt * E; i += ROUTE_THREADS) logits[(int64_t)t0 * E + i] = zl[i];
     }
 
     // one wave per token
@@ -150,7 +171,6 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
         if (ids_in) {
             if (lane < k) pick = ids_in[(int64_t)(t0 + t) * k + lane];
         } else {
-            // scores of this lane's experts; taken experts become -inf (never re-picked)
             uint64_t taken = 0;  // bit j: expert lane + 64 j already picked (E <= 4096)
             for (int r = 0; r < k; ++r) {
                 float best = -INFINITY;
@@ -158,24 +178,30 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
                 for (int j = 0; lane + 64 * j < E; ++j) {
                     if (taken >> j & 1) continue;
                     const int e = lane + 64 * j;
-                    float s = z[e];
-                    if (bias) s = s + bias[e];
-                    if (s > best || (s == best && e < be)) { best = s; be = e; }
+                    float sc = z[e];
+                    if (bias) sc = sc + bias[e];
+                    if (sc > best || (sc == best && e < be)) {
+                        best = sc;
+                        be = e;
+                    }
                 }
 #pragma unroll
                 for (int sft = 32; sft >= 1; sft >>= 1) {
                     const float ob = __shfl_xor(best, sft, 64);
                     const int oe = __shfl_xor(be, sft, 64);
-                    if (ob > best || (ob == best && oe < be)) { best = ob; be = oe; }
+                    if (ob > best || (ob == best && oe < be)) {
+                        best = ob;
+                        be = oe;
+                    }
                 }
                 if (lane == (be & 63)) taken |= 1ull << (be >> 6);
                 if (lane == r) pick = be;
             }
             if (lane < k) ids[(int64_t)(t0 + t) * k + lane] = pick;
         }
-        // softmax of the raw logits over the picks, in double
-        // externally given picks are trusted to lie in [0, E); clamp only to keep the read in bounds
-        double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
+        // softmax of the raw logits over the picks, in double; externally given
+        // picks are trusted to lie in [0, E), clamped only to keep the read in bounds
+        const double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
         double m = zj;
 #pragma unroll
         for (int sft = 32; sft >= 1; sft >>= 1) m = fmax(m, __shfl_xor(m, sft, 64));
@@ -188,9 +214,7 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
 template <int XD, int TB>
 int launch_route(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
                  int32_t* ids, float* w, float* logits, hipStream_t s) {
-    const int xbytes = XD == MOE_X_F32 ? 4 : 2;
-    const size_t lds = (((size_t)H * TB * xbytes + 15) & ~(size_t)15) + sizeof(double) * TB * ROUTE_ECHUNK +
-                       sizeof(float) * TB * E;
+    const size_t lds = sizeof(double) * TB * H + sizeof(float) * TB * E;
     if (lds > 160 * 1024) return moe_fail(MOE_E_SHAPE, "moe_route: H=%d E=%d need %zu B of LDS", H, E, lds);
     const int grid = (T + TB - 1) / TB;
     if (lds > 64 * 1024) {
@@ -209,13 +233,11 @@ int launch_route(const void* x, const void* G, const float* bias, const int32_t*
 template <int XD>
 int route_dispatch(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
                    int32_t* ids, float* w, float* logits, hipStream_t s) {
-    const int xbytes = XD == MOE_X_F32 ? 4 : 2;
     // small batches: one token per workgroup (more workgroups, lower latency);
     // large batches: several tokens share each read of G
-    int tb = T <= 256 ? 1 : 8;
-    while (tb > 1 && ((size_t)H * tb * xbytes > 64 * 1024 || (size_t)E * tb * 4 > 32 * 1024)) tb >>= 1;
+    int tb = T <= 64 ? 1 : 4;
+    while (tb > 1 && sizeof(double) * tb * H + sizeof(float) * tb * E > 80 * 1024) tb >>= 1;
     switch (tb) {
-        case 8: return launch_route<XD, 8>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
         case 4: return launch_route<XD, 4>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
         case 2: return launch_route<XD, 2>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
         default: return launch_route<XD, 1>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
@@ -245,6 +267,9 @@ int moe_route(const void* x, int x_dtype, const void* G, const float* bias, cons
     MOE_REQUIRE(k <= E && k <= MOE_MAX_K && E <= MOE_MAX_E, MOE_E_SHAPE,
                 "moe_route: need k=%d <= E=%d, k <= %d, E <= %d", k, E, MOE_MAX_K, MOE_MAX_E);
     if (T == 0) return moe_ok();
+    MOE_REQUIRE(moe_aligned16(x) && moe_aligned16(G), MOE_E_ALIGN, "moe_route: x and G must be 16-byte aligned");
+    MOE_REQUIRE(H % (x_dtype == MOE_X_F32 ? 4 : 8) == 0, MOE_E_ALIGN,
+                "moe_route: H=%d must fill whole 16-byte granules", H);
     if (x_dtype == MOE_X_F32) return route_dispatch<MOE_X_F32>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, stream);
     if (x_dtype == MOE_X_BF16) return route_dispatch<MOE_X_BF16>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, stream);
     return moe_fail(MOE_E_DTYPE, "moe_route: unknown activation format %d", x_dtype);

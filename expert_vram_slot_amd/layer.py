@@ -73,6 +73,7 @@ class SlotLayer:
         self.side = torch.cuda.Stream(device=dev)
         self.copy = torch.cuda.Stream(device=dev)
         self.pool = cf.ThreadPoolExecutor(max_workers=1)
+        self.ffn_events = None  # (start, end) torch events recorded around moe_ffn_slots when set
 
     def init_cache(self, resident=None):
         cache_init(self.st, resident)
@@ -108,16 +109,21 @@ class SlotLayer:
                 ev_copy = torch.cuda.Event()
                 ev_copy.record(self.copy)
             fut = self.pool.submit(self._host_pass, ev_copy, T)
-        # 3b. gather on the side stream (no-op when nothing missed)
+        # 3b. gather on the side stream (a static cache never loads while running)
         if self.policy != 0 and self.S > 0:
             self.side.wait_event(ev_manage)
             cache_gather(self.miss, self.n_miss, self.S, self.host_store, self.slot_store, self.slab, self.side)
             ev_g = torch.cuda.Event()
             ev_g.record(self.side)
             cur.wait_event(ev_g)
-        # 4. expert FFN over resident slots (zero for the rest)
+        # 4. expert FFN over resident slots (zero for the rest); optional timing events around it
+        ev = getattr(self, "ffn_events", None)
+        if ev:
+            ev[0].record(cur)
         moe_ffn_slots(x, self.x_dtype, self.slot_ids, self.w, T, self.k, self.slot_store, self.slab, max(self.S, 1),
                       self.w_type, self.H, self.I, self.y, self.ws, self.ws_bytes, cur)
+        if ev:
+            ev[1].record(cur)
         # 5. the single add joining the two passes
         if fut is not None:
             fut.result()

@@ -45,7 +45,7 @@
  *   - Identical inputs give bit-identical outputs (fixed reduction orders, no
  *     floating-point atomics).
  *   - Weights are row-major [out][in]: gate Wg[I][H], up Wu[I][H], down
- *     Wd[H][I]; router gate G[H][E].
+ *     Wd[H][I]; router gate G[E][H].
  */
 #ifndef MOE_SLOT_H
 #define MOE_SLOT_H
@@ -146,7 +146,7 @@ int moe_bias_table(const double* b, int E, int n_hot, float cap, float* bias, hi
 
 /* Router, [PGO] "The method in five lines".
  *   x       device [T][H] in x_dtype
- *   G       device [H][E] in x_dtype
+ *   G       device [E][H] in x_dtype (one row per expert)
  *   bias    device float[E] or NULL.  NULL gives exactly the plain top-k of
  *           the logits (the bias is opt-in).
  *   ids_in  device int32[T][k] or NULL.  If given, the picks are taken as is

@@ -95,7 +95,8 @@ def logits(x, x_dtype, G):
     x = _xarr(x, x_dtype)
     G = _xarr(G, x_dtype)
     T, H = x.shape
-    E = G.shape[1]
+    E = G.shape[0]
+    assert G.shape == (E, H)
     z = np.empty((T, E), np.float32)
     _check(lib().oracle_logits(_p(x), x_dtype, _p(G), T, H, E, _p(z)), "logits")
     return z

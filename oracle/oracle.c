@@ -143,14 +143,15 @@ static double x_value(const void* x, int x_dtype, int64_t i) {
 
 /* Router logits.  [PGO] "The method in five lines" picks top-k by the
  * router's logit; the logit is the plain product of the token with the gate
- * matrix G[H][E], summed in double and rounded once to fp32. */
+ * matrix G[E][H] (one row per expert, like every weight stored [out][in]),
+ * summed in double and rounded once to fp32. */
 int oracle_logits(const void* x, int x_dtype, const void* G, int T, int H, int E, float* z) {
     if (T < 0 || H <= 0 || E <= 0) return -1;
     for (int t = 0; t < T; ++t)
         for (int e = 0; e < E; ++e) {
             double acc = 0.0;
             for (int h = 0; h < H; ++h)
-                acc += x_value(x, x_dtype, (int64_t)t * H + h) * x_value(G, x_dtype, (int64_t)h * E + e);
+                acc += x_value(x, x_dtype, (int64_t)t * H + h) * x_value(G, x_dtype, (int64_t)e * H + h);
             z[(int64_t)t * E + e] = (float)acc;
         }
     return 0;

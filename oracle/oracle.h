@@ -35,7 +35,7 @@ int64_t oracle_slab_bytes(int w_type, int H, int I);
  * wg, wu: [I][H]; wd: [H][I]. */
 int oracle_decode_expert(int w_type, const uint8_t* slab, int H, int I, float* wg, float* wu, float* wd);
 
-/* z[t][e] = sum_h x[t][h] G[h][e], accumulated in double, rounded once. */
+/* z[t][e] = sum_h x[t][h] G[e][h], accumulated in double, rounded once. */
 int oracle_logits(const void* x, int x_dtype, const void* G, int T, int H, int E, float* z);
 
 /* Graded selection bias of one layer ([PGO] "The method in five lines"). */

@@ -182,7 +182,8 @@ class LayerInputs:
         self.slab = slab_bytes(self.w_type, self.H, self.I)
         # activations: a fresh batch per (layer, step); expert index slot carries the step
         self.x = normal(key(self.base, TAG_X, layer, step), (self.T, self.H), 1.0, self.x_dtype)
-        self.G = normal(key(self.base, TAG_G, layer, 0), (self.H, self.E), c["sigma_g"], self.x_dtype)
+        # router gate, one row per expert ([out][in] like every weight)
+        self.G = normal(key(self.base, TAG_G, layer, 0), (self.E, self.H), c["sigma_g"], self.x_dtype)
         self.store = slabs(self.w_type, self.base, layer, 0, self.E, self.H, self.I, c["sigma_w"]) if with_store else None
 
     def x_f32(self) -> np.ndarray:

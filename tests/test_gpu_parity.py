@@ -123,8 +123,8 @@ def test_route_ties_go_to_lower_id(m):
     # integer-valued logits with many ties: G picks one column pattern
     T, H, E, k = 8, 16, 64, 6
     x = np.ones((T, H), np.float32)
-    G = np.zeros((H, E), np.float32)
-    G[0, :] = np.arange(E) % 5  # five distinct logit values, many ties
+    G = np.zeros((E, H), np.float32)
+    G[:, 0] = np.arange(E) % 5  # five distinct logit values, many ties
     li = type("L", (), dict(T=T, H=H, E=E, k=k, x=x, G=G, x_dtype=0))
     ids, w, z = gpu_route(m, li)
     np.testing.assert_array_equal(ids, oracle.topk(z, k))

@@ -128,15 +128,15 @@ def test_slab_sizes_match_page_numbers():
 def test_logits_exact_on_small_integers():
     T, H, E = 5, 48, 7
     x = rng.integers(-3, 4, size=(T, H)).astype(np.float32)
-    G = rng.integers(-3, 4, size=(H, E)).astype(np.float32)
+    G = rng.integers(-3, 4, size=(E, H)).astype(np.float32)
     z = oracle.logits(x, 0, G)
-    np.testing.assert_array_equal(z, (x.astype(np.int64) @ G.astype(np.int64)).astype(np.float32))
+    np.testing.assert_array_equal(z, (x.astype(np.int64) @ G.astype(np.int64).T).astype(np.float32))
 
 
 def test_logits_bf16_against_numpy_float64():
     li = synth.LayerInputs("c2", T=6, with_store=False)
     z = oracle.logits(li.x, 1, li.G)
-    ref = (li.x_f32().astype(np.float64) @ li.G_f32().astype(np.float64)).astype(np.float32)
+    ref = (li.x_f32().astype(np.float64) @ li.G_f32().astype(np.float64).T).astype(np.float32)
     ulp = np.spacing(np.abs(ref))
     diff = np.abs(z - ref)
     assert np.all(diff <= ulp)
