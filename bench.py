@@ -34,6 +34,12 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 
+# kernels launched by one moe_ffn_slots call on the bf16 decode path
+FFN_KERNELS = ("k_group", "k_gu", "k_down", "k_reduce")
+# source files whose change invalidates stored HBM counter readings of those kernels
+FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/common.hpp")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -48,11 +54,20 @@ def parse():
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
+    ap.add_argument("--summarize", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                     "COPY_WRITE_DIR"),
+                    help="write a text summary of rocprofv3 CSV output (kernel trace + FETCH_SIZE/WRITE_SIZE runs of "
+                         "this benchmark and of --copy-calibration) to --out; no GPU needed")
+    ap.add_argument("--out", default=None, help="summary file for --summarize")
+    ap.add_argument("--commands", default=None, help="text file with the profiling commands, quoted in the summary")
     return ap.parse_args()
 
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(args)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: the expert-slot layer is a single-GPU path here "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
@@ -177,7 +192,7 @@ def main():
                    "global_batch": T, "layers_rotated": args.layers, "host_threads": nthreads,
                    "host_pass": not args.no_host_pass},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(T),
                      "kernel": "moe_ffn_slots (group, gate/up, down, reduce kernels)",
                      "bytes_per_launch": int(np.mean(per_launch)), "ms_per_launch": round(float(np.mean(ffn_ms_arr)), 5),
                      "distinct_slabs_per_step": round(float(np.mean(distinct)), 2)},
@@ -228,19 +243,147 @@ def measure_gather(m, torch, synth):
             "slab_bytes": slab, "slabs_per_call": n, "link": "pinned hipMemcpyAsync H2D"}
 
 
-def cpu_baseline(synth, T):
+def cpu_baseline(synth, T, n_tok=128):
     """The oracle (single-threaded C) on a bounded sample of the same workload:
-    logits, top-k, weights and the full SwiGLU layer for 8 tokens."""
+    logits, top-k, weights and the full SwiGLU layer (every pick, resident or
+    not) for n_tok tokens of the same layer, on one thread."""
     import oracle
-    li = synth.LayerInputs("c2", T=8)
+    li = synth.LayerInputs("c2", T=n_tok)
     t0 = time.perf_counter()
     z = oracle.logits(li.x, li.x_dtype, li.G)
     ids = oracle.topk(z, li.k)
     w = oracle.route_weights(z, ids)
     oracle.layer(li.w_type, li.store, li.E, li.H, li.I, li.x, li.x_dtype, ids, w)
     dt = time.perf_counter() - t0
-    return {"value": round(8 / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "8 tokens of the same layer (route + full SwiGLU layer in double), single thread"}
+    return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{n_tok} tokens of the same layer: route + full SwiGLU layer in double, single thread, "
+                      f"{dt:.1f} s"}
+
+
+# ------------------------------------------------------------ HBM counters
+
+
+def ffn_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in FFN_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profile_path(T):
+    return os.path.join(PROFILE_DIR, f"moe_ffn_slots_bf16_decode_T{T}.txt")
+
+
+def stored_traffic(T):
+    """HBM bytes per moe_ffn_slots launch from the committed counter summary,
+    or None when there is none for this batch or the kernels changed since."""
+    p = profile_path(T)
+    if not os.path.exists(p):
+        return None
+    rec = None
+    with open(p) as fh:
+        for line in fh:
+            if line.startswith("record: "):
+                rec = json.loads(line[len("record: "):])
+    if not rec or rec.get("ffn_source_sha256") != ffn_source_hash() or rec.get("traffic_bytes_per_launch") is None:
+        return None
+    return rec["traffic_bytes_per_launch"]
+
+
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", f"*{suffix}"), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    if not rows:
+        raise SystemExit(f"no *{suffix} under {d}")
+    return rows
+
+
+def _short(name):
+    n = name.split("(")[0] if "::" not in name else name
+    for k in ("k_group", "k_gu", "k_down", "k_reduce", "k_route", "k_manage", "k_gather", "k_combine",
+              "k_quant_rows", "k_block_sums", "k_pick_static", "k_bias_table", "k_cache_init"):
+        if f"::{k}<" in name or f"::{k}(" in name:
+            i = name.index(k)
+            j = name.find("(", i)
+            return name[i:j]
+    return name[:60]
+
+
+def _counter_per_dispatch(rows, counter):
+    """{kernel short name: [per-dispatch value in KiB]} for one counter."""
+    per = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        per.setdefault(_short(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
+    return per
+
+
+def summarize(args):
+    tr, fe, wr, cfe, cwr = args.summarize
+    T = args.batch
+    stats = _csv_rows(tr, "kernel_stats.csv")
+    fetch = _counter_per_dispatch(_csv_rows(fe, "counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_per_dispatch(_csv_rows(wr, "counter_collection.csv"), "WRITE_SIZE")
+    cfetch = _counter_per_dispatch(_csv_rows(cfe, "counter_collection.csv"), "FETCH_SIZE")
+    cwrite = _counter_per_dispatch(_csv_rows(cwr, "counter_collection.csv"), "WRITE_SIZE")
+
+    def copy_kib(per):
+        # the copy kernel is the only dispatch of --copy-calibration moving ~1 GiB
+        vals = [v for vs in per.values() for v in vs if v > 100_000]
+        return float(np.median(vals))
+
+    gib_kib = (1 << 30) / 1024.0
+    f_fetch = gib_kib / copy_kib(cfetch)   # bytes the counter misses per unit it reports
+    f_write = gib_kib / copy_kib(cwrite)
+    lines = []
+    lines.append(f"rocprofv3 summary: moe_ffn_slots, bf16 decode layer (E=128 top-8, H=2048, I=768, T={T}, "
+                 f"64 static slots)")
+    lines.append("")
+    if args.commands:
+        lines.append("commands (run from the repository root on one MI355X; TMPDIR=/tmp):")
+        with open(args.commands) as fh:
+            lines.extend("  " + l.rstrip() for l in fh if l.strip())
+        lines.append("")
+    lines.append("kernel trace (--kernel-trace --stats), all dispatches of the run:")
+    lines.append(f"  {'kernel':<28}{'calls':>7}{'avg us':>10}{'min us':>10}{'max us':>10}")
+    ffn_avg = 0.0
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
+        nm = _short(r["Name"])
+        avg = float(r["AverageNs"]) / 1e3
+        lines.append(f"  {nm:<28}{int(r['Calls']):>7}{avg:>10.2f}{float(r['MinNs']) / 1e3:>10.2f}"
+                     f"{float(r['MaxNs']) / 1e3:>10.2f}")
+        if nm.split("<")[0] in FFN_KERNELS:
+            ffn_avg += avg
+    lines.append(f"  sum of averages of the moe_ffn_slots kernels ({', '.join(FFN_KERNELS)}): {ffn_avg:.2f} us")
+    lines.append("")
+    lines.append(f"HBM counters (KiB per dispatch, mean over dispatches; calibration: a 1 GiB copy reads "
+                 f"FETCH_SIZE {copy_kib(cfetch):.0f} KiB, WRITE_SIZE {copy_kib(cwrite):.0f} KiB, so factors "
+                 f"{f_fetch:.3f} and {f_write:.3f}):")
+    lines.append(f"  {'kernel':<28}{'n':>5}{'FETCH KiB':>14}{'WRITE KiB':>14}{'scaled MB':>12}")
+    traffic = 0.0
+    for nm in sorted(set(fetch) | set(write)):
+        fv, wv = fetch.get(nm, [0.0]), write.get(nm, [0.0])
+        scaled = (np.mean(fv) * f_fetch + np.mean(wv) * f_write) * 1024
+        lines.append(f"  {nm:<28}{len(fv):>5}{np.mean(fv):>14.1f}{np.mean(wv):>14.1f}{scaled / 1e6:>12.2f}")
+        if nm.split("<")[0] in FFN_KERNELS:
+            traffic += scaled
+    lines.append(f"  moe_ffn_slots per launch (sum over its kernels): {traffic / 1e6:.2f} MB")
+    rec = {"batch": T, "ffn_source_sha256": ffn_source_hash(), "ffn_kernels_avg_us": round(ffn_avg, 3),
+           "traffic_bytes_per_launch": int(traffic), "fetch_factor": round(f_fetch, 4),
+           "write_factor": round(f_write, 4)}
+    lines.append("")
+    lines.append("record: " + json.dumps(rec))
+    out = args.out or profile_path(T)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
 
 
 if __name__ == "__main__":
