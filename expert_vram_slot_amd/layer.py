@@ -8,10 +8,15 @@ work in one unbroken run, all CPU work in another, one add at the end;
 "Porting vllm-expert-cache to NVIDIA GPUs": manage, gather, remap, expert
 FFN over slot space):
 
-  compute stream  moe_route -> cache_manage -> moe_ffn_slots -> moe_combine
-  side stream                    `-> cache_gather --^ (event)
-  copy stream     x, ids, slot_ids, w -> pinned host      (event)
-  CPU thread                       `-> moe_ffn_host_misses -> y_host
+  compute stream  moe_route -> cache_manage -> moe_ffn_slots ........ -> moe_combine
+  side stream                    `-> cache_gather --^ (event)              ^
+  copy stream     x -> host          `-> ids|slot_ids|w -> host (event)    |
+  CPU thread                                  `-> moe_ffn_host_misses -> y_host
+
+The GPU work is queued first and back to back (the CPU runs ahead of it), so
+the device never waits for the host between the router and the FFN; the
+host pass's inputs leave in two copies (x, and one packed block holding the
+picks, their slots and their weights).
 """
 from __future__ import annotations
 
@@ -44,10 +49,13 @@ class SlotLayer:
         self.G, self.bias = G, bias
         self.n_threads = n_threads or host_threads()
         P = T_max * k
+        self.P_max = P
         i32 = dict(dtype=torch.int32, device=dev)
-        self.ids = torch.empty(P, **i32)
-        self.slot_ids = torch.empty(P, **i32)
-        self.w = torch.empty(P, dtype=torch.float32, device=dev)
+        # picks, their slots and their weights in one block (one copy to the host)
+        self.meta = torch.empty(3 * P, **i32)
+        self.ids = self.meta[:P]
+        self.slot_ids = self.meta[P:2 * P]
+        self.w = self.meta[2 * P:].view(torch.float32)
         self.miss = torch.empty(2 * max(S, 1), **i32)
         self.n_miss = torch.zeros(1, **i32)
         self.host_miss = torch.empty(E, **i32)
@@ -66,9 +74,10 @@ class SlotLayer:
         xb = 4 if self.x_dtype == MOE_X_F32 else 2
         pin = dict(pin_memory=True)
         self.h_x = torch.empty(T_max * H * xb, dtype=torch.uint8, **pin)
-        self.h_ids = torch.empty(P, dtype=torch.int32, **pin)
-        self.h_slot = torch.empty(P, dtype=torch.int32, **pin)
-        self.h_w = torch.empty(P, dtype=torch.float32, **pin)
+        self.h_meta = torch.empty(3 * P, dtype=torch.int32, **pin)
+        self.h_ids = self.h_meta[:P]
+        self.h_slot = self.h_meta[P:2 * P]
+        self.h_w = self.h_meta[2 * P:].view(torch.float32)
         self.h_y = torch.empty(T_max * H, dtype=torch.float32, **pin)
         self.side = torch.cuda.Stream(device=dev)
         self.copy = torch.cuda.Stream(device=dev)
@@ -88,28 +97,25 @@ class SlotLayer:
         assert T <= self.T_max
         cur = torch.cuda.current_stream()
         P = T * self.k
+        if host_pass:
+            # 0. the host pass's activations leave while the router runs
+            self.copy.wait_stream(cur)
+            with torch.cuda.stream(self.copy):
+                nx = x.numel() * x.element_size()
+                self.h_x[:nx].copy_(x.reshape(-1).view(torch.uint8), non_blocking=True)
+        if ids_in is not None:
+            # given picks are copied into the packed block (the host pass reads them from there)
+            self.ids[:P].copy_(ids_in.reshape(-1)[:P], non_blocking=True)
         # 1. router (picks, or weights of given picks)
-        moe_route(x, self.x_dtype, self.G, self.bias, ids_in, T, self.H, self.E, self.k, self.ids, self.w, None, cur)
-        ids = self.ids if ids_in is None else ids_in
+        moe_route(x, self.x_dtype, self.G, self.bias, None if ids_in is None else self.ids, T, self.H, self.E,
+                  self.k, self.ids, self.w, None, cur)
+        ids = self.ids
         # 2. cache step: victims, miss list, remap
         cache_manage(self.st, self.policy, ids, P, self.slot_ids, self.miss, self.n_miss, self.host_miss,
                      self.n_host, self.stats, cur)
         ev_manage = torch.cuda.Event()
         ev_manage.record(cur)
-        fut = None
-        if host_pass:
-            # 3a. inputs of the host pass to pinned memory on the copy stream
-            self.copy.wait_event(ev_manage)
-            with torch.cuda.stream(self.copy):
-                nx = x.numel() * x.element_size()
-                self.h_x[:nx].copy_(x.reshape(-1).view(torch.uint8), non_blocking=True)
-                self.h_ids[:P].copy_(ids.reshape(-1)[:P], non_blocking=True)
-                self.h_slot[:P].copy_(self.slot_ids[:P], non_blocking=True)
-                self.h_w[:P].copy_(self.w[:P], non_blocking=True)
-                ev_copy = torch.cuda.Event()
-                ev_copy.record(self.copy)
-            fut = self.pool.submit(self._host_pass, ev_copy, T)
-        # 3b. gather on the side stream (a static cache never loads while running)
+        # 3. gather on the side stream (a static cache never loads while running)
         if self.policy != 0 and self.S > 0:
             self.side.wait_event(ev_manage)
             cache_gather(self.miss, self.n_miss, self.S, self.host_store, self.slot_store, self.slab, self.side)
@@ -124,8 +130,15 @@ class SlotLayer:
                       self.w_type, self.H, self.I, self.y, self.ws, self.ws_bytes, cur)
         if ev:
             ev[1].record(cur)
-        # 5. the single add joining the two passes
-        if fut is not None:
+        if host_pass:
+            # 5. picks, slots and weights to pinned memory (one copy), then the host pass on CPU threads
+            self.copy.wait_event(ev_manage)
+            with torch.cuda.stream(self.copy):
+                self.h_meta.copy_(self.meta, non_blocking=True)
+                ev_copy = torch.cuda.Event()
+                ev_copy.record(self.copy)
+            fut = self.pool.submit(self._host_pass, ev_copy, T)
+            # 6. the single add joining the two passes
             fut.result()
             self.y_host_dev[:T * self.H].copy_(self.h_y[:T * self.H], non_blocking=True)
             moe_combine(self.y, self.y_host_dev, T, self.H, cur)

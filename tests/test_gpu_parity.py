@@ -306,6 +306,40 @@ def test_ffn_ragged_shapes(m, w_type, H, I):
     assert_close(y, yg, w_type, f"w{w_type} H={H} I={I}")
 
 
+@pytest.mark.parametrize("w_type", [1, 2])
+def test_ffn_large_batch_sorted_picks(m, w_type):
+    """T*k above the in-workgroup pick scan: the picks go through the sorting kernel first."""
+    E, k, T, S, H, I = 12, 3, 401, 7, 112, 144
+    rng = np.random.default_rng(17 + w_type)
+    x = synth.normal(synth.key(99, 1, w_type), (T, H), 1.0, 1)
+    store = synth.slabs(w_type, 4321, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=w_type, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(w_type, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, w_type, f"w{w_type} T={T} k={k}")
+
+
+def test_ffn_workspace_reused_across_calls(m):
+    """One workspace for consecutive calls of different sizes (its counters clear themselves)."""
+    big = ffn_case(m, "c2", 64)
+    small = ffn_case(m, "c2", 8, step=3)
+    S = 64
+    ws_bytes = m.moe_ffn_workspace_bytes(64, 8, S, 1, 2048, 768)
+    ws = torch.full((ws_bytes,), 0xAB, dtype=torch.uint8, device="cuda")
+    for li, ids, w, sl, _, yg, _, slots in (big, small, big):
+        x = dev(li.x.view(np.int16))
+        y = torch.full((li.T, li.H), np.nan, dtype=torch.float32, device="cuda")
+        m.moe_ffn_slots(x, 1, dev(sl.astype(np.int32)), dev(w), li.T, li.k, slots, li.slab, S, 1, li.H, li.I, y,
+                        ws, ws_bytes)
+        assert_close(host(y), yg, 1, f"reused workspace T={li.T}")
+
+
 def test_ffn_many_tokens_on_one_slot(m):
     """More tokens on a slot than one pass holds (token chunks of 8)."""
     li = synth.LayerInputs("c2", T=37)
