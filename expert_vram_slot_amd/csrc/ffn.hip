@@ -26,6 +26,7 @@
 #include <math.h>
 
 #include "common.hpp"
+#include "prefill.hpp"
 
 namespace {
 
@@ -37,6 +38,8 @@ constexpr int NTMAX = 8;       // tokens of one slot handled per pass
 constexpr int RPW_GU = 1;      // gate rows (and as many up rows) per wave
 constexpr int RPW_DN = 4;      // down rows per wave
 constexpr int GROUP_THREADS = 1024;
+// bf16 batches with at least this many picks take the MFMA grouped-GEMM path
+constexpr int PF_MIN_P = 2048;
 
 // ------------------------------------------------------------ formats
 
@@ -127,7 +130,7 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) { return (float)__
 // ---------------------------------------------------------- workspace
 
 struct WsLayout {
-    size_t slot_off, pair_list, active, n_active, h, hq, hs, xq, xs, xbs, hbs, part, total;
+    size_t slot_off, pair_list, active, n_active, pf_tiles, h, hq, hs, xq, xs, xbs, hbs, part, total;
 };
 
 WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
@@ -143,6 +146,7 @@ WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
     L.pair_list = take(4 * (P ? P : 1));
     L.active = take(4 * (size_t)S);
     L.n_active = take(16);
+    L.pf_tiles = take(moe_pf_tiles_bytes(T, k, S));
     const size_t hb = (w_type == MOE_W_BF16 || w_type == MOE_W_Q4B32) ? 2 : 4;
     L.h = take(hb * P * I);
     if (w_type == MOE_W_W8A8) {
@@ -578,6 +582,16 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
                        n_active);
     if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
+
+    if (F == MOE_W_BF16 && P >= PF_MIN_P && moe_pf_supported(F, H, I)) {
+        rc = moe_pf_run(x, w, T, k, slot_store, slab_bytes, S, H, I, lay, slot_off, pair_list, active, n_active,
+                        ws + L.pf_tiles, hbuf, part, st);
+        if (rc) return rc;
+        const int64_t n4 = (int64_t)T * (H / 4);
+        hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, slot_ids, T, k, S,
+                           H, y);
+        return moe_check_launch("moe_ffn_slots/reduce");
+    }
 
     const void* gu_act = x;
     const float* xscale = nullptr;

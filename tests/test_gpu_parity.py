@@ -5,6 +5,8 @@ bytes bit-exact; outputs within |d| <= rtol*|ref| + atol, with (rtol, atol)
 = (1e-5, 1e-5*rms) for fp32, (2e-2, 1e-2) for bf16 and (3e-2, 3e-2*rms) for
 int8 and 4-bit weights.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -338,6 +340,65 @@ def test_ffn_workspace_reused_across_calls(m):
         m.moe_ffn_slots(x, 1, dev(sl.astype(np.int32)), dev(w), li.T, li.k, slots, li.slab, S, 1, li.H, li.I, y,
                         ws, ws_bytes)
         assert_close(host(y), yg, 1, f"reused workspace T={li.T}")
+
+
+@pytest.mark.parametrize("T,S", [(300, 20), (257, 24), (1000, 17)])
+def test_ffn_prefill_grouped_gemm(m, T, S):
+    """bf16 batches of >= 2048 picks run on the MFMA grouped GEMM: slots with
+    more picks than one 128-row tile, ragged tiles, non-resident experts."""
+    E, k, H, I = 24, 8, 256, 384
+    rng = np.random.default_rng(T + S)
+    x = synth.normal(synth.key(7, 1, T), (T, H), 1.0, 1)
+    store = synth.slabs(1, 555, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(1, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 1, f"prefill T={T} S={S}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+
+
+@functools.lru_cache(maxsize=1)
+def prefill_inputs():
+    """The 288-expert prefill layer's inputs (10.9 GB of slabs), made once per session."""
+    li = synth.LayerInputs("c5")
+    z = oracle.logits(li.x, 1, li.G)
+    ids = oracle.topk(z, li.k)
+    return li, ids, oracle.route_weights(z, ids)
+
+
+@pytest.mark.parametrize("S", [288, 144])
+def test_ffn_prefill_full_size_sampled(m, S):
+    """The 288-expert prefill layer at full size (2048 tokens, hidden 4096,
+    intermediate 1536): all resident, and the 144-slot variant whose misses
+    return zero; sampled tokens against the oracle, the rest by property."""
+    li, ids, w = prefill_inputs()
+    if S == li.E:
+        resident = np.arange(li.E)
+    else:
+        warm = synth.LayerInputs("c5", T=1024, step=10_000, with_store=False)
+        resident = oracle.pick_static(oracle.topk(oracle.logits(warm.x, 1, warm.G), li.k), li.E, S)
+    e2s = np.full(li.E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    y = run_ffn(m, li, sl, w, dev(li.store[resident]), S)
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(S)
+    sample = np.concatenate([[0, li.T - 1], rng.choice(np.arange(1, li.T - 1), 10, replace=False)])
+    for t in sample:
+        ref = np.zeros(li.H)
+        for j in range(li.k):
+            if sl[t, j] >= 0:
+                ref += w[t, j] * oracle.expert(1, li.store[ids[t, j]], li.H, li.I, li.x[t], 1)
+        assert_close(y[t:t + 1], ref[None, :].astype(np.float32), 1, f"prefill S={S} token {t}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0)
 
 
 def test_ffn_many_tokens_on_one_slot(m):
