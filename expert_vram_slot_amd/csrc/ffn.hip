@@ -10,7 +10,10 @@
 // Pipeline (all on the caller's stream, deterministic):
 //   k_group      stable counting sort of the T*k picks by slot (one workgroup,
 //                ballot-matched ranks, no atomics) -> per-slot pick lists and
-//                the list of slots with work
+//                the list of slots with work; above GROUP_MULTI_P picks the
+//                same sort runs over 1024-pick chunks in two launches
+//                (k_group_hist: per-chunk slot counts; k_group_place: offsets
+//                and ranks, one workgroup per chunk)
 //   k_quant_rows (W8A8) int8 codes + scale per token
 //   k_gu         gate and up rows of a slot against the slot's tokens, SwiGLU
 //                epilogue -> h[pick][I]
@@ -38,6 +41,7 @@ constexpr int NTMAX = 8;       // tokens of one slot handled per pass
 constexpr int RPW_GU = 1;      // gate rows (and as many up rows) per wave
 constexpr int RPW_DN = 4;      // down rows per wave
 constexpr int GROUP_THREADS = 1024;
+constexpr int GROUP_MULTI_P = 4096;  // larger batches sort with one workgroup per 1024 picks
 // bf16 batches with at least this many picks take the MFMA grouped-GEMM path
 constexpr int PF_MIN_P = 2048;
 
@@ -130,7 +134,7 @@ __device__ __forceinline__ float half_bits_to_f32(uint16_t h) { return (float)__
 // ---------------------------------------------------------- workspace
 
 struct WsLayout {
-    size_t slot_off, pair_list, active, n_active, pf_tiles, h, hq, hs, xq, xs, xbs, hbs, part, total;
+    size_t slot_off, pair_list, active, n_active, gcnt, pf_tiles, h, hq, hs, xq, xs, xbs, hbs, part, total;
 };
 
 WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
@@ -146,6 +150,7 @@ WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
     L.pair_list = take(4 * (P ? P : 1));
     L.active = take(4 * (size_t)S);
     L.n_active = take(16);
+    L.gcnt = take(P > (size_t)GROUP_MULTI_P ? 4 * ((P + GROUP_THREADS - 1) / GROUP_THREADS) * (size_t)S : 16);
     L.pf_tiles = take(moe_pf_tiles_bytes(T, k, S));
     const size_t hb = (w_type == MOE_W_BF16 || w_type == MOE_W_Q4B32) ? 2 : 4;
     L.h = take(hb * P * I);
@@ -166,6 +171,22 @@ WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
 
 // ---------------------------------------------------------- grouping
 
+// Rank of this lane's pick among the lanes of its wave holding the same slot
+// (lane order), found with one ballot per bit of the slot id; *count gets the
+// number of such lanes.  Lanes with valid == false take part in the ballots
+// only.
+__device__ __forceinline__ int wave_slot_rank(int s, bool valid, int nbits, int* count) {
+    const uint64_t lt = (1ull << (threadIdx.x & 63)) - 1ull;
+    uint64_t mask = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+        const bool bit = valid && ((s >> b) & 1);
+        const uint64_t bm = __ballot(bit);
+        mask &= bit ? bm : ~bm;
+    }
+    *count = __popcll(mask);
+    return __popcll(mask & lt);
+}
+
 // Stable counting sort of the P picks by slot.  Picks are taken 1024 at a
 // time; inside a wave the picks with the same slot are found with one ballot
 // per slot-id bit, their order is the lane order; per-wave counts are
@@ -177,8 +198,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
     __shared__ int base[MOE_MAX_S];
     __shared__ int ctot[MOE_MAX_S];
     __shared__ int scratch[GROUP_THREADS / 64 + 1];
-    const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-    const uint64_t lt = (1ull << lane) - 1ull;
+    const int tid = threadIdx.x, wid = tid >> 6;
     int nbits = 0;
     while ((1 << nbits) < S) ++nbits;
 
@@ -192,14 +212,9 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             int s = p < P ? slot_ids[p] : -1;
             if (s >= S) s = -1;
             const bool valid = s >= 0;
-            uint64_t mask = __ballot(valid);
-            for (int b = 0; b < nbits; ++b) {
-                const bool bit = valid && ((s >> b) & 1);
-                const uint64_t bm = __ballot(bit);
-                mask &= bit ? bm : ~bm;
-            }
-            const int rank = __popcll(mask & lt);
-            if (valid && rank == 0) wtab[wid][s] = (uint16_t)__popcll(mask);
+            int cnt;
+            const int rank = wave_slot_rank(s, valid, nbits, &cnt);
+            if (valid && rank == 0) wtab[wid][s] = (uint16_t)cnt;
             __syncthreads();
             for (int s2 = tid; s2 < S; s2 += GROUP_THREADS) {
                 int acc = 0;
@@ -234,6 +249,78 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             __syncthreads();
         }
     }
+}
+
+// Per-chunk slot counts: cnt[c][s] = picks of chunk c (1024 picks) with slot s.
+__global__ void __launch_bounds__(GROUP_THREADS) k_group_hist(const int32_t* __restrict__ slot_ids, int P, int S,
+                                                              int32_t* __restrict__ cnt) {
+    __shared__ int c[MOE_MAX_S];
+    const int tid = threadIdx.x;
+    for (int s = tid; s < S; s += GROUP_THREADS) c[s] = 0;
+    __syncthreads();
+    const int p = blockIdx.x * GROUP_THREADS + tid;
+    const int s = p < P ? slot_ids[p] : -1;
+    if (s >= 0 && s < S) atomicAdd(&c[s], 1);  // LDS integer count: order-free
+    __syncthreads();
+    for (int s2 = tid; s2 < S; s2 += GROUP_THREADS) cnt[(size_t)blockIdx.x * S + s2] = c[s2];
+}
+
+// Places chunk c's picks: slot offsets from the per-chunk counts (prefix over
+// slots of the totals, plus the counts of earlier chunks), then the stable
+// rank inside the chunk as in k_group.  Chunk 0 also writes the slot offsets
+// and the slots with work.  Same result as k_group.
+__global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __restrict__ slot_ids, int P, int S,
+                                                               const int32_t* __restrict__ cnt, int nch,
+                                                               int32_t* __restrict__ slot_off,
+                                                               int32_t* __restrict__ pair_list,
+                                                               int32_t* __restrict__ active,
+                                                               int32_t* __restrict__ n_active) {
+    __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
+    __shared__ int base[MOE_MAX_S];
+    __shared__ int scratch[GROUP_THREADS / 64 + 1];
+    const int tid = threadIdx.x, wid = tid >> 6, c = blockIdx.x;
+    int tot = 0, pre = 0;
+    if (tid < S) {
+        for (int cc = 0; cc < nch; ++cc) {
+            const int v = cnt[(size_t)cc * S + tid];
+            tot += v;
+            pre += cc < c ? v : 0;
+        }
+    }
+    int all;
+    const int off = moe::block_exclusive_scan(tot, scratch, &all);
+    if (tid < S) base[tid] = off + pre;
+    if (c == 0) {
+        if (tid < S) slot_off[tid] = off;
+        if (tid == 0) slot_off[S] = all;
+        const int flag = (tid < S && tot > 0) ? 1 : 0;
+        int na;
+        const int apos = moe::block_exclusive_scan(flag, scratch, &na);
+        if (flag) active[apos] = tid;
+        if (tid == 0) *n_active = na;
+    }
+    for (int i = tid; i < (GROUP_THREADS / 64) * S; i += GROUP_THREADS) wtab[i / S][i % S] = 0;
+    __syncthreads();
+    int nbits = 0;
+    while ((1 << nbits) < S) ++nbits;
+    const int p = c * GROUP_THREADS + tid;
+    int s = p < P ? slot_ids[p] : -1;
+    if (s >= S) s = -1;
+    const bool valid = s >= 0;
+    int count;
+    const int rank = wave_slot_rank(s, valid, nbits, &count);
+    if (valid && rank == 0) wtab[wid][s] = (uint16_t)count;
+    __syncthreads();
+    for (int s2 = tid; s2 < S; s2 += GROUP_THREADS) {
+        int acc = 0;
+        for (int w = 0; w < GROUP_THREADS / 64; ++w) {
+            const int v = wtab[w][s2];
+            wtab[w][s2] = (uint16_t)acc;
+            acc += v;
+        }
+    }
+    __syncthreads();
+    if (valid) pair_list[base[s] + wtab[wid][s] + rank] = p;
 }
 
 // ------------------------------------------------------- W8A8 quantiser
@@ -579,9 +666,19 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     float* part = reinterpret_cast<float*>(ws + L.part);
     int rc;
 
-    hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
-                       n_active);
-    if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
+    if (P > GROUP_MULTI_P) {
+        const int nch = (P + GROUP_THREADS - 1) / GROUP_THREADS;
+        int32_t* gcnt = reinterpret_cast<int32_t*>(ws + L.gcnt);
+        hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt);
+        if ((rc = moe_check_launch("moe_ffn_slots/group_hist"))) return rc;
+        hipLaunchKernelGGL(k_group_place, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt, nch, slot_off,
+                           pair_list, active, n_active);
+        if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
+    } else {
+        hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
+                           n_active);
+        if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
+    }
 
     if (F == MOE_W_BF16 && P >= PF_MIN_P && moe_pf_supported(F, H, I)) {
         rc = moe_pf_run(x, w, T, k, slot_store, slab_bytes, S, H, I, lay, slot_off, pair_list, active, n_active,

@@ -308,12 +308,14 @@ def test_ffn_ragged_shapes(m, w_type, H, I):
     assert_close(y, yg, w_type, f"w{w_type} H={H} I={I}")
 
 
-@pytest.mark.parametrize("w_type", [1, 2])
-def test_ffn_large_batch_sorted_picks(m, w_type):
-    """T*k above the in-workgroup pick scan: the picks go through the sorting kernel first."""
-    E, k, T, S, H, I = 12, 3, 401, 7, 112, 144
+@pytest.mark.parametrize("w_type,T", [(1, 401), (2, 401), (2, 1500), (0, 1700)])
+def test_ffn_large_batch_sorted_picks(m, w_type, T):
+    """Large batches on the row-streaming path: one sorting workgroup up to
+    4096 picks, one per 1024 picks above."""
+    E, k, S, H, I = 12, 3, 7, 112, 144
     rng = np.random.default_rng(17 + w_type)
-    x = synth.normal(synth.key(99, 1, w_type), (T, H), 1.0, 1)
+    x_dtype = 0 if w_type == 0 else 1
+    x = synth.normal(synth.key(99, 1, w_type), (T, H), 1.0, x_dtype)
     store = synth.slabs(w_type, 4321, 0, 0, E, H, I, 0.05)
     ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
     w = rng.dirichlet(np.ones(k), T).astype(np.float32)
@@ -321,8 +323,8 @@ def test_ffn_large_batch_sorted_picks(m, w_type):
     e2s = np.full(E, -1, np.int32)
     e2s[resident] = np.arange(S)
     sl = e2s[ids]
-    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=w_type, slab=store.shape[1]))
-    _, yg, _ = oracle.layer(w_type, store, E, H, I, x, 1, ids, w, sl)
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=x_dtype, w_type=w_type, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(w_type, store, E, H, I, x, x_dtype, ids, w, sl)
     y = run_ffn(m, li, sl, w, dev(store[resident]), S)
     assert_close(y, yg, w_type, f"w{w_type} T={T} k={k}")
 
