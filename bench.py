@@ -17,7 +17,20 @@ Infinity Cache cannot hold the expert weights between steps.
 Printed: one JSON line (metric of the layer: tokens/s), with the slot FFN's
 expert-weight HBM rate against the 8 TB/s peak (HIP events around every
 moe_ffn_slots launch of the timed steps), the gather rate against the
-measured host link, and the CPU oracle's rate on a bounded sample.
+measured host link, and the CPU oracle's rate on a bounded sample.  The same
+line carries two more workloads of the layer:
+
+  prefill  the 288-expert bf16 layer (hidden 4096, intermediate 1536, top-8)
+           on 2048 tokens, every expert resident (10.9 GB of slots): route ->
+           manage -> moe_ffn_slots on the MFMA grouped GEMM; HBM and MFMA
+           fractions; plus the same layer at 16384 tokens, the shape where
+           the grouped GEMM is compute-bound (supplemental)
+  dynamic  the 128-expert W8A8 layer under Zipf(0.8) routing with a 32-slot
+           LRU cache, 256 steps of 16 tokens from an empty cache: hit rate per
+           routing id, experts gathered per step, gather GB/s against the
+           measured host link, layer tokens/s with the host pass
+
+`--workload stack` runs the 48-layer, 512-expert 4-bit stack instead.
 """
 from __future__ import annotations
 
@@ -33,6 +46,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFS = 2500.0
 
 # kernels launched by one moe_ffn_slots call on the bf16 decode path
 FFN_KERNELS = ("k_group", "k_gu", "k_down", "k_reduce")
@@ -52,6 +66,10 @@ def parse():
     ap.add_argument("--no-host-pass", action="store_true", help="GPU pass only (not the headline)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-gather", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-dynamic", action="store_true")
+    ap.add_argument("--workload", choices=["decode", "stack"], default="decode")
+    ap.add_argument("--stack-steps", type=int, default=20, help="timed 48-layer steps at T=1 (half at T=32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
     ap.add_argument("--summarize", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
@@ -87,7 +105,12 @@ def main():
 
     import expert_vram_slot_amd as m
     import synth
-    from expert_vram_slot_amd.layer import SlotLayer, host_threads
+    from expert_vram_slot_amd.layer import SlotLayer, SlotStack, host_threads
+
+    if args.workload == "stack":
+        out = bench_stack(m, torch, synth, SlotStack, args.threads or host_threads(), args)
+        print(json.dumps(out), flush=True)
+        return
 
     cfg = "c2"
     c = synth.CONFIGS[cfg]
@@ -198,11 +221,215 @@ def main():
                      "distinct_slabs_per_step": round(float(np.mean(distinct)), 2)},
     }
 
+    del layers
+    link = None
     if not args.no_gather:
         out["gather"] = measure_gather(m, torch, synth)
+        link = out["gather"]["link_gbs"]
+    if not args.no_prefill:
+        out["prefill"] = bench_prefill(m, torch, synth, SlotLayer)
+    if not args.no_dynamic:
+        out["dynamic"] = bench_dynamic(m, torch, synth, SlotLayer, nthreads, link)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, T)
     print(json.dumps(out), flush=True)
+
+
+def bench_prefill(m, torch, synth, SlotLayer, steps=10, warmup=2):
+    """The 288-expert prefill layer, all experts resident; one step = route ->
+    manage -> moe_ffn_slots for 2048 tokens (no host pass: nothing misses)."""
+    c = synth.CONFIGS["c5"]
+    E, k, H, I, T = c["E"], c["k"], c["H"], c["I"], c["T"]
+    base = synth.config_seed("c5")
+    slab = synth.slab_bytes(synth.W_BF16, H, I)
+    store = torch.empty((E, slab), dtype=torch.uint8)
+    synth.slabs_into(store.data_ptr(), synth.W_BF16, base, 0, 0, E, H, I, c["sigma_w"], slab)
+    slots = store.cuda()
+    G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
+    xs = [torch.from_numpy(synth.normal(synth.key(base, synth.TAG_X, 0, st), (T, H), 1.0, 1).view(np.int16)).cuda()
+          for st in range(2)]
+    L = SlotLayer(E=E, k=k, H=H, I=I, S=E, w_type=synth.W_BF16, T_max=T, policy="static", host_store=store,
+                  slot_store=slots, G=G)
+    L.init_cache(torch.arange(E, dtype=torch.int32, device="cuda"))
+    ev = []
+    for i in range(warmup + steps):
+        rec = i >= warmup
+        if i == warmup:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+        L.ffn_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) if rec else None
+        L.step(xs[i % 2], T, host_pass=False)
+        if rec:
+            ev.append(L.ffn_events)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ffn_ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    P = T * k
+    byts = E * slab + T * H * 2 + T * H * 4  # every slab is touched at 2048 tokens
+    flops = 2.0 * P * 3 * H * I
+    out = {"workload": "288-expert bf16 MoE layer, H=4096 I=1536 top-8, 2048 tokens, all 288 experts resident",
+           "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(elapsed / steps * 1e3, 4),
+           "ffn_ms": round(ffn_ms, 4), "ffn_gbs": round(byts / ffn_ms / 1e6, 1),
+           "hbm_frac": round(byts / ffn_ms / 1e6 / HBM_PEAK_GBS, 4),
+           "ffn_tflops": round(flops / ffn_ms / 1e9, 1),
+           "mfma_frac": round(flops / ffn_ms / 1e9 / MFMA_BF16_PEAK_TFS, 4)}
+    # supplemental: 16384 tokens (about 455 rows per expert), where the grouped GEMM is compute-bound
+    T2 = 16384
+    x2 = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_X, 0, 99), (T2, H), 1.0, 1).view(np.int16)).cuda()
+    ids = torch.empty((T2, k), dtype=torch.int32, device="cuda")
+    w = torch.empty((T2, k), dtype=torch.float32, device="cuda")
+    m.moe_route(x2, 1, G, None, None, T2, H, E, k, ids, w, None)
+    ws_b = m.moe_ffn_workspace_bytes(T2, k, E, 1, H, I)
+    ws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+    y = torch.empty((T2, H), dtype=torch.float32, device="cuda")
+    m.moe_ffn_slots(x2, 1, ids, w, T2, k, slots, slab, E, 1, H, I, y, ws, ws_b)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(3):
+        m.moe_ffn_slots(x2, 1, ids, w, T2, k, slots, slab, E, 1, H, I, y, ws, ws_b)
+    e1.record()
+    torch.cuda.synchronize()
+    ms2 = e0.elapsed_time(e1) / 3
+    flops2 = 2.0 * T2 * k * 3 * H * I
+    out["supplemental_16384_tokens"] = {"ffn_ms": round(ms2, 3), "ffn_tflops": round(flops2 / ms2 / 1e9, 1),
+                                        "mfma_frac": round(flops2 / ms2 / 1e9 / MFMA_BF16_PEAK_TFS, 4)}
+    return out
+
+
+def bench_dynamic(m, torch, synth, SlotLayer, nthreads, link_gbs, steps=256, warmup=8):
+    """128-expert W8A8 layer, Zipf(0.8) routing ids (permutation per layer),
+    32 LRU slots starting empty, 256 steps of 16 tokens; x fresh per step."""
+    c = synth.CONFIGS["c3"]
+    E, k, H, I, S, T = c["E"], c["k"], c["H"], c["I"], c["S"], c["T"]
+    base = synth.config_seed("c3")
+    slab = synth.slab_bytes(synth.W_W8A8, H, I)
+    store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
+    synth.slabs_into(store.data_ptr(), synth.W_W8A8, base, 0, 0, E, H, I, c["sigma_w"], slab)
+    slots = torch.empty((S, slab), dtype=torch.uint8, device="cuda")
+    G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
+    ids_all = synth.zipf_ids(synth.key(base, synth.TAG_ZIPF_PERM), synth.key(base, synth.TAG_ZIPF_DRAW),
+                             (warmup + steps) * T, E, k, c["zipf_s"])
+    ids_all = torch.from_numpy(ids_all).cuda().reshape(warmup + steps, T * k)
+    xs = torch.from_numpy(np.stack([synth.normal(synth.key(base, synth.TAG_X, 0, st), (T, H), 1.0, 1)
+                                    for st in range(warmup + steps)]).view(np.int16)).cuda()
+    L = SlotLayer(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_W8A8, T_max=T, policy="lru", host_store=store,
+                  slot_store=slots, G=G, n_threads=nthreads)
+    acc = torch.zeros(4, dtype=torch.int64, device="cuda")
+    gev, fev = [], []
+    for phase in ("warmup", "timed"):
+        L.init_cache(None)  # empty cache
+        n = warmup if phase == "warmup" else steps
+        off = 0 if phase == "warmup" else warmup
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n):
+            timed = phase == "timed"
+            if timed:
+                L.gather_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                L.ffn_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+            L.step(xs[off + i], T, ids_in=ids_all[off + i])
+            if timed:
+                acc += L.stats
+                gev.append(L.gather_events)
+                fev.append(L.ffn_events)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+    L.gather_events = L.ffn_events = None
+    hits, distinct, gathered, host = (int(v) for v in acc.cpu())
+    g_ms = float(np.sum([a.elapsed_time(b) for a, b in gev]))
+    g_bytes = gathered * slab
+    g_gbs = g_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else None
+    out = {"workload": "128-expert W8A8 MoE layer, H=2048 I=768 top-8, Zipf(0.8) ids, 32 LRU slots from empty, "
+                       f"{steps} steps x {T} tokens, host pass on {nthreads} threads",
+           "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(elapsed / steps * 1e3, 4),
+           "hit_rate": round(hits / (steps * T * k), 4), "distinct_per_step": round(distinct / steps, 2),
+           "gathered_per_step": round(gathered / steps, 2), "host_experts_per_step": round(host / steps, 2),
+           "gather_gbs": None if g_gbs is None else round(g_gbs, 2),
+           "gather_link_frac": None if (g_gbs is None or not link_gbs) else round(g_gbs / link_gbs, 4),
+           "gather_bytes_per_step": int(g_bytes / steps),
+           "ffn_ms": round(float(np.mean([a.elapsed_time(b) for a, b in fev])), 4)}
+    return out
+
+
+def bench_stack(m, torch, synth, SlotStack, nthreads, args, n_base=4):
+    """The 48-layer stack of 512-expert top-10 layers (hidden 2048,
+    intermediate 512) with 4-bit block weights (43.5 GB pinned host store),
+    192 hot experts per layer resident in VRAM (16.3 GB), graded bias with
+    cap -1 from per-layer Dirichlet(0.3) brightness.  Layers 0..3 draw their
+    weights from the seeded generator; layer l >= 4 holds the experts of layer
+    l % 4 in a per-layer permuted order (distinct memory per layer, same
+    weight distribution) to keep set-up within a minute."""
+    c = synth.CONFIGS["c4"]
+    E, k, H, I, S, NL = c["E"], c["k"], c["H"], c["I"], c["S"], c["layers"]
+    base = synth.config_seed("c4")
+    slab = synth.slab_bytes(synth.W_Q4B32, H, I)
+    t_setup = time.perf_counter()
+    bases = [synth.slabs(synth.W_Q4B32, base, l, 0, E, H, I, c["sigma_w"]) for l in range(n_base)]
+    specs = []
+    for l in range(NL):
+        b = synth.dirichlet(synth.key(base, synth.TAG_B, l), E, c["alpha"])
+        resident = np.lexsort((np.arange(E), -b))[:S].astype(np.int32)
+        hs = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
+        if l < n_base:
+            hs.numpy()[:] = bases[l]
+        else:
+            hs.numpy()[:] = bases[l % n_base][np.random.default_rng(1000 + l).permutation(E)]
+        bias = torch.empty(E, dtype=torch.float32, device="cuda")
+        m.moe_bias_table(torch.from_numpy(b).cuda(), E, S, c["cap"], bias)
+        G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, l), (E, H), c["sigma_g"], 1)
+                             .view(np.int16)).cuda()
+        specs.append(dict(host_store=hs, slot_store=hs[torch.from_numpy(resident.astype(np.int64))].cuda(), G=G,
+                          bias=bias, resident=torch.from_numpy(resident).cuda()))
+    del bases
+    stack = SlotStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_Q4B32, T_max=32, layers=specs, n_threads=nthreads)
+    torch.cuda.synchronize()
+    t_setup = time.perf_counter() - t_setup
+    out = {"metric": "MoE-layer tokens/s; expert-weight HBM GB/s as % of peak; gather GB/s",
+           "workload": "48 x 512-expert top-10 4-bit stack, H=2048 I=512, graded bias cap -1, 192 resident per "
+                       f"layer, host pass on {nthreads} threads", "data": "synthetic", "setup_s": round(t_setup, 1),
+           "host_store_gb": round(NL * E * slab / 1e9, 2), "slot_store_gb": round(NL * S * slab / 1e9, 2)}
+    ids2 = torch.empty(32 * k, dtype=torch.int32, device="cuda")
+    w2 = torch.empty(32 * k, dtype=torch.float32, device="cuda")
+    for T, steps in ((1, args.stack_steps), (32, max(2, args.stack_steps // 2))):
+        xs = [torch.from_numpy(synth.normal(synth.key(base, synth.TAG_X, 0, st), (T, H), 1.0, 1).view(np.int16))
+              .cuda() for st in range(steps + 2)]
+        for i in range(2):
+            stack.step(xs[i], T)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            stack.step(xs[2 + i], T)
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
+        # accounting replay of the same steps (untimed): cache stats, FFN events, unbiased routing
+        acc = torch.zeros(4, dtype=torch.int64, device="cuda")
+        nob = torch.zeros(1, dtype=torch.int64, device="cuda")
+        evs = []
+
+        def on_layer(l, L, xl, y):
+            acc.add_(L.stats)
+            m.moe_route(xl, 1, L.G, None, None, T, H, E, k, ids2, w2, None)
+            e2s = stack.states[l][1]
+            nob.add_((e2s[ids2[:T * k].long()] >= 0).sum())
+
+        for i in range(steps):
+            stack.step(xs[2 + i], T, on_layer=on_layer, ffn_events=evs)
+        torch.cuda.synchronize()
+        hits, distinct, gathered, host = (int(v) for v in acc.cpu())
+        ffn_ms = float(np.sum([a.elapsed_time(b) for a, b in evs]))
+        resident_slabs = distinct - host
+        byts = resident_slabs * slab + steps * NL * T * H * 6
+        picks = steps * NL * T * k
+        out[f"T{T}"] = {"tokens_per_s": round(T * steps / elapsed, 2), "ms_per_step": round(elapsed / steps * 1e3, 3),
+                        "ffn_ms_per_step": round(ffn_ms / steps, 4),
+                        "ffn_gbs": round(byts / (ffn_ms * 1e-3) / 1e9, 1),
+                        "hbm_frac": round(byts / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                        "hit_rate_with_bias": round(hits / picks, 4),
+                        "hit_rate_without_bias": round(int(nob.item()) / picks, 4),
+                        "resident_experts_per_layer": round(resident_slabs / (steps * NL), 2),
+                        "host_experts_per_layer": round(host / (steps * NL), 2)}
+    return out
 
 
 def measure_gather(m, torch, synth):

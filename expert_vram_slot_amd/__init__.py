@@ -64,6 +64,7 @@ def lib():
             "moe_ffn_slots": (i32, [vp, i32, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, vp, sz, vp]),
             "moe_ffn_host_misses": (i32, [vp, i32, vp, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, i32]),
             "moe_combine": (i32, [vp, vp, i32, i32, vp]),
+            "moe_residual": (i32, [vp, i32, vp, vp, i32, i32, vp]),
             "moe_host_alloc": (vp, [sz]),
             "moe_host_free": (i32, [vp]),
         }
@@ -166,6 +167,10 @@ def moe_ffn_host_misses(x_h, x_dtype, ids_h, slot_ids_h, w_h, T, k, host_store, 
 
 def moe_combine(y, y_add, T, H, stream=None):
     return _check("moe_combine", lib().moe_combine(_p(y), _p(y_add), T, H, _stream(stream)))
+
+
+def moe_residual(x, x_dtype, y, x_out, T, H, stream=None):
+    return _check("moe_residual", lib().moe_residual(_p(x), x_dtype, _p(y), _p(x_out), T, H, _stream(stream)))
 
 
 def moe_host_alloc(nbytes: int) -> int:

@@ -26,7 +26,8 @@ import os
 import torch
 
 from . import (MOE_W_F32, MOE_X_BF16, MOE_X_F32, POLICIES, cache_gather, cache_init, cache_manage, cache_state,
-               moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_route, moe_slab_layout)
+               moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_residual, moe_route,
+               moe_slab_layout)
 
 
 def host_threads() -> int:
@@ -82,7 +83,8 @@ class SlotLayer:
         self.side = torch.cuda.Stream(device=dev)
         self.copy = torch.cuda.Stream(device=dev)
         self.pool = cf.ThreadPoolExecutor(max_workers=1)
-        self.ffn_events = None  # (start, end) torch events recorded around moe_ffn_slots when set
+        self.ffn_events = None     # (start, end) torch events recorded around moe_ffn_slots when set
+        self.gather_events = None  # (start, end) torch events recorded around cache_gather when set
 
     def init_cache(self, resident=None):
         cache_init(self.st, resident)
@@ -118,7 +120,12 @@ class SlotLayer:
         # 3. gather on the side stream (a static cache never loads while running)
         if self.policy != 0 and self.S > 0:
             self.side.wait_event(ev_manage)
+            gev = self.gather_events
+            if gev:
+                gev[0].record(self.side)
             cache_gather(self.miss, self.n_miss, self.S, self.host_store, self.slot_store, self.slab, self.side)
+            if gev:
+                gev[1].record(self.side)
             ev_g = torch.cuda.Event()
             ev_g.record(self.side)
             cur.wait_event(ev_g)
@@ -143,3 +150,70 @@ class SlotLayer:
             self.y_host_dev[:T * self.H].copy_(self.h_y[:T * self.H], non_blocking=True)
             moe_combine(self.y, self.y_host_dev, T, self.H, cur)
         return self.y[:T * self.H].view(T, self.H)
+
+
+class SlotStack:
+    """Stacked expert-slot MoE layers joined by a residual stream kept in the
+    activation format: x_{l+1} = x_l + y_l ("Nudge, don't cut", "Experts that
+    don't fit": a deep model of routed layers).
+
+    Each layer brings its pinned host store, slot store, router gate,
+    optional bias table and static resident set; the step buffers, streams
+    and host-pass worker are shared by all layers (they run one after the
+    other).
+    """
+
+    def __init__(self, *, E, k, H, I, S, w_type, T_max, layers, n_threads=None, device="cuda"):
+        self.layers = layers
+        first = layers[0]
+        self.layer = SlotLayer(E=E, k=k, H=H, I=I, S=S, w_type=w_type, T_max=T_max, policy="static",
+                               host_store=first["host_store"], slot_store=first["slot_store"], G=first["G"],
+                               bias=first.get("bias"), n_threads=n_threads, device=device)
+        dev = torch.device(device)
+        self.states = []
+        for spec in layers:
+            e2s = torch.empty(E, dtype=torch.int32, device=dev)
+            s2e = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+            last = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+            freq = torch.empty(max(S, 1), dtype=torch.int32, device=dev)
+            step = torch.zeros(1, dtype=torch.int32, device=dev)
+            st = cache_state(e2s, s2e, last, freq, step, E, S)
+            cache_init(st, spec["resident"])
+            self.states.append((st, e2s, s2e, last, freq, step))
+        xb = 4 if self.layer.x_dtype == MOE_X_F32 else 2
+        self.xbuf = [torch.empty(T_max * H * xb, dtype=torch.uint8, device=dev) for _ in range(2)]
+        self.H = H
+
+    def bind(self, l):
+        """Point the shared step machinery at layer l."""
+        L, spec = self.layer, self.layers[l]
+        L.host_store, L.slot_store, L.G, L.bias = spec["host_store"], spec["slot_store"], spec["G"], spec.get("bias")
+        L.st = self.states[l][0]
+        return L
+
+    def step(self, x, T, host_pass=True, trace=None, on_layer=None, ffn_events=None):
+        """All layers for T tokens of x (device [T][H] in the activation
+        format); returns the last layer's residual output (a view of an
+        internal buffer).  `trace`, if a list, receives per layer a copy of
+        (x_l, ids, slot_ids, w, y_l) for checking; `on_layer(l, L, x_l, y_l)`
+        is called after each layer's step; `ffn_events`, if a list, receives
+        per layer the (start, end) events around moe_ffn_slots."""
+        cur = x.reshape(-1)
+        nb = T * self.H * (4 if self.layer.x_dtype == MOE_X_F32 else 2)
+        for l in range(len(self.layers)):
+            L = self.bind(l)
+            if ffn_events is not None:
+                L.ffn_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                ffn_events.append(L.ffn_events)
+            xl = cur.view(x.dtype).view(T, self.H)
+            y = L.step(xl, T, host_pass=host_pass)
+            L.ffn_events = None
+            if trace is not None:
+                P = T * L.k
+                trace.append((xl.clone(), L.ids[:P].clone(), L.slot_ids[:P].clone(), L.w[:P].clone(), y.clone()))
+            if on_layer is not None:
+                on_layer(l, L, xl, y)
+            nxt = self.xbuf[l % 2][:nb]
+            moe_residual(cur, L.x_dtype, y, nxt, T, self.H)
+            cur = nxt
+        return cur.view(x.dtype).view(T, self.H)

@@ -193,7 +193,7 @@ int cache_pick_static(const int32_t* ids, int n_ids, int E, int S, int32_t* resi
  * use, ties to the lower slot.  A hit refreshes last (LFU: count + 1 per
  * step); an inserted expert starts at last = step, freq = 1.  STATIC never
  * changes the maps.  Overflow (more misses than victims) is not an error.
- * Errors: ARG, SHAPE (n_ids > 65536 or limits), HIP. */
+ * Errors: ARG, SHAPE (n_ids > 2^24, E or S beyond the limits), HIP. */
 int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int n_ids, int32_t* slot_ids,
                  int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host, int32_t* stats,
                  hipStream_t stream);
@@ -250,6 +250,16 @@ int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* ids_h, cons
 /* y[i] = fl32(y[i] + y_add[i]) for T*H floats on the device: the single add
  * that joins the two passes ([RTX] transcript). */
 int moe_combine(float* y, const float* y_add, int T, int H, hipStream_t stream);
+
+/* Residual join of stacked layers ([PGO] "Experts that don't fit": the
+ * routed layers follow one another in a deep model; each adds its output to
+ * the activations it read):
+ *   x      device [T][H] in x_dtype (MOE_X_BF16 or MOE_X_F32)
+ *   y      device float[T][H], the layer's output
+ *   x_out  device [T][H] in x_dtype out; may alias x
+ * bf16: x_out = RNE_bf16(fl32(x + y)); fp32: x_out = fl32(x + y).
+ * Errors: ARG, DTYPE, HIP. */
+int moe_residual(const void* x, int x_dtype, const float* y, void* x_out, int T, int H, hipStream_t stream);
 
 /* Pinned, device-mapped host memory for the host expert store. */
 void* moe_host_alloc(size_t bytes);

@@ -53,9 +53,10 @@ def lib():
         L.oracle_manage.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.oracle_gather.argtypes = [vp, i32, vp, vp, i64]
         L.oracle_pick_static.argtypes = [vp, i32, i32, i32, vp]
+        L.oracle_residual.argtypes = [vp, i32, vp, i32, i32, vp]
         for f in ("oracle_decode_expert", "oracle_logits", "oracle_bias_table", "oracle_topk",
                   "oracle_route_weights", "oracle_expert", "oracle_layer", "oracle_manage", "oracle_gather",
-                  "oracle_pick_static"):
+                  "oracle_pick_static", "oracle_residual"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -194,4 +195,14 @@ def pick_static(ids, E, S):
     ids = _c(ids, np.int32).reshape(-1)
     out = np.empty(S, np.int32)
     _check(lib().oracle_pick_static(_p(ids), ids.shape[0], E, S, _p(out)), "pick_static")
+    return out
+
+
+def residual(x, x_dtype, y):
+    """Next layer's input: bf16(x + y) (bit patterns) for bf16 streams, x + y for fp32."""
+    x = _xarr(x, x_dtype)
+    y = _c(y, np.float32)
+    T, H = x.shape
+    out = np.empty_like(x)
+    _check(lib().oracle_residual(_p(x), x_dtype, _p(y), T, H, _p(out)), "residual")
     return out

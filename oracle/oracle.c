@@ -481,6 +481,25 @@ int oracle_gather(const int32_t* miss, int n_miss, const uint8_t* host_store, ui
     return 0;
 }
 
+/* Residual join of stacked layers ([PGO] "Experts that don't fit": the
+ * routed layers follow one another; each adds its output to what it read).
+ * The stream keeps its storage format: bf16 streams get the fp32 sum
+ * rounded to bf16 (nearest, ties to even), fp32 streams the fp32 sum. */
+int oracle_residual(const void* x, int x_dtype, const float* y, int T, int H, void* out) {
+    const int64_t n = (int64_t)T * H;
+    for (int64_t i = 0; i < n; ++i) {
+        if (x_dtype == ORC_X_BF16) {
+            const float v = round_bf16(bf16_value(((const uint16_t*)x)[i]) + y[i]);
+            uint32_t b;
+            memcpy(&b, &v, 4);
+            ((uint16_t*)out)[i] = (uint16_t)(b >> 16);
+        } else {
+            ((float*)out)[i] = ((const float*)x)[i] + y[i];
+        }
+    }
+    return 0;
+}
+
 /* Static resident set ([RTX] transcript: the set is chosen once before the
  * run from a profile of what the router picks, then never changes): count
  * picks per expert over a profile batch and keep the S most picked, ties to

@@ -65,6 +65,9 @@ int oracle_manage(int policy, int E, int S, int32_t* e2s, int32_t* s2e, uint32_t
 int oracle_gather(const int32_t* miss, int n_miss, const uint8_t* host_store, uint8_t* slot_store,
                   int64_t slab_bytes);
 
+/* Residual join of stacked layers: bf16(x + y) for bf16 streams, x + y for fp32. */
+int oracle_residual(const void* x, int x_dtype, const float* y, int T, int H, void* out);
+
 /* Static resident set: the S most-picked experts of a profile batch. */
 int oracle_pick_static(const int32_t* ids, int n_ids, int E, int S, int32_t* resident);
 

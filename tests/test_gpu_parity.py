@@ -481,3 +481,70 @@ def test_layer_step_two_passes_sum_to_oracle(m, cfg, T):
     assert_close(y, yf, li.w_type, f"{cfg} layer")
     st = host(L.stats)
     assert st[3] == len(set(ids_o.reshape(-1).tolist()) - set(resident.tolist()))
+
+
+# ---------------------------------------------------------- layer stack
+
+
+@functools.lru_cache(maxsize=1)
+def stack_layers(n_layers=3):
+    """Layers of the 48 x 512-expert 4-bit stack (full per-layer shape) with
+    their brightness profiles, hot/resident sets and stores."""
+    out = []
+    for l in range(n_layers):
+        li = synth.LayerInputs("c4", layer=l, T=1)
+        b = synth.dirichlet(synth.key(li.base, synth.TAG_B, l), li.E, li.c["alpha"])
+        resident = np.lexsort((np.arange(li.E), -b))[:li.c["S"]].astype(np.int32)
+        out.append((li, b, resident))
+    return out
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_stack_teacher_forced_per_layer(m, T):
+    """Three layers of the 4-bit stack with the graded bias and 192 resident
+    experts per layer, run as a stack; every layer checked on the inputs the
+    GPU gave it: ids and slots bitwise, weights fp32, output 4-bit tolerance,
+    the residual stream bitwise."""
+    from expert_vram_slot_amd.layer import SlotStack
+    layers = stack_layers()
+    li0 = layers[0][0]
+    E, k, H, I, S, cap = li0.E, li0.k, li0.H, li0.I, li0.c["S"], li0.c["cap"]
+    specs = []
+    for li, b, resident in layers:
+        bias = torch.empty(E, dtype=torch.float32, device="cuda")
+        m.moe_bias_table(dev(b), E, S, cap, bias)
+        specs.append(dict(host_store=torch.from_numpy(li.store).pin_memory(), slot_store=dev(li.store[resident]),
+                          G=dev(li.G.view(np.int16)), bias=bias, resident=dev(resident)))
+    stack = SlotStack(E=E, k=k, H=H, I=I, S=S, w_type=3, T_max=T, layers=specs)
+    x0 = synth.LayerInputs("c4", layer=0, T=T, with_store=False).x
+    trace = []
+    out = host(stack.step(dev(x0.view(np.int16)), T, trace=trace)).view(np.uint16)
+    assert np.array_equal(host(trace[0][0]).view(np.uint16), x0)
+    for l, ((li, b, resident), (xl, ids, sl, w, y)) in enumerate(zip(layers, trace)):
+        xl = host(xl).view(np.uint16)
+        z = oracle.logits(xl, 1, li.G)
+        ids_o = oracle.topk(z, k, oracle.bias_table(b, S, cap))
+        w_o = oracle.route_weights(z, ids_o)
+        np.testing.assert_array_equal(host(ids).reshape(T, k), ids_o, err_msg=f"layer {l} ids")
+        e2s = np.full(E, -1, np.int32)
+        e2s[resident] = np.arange(S)
+        np.testing.assert_array_equal(host(sl).reshape(T, k), e2s[ids_o], err_msg=f"layer {l} slots")
+        assert_close(host(w).reshape(T, k), w_o, 0, f"layer {l} weights")
+        yf, _, _ = oracle.layer(3, li.store, E, H, I, xl, 1, ids_o, w_o, e2s[ids_o])
+        y = host(y)
+        assert_close(y, yf, 3, f"layer {l} output")
+        nxt = oracle.residual(xl, 1, y)
+        got = host(trace[l + 1][0]).view(np.uint16) if l + 1 < len(trace) else out
+        np.testing.assert_array_equal(got, nxt, err_msg=f"layer {l} residual")
+
+
+def test_residual_matches_oracle(m):
+    x = synth.normal(synth.key(5, 1), (33, 2048), 1.0, 1)
+    y = synth.normal(synth.key(5, 2), (33, 2048), 0.5, 0)
+    xo = torch.empty((33, 2048), dtype=torch.int16, device="cuda")
+    m.moe_residual(dev(x.view(np.int16)), 1, dev(y), xo, 33, 2048)
+    np.testing.assert_array_equal(host(xo).view(np.uint16), oracle.residual(x, 1, y))
+    xf = synth.normal(synth.key(5, 3), (7, 64), 1.0, 0)
+    xfo = torch.empty((7, 64), dtype=torch.float32, device="cuda")
+    m.moe_residual(dev(xf), 0, dev(y[:7, :64].copy()), xfo, 7, 64)
+    np.testing.assert_array_equal(host(xfo), oracle.residual(xf, 0, y[:7, :64]))

@@ -629,3 +629,18 @@ def test_generator_dirichlet_and_zipf():
     assert all(len(set(r)) == 8 for r in ids)
     cnt = np.bincount(ids.reshape(-1), minlength=128)
     assert cnt.max() > 4 * max(cnt.min(), 1)
+
+
+def test_residual_rounds_to_nearest_even_bf16():
+    """Stack join x + y kept in bf16: exact sums stay, halfway cases go to the
+    even neighbour, and fp32 streams add in fp32."""
+    one = 0x3F80  # 1.0
+    x = np.array([[one, one, one, one, 0xBF80, 0x0000]], np.uint16)
+    # 1 + 2^-8 (exact bf16 step 2^-7 -> halfway, tie to even 1.0); 1 + 3*2^-8 (halfway, to 1 + 2^-6)
+    # 1 + 2^-7 (exact); 1 + 0.75*2^-7 (rounds up); -1 + 1 = +0; 0 + 0 = 0
+    y = np.array([[2.0 ** -8, 3 * 2.0 ** -8, 2.0 ** -7, 0.75 * 2.0 ** -7, 1.0, 0.0]], np.float32)
+    got = oracle.residual(x, 1, y)
+    want = [0x3F80, 0x3F82, 0x3F81, 0x3F81, 0x0000, 0x0000]
+    assert got.reshape(-1).tolist() == want
+    xf = np.array([[1.5, -2.25]], np.float32)
+    np.testing.assert_array_equal(oracle.residual(xf, 0, np.array([[0.25, 0.25]], np.float32)), [[1.75, -2.0]])
