@@ -387,39 +387,60 @@ struct ActRows {
 };
 
 // Dot products of ROWS weight rows with NT activation rows over KG 16-byte
-// granules.  Lane l takes granules l, l + 64, ...: a chunk is 64 granules of
-// every row.  Chunks go in groups of NCHG whose weight loads are all issued
-// before the first is used; granules past the end read a clamped, in-bounds
-// granule with zero weights.  acc[r * NT + t].
-template <int F, int ROWS, int NT, int NCHG>
+// granules.  The wave's lanes form 64 / LPR groups of LPR lanes; group s
+// takes rows s, s + 64/LPR, ... and lane l of a group reads granules l,
+// l + LPR, ... of its rows, so one wave load covers 64 / LPR rows (rows of
+// fewer than 64 granules keep every lane busy).  Chunks of LPR granules go in
+// groups of NCHG whose weight loads are all issued before the first is used;
+// granules past the end read a clamped, in-bounds granule with zero weights.
+// acc[i * NT + t] holds the lane's partial sum of its i-th row and token t.
+template <int F, int ROWS, int NT, int NCHG, int LPR>
 __device__ __forceinline__ void gemv_rows(const RowPtrs<ROWS>& rp, const ActRows& ar, const int (&arow)[NT], int KG,
-                                          int lane, typename Fmt<F>::Acc (&acc)[ROWS * NT]) {
+                                          int lane, typename Fmt<F>::Acc (&acc)[(ROWS * LPR / 64) * NT]) {
     constexpr int XG = Fmt<F>::EPG * Fmt<F>::ABYTES;  // activation bytes per weight granule
-    for (int g0 = 0; g0 < KG; g0 += 64 * NCHG) {
-        v4u w[NCHG][ROWS];
-        float qs[NCHG][ROWS];
+    constexpr int RPI = 64 / LPR;                      // rows per wave load
+    constexpr int RL = ROWS / RPI;                     // rows per lane
+    static_assert(ROWS % RPI == 0, "rows must fill the lane groups");
+    const int sub = lane / LPR, gl = lane % LPR;
+    // this lane's rows: sub + RPI * i (selected with constant indices only)
+    const unsigned char* wrow[RL];
+    const unsigned char* srow[RL];
+#pragma unroll
+    for (int i = 0; i < RL; ++i) {
+        wrow[i] = rp.w[i * RPI];
+        srow[i] = rp.s[i * RPI];
+#pragma unroll
+        for (int u = 1; u < RPI; ++u)
+            if (sub == u) {
+                wrow[i] = rp.w[i * RPI + u];
+                srow[i] = rp.s[i * RPI + u];
+            }
+    }
+    for (int g0 = 0; g0 < KG; g0 += LPR * NCHG) {
+        v4u w[NCHG][RL];
+        float qs[NCHG][RL];
         int gj[NCHG];
         bool on[NCHG];
 #pragma unroll
         for (int j = 0; j < NCHG; ++j) {
-            const int g = g0 + 64 * j + lane;
+            const int g = g0 + LPR * j + gl;
             on[j] = g < KG;
             gj[j] = on[j] ? g : KG - 1;
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
-                w[j][r] = load_weights(reinterpret_cast<const v4u*>(rp.w[r] + (size_t)gj[j] * 16));
-                qs[j][r] = 0.0f;
+            for (int i = 0; i < RL; ++i) {
+                w[j][i] = load_weights(reinterpret_cast<const v4u*>(wrow[i] + (size_t)gj[j] * 16));
+                qs[j][i] = 0.0f;
                 if constexpr (F == MOE_W_Q4B32)
-                    qs[j][r] = half_bits_to_f32(reinterpret_cast<const uint16_t*>(rp.s[r])[gj[j]]);
+                    qs[j][i] = half_bits_to_f32(reinterpret_cast<const uint16_t*>(srow[i])[gj[j]]);
             }
         }
 #pragma unroll
         for (int j = 0; j < NCHG; ++j) {
 #pragma unroll
-            for (int r = 0; r < ROWS; ++r) {
+            for (int i = 0; i < RL; ++i) {
                 if (!on[j]) {
-                    w[j][r] = v4u{0u, 0u, 0u, 0u};
-                    qs[j][r] = 0.0f;
+                    w[j][i] = v4u{0u, 0u, 0u, 0u};
+                    qs[j][i] = 0.0f;
                 }
             }
 #pragma unroll
@@ -428,15 +449,29 @@ __device__ __forceinline__ void gemv_rows(const RowPtrs<ROWS>& rp, const ActRows
                 float xsum = 0.0f;
                 if constexpr (F == MOE_W_Q4B32) xsum = ar.bsum[(size_t)arow[t] * KG + gj[j]];
 #pragma unroll
-                for (int r = 0; r < ROWS; ++r) granule_dot<F>(w[j][r], xa, qs[j][r], xsum, acc[r * NT + t]);
+                for (int i = 0; i < RL; ++i) granule_dot<F>(w[j][i], xa, qs[j][i], xsum, acc[i * NT + t]);
             }
         }
     }
 }
 
-// Chunk-group size for a row of KG granules: the whole row when it has at
-// most 4 chunks, else groups of 4.
-__host__ __device__ constexpr int chunk_group(int KG) { return KG <= 64 ? 1 : KG <= 128 ? 2 : KG <= 192 ? 3 : 4; }
+// Chunk-group size for a row of KG granules read LPR at a time: the whole
+// row when it has at most 4 chunks, else groups of 4.
+__host__ __device__ constexpr int chunk_group(int KG, int LPR = 64) {
+    return KG <= LPR ? 1 : KG <= 2 * LPR ? 2 : KG <= 3 * LPR ? 3 : 4;
+}
+
+// Lanes per row of the down projection.  Narrower lane groups keep every
+// lane busy on short rows but give each lane fewer rows to share one
+// activation read with; that pays for fp32/bf16 (one activation byte per
+// weight byte), not for int8 and 4-bit weights, whose activations are as
+// large as (int8) or four times (4-bit against bf16) the weight bytes.
+__host__ __device__ constexpr int down_lpr(int KG, int w_type) {
+    return (w_type == MOE_W_W8A8 || w_type == MOE_W_Q4B32 || KG % 64 == 0 || KG >= 128) ? 64
+           : KG % 32 == 0                                                              ? 32
+           : KG % 16 == 0                                                              ? 16
+                                                                                       : 64;
+}
 
 #define MOE_NCHG_DISPATCH(KG, BODY)              \
     do {                                         \
@@ -446,6 +481,22 @@ __host__ __device__ constexpr int chunk_group(int KG) { return KG <= 64 ? 1 : KG
             case 3: BODY(3); break;              \
             default: BODY(4); break;             \
         }                                        \
+    } while (0)
+
+#define MOE_DOWN_DISPATCH(KG, BODY)                                   \
+    do {                                                              \
+        const int lpr_ = down_lpr(KG, F);                             \
+        const int g_ = chunk_group(KG, lpr_);                         \
+        if (lpr_ == 16) {                                             \
+            if (g_ == 1) BODY(1, 16); else if (g_ == 2) BODY(2, 16);  \
+            else if (g_ == 3) BODY(3, 16); else BODY(4, 16);          \
+        } else if (lpr_ == 32) {                                      \
+            if (g_ == 1) BODY(1, 32); else if (g_ == 2) BODY(2, 32);  \
+            else if (g_ == 3) BODY(3, 32); else BODY(4, 32);          \
+        } else {                                                      \
+            if (g_ == 1) BODY(1, 64); else if (g_ == 2) BODY(2, 64);  \
+            else if (g_ == 3) BODY(3, 64); else BODY(4, 64);          \
+        }                                                             \
     } while (0)
 
 // Picks of one pass (uniform across the wave): pick[t] for t < nt, the last
@@ -472,7 +523,7 @@ __device__ __forceinline__ void gu_pass(const RowPtrs<2 * RPW_GU>& rp, const Sla
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    gemv_rows<F, ROWS, NT, NCHG>(rp, ar, tok, H / Fmt<F>::EPG, lane, acc);
+    gemv_rows<F, ROWS, NT, NCHG, 64>(rp, ar, tok, H / Fmt<F>::EPG, lane, acc);
     int idx;
     Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
     const Acc up = __shfl_xor(v, 32, 64);
@@ -549,25 +600,29 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
     }
 }
 
-template <int F, int NT, int NCHG>
+template <int F, int NT, int NCHG, int LPR>
 __device__ __forceinline__ void down_pass(const RowPtrs<RPW_DN>& rp, const SlabView& sv, const unsigned char* slab,
                                           const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
                                           int H, int I, int r_base, const float* __restrict__ hscale,
                                           const float* __restrict__ wts, float* __restrict__ part) {
     using Acc = typename Fmt<F>::Acc;
-    constexpr int V = RPW_DN * NT;
+    constexpr int RPI = 64 / LPR;
+    constexpr int V = (RPW_DN / RPI) * NT;  // values per lane
+    static_assert(V <= LPR, "a lane group reduces at most LPR values at once");
     const int lane = threadIdx.x & 63;
     int pick[NT];
     pass_picks<NT>(pair_list, p, nt, pick);
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    gemv_rows<F, RPW_DN, NT, NCHG>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
-    int idx;
-    Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
-    if (moe::multi_sum_holder<V>(lane)) {
-        const int r = idx / NT, t = idx % NT;
-        const int row = r_base + r;
+    gemv_rows<F, RPW_DN, NT, NCHG, LPR>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
+    // reduce inside each group of LPR lanes (strides LPR/2 .. 1)
+    int idx = 0;
+    moe::multi_sum_level<V, LPR / 2>(acc, lane, idx);
+    const Acc v = acc[0];
+    if ((lane & (LPR / V - 1)) == 0) {
+        const int i = idx / NT, t = idx % NT;
+        const int row = r_base + lane / LPR + RPI * i;
         if (row < H && t < nt) {
             const int pk = pick[t];
             float o;
@@ -580,7 +635,7 @@ __device__ __forceinline__ void down_pass(const RowPtrs<RPW_DN>& rp, const SlabV
     }
 }
 
-template <int F, int NCHG>
+template <int F, int NCHG, int LPR>
 __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* __restrict__ hact,
                                                       const float* __restrict__ hscale,
                                                       const float* __restrict__ hbsum, const float* __restrict__ wts,
@@ -607,7 +662,8 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
     const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
     for (int c0 = 0; c0 < ns; c0 += NTMAX) {
         const int nt = min(NTMAX, ns - c0);
-#define MOE_DN(N) down_pass<F, N, NCHG>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
+#define MOE_DN(N) \
+    down_pass<F, N, NCHG, LPR>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
         MOE_NT_DISPATCH(nt, MOE_DN);
 #undef MOE_DN
     }
@@ -740,10 +796,10 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     }
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
     const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
-#define MOE_LAUNCH_DN(G)                                                                                          \
-    hipLaunchKernelGGL((k_down<F, G>), dim3(S * tiles_dn), dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, w, \
-                       H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
-    MOE_NCHG_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
+#define MOE_LAUNCH_DN(G, LP)                                                                                 \
+    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(S * tiles_dn), dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, \
+                       w, H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
+    MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
 #undef MOE_LAUNCH_DN
     if ((rc = moe_check_launch("moe_ffn_slots/down"))) return rc;
 

@@ -83,6 +83,56 @@ __device__ __forceinline__ void widen(const v4u& g, double (&d)[XD == MOE_X_F32 
     }
 }
 
+// Top-k of one token's selection scores fl32(z + bias) on (score desc, id
+// asc) by one wave: k rounds of a wave arg-max over the experts not yet
+// taken; lane j < k ends up holding the j-th pick.  Then the softmax of the
+// raw logits over the picks, in double.  Given picks (ids_in) are trusted to
+// lie in [0, E) and clamped only to keep the read in bounds.
+__device__ __forceinline__ void topk_softmax(const float* z, const float* __restrict__ bias,
+                                             const int32_t* __restrict__ ids_in, int E, int k, int t,
+                                             int32_t* __restrict__ ids, float* __restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    int32_t pick = -1;
+    if (ids_in) {
+        if (lane < k) pick = ids_in[(int64_t)t * k + lane];
+    } else {
+        uint64_t taken = 0;  // bit j: expert lane + 64 j already picked (E <= 4096)
+        for (int r = 0; r < k; ++r) {
+            float best = -INFINITY;
+            int be = 0x7FFFFFFF;
+            for (int j = 0; lane + 64 * j < E; ++j) {
+                if (taken >> j & 1) continue;
+                const int e = lane + 64 * j;
+                float sc = z[e];
+                if (bias) sc = sc + bias[e];
+                if (sc > best || (sc == best && e < be)) {
+                    best = sc;
+                    be = e;
+                }
+            }
+#pragma unroll
+            for (int sft = 32; sft >= 1; sft >>= 1) {
+                const float ob = __shfl_xor(best, sft, 64);
+                const int oe = __shfl_xor(be, sft, 64);
+                if (ob > best || (ob == best && oe < be)) {
+                    best = ob;
+                    be = oe;
+                }
+            }
+            if (lane == (be & 63)) taken |= 1ull << (be >> 6);
+            if (lane == r) pick = be;
+        }
+        if (lane < k) ids[(int64_t)t * k + lane] = pick;
+    }
+    const double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
+    double m = zj;
+#pragma unroll
+    for (int sft = 32; sft >= 1; sft >>= 1) m = fmax(m, __shfl_xor(m, sft, 64));
+    const double ej = lane < k ? exp(zj - m) : 0.0;
+    const double sum = moe::wave_sum(ej);
+    if (lane < k) w[(int64_t)t * k + lane] = (float)(ej / sum);
+}
+
 // One workgroup routes TB consecutive tokens.  Logits: G is [E][H]; each wave
 // takes ROUTE_RW expert rows per pass, its lanes read consecutive 16-byte
 // granules of a row, the tokens sit in LDS widened to double, partial sums
@@ -165,50 +215,123 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
     }
 
     // one wave per token
-    for (int t = wv; t < nt; t += ROUTE_KSPLIT) {
-        const float* z = zl + t * E;
-        int32_t pick = -1;  // lane j < k ends up holding the j-th pick
-        if (ids_in) {
-            if (lane < k) pick = ids_in[(int64_t)(t0 + t) * k + lane];
-        } else {
-            uint64_t taken = 0;  // bit j: expert lane + 64 j already picked (E <= 4096)
-            for (int r = 0; r < k; ++r) {
-                float best = -INFINITY;
-                int be = 0x7FFFFFFF;
-                for (int j = 0; lane + 64 * j < E; ++j) {
-                    if (taken >> j & 1) continue;
-                    const int e = lane + 64 * j;
-                    float sc = z[e];
-                    if (bias) sc = sc + bias[e];
-                    if (sc > best || (sc == best && e < be)) {
-                        best = sc;
-                        be = e;
-                    }
-                }
-#pragma unroll
-                for (int sft = 32; sft >= 1; sft >>= 1) {
-                    const float ob = __shfl_xor(best, sft, 64);
-                    const int oe = __shfl_xor(be, sft, 64);
-                    if (ob > best || (ob == best && oe < be)) {
-                        best = ob;
-                        be = oe;
-                    }
-                }
-                if (lane == (be & 63)) taken |= 1ull << (be >> 6);
-                if (lane == r) pick = be;
-            }
-            if (lane < k) ids[(int64_t)(t0 + t) * k + lane] = pick;
-        }
-        // softmax of the raw logits over the picks, in double; externally given
-        // picks are trusted to lie in [0, E), clamped only to keep the read in bounds
-        const double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
-        double m = zj;
-#pragma unroll
-        for (int sft = 32; sft >= 1; sft >>= 1) m = fmax(m, __shfl_xor(m, sft, 64));
-        const double ej = lane < k ? exp(zj - m) : 0.0;
-        const double sum = moe::wave_sum(ej);
-        if (lane < k) w[(int64_t)(t0 + t) * k + lane] = (float)(ej / sum);
+    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax(zl + t * E, bias, ids_in, E, k, t0 + t, ids, w);
+}
+
+// ----------------------------------------------------- two-kernel router
+
+// Logits of TB tokens against one block of 4 * RW expert rows per
+// workgroup, written to z[T][E]: the tokens sit in LDS in their own format
+// and are widened to double where used; each wave takes RW rows, its lanes
+// read consecutive 16-byte granules of each row, fp64 FMAs, one multi-value
+// butterfly per wave, rounded once to fp32.  Many workgroups share G, so
+// small batches are not limited by one workgroup's read of the whole gate.
+template <int XD, int TB, int RW>
+__global__ void __launch_bounds__(ROUTE_THREADS) k_logits(const void* __restrict__ x, const void* __restrict__ G,
+                                                          int T, int H, int E, float* __restrict__ z) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    constexpr int EPG = XD == MOE_X_F32 ? 4 : 8;
+    constexpr int XB = XD == MOE_X_F32 ? 4 : 2;
+    constexpr int V = RW * TB;
+    const int t0 = blockIdx.x * TB;
+    const int nt = min(TB, T - t0);
+    const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+    const int ebase = blockIdx.y * (ROUTE_KSPLIT * RW) + wv * RW;
+    const int KG = H / EPG;
+    const size_t row_bytes = (size_t)KG * 16;
+    // tokens to LDS, 16 bytes per thread and step; rows past T are zero
+    const unsigned char* xb = reinterpret_cast<const unsigned char*>(x);
+    for (int i = threadIdx.x; i < TB * KG; i += ROUTE_THREADS) {
+        const int t = i / KG, g = i % KG;
+        v4u v = v4u{0u, 0u, 0u, 0u};
+        if (t < nt) v = *reinterpret_cast<const v4u*>(xb + (size_t)(t0 + t) * row_bytes + (size_t)g * 16);
+        *reinterpret_cast<v4u*>(smem + (size_t)t * row_bytes + (size_t)g * 16) = v;
     }
+    __syncthreads();
+    if (ebase >= E) return;
+    const unsigned char* Gb = reinterpret_cast<const unsigned char*>(G);
+    double acc[V];
+#pragma unroll
+    for (int i = 0; i < V; ++i) acc[i] = 0.0;
+    for (int g0 = 0; g0 < KG; g0 += 64) {
+        const int g = g0 + lane;
+        const bool on = g < KG;
+        const int gc = on ? g : KG - 1;
+        v4u gr[RW];
+#pragma unroll
+        for (int r = 0; r < RW; ++r) {
+            const int e = min(ebase + r, E - 1);  // rows past E are computed on a valid row and dropped
+            gr[r] = *reinterpret_cast<const v4u*>(Gb + e * row_bytes + (size_t)gc * 16);
+            if (!on) gr[r] = v4u{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int t = 0; t < TB; ++t) {
+            double xv[EPG];
+            widen<XD>(*reinterpret_cast<const v4u*>(smem + (size_t)t * row_bytes + (size_t)gc * 16), xv);
+#pragma unroll
+            for (int r = 0; r < RW; ++r) {
+                double gd[EPG];
+                widen<XD>(gr[r], gd);
+                double a = acc[r * TB + t];
+#pragma unroll
+                for (int i = 0; i < EPG; ++i) a = fma(xv[i], gd[i], a);
+                acc[r * TB + t] = a;
+            }
+        }
+    }
+    int idx;
+    const double v = moe::wave_multi_sum<V>(acc, lane, idx);
+    if (moe::multi_sum_holder<V>(lane)) {
+        const int r = idx / TB, t = idx % TB;
+        const int e = ebase + r;
+        if (e < E && t < nt) z[(int64_t)(t0 + t) * E + e] = (float)v;
+    }
+    (void)XB;
+}
+
+// Top-k and weights from z[T][E], one wave per token; the token's logits are
+// staged in LDS first (k rounds read them).
+__global__ void __launch_bounds__(ROUTE_THREADS) k_topk(const float* __restrict__ z, const float* __restrict__ bias,
+                                                        const int32_t* __restrict__ ids_in, int T, int E, int k,
+                                                        int32_t* __restrict__ ids, float* __restrict__ w) {
+    extern __shared__ __align__(16) unsigned char smem[];
+    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int t = blockIdx.x * ROUTE_KSPLIT + wv;
+    if (t >= T) return;
+    float* zl = reinterpret_cast<float*>(smem) + (size_t)wv * E;
+    for (int e = lane; e < E; e += 64) zl[e] = z[(int64_t)t * E + e];
+    topk_softmax(zl, bias, ids_in, E, k, t, ids, w);
+}
+
+template <int XD, int TB>
+int launch_logits(const void* x, const void* G, int T, int H, int E, float* z, hipStream_t s) {
+    constexpr int RW = 4;
+    const size_t lds = (size_t)TB * H * (XD == MOE_X_F32 ? 4 : 2);
+    const dim3 grid((T + TB - 1) / TB, (E + ROUTE_KSPLIT * RW - 1) / (ROUTE_KSPLIT * RW));
+    hipLaunchKernelGGL((k_logits<XD, TB, RW>), grid, dim3(ROUTE_THREADS), lds, s, x, G, T, H, E, z);
+    return moe_check_launch("moe_route/logits");
+}
+
+template <int XD>
+int route_split(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
+                int32_t* ids, float* w, float* logits, hipStream_t s) {
+    // tokens per workgroup: more for larger batches (fewer reads of G), within 64 KiB of LDS
+    const size_t xrow = (size_t)H * (XD == MOE_X_F32 ? 4 : 2);
+    int tb = T >= 512 ? 8 : T >= 128 ? 4 : T >= 32 ? 2 : 1;
+    while (tb > 1 && tb * xrow > 64 * 1024) tb >>= 1;
+    if (xrow > 64 * 1024) return moe_fail(MOE_E_SHAPE, "moe_route: H=%d is too long for one token in LDS", H);
+    int rc;
+    switch (tb) {
+        case 8: rc = launch_logits<XD, 8>(x, G, T, H, E, logits, s); break;
+        case 4: rc = launch_logits<XD, 4>(x, G, T, H, E, logits, s); break;
+        case 2: rc = launch_logits<XD, 2>(x, G, T, H, E, logits, s); break;
+        default: rc = launch_logits<XD, 1>(x, G, T, H, E, logits, s); break;
+    }
+    if (rc) return rc;
+    const size_t lds = (size_t)ROUTE_KSPLIT * E * sizeof(float);
+    hipLaunchKernelGGL(k_topk, dim3((T + ROUTE_KSPLIT - 1) / ROUTE_KSPLIT), dim3(ROUTE_THREADS), lds, s, logits, bias,
+                       ids_in, T, E, k, ids, w);
+    return moe_check_launch("moe_route/topk");
 }
 
 template <int XD, int TB>
@@ -233,6 +356,9 @@ int launch_route(const void* x, const void* G, const float* bias, const int32_t*
 template <int XD>
 int route_dispatch(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
                    int32_t* ids, float* w, float* logits, hipStream_t s) {
+    // with a logits buffer the logits and the top-k run as two kernels (many
+    // workgroups share the gate); without one, one fused kernel per token block
+    if (logits) return route_split<XD>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
     // small batches: one token per workgroup (more workgroups, lower latency);
     // large batches: several tokens share each read of G
     int tb = T <= 64 ? 1 : 4;

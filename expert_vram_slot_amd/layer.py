@@ -57,6 +57,8 @@ class SlotLayer:
         self.ids = self.meta[:P]
         self.slot_ids = self.meta[P:2 * P]
         self.w = self.meta[2 * P:].view(torch.float32)
+        # router logits (also lets the router run as logits + top-k kernels)
+        self.logits = torch.empty(T_max * E, dtype=torch.float32, device=dev)
         self.miss = torch.empty(2 * max(S, 1), **i32)
         self.n_miss = torch.zeros(1, **i32)
         self.host_miss = torch.empty(E, **i32)
@@ -110,7 +112,7 @@ class SlotLayer:
             self.ids[:P].copy_(ids_in.reshape(-1)[:P], non_blocking=True)
         # 1. router (picks, or weights of given picks)
         moe_route(x, self.x_dtype, self.G, self.bias, None if ids_in is None else self.ids, T, self.H, self.E,
-                  self.k, self.ids, self.w, None, cur)
+                  self.k, self.ids, self.w, self.logits, cur)
         ids = self.ids
         # 2. cache step: victims, miss list, remap
         cache_manage(self.st, self.policy, ids, P, self.slot_ids, self.miss, self.n_miss, self.host_miss,

@@ -59,17 +59,19 @@ def x_torch_dtype(x_dtype):
 # ------------------------------------------------------------------ router
 
 
-def gpu_route(m, li, bias=None, ids_in=None):
+def gpu_route(m, li, bias=None, ids_in=None, with_logits=True):
+    """moe_route on the GPU; with a logits buffer it runs as logits + top-k
+    kernels, without one as the fused per-token-block kernel (z is None)."""
     T, H, E, k = li.T, li.H, li.E, li.k
     x = dev(li.x.view(np.int16) if li.x_dtype else li.x)
     G = dev(li.G.view(np.int16) if li.x_dtype else li.G)
     ids = torch.full((T, k), -7, dtype=torch.int32, device="cuda")
     w = torch.empty((T, k), dtype=torch.float32, device="cuda")
-    z = torch.empty((T, E), dtype=torch.float32, device="cuda")
+    z = torch.empty((T, E), dtype=torch.float32, device="cuda") if with_logits else None
     b = None if bias is None else dev(bias)
     ii = None if ids_in is None else dev(ids_in)
     m.moe_route(x, li.x_dtype, G, b, ii, T, H, E, k, ids, w, z)
-    return host(ids), host(w), host(z)
+    return host(ids), host(w), None if z is None else host(z)
 
 
 def check_route(m, li, bias=None):
@@ -92,6 +94,19 @@ def check_route(m, li, bias=None):
 def test_route_matches_oracle(m, cfg, T):
     li = synth.LayerInputs(cfg, T=T, with_store=False)
     check_route(m, li)
+
+
+@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 1), ("c2", 64), ("c4", 32), ("c2", 300)])
+def test_route_fused_kernel_matches_oracle(m, cfg, T):
+    """Without a logits buffer the router runs as one fused kernel per token block."""
+    li = synth.LayerInputs(cfg, T=T, with_store=False)
+    ids, w, _ = gpu_route(m, li, with_logits=False)
+    zo = oracle.logits(li.x, li.x_dtype, li.G)
+    np.testing.assert_array_equal(ids, oracle.topk(zo, li.k))
+    np.testing.assert_allclose(w, oracle.route_weights(zo, ids), rtol=4e-6, atol=1e-9)
+    ids2, w2, z2 = gpu_route(m, li)
+    np.testing.assert_array_equal(ids2, ids)
+    np.testing.assert_allclose(w2, w, rtol=4e-6, atol=1e-9)
 
 
 def test_route_prefill_shape(m):
