@@ -48,8 +48,10 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 
-# kernels launched by one moe_ffn_slots call on the bf16 decode path
+# kernels launched by one moe_ffn_slots call on the bf16 decode path (hidden 2048 -> gate/up rows of 256
+# granules in groups of 4 chunks; intermediate 768 -> down rows of 96 granules, 32 lanes per row, 3 chunks)
 FFN_KERNELS = ("k_group", "k_gu", "k_down", "k_reduce")
+FFN_ANCHOR = "k_gu<1, 4>"
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/common.hpp")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
@@ -105,10 +107,10 @@ def main():
 
     import expert_vram_slot_amd as m
     import synth
-    from expert_vram_slot_amd.layer import SlotLayer, SlotStack, host_threads
+    from expert_vram_slot_amd.layer import NativeStack, SlotLayer, SlotStack, host_threads
 
     if args.workload == "stack":
-        out = bench_stack(m, torch, synth, SlotStack, args.threads or host_threads(), args)
+        out = bench_stack(m, torch, synth, SlotStack, NativeStack, args.threads or host_threads(), args)
         print(json.dumps(out), flush=True)
         return
 
@@ -125,6 +127,7 @@ def main():
 
     # ---- per-layer inputs: pinned host store, router gate, static resident set, slot store
     layers = []
+    specs = []
     n_x = 8
     for l in range(args.layers):
         store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
@@ -148,9 +151,29 @@ def main():
         xs = [torch.from_numpy(synth.normal(synth.key(base, synth.TAG_X, l, s), (T, H), 1.0, x_dtype)
                                .view(np.int16)).to(dev) for s in range(n_x)]
         layers.append((L, xs))
+        specs.append(dict(host_store=store, slot_store=slots, G=G, bias=None, resident=resident))
+    # the layer step as a user runs it: the library's native driver, one call per step
+    native = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=w_type, T_max=T, layers=specs, n_threads=nthreads)
     torch.cuda.synchronize()
 
-    # ---- timed steps; events around every moe_ffn_slots launch (compute stream)
+    def native_step(i):
+        l = i % len(layers)
+        native.layer_step(l, layers[l][1][(i // len(layers)) % n_x], T, host_pass=not args.no_host_pass)
+
+    for i in range(args.warmup):
+        native_step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        native_step(args.warmup + i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed / args.steps * 1e3
+    value = T * args.steps / elapsed
+
+    # ---- the same steps again on the GPU alone (route -> manage -> moe_ffn_slots, no host pass), issued
+    # from Python with HIP events around every moe_ffn_slots launch on the compute stream: the FFN's
+    # duration for the roofline, free of gaps from CPU threads competing with the launching thread
     ffn_ms = []
     ffn_bytes = []
     ev_pairs = []
@@ -163,22 +186,20 @@ def main():
             L.ffn_events = (e0, e1)
         else:
             L.ffn_events = None
-        L.step(x, T, host_pass=not args.no_host_pass)
+        L.step(x, T, host_pass=False)
         if record:
             ev_pairs.append((e0, e1, L))
 
     for i in range(args.warmup):
         one_step(i, False)
     torch.cuda.synchronize()
-    t0 = time.perf_counter()
+    t1 = time.perf_counter()
     for i in range(args.steps):
         one_step(args.warmup + i, True)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_py = time.perf_counter() - t1
     for e0, e1, L in ev_pairs:
         ffn_ms.append(e0.elapsed_time(e1))
-    ms_per_step = elapsed / args.steps * 1e3
-    value = T * args.steps / elapsed
 
     # algorithmic bytes of one moe_ffn_slots launch: every distinct resident slab the step touched, read
     # once, plus x in and y out.  Distinct slabs per step: rerun each timed step's routing (untimed).
@@ -213,7 +234,8 @@ def main():
         "config": {"workload": f"qwen3-30b-a3b-shaped MoE layer, bf16, E=128 top-8, H=2048 I=768, decode T={T}, "
                                f"static 64-slot cache + host pass of the other 64 experts",
                    "global_batch": T, "layers_rotated": args.layers, "host_threads": nthreads,
-                   "host_pass": not args.no_host_pass},
+                   "host_pass": not args.no_host_pass, "driver": "native moe_layer_step",
+                   "gpu_only_step_ms": round(elapsed_py / args.steps * 1e3, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(T),
                      "kernel": "moe_ffn_slots (group, gate/up, down, reduce kernels)",
@@ -222,6 +244,7 @@ def main():
     }
 
     del layers
+    native.close()
     link = None
     if not args.no_gather:
         out["gather"] = measure_gather(m, torch, synth)
@@ -352,7 +375,7 @@ def bench_dynamic(m, torch, synth, SlotLayer, nthreads, link_gbs, steps=256, war
     return out
 
 
-def bench_stack(m, torch, synth, SlotStack, nthreads, args, n_base=4):
+def bench_stack(m, torch, synth, SlotStack, NativeStack, nthreads, args, n_base=4):
     """The 48-layer stack of 512-expert top-10 layers (hidden 2048,
     intermediate 512) with 4-bit block weights (43.5 GB pinned host store),
     192 hot experts per layer resident in VRAM (16.3 GB), graded bias with
@@ -383,6 +406,7 @@ def bench_stack(m, torch, synth, SlotStack, nthreads, args, n_base=4):
                           bias=bias, resident=torch.from_numpy(resident).cuda()))
     del bases
     stack = SlotStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_Q4B32, T_max=32, layers=specs, n_threads=nthreads)
+    native = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_Q4B32, T_max=32, layers=specs, n_threads=nthreads)
     torch.cuda.synchronize()
     t_setup = time.perf_counter() - t_setup
     out = {"metric": "MoE-layer tokens/s; expert-weight HBM GB/s as % of peak; gather GB/s",
@@ -395,14 +419,16 @@ def bench_stack(m, torch, synth, SlotStack, nthreads, args, n_base=4):
         xs = [torch.from_numpy(synth.normal(synth.key(base, synth.TAG_X, 0, st), (T, H), 1.0, 1).view(np.int16))
               .cuda() for st in range(steps + 2)]
         for i in range(2):
-            stack.step(xs[i], T)
+            native.step(xs[i], T)
         torch.cuda.synchronize()
+        native.stats(reset=True)
         t0 = time.perf_counter()
         for i in range(steps):
-            stack.step(xs[2 + i], T)
+            native.step(xs[2 + i], T)
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
-        # accounting replay of the same steps (untimed): cache stats, FFN events, unbiased routing
+        n_hits, n_distinct, _, n_host = native.stats(reset=True)
+        # replay of the same steps from Python (untimed): FFN events and the unbiased routing
         acc = torch.zeros(4, dtype=torch.int64, device="cuda")
         nob = torch.zeros(1, dtype=torch.int64, device="cuda")
         evs = []
@@ -417,11 +443,13 @@ def bench_stack(m, torch, synth, SlotStack, nthreads, args, n_base=4):
             stack.step(xs[2 + i], T, on_layer=on_layer, ffn_events=evs)
         torch.cuda.synchronize()
         hits, distinct, gathered, host = (int(v) for v in acc.cpu())
+        assert (hits, distinct, host) == (n_hits, n_distinct, n_host), "replay differs from the timed steps"
         ffn_ms = float(np.sum([a.elapsed_time(b) for a, b in evs]))
         resident_slabs = distinct - host
         byts = resident_slabs * slab + steps * NL * T * H * 6
         picks = steps * NL * T * k
         out[f"T{T}"] = {"tokens_per_s": round(T * steps / elapsed, 2), "ms_per_step": round(elapsed / steps * 1e3, 3),
+                        "driver": "native moe_stack_step",
                         "ffn_ms_per_step": round(ffn_ms / steps, 4),
                         "ffn_gbs": round(byts / (ffn_ms * 1e-3) / 1e9, 1),
                         "hbm_frac": round(byts / (ffn_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -429,6 +457,7 @@ def bench_stack(m, torch, synth, SlotStack, nthreads, args, n_base=4):
                         "hit_rate_without_bias": round(int(nob.item()) / picks, 4),
                         "resident_experts_per_layer": round(resident_slabs / (steps * NL), 2),
                         "host_experts_per_layer": round(host / (steps * NL), 2)}
+    native.close()
     return out
 
 
@@ -533,8 +562,9 @@ def _csv_rows(d, suffix):
 
 def _short(name):
     n = name.split("(")[0] if "::" not in name else name
-    for k in ("k_group", "k_gu", "k_down", "k_reduce", "k_route", "k_manage", "k_gather", "k_combine",
-              "k_quant_rows", "k_block_sums", "k_pick_static", "k_bias_table", "k_cache_init"):
+    for k in ("k_group_hist", "k_group_place", "k_group", "k_gu", "k_down", "k_reduce", "k_route", "k_logits",
+              "k_topk", "k_manage", "k_gather", "k_combine", "k_quant_rows", "k_block_sums", "k_pick_static",
+              "k_bias_table", "k_cache_init", "k_pf_gemm", "k_pf_tiles", "k_residual_bf16", "k_residual_f32"):
         if f"::{k}<" in name or f"::{k}(" in name:
             i = name.index(k)
             j = name.find("(", i)
@@ -552,12 +582,39 @@ def _counter_per_dispatch(rows, counter):
     return per
 
 
+def _ffn_launches(rows, key):
+    """Group per-dispatch rows into decode moe_ffn_slots launches: each anchor
+    (the bf16 decode gate/up kernel) with the closest earlier k_group and the
+    closest later k_down and k_reduce by dispatch id.  Returns a list of
+    {kernel short name: row}."""
+    by_id = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
+    names = [_short(r["Kernel_Name"]) for r in by_id]
+    launches = []
+    for i, nm in enumerate(names):
+        if nm != FFN_ANCHOR:
+            continue
+        got = {nm: by_id[i]}
+        for j in range(i - 1, max(-1, i - 50), -1):
+            if names[j] == "k_group":
+                got["k_group"] = by_id[j]
+                break
+        for want in ("k_down", "k_reduce"):
+            for j in range(i + 1, min(len(names), i + 50)):
+                if names[j].split("<")[0] == want:
+                    got[names[j]] = by_id[j]
+                    break
+        if len(got) == 4:
+            launches.append(got)
+    return launches
+
+
 def summarize(args):
     tr, fe, wr, cfe, cwr = args.summarize
     T = args.batch
     stats = _csv_rows(tr, "kernel_stats.csv")
-    fetch = _counter_per_dispatch(_csv_rows(fe, "counter_collection.csv"), "FETCH_SIZE")
-    write = _counter_per_dispatch(_csv_rows(wr, "counter_collection.csv"), "WRITE_SIZE")
+    trace = _csv_rows(tr, "kernel_trace.csv")
+    frows = [r for r in _csv_rows(fe, "counter_collection.csv") if r["Counter_Name"] == "FETCH_SIZE"]
+    wrows = [r for r in _csv_rows(wr, "counter_collection.csv") if r["Counter_Name"] == "WRITE_SIZE"]
     cfetch = _counter_per_dispatch(_csv_rows(cfe, "counter_collection.csv"), "FETCH_SIZE")
     cwrite = _counter_per_dispatch(_csv_rows(cwr, "counter_collection.csv"), "WRITE_SIZE")
 
@@ -578,33 +635,41 @@ def summarize(args):
         with open(args.commands) as fh:
             lines.extend("  " + l.rstrip() for l in fh if l.strip())
         lines.append("")
-    lines.append("kernel trace (--kernel-trace --stats), all dispatches of the run:")
-    lines.append(f"  {'kernel':<28}{'calls':>7}{'avg us':>10}{'min us':>10}{'max us':>10}")
-    ffn_avg = 0.0
-    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"])):
-        nm = _short(r["Name"])
-        avg = float(r["AverageNs"]) / 1e3
-        lines.append(f"  {nm:<28}{int(r['Calls']):>7}{avg:>10.2f}{float(r['MinNs']) / 1e3:>10.2f}"
-                     f"{float(r['MaxNs']) / 1e3:>10.2f}")
-        if nm.split("<")[0] in FFN_KERNELS:
-            ffn_avg += avg
-    lines.append(f"  sum of averages of the moe_ffn_slots kernels ({', '.join(FFN_KERNELS)}): {ffn_avg:.2f} us")
+    lines.append("kernel trace (--kernel-trace --stats), every kernel of the run (all benchmark legs):")
+    lines.append(f"  {'kernel':<34}{'calls':>7}{'avg us':>10}{'min us':>10}{'max us':>10}")
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:24]:
+        lines.append(f"  {_short(r['Name']):<34}{int(r['Calls']):>7}{float(r['AverageNs']) / 1e3:>10.2f}"
+                     f"{float(r['MinNs']) / 1e3:>10.2f}{float(r['MaxNs']) / 1e3:>10.2f}")
     lines.append("")
-    lines.append(f"HBM counters (KiB per dispatch, mean over dispatches; calibration: a 1 GiB copy reads "
-                 f"FETCH_SIZE {copy_kib(cfetch):.0f} KiB, WRITE_SIZE {copy_kib(cwrite):.0f} KiB, so factors "
-                 f"{f_fetch:.3f} and {f_write:.3f}):")
-    lines.append(f"  {'kernel':<28}{'n':>5}{'FETCH KiB':>14}{'WRITE KiB':>14}{'scaled MB':>12}")
+    launches = _ffn_launches(trace, "trace")
+    per_k = {}
+    for L in launches:
+        for nm, r in L.items():
+            per_k.setdefault(nm, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines.append(f"decode moe_ffn_slots launches found in the trace: {len(launches)} (each: k_group, {FFN_ANCHOR}, "
+                 f"its k_down and k_reduce, by dispatch id)")
+    ffn_avg = 0.0
+    for nm, v in per_k.items():
+        lines.append(f"  {nm:<34}{np.mean(v):>10.2f} us")
+        ffn_avg += float(np.mean(v))
+    lines.append(f"  sum per launch (kernel time): {ffn_avg:.2f} us")
+    lines.append("")
+    lines.append(f"HBM counters per decode moe_ffn_slots launch (KiB per dispatch, mean over launches; "
+                 f"calibration: a 1 GiB copy reads FETCH_SIZE {copy_kib(cfetch):.0f} KiB, WRITE_SIZE "
+                 f"{copy_kib(cwrite):.0f} KiB, so factors {f_fetch:.3f} and {f_write:.3f}):")
+    lines.append(f"  {'kernel':<34}{'FETCH KiB':>14}{'WRITE KiB':>14}{'scaled MB':>12}")
+    fl, wl = _ffn_launches(frows, "fetch"), _ffn_launches(wrows, "write")
     traffic = 0.0
-    for nm in sorted(set(fetch) | set(write)):
-        fv, wv = fetch.get(nm, [0.0]), write.get(nm, [0.0])
-        scaled = (np.mean(fv) * f_fetch + np.mean(wv) * f_write) * 1024
-        lines.append(f"  {nm:<28}{len(fv):>5}{np.mean(fv):>14.1f}{np.mean(wv):>14.1f}{scaled / 1e6:>12.2f}")
-        if nm.split("<")[0] in FFN_KERNELS:
-            traffic += scaled
-    lines.append(f"  moe_ffn_slots per launch (sum over its kernels): {traffic / 1e6:.2f} MB")
+    for nm in (fl[0].keys() if fl else []):
+        fv = float(np.mean([float(L[nm]["Counter_Value"]) for L in fl]))
+        wv = float(np.mean([float(L[nm]["Counter_Value"]) for L in wl])) if wl and nm in wl[0] else 0.0
+        scaled = (fv * f_fetch + wv * f_write) * 1024
+        traffic += scaled
+        lines.append(f"  {nm:<34}{fv:>14.1f}{wv:>14.1f}{scaled / 1e6:>12.2f}")
+    lines.append(f"  per launch (sum over its kernels): {traffic / 1e6:.2f} MB over {len(fl)} / {len(wl)} launches")
     rec = {"batch": T, "ffn_source_sha256": ffn_source_hash(), "ffn_kernels_avg_us": round(ffn_avg, 3),
-           "traffic_bytes_per_launch": int(traffic), "fetch_factor": round(f_fetch, 4),
-           "write_factor": round(f_write, 4)}
+           "launches": len(launches), "traffic_bytes_per_launch": int(traffic) if fl else None,
+           "fetch_factor": round(f_fetch, 4), "write_factor": round(f_write, 4)}
     lines.append("")
     lines.append("record: " + json.dumps(rec))
     out = args.out or profile_path(T)

@@ -39,6 +39,12 @@ class SlabLayout(ctypes.Structure):
     _fields_ = [("w", ctypes.c_int64 * 3), ("s", ctypes.c_int64 * 3), ("total", ctypes.c_int64)]
 
 
+class LayerDesc(ctypes.Structure):
+    """moe_layer_desc: one layer as the native step driver sees it."""
+    _fields_ = [("G", ctypes.c_void_p), ("bias", ctypes.c_void_p), ("state", CacheState), ("policy", ctypes.c_int),
+                ("slot_store", ctypes.c_void_p), ("host_store", ctypes.c_void_p), ("slab_bytes", ctypes.c_size_t)]
+
+
 _lib = None
 
 
@@ -65,6 +71,12 @@ def lib():
             "moe_ffn_host_misses": (i32, [vp, i32, vp, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, i32]),
             "moe_combine": (i32, [vp, vp, i32, i32, vp]),
             "moe_residual": (i32, [vp, i32, vp, vp, i32, i32, vp]),
+            "moe_step_create": (vp, [i32, i32, i32, i32, i32, i32, i32]),
+            "moe_step_destroy": (None, [vp]),
+            "moe_step_output": (vp, [vp]),
+            "moe_step_stats": (i32, [vp, ctypes.POINTER(ctypes.c_int64), i32]),
+            "moe_layer_step": (i32, [vp, ctypes.POINTER(LayerDesc), vp, i32, vp, i32, i32, vp, vp, vp, vp]),
+            "moe_stack_step": (i32, [vp, ctypes.POINTER(LayerDesc), i32, vp, i32, i32, i32, vp, vp, vp, vp]),
             "moe_host_alloc": (vp, [sz]),
             "moe_host_free": (i32, [vp]),
         }
@@ -171,6 +183,39 @@ def moe_combine(y, y_add, T, H, stream=None):
 
 def moe_residual(x, x_dtype, y, x_out, T, H, stream=None):
     return _check("moe_residual", lib().moe_residual(_p(x), x_dtype, _p(y), _p(x_out), T, H, _stream(stream)))
+
+
+def moe_step_create(T_max, E, k, H, I, S, w_type):
+    """Handle of the native step driver (owns its device / pinned buffers and events)."""
+    h = lib().moe_step_create(T_max, E, k, H, I, S, w_type)
+    if not h:
+        raise MoeError("moe_step_create", MOE_E_NOMEM, (lib().moe_last_error() or b"").decode())
+    return h
+
+
+def moe_step_destroy(h):
+    lib().moe_step_destroy(h)
+
+
+def moe_step_output(h):
+    return lib().moe_step_output(h)
+
+
+def moe_step_stats(h, reset=False):
+    out = (ctypes.c_int64 * 4)()
+    _check("moe_step_stats", lib().moe_step_stats(h, out, int(reset)))
+    return [int(v) for v in out]
+
+
+def moe_layer_step(h, desc, x, T, ids_in, host_pass, n_threads, y_out, s0, s_side, s_copy):
+    return _check("moe_layer_step", lib().moe_layer_step(h, ctypes.byref(desc), _p(x), T, _p(ids_in),
+                                                         int(host_pass), n_threads, _p(y_out), _stream(s0),
+                                                         _stream(s_side), _stream(s_copy)))
+
+
+def moe_stack_step(h, descs, x, T, host_pass, n_threads, x_out, s0, s_side, s_copy):
+    return _check("moe_stack_step", lib().moe_stack_step(h, descs, len(descs), _p(x), T, int(host_pass), n_threads,
+                                                         _p(x_out), _stream(s0), _stream(s_side), _stream(s_copy)))
 
 
 def moe_host_alloc(nbytes: int) -> int:

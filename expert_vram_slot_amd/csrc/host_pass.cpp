@@ -33,6 +33,9 @@ class Pool {
    public:
     // Run fn(item) for item in [0, n) on `threads` threads (the caller
     // included).  Items are handed out dynamically; each runs exactly once.
+    // Idle workers spin for a short while before they sleep, so the phases
+    // of one call, and calls that follow each other closely, start without a
+    // wake-up delay.
     void run(int threads, int n, const std::function<void(int)>& fn) {
         if (n <= 0) return;
         threads = std::max(1, std::min({threads, n, 64}));
@@ -49,29 +52,35 @@ class Pool {
             std::lock_guard<std::mutex> lk(mu_);
             fn_ = &fn;
             n_ = n;
-            next_.store(0);
-            enlisted_ = threads - 1;  // workers 0 .. threads-2 take part
-            pending_ = threads - 1;
-            ++gen_;
+            next_.store(0, std::memory_order_relaxed);
+            pending_.store(threads - 1, std::memory_order_relaxed);
+            // generation and the number of workers taking part, published together
+            word_.store(((word_.load(std::memory_order_relaxed) >> 8) + 1) << 8 | (uint64_t)(threads - 1),
+                        std::memory_order_release);
         }
         cv_.notify_all();
         work();
-        std::unique_lock<std::mutex> lk(mu_);
-        done_cv_.wait(lk, [&] { return pending_ == 0; });
+        for (int i = 0; i < kSpin && pending_.load(std::memory_order_acquire) != 0; ++i) _mm_pause();
+        if (pending_.load(std::memory_order_acquire) != 0) {
+            std::unique_lock<std::mutex> lk(mu_);
+            done_cv_.wait(lk, [&] { return pending_.load(std::memory_order_acquire) == 0; });
+        }
         fn_ = nullptr;
     }
 
     ~Pool() {
         {
             std::lock_guard<std::mutex> lk(mu_);
-            stop_ = true;
-            ++gen_;
+            stop_.store(true);
+            word_.fetch_add(1 << 8);
         }
         cv_.notify_all();
         for (auto& t : workers_) t.join();
     }
 
    private:
+    static constexpr int kSpin = 1000;  // pause instructions (tens of microseconds)
+
     void work() {
         for (;;) {
             const int i = next_.fetch_add(1);
@@ -82,16 +91,24 @@ class Pool {
     void loop(int id) {
         uint64_t seen = 0;
         for (;;) {
-            {
-                std::unique_lock<std::mutex> lk(mu_);
-                cv_.wait(lk, [&] { return stop_ || gen_ != seen; });
-                if (stop_) return;
-                seen = gen_;
-                if (id >= enlisted_) continue;
+            uint64_t w = word_.load(std::memory_order_acquire);
+            for (int i = 0; (w >> 8) == (seen >> 8) && i < kSpin; ++i) {
+                _mm_pause();
+                w = word_.load(std::memory_order_acquire);
             }
+            if ((w >> 8) == (seen >> 8)) {
+                std::unique_lock<std::mutex> lk(mu_);
+                cv_.wait(lk, [&] { return stop_.load() || (word_.load() >> 8) != (seen >> 8); });
+                w = word_.load(std::memory_order_acquire);
+            }
+            if (stop_.load()) return;
+            seen = w;
+            if (id >= (int)(w & 0xFF)) continue;  // not taking part in this call
             work();
-            std::lock_guard<std::mutex> lk(mu_);
-            if (--pending_ == 0) done_cv_.notify_all();
+            if (pending_.fetch_sub(1, std::memory_order_acq_rel) == 1) {
+                std::lock_guard<std::mutex> lk(mu_);
+                done_cv_.notify_all();
+            }
         }
     }
 
@@ -100,9 +117,10 @@ class Pool {
     std::vector<std::thread> workers_;
     const std::function<void(int)>* fn_ = nullptr;
     std::atomic<int> next_{0};
-    int n_ = 0, enlisted_ = 0, pending_ = 0;
-    uint64_t gen_ = 0;
-    bool stop_ = false;
+    std::atomic<int> pending_{0};
+    std::atomic<uint64_t> word_{0};  // generation << 8 | workers taking part
+    std::atomic<bool> stop_{false};
+    int n_ = 0;
 };
 
 Pool& pool() {
@@ -169,6 +187,28 @@ int32_t dot_i8(const int8_t* w, const int8_t* x, int n) {
     return acc;
 }
 
+// Same exact integer dot with AVX-512BW: int8 widened to int16, pairwise
+// products summed into int32 (|acc| stays far below 2^31), n % 32 == 0.
+__attribute__((target("avx512f,avx512bw"))) int32_t dot_i8_avx512(const int8_t* w, const int8_t* x, int n) {
+    __m512i acc = _mm512_setzero_si512();
+    for (int i = 0; i < n; i += 32) {
+        const __m512i wv = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + i)));
+        const __m512i xv = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(x + i)));
+        acc = _mm512_add_epi32(acc, _mm512_madd_epi16(wv, xv));
+    }
+    return _mm512_reduce_add_epi32(acc);
+}
+
+bool have_avx512bw() {
+    static const bool v = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+    return v;
+}
+
+bool have_avx512vl() {
+    static const bool v = __builtin_cpu_supports("avx512vl");
+    return v;
+}
+
 // 4-bit row (nibble plane row + fp16 scales) against fp32 activations
 float dot_q4(const uint8_t* q, const uint16_t* sc, const float* x, int n) {
     float acc = 0.0f;
@@ -183,6 +223,60 @@ float dot_q4(const uint8_t* q, const uint16_t* sc, const float* x, int n) {
         acc += half_to_float(sc[b]) * d;
     }
     return acc;
+}
+
+// 4-bit row against bf16 activations with AVX-512 BF16: each code q is put in
+// the mantissa of 0x4300 (the bf16 value 128 + q, exact), one dpbf16 gives
+// sum (q + 128) x over a 32-weight block, and the block's sum of x removes
+// the offset: sum (q - 8) x = sum (q + 128) x - 136 sum x.  Low nibbles are
+// inputs 0..15 of a block, high nibbles 16..31.  xsum: per-block sums of x.
+// one 32-weight block: acc += s * dpbf16(128 + q, x)
+__attribute__((target("avx512f,avx512bw,avx512bf16"), always_inline)) inline void q4_block(const uint8_t* q,
+                                                                                           const uint16_t* xb,
+                                                                                           float s, __m512& acc) {
+    const __m128i m4 = _mm_set1_epi8(0x0F);
+    const __m128i v = _mm_loadu_si128(reinterpret_cast<const __m128i*>(q));
+    const __m128i lo = _mm_and_si128(v, m4);
+    const __m128i hi = _mm_and_si128(_mm_srli_epi16(v, 4), m4);
+    const __m512i w16 = _mm512_or_si512(_mm512_cvtepu8_epi16(_mm256_set_m128i(hi, lo)), _mm512_set1_epi16(0x4300));
+    const __m512i xv = _mm512_loadu_si512(reinterpret_cast<const void*>(xb));
+    const __m512 d = _mm512_dpbf16_ps(_mm512_setzero_ps(), (__m512bh)w16, (__m512bh)xv);
+    acc = _mm512_fmadd_ps(_mm512_set1_ps(s), d, acc);
+}
+
+__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) float dot_q4_avx512(const uint8_t* q,
+                                                                                      const uint16_t* sc,
+                                                                                      const uint16_t* xb,
+                                                                                      const float* xsum, int n) {
+    __m512 acc0 = _mm512_setzero_ps(), acc1 = _mm512_setzero_ps(), corr = _mm512_setzero_ps();
+    const int nb = n / 32;
+    int b0 = 0;
+    for (; b0 + 16 <= nb; b0 += 16) {  // 16 scales at a time; the offset term as one vector FMA
+        const __m512 s16 = _mm512_cvtph_ps(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(sc + b0)));
+        corr = _mm512_fmadd_ps(s16, _mm512_loadu_ps(xsum + b0), corr);
+        alignas(64) float sa[16];
+        _mm512_store_ps(sa, s16);
+        for (int j = 0; j < 16; j += 2) {
+            q4_block(q + 16 * (b0 + j), xb + 32 * (b0 + j), sa[j], acc0);
+            q4_block(q + 16 * (b0 + j + 1), xb + 32 * (b0 + j + 1), sa[j + 1], acc1);
+        }
+    }
+    float tail = 0.0f;
+    for (; b0 < nb; ++b0) {
+        const float s = _cvtsh_ss(sc[b0]);
+        q4_block(q + 16 * b0, xb + 32 * b0, s, acc0);
+        tail += s * xsum[b0];
+    }
+    return _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1)) - 136.0f * (_mm512_reduce_add_ps(corr) + tail);
+}
+
+// per-block (32 inputs) sums of bf16 rows, fp32 in input order
+void block_sums(const uint16_t* x, int n, float* out) {
+    for (int b = 0; b < n / 32; ++b) {
+        float s = 0.0f;
+        for (int j = 0; j < 32; ++j) s += bf16f(x[32 * b + j]);
+        out[b] = s;
+    }
 }
 
 // symmetric int8 quantisation, fp32 decisions (as on the GPU)
@@ -240,6 +334,13 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     std::vector<int8_t> xq;
     std::vector<float> xs;
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x_h);
+    const bool q4_fast = w_type == MOE_W_Q4B32 && have_avx512bf16() && have_avx512bw() && have_avx512vl();
+    const bool i8_fast = w_type == MOE_W_W8A8 && have_avx512bw() && H % 32 == 0 && I % 32 == 0;
+    std::vector<float> xbs;  // 4-bit: per-block sums of x
+    if (q4_fast) {
+        xbs.resize((size_t)T * (H / 32));
+        for (int t = 0; t < T; ++t) block_sums(xb + (size_t)t * H, H, &xbs[(size_t)t * (H / 32)]);
+    }
     if (w_type == MOE_W_F32) {
         xf.assign(reinterpret_cast<const float*>(x_h), reinterpret_cast<const float*>(x_h) + (size_t)T * H);
     } else if (w_type == MOE_W_Q4B32 || w_type == MOE_W_W8A8) {
@@ -283,16 +384,23 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                         const int8_t* wu = reinterpret_cast<const int8_t*>(slab + lay.w[1]) + (size_t)r * H;
                         const float sg = reinterpret_cast<const float*>(slab + lay.s[0])[r];
                         const float su = reinterpret_cast<const float*>(slab + lay.s[1])[r];
-                        g = ((float)dot_i8(wg, &xq[(size_t)t * H], H) * xs[t]) * sg;
-                        u = ((float)dot_i8(wu, &xq[(size_t)t * H], H) * xs[t]) * su;
+                        const int8_t* xr = &xq[(size_t)t * H];
+                        g = ((float)(i8_fast ? dot_i8_avx512(wg, xr, H) : dot_i8(wg, xr, H)) * xs[t]) * sg;
+                        u = ((float)(i8_fast ? dot_i8_avx512(wu, xr, H) : dot_i8(wu, xr, H)) * xs[t]) * su;
                     } break;
                     default: {
                         const uint8_t* qg = slab + lay.w[0] + (size_t)r * (H / 2);
                         const uint8_t* qu = slab + lay.w[1] + (size_t)r * (H / 2);
                         const uint16_t* sg = reinterpret_cast<const uint16_t*>(slab + lay.s[0]) + (size_t)r * (H / 32);
                         const uint16_t* su = reinterpret_cast<const uint16_t*>(slab + lay.s[1]) + (size_t)r * (H / 32);
-                        g = dot_q4(qg, sg, &xf[(size_t)t * H], H);
-                        u = dot_q4(qu, su, &xf[(size_t)t * H], H);
+                        if (q4_fast) {
+                            const float* bs = &xbs[(size_t)t * (H / 32)];
+                            g = dot_q4_avx512(qg, sg, xb + (size_t)t * H, bs, H);
+                            u = dot_q4_avx512(qu, su, xb + (size_t)t * H, bs, H);
+                        } else {
+                            g = dot_q4(qg, sg, &xf[(size_t)t * H], H);
+                            u = dot_q4(qu, su, &xf[(size_t)t * H], H);
+                        }
                     } break;
                 }
                 float h;
@@ -313,10 +421,15 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
         for (int p : order) hs[p] = quant_row(&hf[(size_t)p * I], I, &hq[(size_t)p * I]);
     }
     std::vector<uint16_t> hb;
-    if (w_type == MOE_W_BF16 && bf16_fast) {
+    std::vector<float> hbs;  // 4-bit: per-block sums of h
+    if ((w_type == MOE_W_BF16 && bf16_fast) || q4_fast) {
         hb.resize((size_t)P * I);
         for (int p : order)
             for (int i = 0; i < I; ++i) hb[(size_t)p * I + i] = f2bf(hf[(size_t)p * I + i]);
+    }
+    if (q4_fast) {
+        hbs.resize((size_t)P * (I / 32));
+        for (int p : order) block_sums(&hb[(size_t)p * I], I, &hbs[(size_t)p * (I / 32)]);
     }
 
     // phase 2: down rows -> part[p][m] = w * o
@@ -347,12 +460,14 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                     case MOE_W_W8A8: {
                         const int8_t* wd = reinterpret_cast<const int8_t*>(slab + lay.w[2]) + (size_t)m * I;
                         const float sd = reinterpret_cast<const float*>(slab + lay.s[2])[m];
-                        o = ((float)dot_i8(wd, &hq[(size_t)p * I], I) * hs[p]) * sd;
+                        const int8_t* hr = &hq[(size_t)p * I];
+                        o = ((float)(i8_fast ? dot_i8_avx512(wd, hr, I) : dot_i8(wd, hr, I)) * hs[p]) * sd;
                     } break;
                     default: {
                         const uint8_t* qd = slab + lay.w[2] + (size_t)m * (I / 2);
                         const uint16_t* sd = reinterpret_cast<const uint16_t*>(slab + lay.s[2]) + (size_t)m * (I / 32);
-                        o = dot_q4(qd, sd, &hf[(size_t)p * I], I);
+                        o = q4_fast ? dot_q4_avx512(qd, sd, &hb[(size_t)p * I], &hbs[(size_t)p * (I / 32)], I)
+                                    : dot_q4(qd, sd, &hf[(size_t)p * I], I);
                     } break;
                 }
                 part[(size_t)p * H + m] = w_h[p] * o;

@@ -1,0 +1,232 @@
+// Native driver of one expert-slot layer step, and of a stack of such layers
+// joined by a residual stream: the entry points of moe_slot.h issued in the
+// order the method needs them, with no interpreter between the calls.
+//
+// sozai.app transcript "rtx-3060-run-35b-llamacpp", "Full Transcript": all the
+// GPU work of a layer runs as one unbroken sequence and the experts that stay
+// in RAM are run by the CPU meanwhile; one add joins the two.  "Porting
+// vllm-expert-cache to NVIDIA GPUs", "What this package does": manage, gather
+// and remap come before the expert FFN, which runs in slot space.
+//
+//   compute  [x -> host]  moe_route -> cache_manage -> (wait gather) -> moe_ffn_slots
+//                                                       -> y_host -> moe_combine [-> moe_residual]
+//   side                            `-> cache_gather (dynamic caches only)
+//   copy     x -> host (pinned);      picks | slots | weights -> host (pinned)
+//   caller's CPU thread               moe_ffn_host_misses once the picks are on the host
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include <new>
+
+#include "../../include/moe_slot.h"
+
+int moe_fail(int code, const char* fmt, ...);
+int moe_ok();
+
+struct moe_step {
+    int T_max, E, k, H, I, S, w_type, x_dtype;
+    size_t slab_bytes, ffn_ws_bytes;
+    // device
+    int32_t* meta;  // [3][T_max * k] picks, slots, weights, then 4 cache counters (one copy to the host)
+    float* logits;  // [T_max][E]
+    int32_t *miss, *n_miss, *host_miss, *n_host;
+    void* ffn_ws;
+    float *y, *y_host_dev;
+    void* xbuf[2];  // residual stream of a stack
+    // pinned host
+    void* h_x;
+    int32_t* h_meta;
+    float* h_y;
+    hipEvent_t ev_x, ev_manage, ev_gather, ev_copy;
+    int64_t stats_sum[4];  // cache counters summed over host-pass steps
+};
+
+namespace {
+
+int hip_fail(const char* what, hipError_t e) {
+    (void)hipGetLastError();
+    return moe_fail(MOE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+void release(moe_step* h) {
+    if (!h) return;
+    void* dev[] = {h->meta, h->logits, h->miss, h->n_miss, h->host_miss, h->n_host, h->ffn_ws,
+                   h->y, h->y_host_dev, h->xbuf[0], h->xbuf[1]};
+    for (void* p : dev)
+        if (p) (void)hipFree(p);
+    void* host[] = {h->h_x, h->h_meta, h->h_y};
+    for (void* p : host)
+        if (p) (void)hipHostFree(p);
+    hipEvent_t evs[] = {h->ev_x, h->ev_manage, h->ev_gather, h->ev_copy};
+    for (hipEvent_t e : evs)
+        if (e) (void)hipEventDestroy(e);
+    delete h;
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_step* moe_step_create(int T_max, int E, int k, int H, int I, int S, int w_type) {
+    if (T_max < 1 || E < 1 || k < 1 || k > E || H < 1 || I < 1 || S < 0 || S > E) {
+        moe_fail(MOE_E_ARG, "moe_step_create: T_max=%d E=%d k=%d H=%d I=%d S=%d out of range", T_max, E, k, H, I, S);
+        return nullptr;
+    }
+    moe_slab_layout_t lay;
+    if (moe_slab_layout(w_type, H, I, &lay)) return nullptr;
+    moe_step* h = new (std::nothrow) moe_step();
+    if (!h) {
+        moe_fail(MOE_E_NOMEM, "moe_step_create: out of host memory");
+        return nullptr;
+    }
+    h->T_max = T_max;
+    h->E = E;
+    h->k = k;
+    h->H = H;
+    h->I = I;
+    h->S = S;
+    h->w_type = w_type;
+    h->x_dtype = w_type == MOE_W_F32 ? MOE_X_F32 : MOE_X_BF16;
+    h->slab_bytes = (size_t)((lay.total + 15) / 16 * 16);
+    const size_t P = (size_t)T_max * k;
+    const size_t xb = h->x_dtype == MOE_X_F32 ? 4 : 2;
+    const int Sw = S > 0 ? S : 1;
+    h->ffn_ws_bytes = moe_ffn_workspace_bytes(T_max, k, Sw, w_type, H, I);
+    struct {
+        void** p;
+        size_t n;
+    } dev[] = {{(void**)&h->meta, 12 * P + 16},
+               {(void**)&h->logits, 4 * (size_t)T_max * E},
+               {(void**)&h->miss, 8 * (size_t)Sw},
+               {(void**)&h->n_miss, 16},
+               {(void**)&h->host_miss, 4 * (size_t)E},
+               {(void**)&h->n_host, 16},
+               {&h->ffn_ws, h->ffn_ws_bytes},
+               {(void**)&h->y, 4 * (size_t)T_max * H},
+               {(void**)&h->y_host_dev, 4 * (size_t)T_max * H},
+               {&h->xbuf[0], xb * T_max * H},
+               {&h->xbuf[1], xb * T_max * H}};
+    for (auto& d : dev) {
+        hipError_t e = hipMalloc(d.p, d.n);
+        if (e != hipSuccess) {
+            hip_fail("moe_step_create: hipMalloc", e);
+            release(h);
+            return nullptr;
+        }
+    }
+    struct {
+        void** p;
+        size_t n;
+    } host[] = {{&h->h_x, xb * T_max * H}, {(void**)&h->h_meta, 12 * P + 16}, {(void**)&h->h_y, 4 * (size_t)T_max * H}};
+    for (auto& d : host) {
+        hipError_t e = hipHostMalloc(d.p, d.n, hipHostMallocDefault);
+        if (e != hipSuccess) {
+            hip_fail("moe_step_create: hipHostMalloc", e);
+            release(h);
+            return nullptr;
+        }
+    }
+    hipEvent_t* evs[] = {&h->ev_x, &h->ev_manage, &h->ev_gather, &h->ev_copy};
+    for (hipEvent_t* e : evs) {
+        hipError_t r = hipEventCreateWithFlags(e, hipEventDisableTiming);
+        if (r != hipSuccess) {
+            hip_fail("moe_step_create: hipEventCreate", r);
+            release(h);
+            return nullptr;
+        }
+    }
+    moe_ok();
+    return h;
+}
+
+void moe_step_destroy(moe_step* h) { release(h); }
+
+const float* moe_step_output(const moe_step* h) { return h ? h->y : nullptr; }
+
+int moe_step_stats(moe_step* h, int64_t* out, int reset) {
+    if (!h || !out) return moe_fail(MOE_E_ARG, "moe_step_stats: NULL argument");
+    memcpy(out, h->stats_sum, sizeof(h->stats_sum));
+    if (reset) memset(h->stats_sum, 0, sizeof(h->stats_sum));
+    return moe_ok();
+}
+
+int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, const int32_t* ids_in, int host_pass,
+                   int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy) {
+    if (!h || !L || !x) return moe_fail(MOE_E_ARG, "moe_layer_step: NULL argument");
+    if (T < 0 || T > h->T_max) return moe_fail(MOE_E_SHAPE, "moe_layer_step: T=%d outside [0, %d]", T, h->T_max);
+    if (L->state.E != h->E || L->state.S != h->S || L->slab_bytes < h->slab_bytes)
+        return moe_fail(MOE_E_SHAPE, "moe_layer_step: layer (E=%d, S=%d, slab %zu) does not match the step (E=%d, S=%d)",
+                        L->state.E, L->state.S, L->slab_bytes, h->E, h->S);
+    if (T == 0) return moe_ok();
+    const int P = T * h->k, Pm = h->T_max * h->k;
+    const size_t xbytes = (size_t)T * h->H * (h->x_dtype == MOE_X_F32 ? 4 : 2);
+    float* y = y_out ? y_out : h->y;
+    int32_t* ids = h->meta;
+    int32_t* slot_ids = h->meta + Pm;
+    float* w = reinterpret_cast<float*>(h->meta + 2 * Pm);
+    hipError_t e;
+    int rc;
+    if (host_pass) {  // the host pass's activations leave while the router runs
+        if ((e = hipEventRecord(h->ev_x, s0)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+        if ((e = hipStreamWaitEvent(s_copy, h->ev_x, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
+        if ((e = hipMemcpyAsync(h->h_x, x, xbytes, hipMemcpyDeviceToHost, s_copy)) != hipSuccess)
+            return hip_fail("moe_layer_step: x to host", e);
+    }
+    if (ids_in) {
+        if ((e = hipMemcpyAsync(ids, ids_in, (size_t)P * 4, hipMemcpyDeviceToDevice, s0)) != hipSuccess)
+            return hip_fail("moe_layer_step: given picks", e);
+    }
+    if ((rc = moe_route(x, h->x_dtype, L->G, L->bias, ids_in ? ids : nullptr, T, h->H, h->E, h->k, ids, w, h->logits,
+                        s0)))
+        return rc;
+    if ((rc = cache_manage(&L->state, L->policy, ids, P, slot_ids, h->miss, h->n_miss, h->host_miss, h->n_host,
+                           h->meta + 3 * Pm, s0)))
+        return rc;
+    if ((e = hipEventRecord(h->ev_manage, s0)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+    if (L->policy != MOE_STATIC && h->S > 0) {
+        if ((e = hipStreamWaitEvent(s_side, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
+        if ((rc = cache_gather(h->miss, h->n_miss, h->S, L->host_store, L->slot_store, L->slab_bytes, s_side)))
+            return rc;
+        if ((e = hipEventRecord(h->ev_gather, s_side)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+        if ((e = hipStreamWaitEvent(s0, h->ev_gather, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
+    }
+    if ((rc = moe_ffn_slots(x, h->x_dtype, slot_ids, w, T, h->k, L->slot_store, L->slab_bytes, h->S > 0 ? h->S : 1,
+                            h->w_type, h->H, h->I, y, h->ffn_ws, h->ffn_ws_bytes, s0)))
+        return rc;
+    if (!host_pass) return moe_ok();
+    // picks, slots and weights to pinned memory in one copy, then the host pass on this thread
+    if ((e = hipStreamWaitEvent(s_copy, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
+    if ((e = hipMemcpyAsync(h->h_meta, h->meta, (size_t)12 * Pm + 16, hipMemcpyDeviceToHost, s_copy)) != hipSuccess)
+        return hip_fail("moe_layer_step: picks to host", e);
+    if ((e = hipEventRecord(h->ev_copy, s_copy)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+    if ((e = hipEventSynchronize(h->ev_copy)) != hipSuccess) return hip_fail("moe_layer_step: wait for picks", e);
+    const int32_t* h_ids = h->h_meta;
+    const int32_t* h_slot = h->h_meta + Pm;
+    const float* h_w = reinterpret_cast<const float*>(h->h_meta + 2 * Pm);
+    for (int i = 0; i < 4; ++i) h->stats_sum[i] += h->h_meta[3 * Pm + i];
+    int misses = 0;
+    for (int p = 0; p < P; ++p) misses += h_slot[p] < 0;
+    if (misses == 0) return moe_ok();  // every pick resident: nothing to add
+    if ((rc = moe_ffn_host_misses(h->h_x, h->x_dtype, h_ids, h_slot, h_w, T, h->k, L->host_store, L->slab_bytes, h->E,
+                                  h->w_type, h->H, h->I, h->h_y, n_threads)))
+        return rc;
+    if ((e = hipMemcpyAsync(h->y_host_dev, h->h_y, (size_t)T * h->H * 4, hipMemcpyHostToDevice, s0)) != hipSuccess)
+        return hip_fail("moe_layer_step: host result to device", e);
+    return moe_combine(y, h->y_host_dev, T, h->H, s0);
+}
+
+int moe_stack_step(moe_step* h, const moe_layer_desc* layers, int n_layers, const void* x, int T, int host_pass,
+                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy) {
+    if (!h || !layers || n_layers < 1 || !x || !x_out) return moe_fail(MOE_E_ARG, "moe_stack_step: bad arguments");
+    const void* cur = x;
+    for (int l = 0; l < n_layers; ++l) {
+        int rc = moe_layer_step(h, &layers[l], cur, T, nullptr, host_pass, n_threads, nullptr, s0, s_side, s_copy);
+        if (rc) return rc;
+        void* nxt = l + 1 == n_layers ? x_out : h->xbuf[l & 1];
+        if ((rc = moe_residual(cur, h->x_dtype, h->y, nxt, T, h->H, s0))) return rc;
+        cur = nxt;
+    }
+    return moe_ok();
+}
+
+}  // extern "C"

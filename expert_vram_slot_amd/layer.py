@@ -25,9 +25,10 @@ import os
 
 import torch
 
-from . import (MOE_W_F32, MOE_X_BF16, MOE_X_F32, POLICIES, cache_gather, cache_init, cache_manage, cache_state,
-               moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_residual, moe_route,
-               moe_slab_layout)
+from . import (MOE_W_F32, MOE_X_BF16, MOE_X_F32, POLICIES, LayerDesc, cache_gather, cache_init, cache_manage,
+               cache_state, moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_layer_step,
+               moe_residual, moe_route, moe_slab_layout, moe_stack_step, moe_step_create, moe_step_destroy,
+               moe_step_stats)
 
 
 def host_threads() -> int:
@@ -219,3 +220,75 @@ class SlotStack:
             moe_residual(cur, L.x_dtype, y, nxt, T, self.H)
             cur = nxt
         return cur.view(x.dtype).view(T, self.H)
+
+
+class NativeStack:
+    """The same layers as SlotStack driven by the library's native step
+    driver (moe_layer_step / moe_stack_step): one call per layer or per whole
+    stack, no Python between the entry points of a step.
+
+    layers: list of dicts with host_store (pinned), slot_store, G, bias (or
+    None), resident (device int32 [S], or None for an empty dynamic cache)
+    and optionally policy ("static" by default).
+    """
+
+    def __init__(self, *, E, k, H, I, S, w_type, T_max, layers, n_threads=None, device="cuda"):
+        dev = torch.device(device)
+        self.E, self.k, self.H, self.I, self.S, self.T_max = E, k, H, I, S, T_max
+        self.x_dtype = MOE_X_F32 if w_type == MOE_W_F32 else MOE_X_BF16
+        self.n_threads = n_threads or host_threads()
+        self.h = moe_step_create(T_max, E, k, H, I, S, w_type)
+        self.side = torch.cuda.Stream(device=dev)
+        self.copy = torch.cuda.Stream(device=dev)
+        self.keep = []  # tensors the descriptors point at
+        descs = (LayerDesc * len(layers))()
+        for i, spec in enumerate(layers):
+            i32 = dict(dtype=torch.int32, device=dev)
+            st_t = [torch.empty(E, **i32), torch.empty(max(S, 1), **i32), torch.empty(max(S, 1), **i32),
+                    torch.empty(max(S, 1), **i32), torch.zeros(1, **i32)]
+            st = cache_state(*st_t, E, S)
+            cache_init(st, spec.get("resident"))
+            self.keep.append((st_t, spec))
+            d = descs[i]
+            d.G = spec["G"].data_ptr()
+            d.bias = spec["bias"].data_ptr() if spec.get("bias") is not None else None
+            d.state = st
+            d.policy = POLICIES.get(spec.get("policy", "static"), spec.get("policy", 0))
+            d.slot_store = spec["slot_store"].data_ptr()
+            d.host_store = spec["host_store"].data_ptr()
+            d.slab_bytes = int(spec["host_store"].shape[1])
+        self.descs = descs
+        xb = 4 if self.x_dtype == MOE_X_F32 else 2
+        self.out = torch.empty(T_max * H * xb, dtype=torch.uint8, device=dev)
+        self.y = torch.empty(T_max * H, dtype=torch.float32, device=dev)
+
+    def e2s(self, l):
+        return self.keep[l][0][0]
+
+    def layer_step(self, l, x, T, ids_in=None, host_pass=True):
+        """One layer; returns y [T][H] fp32 (a view of this object's output buffer)."""
+        moe_layer_step(self.h, self.descs[l], x, T, ids_in, host_pass, self.n_threads, self.y,
+                       torch.cuda.current_stream(), self.side, self.copy)
+        return self.y[:T * self.H].view(T, self.H)
+
+    def step(self, x, T, host_pass=True):
+        """All layers with the residual join; returns the last residual output [T][H]."""
+        moe_stack_step(self.h, self.descs, x, T, host_pass, self.n_threads, self.out, torch.cuda.current_stream(),
+                       self.side, self.copy)
+        nb = T * self.H * (4 if self.x_dtype == MOE_X_F32 else 2)
+        return self.out[:nb].view(x.dtype).view(T, self.H)
+
+    def stats(self, reset=False):
+        return moe_step_stats(self.h, reset)
+
+    def close(self):
+        if self.h:
+            moe_step_destroy(self.h)
+            self.h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+

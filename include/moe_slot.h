@@ -265,6 +265,68 @@ int moe_residual(const void* x, int x_dtype, const float* y, void* x_out, int T,
 void* moe_host_alloc(size_t bytes);
 int moe_host_free(void* p);
 
+/* ------------------------------------------------------------------------
+ * Native step driver.  The entry points above issued in the order of one
+ * layer step ([RTX] "Full Transcript": the GPU work of a layer runs as one
+ * unbroken sequence while the CPU runs the experts that stay in RAM; one add
+ * joins them.  [VEC] "What this package does": manage, gather and remap
+ * before the expert FFN), without an interpreter between the calls.
+ *
+ * A layer as the driver sees it (every pointer owned by the caller):
+ *   G           device [E][H] router gate (activation format)
+ *   bias        device float[E] selection bias or NULL
+ *   state       the layer's cache state (device arrays)
+ *   policy      MOE_STATIC / MOE_LRU / MOE_LFU
+ *   slot_store  device [S][slab_bytes]
+ *   host_store  pinned, device-mapped host [E][slab_bytes]
+ */
+typedef struct {
+    const void* G;
+    const float* bias;
+    moe_cache_state state;
+    int policy;
+    void* slot_store;
+    const void* host_store;
+    size_t slab_bytes;
+} moe_layer_desc;
+
+/* Buffers, events and pinned staging of one step shape (T <= T_max tokens
+ * over E experts, top-k, S slots, one weight format).  Created once: this is
+ * where the driver allocates (device memory, pinned host memory, events);
+ * the step calls allocate nothing.  NULL on failure (reason in
+ * moe_last_error). */
+typedef struct moe_step moe_step;
+moe_step* moe_step_create(int T_max, int E, int k, int H, int I, int S, int w_type);
+void moe_step_destroy(moe_step* h);
+/* device float[T_max][H]: y of the last moe_layer_step called with
+ * y_out = NULL (valid in stream order). */
+const float* moe_step_output(const moe_step* h);
+/* Cache counters (cache_manage's stats: routing ids resident at entry,
+ * distinct experts needed, gathered, host misses) summed over the steps run
+ * with the host pass; out int64[4]; reset != 0 clears the sums. */
+int moe_step_stats(moe_step* h, int64_t* out, int reset);
+
+/* One layer step for T tokens of x (device [T][H], activation format):
+ * moe_route (ids_in: given device picks [T][k] or NULL) -> cache_manage ->
+ * cache_gather on s_side (dynamic caches) -> moe_ffn_slots on s0, and with
+ * host_pass != 0: x and the picks go to pinned memory on s_copy, this thread
+ * waits for them and runs moe_ffn_host_misses on n_threads threads, the
+ * result is added on s0 (moe_combine).  y_out: device float[T][H] out, or
+ * NULL for the driver's own buffer (moe_step_output); final in s0's order
+ * when the call returns.  The three streams must be distinct streams of one
+ * device.  Errors: those of the entry points it calls; SHAPE when the layer
+ * does not match the step. */
+int moe_layer_step(moe_step* h, const moe_layer_desc* layer, const void* x, int T, const int32_t* ids_in,
+                   int host_pass, int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side,
+                   hipStream_t s_copy);
+
+/* n_layers layer steps joined by moe_residual: x_{l+1} = x_l + y_l in the
+ * activation format ([PGO] "Experts that don't fit": a deep model of routed
+ * layers).  x_out: device [T][H] out, the last layer's residual output (may
+ * not alias x). */
+int moe_stack_step(moe_step* h, const moe_layer_desc* layers, int n_layers, const void* x, int T, int host_pass,
+                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy);
+
 #ifdef __cplusplus
 }
 #endif

@@ -563,3 +563,100 @@ def test_residual_matches_oracle(m):
     xfo = torch.empty((7, 64), dtype=torch.float32, device="cuda")
     m.moe_residual(dev(xf), 0, dev(y[:7, :64].copy()), xfo, 7, 64)
     np.testing.assert_array_equal(host(xfo), oracle.residual(xf, 0, y[:7, :64]))
+
+
+# ------------------------------------------------------- native step driver
+
+
+def _layer_spec(li, resident, policy="static", S=None):
+    S = len(resident) if S is None else S
+    slots = torch.zeros((max(S, 1), li.slab), dtype=torch.uint8, device="cuda")
+    if policy == "static":
+        slots[:len(resident)] = dev(li.store[np.asarray(resident)])
+    return dict(host_store=torch.from_numpy(li.store).pin_memory(), slot_store=slots,
+                G=dev(li.G.view(np.int16) if li.x_dtype else li.G), bias=None,
+                resident=dev(np.asarray(resident, np.int32)) if policy == "static" else None, policy=policy)
+
+
+@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 8)])
+def test_native_layer_step_equals_python_orchestration(m, cfg, T):
+    """moe_layer_step issues the same kernels as SlotLayer: identical bits, and the oracle's layer."""
+    from expert_vram_slot_amd.layer import NativeStack, SlotLayer
+    li = synth.LayerInputs(cfg, T=T)
+    z = oracle.logits(li.x, li.x_dtype, li.G)
+    ids = oracle.topk(z, li.k)
+    w = oracle.route_weights(z, ids)
+    S = li.c["S"]
+    resident = li.c.get("resident") or oracle.pick_static(ids, li.E, S)
+    spec = _layer_spec(li, resident)
+    nat = NativeStack(E=li.E, k=li.k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, layers=[spec])
+    x = dev(li.x.view(np.int16) if li.x_dtype else li.x)
+    y_nat = host(nat.layer_step(0, x, T))
+    L = SlotLayer(E=li.E, k=li.k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, policy="static",
+                  host_store=spec["host_store"], slot_store=spec["slot_store"], G=spec["G"])
+    L.init_cache(spec["resident"])
+    y_py = host(L.step(x, T))
+    np.testing.assert_array_equal(y_nat, y_py)
+    yf, _, _ = oracle.layer(li.w_type, li.store, li.E, li.H, li.I, li.x, li.x_dtype, ids, w)
+    assert_close(y_nat, yf, li.w_type, f"native {cfg} T={T}")
+    hits, distinct, gathered, nhost = nat.stats()
+    e2s = np.full(li.E, -1, np.int32)
+    e2s[np.asarray(resident)] = np.arange(S)
+    assert hits == int(np.sum(e2s[ids] >= 0)) and gathered == 0
+    nat.close()
+
+
+def test_native_dynamic_cache_steps(m):
+    """A W8A8 layer with 32 LRU slots from empty, Zipf picks given: each step
+    of the native driver equals the Python orchestration bit for bit, and the
+    oracle's layer with the oracle's cache state machine."""
+    from expert_vram_slot_amd.layer import NativeStack, SlotLayer
+    li = synth.LayerInputs("c3", T=16)
+    E, k, S, T = li.E, li.k, 32, 16
+    steps = 6
+    seq = synth.zipf_ids(synth.key(li.base, synth.TAG_ZIPF_PERM), synth.key(li.base, synth.TAG_ZIPF_DRAW),
+                         steps * T, E, k, 0.8).reshape(steps, T, k)
+    spec = _layer_spec(li, [], policy="lru", S=S)
+    spec_py = dict(spec, slot_store=torch.zeros_like(spec["slot_store"]))
+    nat = NativeStack(E=E, k=k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, layers=[spec])
+    L = SlotLayer(E=E, k=k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, policy="lru",
+                  host_store=spec_py["host_store"], slot_store=spec_py["slot_store"], G=spec_py["G"])
+    L.init_cache(None)
+    cache = oracle.Cache(E, S, "lru")
+    for st in range(steps):
+        x_np = synth.normal(synth.key(li.base, synth.TAG_X, 0, 100 + st), (T, li.H), 1.0, 1)
+        x = dev(x_np.view(np.int16))
+        ids_in = dev(seq[st])
+        y_nat = host(nat.layer_step(0, x, T, ids_in=ids_in))
+        y_py = host(L.step(x, T, ids_in=ids_in))
+        np.testing.assert_array_equal(y_nat, y_py, err_msg=f"step {st}")
+        z = oracle.logits(x_np, 1, li.G)
+        w = oracle.route_weights(z, seq[st])
+        sl = cache.manage(seq[st])["slot_ids"].reshape(T, k)
+        yf, _, _ = oracle.layer(li.w_type, li.store, E, li.H, li.I, x_np, 1, seq[st], w, sl)
+        assert_close(y_nat, yf, li.w_type, f"dynamic step {st}")
+    np.testing.assert_array_equal(host(nat.e2s(0)), cache.e2s)
+    nat.close()
+
+
+@pytest.mark.parametrize("T", [1, 32])
+def test_native_stack_equals_python_stack(m, T):
+    from expert_vram_slot_amd.layer import NativeStack, SlotStack
+    layers = stack_layers()
+    li0 = layers[0][0]
+    E, k, H, I, S, cap = li0.E, li0.k, li0.H, li0.I, li0.c["S"], li0.c["cap"]
+    specs = []
+    for li, b, resident in layers:
+        bias = torch.empty(E, dtype=torch.float32, device="cuda")
+        m.moe_bias_table(dev(b), E, S, cap, bias)
+        specs.append(dict(host_store=torch.from_numpy(li.store).pin_memory(), slot_store=dev(li.store[resident]),
+                          G=dev(li.G.view(np.int16)), bias=bias, resident=dev(resident)))
+    x0 = dev(synth.LayerInputs("c4", layer=0, T=T, with_store=False).x.view(np.int16))
+    py = SlotStack(E=E, k=k, H=H, I=I, S=S, w_type=3, T_max=T, layers=specs)
+    out_py = host(py.step(x0, T))
+    nat = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=3, T_max=T, layers=specs)
+    out_nat = host(nat.step(x0, T))
+    np.testing.assert_array_equal(out_nat, out_py)
+    out_nat2 = host(nat.step(x0, T))
+    np.testing.assert_array_equal(out_nat2, out_py)
+    nat.close()
