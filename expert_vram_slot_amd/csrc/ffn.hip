@@ -37,13 +37,16 @@ using v4u = uint32_t __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int FFN_THREADS = 256;
-constexpr int NTMAX = 8;       // tokens of one slot handled per pass
+constexpr int NTMAX = 4;       // tokens of one slot handled per pass
 constexpr int RPW_GU = 1;      // gate rows (and as many up rows) per wave
 constexpr int RPW_DN = 4;      // down rows per wave
 constexpr int GROUP_THREADS = 1024;
+constexpr int GU_REP = 1;  // row tiles per gate/up workgroup (taken one after the other)
+constexpr int DN_REP = 1;  // row tiles per down workgroup
+constexpr bool X_PREFETCH = true;  // activation granules one chunk ahead (16-byte activation granules)
 constexpr int GROUP_MULTI_P = 4096;  // larger batches sort with one workgroup per 1024 picks
 // bf16 batches with at least this many picks take the MFMA grouped-GEMM path
-constexpr int PF_MIN_P = 2048;
+constexpr int PF_MIN_P = 512;
 
 // ------------------------------------------------------------ formats
 
@@ -130,6 +133,29 @@ __device__ __forceinline__ void granule_dot(const v4u& w, const unsigned char* x
 
 __device__ __forceinline__ float half_bits_to_f32(uint16_t h) { return (float)__builtin_bit_cast(_Float16, h); }
 
+// granule_dot for formats whose activation granule is 16 bytes (fp32, bf16,
+// int8), with that granule already in registers.
+template <int F>
+__device__ __forceinline__ void granule_dot_reg(const v4u& w, const v4u& xv, typename Fmt<F>::Acc& acc) {
+    static_assert(F != MOE_W_Q4B32, "4-bit activations span 64 bytes per granule");
+    if constexpr (F == MOE_W_F32) {
+        acc = fmaf(__uint_as_float(w.x), __uint_as_float(xv.x), acc);
+        acc = fmaf(__uint_as_float(w.y), __uint_as_float(xv.y), acc);
+        acc = fmaf(__uint_as_float(w.z), __uint_as_float(xv.z), acc);
+        acc = fmaf(__uint_as_float(w.w), __uint_as_float(xv.w), acc);
+    } else if constexpr (F == MOE_W_BF16) {
+        acc = dot2bf(w.x, xv.x, acc);
+        acc = dot2bf(w.y, xv.y, acc);
+        acc = dot2bf(w.z, xv.z, acc);
+        acc = dot2bf(w.w, xv.w, acc);
+    } else {
+        acc = __builtin_amdgcn_sdot4((int)w.x, (int)xv.x, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.y, (int)xv.y, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.z, (int)xv.z, acc, false);
+        acc = __builtin_amdgcn_sdot4((int)w.w, (int)xv.w, acc, false);
+    }
+}
+
 
 // ---------------------------------------------------------- workspace
 
@@ -187,13 +213,30 @@ __device__ __forceinline__ int wave_slot_rank(int s, bool valid, int nbits, int*
     return __popcll(mask & lt);
 }
 
+// Tiles of the grouped GEMM: ceil(cnt / MOE_PF_MT) per slot, slots in
+// ascending order.  Called by the whole workgroup (thread s holds slot s's
+// pick count and offset; S <= blockDim.x); tiles == NULL writes nothing.
+__device__ __forceinline__ void write_pf_tiles(int cnt, int off, int S, int* scratch, moe_pf_tile* tiles,
+                                               int32_t* n_tiles) {
+    if (!tiles) return;
+    const int s = threadIdx.x;
+    const int nc = (s < S) ? (cnt + MOE_PF_MT - 1) / MOE_PF_MT : 0;
+    int tot;
+    const int toff = moe::block_exclusive_scan(nc, scratch, &tot);
+    for (int c = 0; c < nc; ++c)
+        tiles[toff + c] = moe_pf_tile{off + c * MOE_PF_MT, min(MOE_PF_MT, cnt - c * MOE_PF_MT), s, 0};
+    if (threadIdx.x == 0) *n_tiles = tot;
+}
+
 // Stable counting sort of the P picks by slot.  Picks are taken 1024 at a
 // time; inside a wave the picks with the same slot are found with one ballot
 // per slot-id bit, their order is the lane order; per-wave counts are
 // prefix-summed per slot across the 16 waves.  Pass 0 counts, pass 1 places.
 __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restrict__ slot_ids, int P, int S,
                                                          int32_t* __restrict__ slot_off, int32_t* __restrict__ pair_list,
-                                                         int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+                                                         int32_t* __restrict__ active, int32_t* __restrict__ n_active,
+                                                         moe_pf_tile* __restrict__ pf_tiles,
+                                                         int32_t* __restrict__ pf_n_tiles) {
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
     __shared__ int ctot[MOE_MAX_S];
@@ -246,6 +289,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             const int apos = moe::block_exclusive_scan(flag, scratch, &na);
             if (flag) active[apos] = tid;
             if (tid == 0) *n_active = na;
+            write_pf_tiles(cnt, off, S, scratch, pf_tiles, pf_n_tiles);
             __syncthreads();
         }
     }
@@ -274,7 +318,9 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
                                                                int32_t* __restrict__ slot_off,
                                                                int32_t* __restrict__ pair_list,
                                                                int32_t* __restrict__ active,
-                                                               int32_t* __restrict__ n_active) {
+                                                               int32_t* __restrict__ n_active,
+                                                               moe_pf_tile* __restrict__ pf_tiles,
+                                                               int32_t* __restrict__ pf_n_tiles) {
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
     __shared__ int scratch[GROUP_THREADS / 64 + 1];
@@ -298,6 +344,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
         const int apos = moe::block_exclusive_scan(flag, scratch, &na);
         if (flag) active[apos] = tid;
         if (tid == 0) *n_active = na;
+        write_pf_tiles(tot, off, S, scratch, pf_tiles, pf_n_tiles);
     }
     for (int i = tid; i < (GROUP_THREADS / 64) * S; i += GROUP_THREADS) wtab[i / S][i % S] = 0;
     __syncthreads();
@@ -443,13 +490,37 @@ __device__ __forceinline__ void gemv_rows(const RowPtrs<ROWS>& rp, const ActRows
                     qs[j][i] = 0.0f;
                 }
             }
+        }
+        if constexpr (F == MOE_W_Q4B32 || !X_PREFETCH) {
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const unsigned char* xa = ar.base + (size_t)arow[t] * ar.row_bytes + (size_t)gj[j] * XG;
-                float xsum = 0.0f;
-                if constexpr (F == MOE_W_Q4B32) xsum = ar.bsum[(size_t)arow[t] * KG + gj[j]];
+            for (int j = 0; j < NCHG; ++j) {
 #pragma unroll
-                for (int i = 0; i < RL; ++i) granule_dot<F>(w[j][i], xa, qs[j][i], xsum, acc[i * NT + t]);
+                for (int t = 0; t < NT; ++t) {
+                    const unsigned char* xa = ar.base + (size_t)arow[t] * ar.row_bytes + (size_t)gj[j] * XG;
+                    float xsum = 0.0f;
+                    if constexpr (F == MOE_W_Q4B32) xsum = ar.bsum[(size_t)arow[t] * KG + gj[j]];
+#pragma unroll
+                    for (int i = 0; i < RL; ++i) granule_dot<F>(w[j][i], xa, qs[j][i], xsum, acc[i * NT + t]);
+                }
+            }
+        } else {
+            // activation granules of every token: chunk j + 1 in flight while chunk j is used
+            v4u xr[2][NT];
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                xr[0][t] = *reinterpret_cast<const v4u*>(ar.base + (size_t)arow[t] * ar.row_bytes + (size_t)gj[0] * 16);
+#pragma unroll
+            for (int j = 0; j < NCHG; ++j) {
+                if (j + 1 < NCHG) {
+#pragma unroll
+                    for (int t = 0; t < NT; ++t)
+                        xr[(j + 1) & 1][t] = *reinterpret_cast<const v4u*>(ar.base + (size_t)arow[t] * ar.row_bytes +
+                                                                           (size_t)gj[j + 1] * 16);
+                }
+#pragma unroll
+                for (int t = 0; t < NT; ++t)
+#pragma unroll
+                    for (int i = 0; i < RL; ++i) granule_dot_reg<F>(w[j][i], xr[j & 1][t], acc[i * NT + t]);
             }
         }
     }
@@ -573,10 +644,15 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
                                                     const int32_t* __restrict__ n_active, void* __restrict__ hbuf,
                                                     int tiles) {
     constexpr int ROWS = 2 * RPW_GU;
-    const int a = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int tiles_l = (tiles + GU_REP - 1) / GU_REP;  // workgroups per slot
+    const int a = blockIdx.x / tiles_l;
     if (a >= *n_active) return;
     const int s = active[a];
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
+#pragma unroll
+    for (int rep = 0; rep < GU_REP; ++rep) {
+    const int tile = blockIdx.x % tiles_l + rep * tiles_l;
+    if (tile >= tiles) break;
     const int r_base = tile * (4 * RPW_GU) + (threadIdx.x >> 6) * RPW_GU;
     const int KG = H / Fmt<F>::EPG;
     const size_t row_bytes = (size_t)KG * 16;
@@ -597,6 +673,7 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
 #define MOE_GU(N) gu_pass<F, N, NCHG>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, k, r_base, xscale, hbuf)
         MOE_NT_DISPATCH(nt, MOE_GU);
 #undef MOE_GU
+    }
     }
 }
 
@@ -644,10 +721,15 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, float* __restrict__ part,
                                                       int tiles) {
-    const int a = blockIdx.x / tiles, tile = blockIdx.x % tiles;
+    const int tiles_l = (tiles + DN_REP - 1) / DN_REP;  // workgroups per slot
+    const int a = blockIdx.x / tiles_l;
     if (a >= *n_active) return;
     const int s = active[a];
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
+#pragma unroll
+    for (int rep = 0; rep < DN_REP; ++rep) {
+    const int tile = blockIdx.x % tiles_l + rep * tiles_l;
+    if (tile >= tiles) break;
     const int r_base = tile * (4 * RPW_DN) + (threadIdx.x >> 6) * RPW_DN;
     const int KG = I / Fmt<F>::EPG;
     const size_t row_bytes = (size_t)KG * 16;
@@ -666,6 +748,7 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
     down_pass<F, N, NCHG, LPR>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
         MOE_NT_DISPATCH(nt, MOE_DN);
 #undef MOE_DN
+    }
     }
 }
 
@@ -721,6 +804,12 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     void* hbuf = ws + L.h;
     float* part = reinterpret_cast<float*>(ws + L.part);
     int rc;
+    // bf16 batches of PF_MIN_P picks or more run on the MFMA grouped GEMM; the sort writes its tile list
+    const bool use_pf = F == MOE_W_BF16 && P >= PF_MIN_P && moe_pf_supported(F, H, I);
+    moe_pf_tile* pf_tiles = use_pf ? reinterpret_cast<moe_pf_tile*>(ws + L.pf_tiles) : nullptr;
+    int32_t* pf_n_tiles = use_pf ? reinterpret_cast<int32_t*>(ws + L.pf_tiles + (size_t)moe_pf_max_tiles(T, k, S) *
+                                                                                     sizeof(moe_pf_tile))
+                                 : nullptr;
 
     if (P > GROUP_MULTI_P) {
         const int nch = (P + GROUP_THREADS - 1) / GROUP_THREADS;
@@ -728,17 +817,17 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt);
         if ((rc = moe_check_launch("moe_ffn_slots/group_hist"))) return rc;
         hipLaunchKernelGGL(k_group_place, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt, nch, slot_off,
-                           pair_list, active, n_active);
+                           pair_list, active, n_active, pf_tiles, pf_n_tiles);
         if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
     } else {
         hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
-                           n_active);
+                           n_active, pf_tiles, pf_n_tiles);
         if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
     }
 
-    if (F == MOE_W_BF16 && P >= PF_MIN_P && moe_pf_supported(F, H, I)) {
-        rc = moe_pf_run(x, w, T, k, slot_store, slab_bytes, S, H, I, lay, slot_off, pair_list, active, n_active,
-                        ws + L.pf_tiles, hbuf, part, st);
+    if (use_pf) {
+        rc = moe_pf_run(x, w, T, k, slot_store, slab_bytes, S, H, I, lay, pair_list, ws + L.pf_tiles, hbuf, part,
+                        st);
         if (rc) return rc;
         const int64_t n4 = (int64_t)T * (H / 4);
         hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, slot_ids, T, k, S,
@@ -769,7 +858,8 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
     const int tiles_gu = (I + 4 * RPW_GU - 1) / (4 * RPW_GU);
 #define MOE_LAUNCH_GU(G)                                                                                       \
-    hipLaunchKernelGGL((k_gu<F, G>), dim3(S * tiles_gu), dim3(FFN_THREADS), 0, st, gv, gu_act, xscale, xbsum, H, \
+    hipLaunchKernelGGL((k_gu<F, G>), dim3(S * ((tiles_gu + GU_REP - 1) / GU_REP)), dim3(FFN_THREADS), 0, st, gv,    \
+                       gu_act, xscale, xbsum, H,                                                                    \
                        I, k, slot_off, pair_list, active, n_active, hbuf, tiles_gu)
     MOE_NCHG_DISPATCH(H / Fmt<F>::EPG, MOE_LAUNCH_GU);
 #undef MOE_LAUNCH_GU
@@ -797,7 +887,8 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
     const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
 #define MOE_LAUNCH_DN(G, LP)                                                                                 \
-    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(S * tiles_dn), dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, \
+    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(S * ((tiles_dn + DN_REP - 1) / DN_REP)), dim3(FFN_THREADS), 0, st, \
+                       dv, dn_act, hscale, hbsum,                                                                   \
                        w, H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
     MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
 #undef MOE_LAUNCH_DN

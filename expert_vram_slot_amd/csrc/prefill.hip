@@ -7,16 +7,17 @@
 // this package does": the expert FFN runs in slot space), arranged as grouped
 // GEMMs once a slot holds tens of tokens:
 //
-//   k_group      picks sorted by slot (shared with the decode path)
-//   k_pf_tiles   the list of (slot, up to PF_MT consecutive picks) tiles
+//   k_group      picks sorted by slot (shared with the decode path), and the
+//                list of (slot, up to PF_MT consecutive picks) tiles
 //   k_pf_gemm<GU>   [g | u] = X_s [W_g; W_u]^T per tile of 64 h columns,
 //                   SwiGLU epilogue, h (bf16, RNE) stored in sorted-pick order
 //   k_pf_gemm<DOWN> O = H_s W_d^T per tile of 128 output columns,
 //                   part[pick] = w * O (fp32)
 //   k_reduce     y[t] = sum over resident picks in top-k order (decode path's)
 //
-// A workgroup owns PF_MT = 128 token rows x 128 weight rows and walks K in
-// steps of 64.  Each k-step is fetched into registers two steps ahead and
+// A workgroup owns PF_MT = 128 token rows x NB * 32 weight rows (NB = 4 for
+// large batches; NB = 2 for decode-sized ones, which gives twice the
+// workgroups and three of them per CU) and walks K in steps of 64.  Each k-step is fetched into registers two steps ahead and
 // stored to one of two LDS buffers; 16-byte chunks are XOR-swizzled per row
 // so that both the stores and the MFMA operand reads are free of bank
 // conflicts.  Each wave owns 32 of the token rows; a wave whose rows are all
@@ -36,14 +37,15 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 using v4u = uint32_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_THREADS = 256;
-constexpr int PF_MT = 128;         // token rows per tile
+constexpr int PF_MT = MOE_PF_MT;   // token rows per tile
 constexpr int PF_NT = 128;         // weight rows per tile
 constexpr int PF_KT = 64;          // k per step (128 bytes of bf16 per row)
 constexpr int PF_ROWB = PF_KT * 2; // bytes of one row of a k-step
-constexpr int PF_TILE_BYTES = PF_MT * PF_ROWB;  // 16 KiB, same for A and B
-constexpr int PF_LDS = 2 * 2 * PF_TILE_BYTES;   // two buffers of A and B
+constexpr int PF_TILE_BYTES = PF_MT * PF_ROWB;  // 16 KiB: the A tile of one k-step
+// LDS of a workgroup whose B tile has NB blocks of 32 weight rows: two buffers of A and B
+constexpr int pf_lds_bytes(int NB) { return 2 * (PF_TILE_BYTES + NB * 32 * PF_ROWB); }
 constexpr int PF_XCD = 8;
-constexpr int PF_TILE_THREADS = 1024;
+constexpr int PF_BIG_P = 4096;  // picks from which the weight tiles are full height
 
 enum { PF_GU = 0, PF_DOWN = 1 };
 
@@ -52,46 +54,7 @@ enum { PF_GU = 0, PF_DOWN = 1 };
 // land on distinct chunks.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-struct PfTile {
-    int p0;     // first position in the slot-sorted pick list
-    int rows;   // picks of the tile (1..PF_MT)
-    int slot;
-    int pad;
-};
-
-// One workgroup: the tiles of every active slot, ceil(n_s / PF_MT) each.
-__global__ void __launch_bounds__(PF_TILE_THREADS) k_pf_tiles(const int32_t* __restrict__ slot_off,
-                                                              const int32_t* __restrict__ active,
-                                                              const int32_t* __restrict__ n_active,
-                                                              PfTile* __restrict__ tiles, int32_t* __restrict__ n_tiles,
-                                                              int max_tiles) {
-    __shared__ int scratch[PF_TILE_THREADS / 64 + 1];
-    __shared__ int base;
-    const int na = *n_active;
-    if (threadIdx.x == 0) base = 0;
-    __syncthreads();
-    for (int a0 = 0; a0 < na; a0 += PF_TILE_THREADS) {
-        const int a = a0 + threadIdx.x;
-        int s = -1, p0 = 0, ns = 0, nc = 0;
-        if (a < na) {
-            s = active[a];
-            p0 = slot_off[s];
-            ns = slot_off[s + 1] - p0;
-            nc = (ns + PF_MT - 1) / PF_MT;
-        }
-        int tot;
-        const int off = moe::block_exclusive_scan(nc, scratch, &tot);
-        const int b = base;
-        for (int c = 0; c < nc; ++c) {
-            const int e = b + off + c;
-            if (e < max_tiles) tiles[e] = PfTile{p0 + c * PF_MT, min(PF_MT, ns - c * PF_MT), s, 0};
-        }
-        __syncthreads();
-        if (threadIdx.x == 0) base = b + tot;
-        __syncthreads();
-    }
-    if (threadIdx.x == 0) *n_tiles = min(base, max_tiles);
-}
+using PfTile = moe_pf_tile;
 
 struct PfArgs {
     const unsigned char* slots;  // slot store
@@ -114,8 +77,10 @@ __device__ __forceinline__ v4u ld16_nt(const unsigned char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
 }
 
-template <int MODE>
+template <int MODE, int NB>
 __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
+    constexpr int HC = NB * 16;                          // gate/up: h columns per tile
+    constexpr int B_BYTES = NB * 32 * PF_ROWB;           // B tile of one k-step
     extern __shared__ __attribute__((aligned(16))) unsigned char pf_lds[];
     // workgroup -> (tile, column tile): the column tiles of one token tile share an XCD
     const int b = blockIdx.x;
@@ -128,10 +93,10 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
     const size_t row_bytes = (size_t)g.K * 2;
 
-    // this thread's 4 A rows and 4 B rows (row = q * 32 + tid / 8, chunk tid % 8)
+    // this thread's 4 A rows and NB B rows (row = q * 32 + tid / 8, chunk tid % 8)
     const int lrow = tid >> 3, chunk = tid & 7;
     const unsigned char* arow[4];
-    const unsigned char* brow[4];
+    const unsigned char* brow[NB];
     int soff[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -142,68 +107,70 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
         if constexpr (MODE == PF_GU) arow_idx = g.pair_list[pos] / g.k;   // token of the pick
         else arow_idx = pos;                                             // h row in sorted order
         arow[q] = g.act + (size_t)arow_idx * row_bytes + chunk * 16;
-        int wr;
-        int64_t plane;
-        if constexpr (MODE == PF_GU) {  // rows 0..63 gate, 64..127 up, of h columns jn*64 ..
-            plane = r < 64 ? g.w0 : g.w1;
-            wr = jn * 64 + (r & 63);
-        } else {
-            plane = g.w0;
-            wr = jn * PF_NT + r;
-        }
-        brow[q] = slab + plane + (size_t)wr * row_bytes + chunk * 16;
         soff[q] = r * PF_ROWB + ((chunk ^ swz(r)) * 16);
+        if (q < NB) {
+            int wr;
+            int64_t plane;
+            if constexpr (MODE == PF_GU) {  // rows 0..HC-1 gate, HC..2HC-1 up, of h columns jn*HC ..
+                plane = r < HC ? g.w0 : g.w1;
+                wr = jn * HC + (r < HC ? r : r - HC);
+            } else {
+                plane = g.w0;
+                wr = jn * (NB * 32) + r;
+            }
+            brow[q < NB ? q : 0] = slab + plane + (size_t)wr * row_bytes + chunk * 16;
+        }
     }
 
     // operand read offsets: A row wv*32 + lane%32, B rows nb*32 + lane%32; k half = lane/32
     const int mrow = wv * 32 + (lane & 31);
     const int khalf = lane >> 5;
-    int a_off[4], b_off[4][4];
+    int a_off[4], b_off[4][NB];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
         a_off[ks] = mrow * PF_ROWB + (((ks * 2 + khalf) ^ swz(mrow)) * 16);
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
+        for (int nb = 0; nb < NB; ++nb) {
             const int r = nb * 32 + (lane & 31);
             b_off[ks][nb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
         }
     }
     const bool active_wave = wv * 32 < tl.rows;
 
-    f32x16 acc[4];
+    f32x16 acc[NB];
 #pragma unroll
-    for (int nb = 0; nb < 4; ++nb)
+    for (int nb = 0; nb < NB; ++nb)
 #pragma unroll
         for (int x = 0; x < 16; ++x) acc[nb][x] = 0.0f;
 
     const int nk = g.K / PF_KT;
-    v4u ra[2][4], rb[2][4];
-    auto fetch = [&](v4u (&a)[4], v4u (&w)[4], int kt) {
+    v4u ra[2][4], rb[2][NB];
+    auto fetch = [&](v4u (&a)[4], v4u (&w)[NB], int kt) {
         const size_t ko = (size_t)kt * PF_ROWB;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             a[q] = ld16(arow[q] + ko);
-            w[q] = ld16_nt(brow[q] + ko);
+            if (q < NB) w[q < NB ? q : 0] = ld16_nt(brow[q < NB ? q : 0] + ko);
         }
     };
-    auto stash = [&](const v4u (&a)[4], const v4u (&w)[4], int buf) {
-        unsigned char* A = pf_lds + buf * 2 * PF_TILE_BYTES;
+    auto stash = [&](const v4u (&a)[4], const v4u (&w)[NB], int buf) {
+        unsigned char* A = pf_lds + buf * (PF_TILE_BYTES + B_BYTES);
         unsigned char* B = A + PF_TILE_BYTES;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             *reinterpret_cast<v4u*>(A + soff[q]) = a[q];
-            *reinterpret_cast<v4u*>(B + soff[q]) = w[q];
+            if (q < NB) *reinterpret_cast<v4u*>(B + soff[q]) = w[q < NB ? q : 0];
         }
     };
     auto compute = [&](int buf) {
         if (!active_wave) return;
-        const unsigned char* A = pf_lds + buf * 2 * PF_TILE_BYTES;
+        const unsigned char* A = pf_lds + buf * (PF_TILE_BYTES + B_BYTES);
         const unsigned char* B = A + PF_TILE_BYTES;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(A + a_off[ks]));
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) {
+            for (int nb = 0; nb < NB; ++nb) {
                 const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(B + b_off[ks][nb]));
                 acc[nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc[nb], 0, 0, 0);
             }
@@ -242,10 +209,10 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
         for (int x = 0; x < 16; ++x) {
             const int r = wv * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
             if (r >= tl.rows) continue;
-            const size_t hrow = (size_t)(tl.p0 + r) * g.N + jn * 64;
+            const size_t hrow = (size_t)(tl.p0 + r) * g.N + jn * HC;
 #pragma unroll
-            for (int half = 0; half < 2; ++half) {
-                const float gv = acc[half][x], uv = acc[2 + half][x];
+            for (int half = 0; half < NB / 2; ++half) {
+                const float gv = acc[half][x], uv = acc[NB / 2 + half][x];
                 const float hv = gv / (1.0f + expf(-gv)) * uv;
                 h[hrow + half * 32 + col] = moe::f32_to_bf16(hv);
             }
@@ -258,11 +225,42 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
             if (r >= tl.rows) continue;
             const int pk = g.pair_list[tl.p0 + r];
             const float wt = g.wts[pk];
-            float* prow = part + (size_t)pk * g.N + jn * PF_NT;
+            float* prow = part + (size_t)pk * g.N + jn * (NB * 32);
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb) prow[nb * 32 + col] = wt * acc[nb][x];
+            for (int nb = 0; nb < NB; ++nb) prow[nb * 32 + col] = wt * acc[nb][x];
         }
     }
+}
+
+template <int NB>
+int pf_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
+              const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
+              int max_tiles, void* hbuf, float* part, hipStream_t st) {
+    static bool lds_set = false;  // once per process: the kernels need more than 64 KiB of LDS only at NB = 4
+    const int lds = pf_lds_bytes(NB);
+    if (!lds_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_GU, NB>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_DOWN, NB>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+            (void)hipGetLastError();
+            return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the prefill kernels", lds);
+        }
+        lds_set = true;
+    }
+    const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
+    PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
+              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / (NB * 16)};
+    hipLaunchKernelGGL((k_pf_gemm<PF_GU, NB>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
+                       dim3(PF_THREADS), lds, st, gu);
+    int rc;
+    if ((rc = moe_check_launch("moe_ffn_slots/prefill_gate_up"))) return rc;
+    PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
+              reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k,
+              H / (NB * 32)};
+    hipLaunchKernelGGL((k_pf_gemm<PF_DOWN, NB>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+                       dim3(PF_THREADS), lds, st, dn);
+    return moe_check_launch("moe_ffn_slots/prefill_down");
 }
 
 }  // namespace
@@ -272,48 +270,25 @@ bool moe_pf_supported(int w_type, int H, int I) {
     return w_type == MOE_W_BF16 && H % 128 == 0 && I % 128 == 0;
 }
 
-size_t moe_pf_tiles_bytes(int T, int k, int S) {
-    const size_t P = (size_t)T * k;
-    const size_t max_tiles = (size_t)(S < (int)P ? S : (int)P) + P / PF_MT + 1;
-    return max_tiles * sizeof(PfTile) + 16;
+int moe_pf_max_tiles(int T, int k, int S) {
+    const int P = T * k;
+    return (S < P ? S : P) + P / PF_MT + 1;  // bounds the sum over slots of ceil(n_s / PF_MT)
 }
 
+size_t moe_pf_tiles_bytes(int T, int k, int S) { return (size_t)moe_pf_max_tiles(T, k, S) * sizeof(PfTile) + 16; }
+
 int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_store, size_t slab_bytes, int S, int H,
-               int I, const moe_slab_layout_t& lay, const int32_t* slot_off, const int32_t* pair_list,
-               const int32_t* active, const int32_t* n_active, void* tiles_ws, void* hbuf, float* part,
+               int I, const moe_slab_layout_t& lay, const int32_t* pair_list, void* tiles_ws, void* hbuf, float* part,
                hipStream_t st) {
     const int P = T * k;
-    const int max_tiles = (S < P ? S : P) + P / PF_MT + 1;
-    PfTile* tiles = reinterpret_cast<PfTile*>(tiles_ws);
-    int32_t* n_tiles = reinterpret_cast<int32_t*>(reinterpret_cast<unsigned char*>(tiles_ws) +
-                                                  (size_t)max_tiles * sizeof(PfTile));
-    hipLaunchKernelGGL(k_pf_tiles, dim3(1), dim3(PF_TILE_THREADS), 0, st, slot_off, active, n_active, tiles, n_tiles,
-                       max_tiles);
-    int rc = moe_check_launch("moe_ffn_slots/prefill_tiles");
-    if (rc) return rc;
+    const int max_tiles = moe_pf_max_tiles(T, k, S);
+    const PfTile* tiles = reinterpret_cast<const PfTile*>(tiles_ws);
+    const int32_t* n_tiles = reinterpret_cast<const int32_t*>(reinterpret_cast<unsigned char*>(tiles_ws) +
+                                                              (size_t)max_tiles * sizeof(PfTile));
 
-    static bool lds_set = false;
-    if (!lds_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_GU>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_DOWN>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, PF_LDS) != hipSuccess) {
-            (void)hipGetLastError();
-            return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the prefill kernels", PF_LDS);
-        }
-        lds_set = true;
-    }
-    const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
-
-    PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
-              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / 64};
-    hipLaunchKernelGGL((k_pf_gemm<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)), dim3(PF_THREADS),
-                       PF_LDS, st, gu);
-    if ((rc = moe_check_launch("moe_ffn_slots/prefill_gate_up"))) return rc;
-
-    PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
-              reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k, H / PF_NT};
-    hipLaunchKernelGGL((k_pf_gemm<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)), dim3(PF_THREADS),
-                       PF_LDS, st, dn);
-    return moe_check_launch("moe_ffn_slots/prefill_down");
+    // decode-sized batches: half-height weight tiles (twice the workgroups, 3 per CU)
+    return P < PF_BIG_P ? pf_launch<2>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
+                                       max_tiles, hbuf, part, st)
+                        : pf_launch<4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
+                                       max_tiles, hbuf, part, st);
 }

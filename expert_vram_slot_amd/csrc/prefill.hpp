@@ -3,14 +3,26 @@
 
 #include "common.hpp"
 
+// A token tile of the grouped GEMM: up to MOE_PF_MT consecutive picks of one
+// slot in the slot-sorted pick list.  Written by the pick-sorting kernels.
+constexpr int MOE_PF_MT = 128;
+struct moe_pf_tile {
+    int p0;    // first position in the slot-sorted pick list
+    int rows;  // picks of the tile (1..MOE_PF_MT)
+    int slot;
+    int pad;
+};
+
 // True when the MFMA path handles this weight format and shape.
 bool moe_pf_supported(int w_type, int H, int I);
-// Workspace bytes of the tile list for T*k picks over S slots.
+// Workspace bytes of the tile list for T*k picks over S slots (the list,
+// then its length as one int32).
 size_t moe_pf_tiles_bytes(int T, int k, int S);
-// Gate/up and down grouped GEMMs over the slot-sorted picks (slot_off,
-// pair_list, active, n_active from the sorting kernel); h goes to hbuf in
-// sorted order, w * (W_d h) to part[pick][H].  Enqueued on `st`.
+// Largest number of tiles T*k picks over S slots can need.
+int moe_pf_max_tiles(int T, int k, int S);
+// Gate/up and down grouped GEMMs over the slot-sorted picks (pair_list and
+// the tile list written by the sorting kernels); h goes to hbuf in sorted
+// order, w * (W_d h) to part[pick][H].  Enqueued on `st`.
 int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_store, size_t slab_bytes, int S, int H,
-               int I, const moe_slab_layout_t& lay, const int32_t* slot_off, const int32_t* pair_list,
-               const int32_t* active, const int32_t* n_active, void* tiles_ws, void* hbuf, float* part,
-               hipStream_t st);
+               int I, const moe_slab_layout_t& lay, const int32_t* pair_list, void* tiles_ws, void* hbuf,
+               float* part, hipStream_t st);
