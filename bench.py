@@ -48,12 +48,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 
-# kernels launched by one moe_ffn_slots call on the bf16 decode path (hidden 2048 -> gate/up rows of 256
-# granules in groups of 4 chunks; intermediate 768 -> down rows of 96 granules, 32 lanes per row, 3 chunks)
-FFN_KERNELS = ("k_group", "k_gu", "k_down", "k_reduce")
-FFN_ANCHOR = "k_gu<1, 4>"
+# kernels launched, in order, by one moe_ffn_slots call on the bf16 decode batch of 64 tokens (512 picks):
+# the pick sort, the MFMA gate/up and down grouped GEMMs with half-height weight tiles, the reduction
+FFN_SEQ = ("k_group", "k_pf_gemm<0, 2>", "k_pf_gemm<1, 2>", "k_reduce")
 # source files whose change invalidates stored HBM counter readings of those kernels
-FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/common.hpp")
+FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
+               "expert_vram_slot_amd/csrc/prefill.hpp", "expert_vram_slot_amd/csrc/common.hpp")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
 
 
@@ -238,7 +238,7 @@ def main():
                    "gpu_only_step_ms": round(elapsed_py / args.steps * 1e3, 4)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(T),
-                     "kernel": "moe_ffn_slots (group, gate/up, down, reduce kernels)",
+                     "kernel": "moe_ffn_slots (pick sort, MFMA gate/up and down grouped GEMMs, reduction)",
                      "bytes_per_launch": int(np.mean(per_launch)), "ms_per_launch": round(float(np.mean(ffn_ms_arr)), 5),
                      "distinct_slabs_per_step": round(float(np.mean(distinct)), 2)},
     }
@@ -583,27 +583,27 @@ def _counter_per_dispatch(rows, counter):
 
 
 def _ffn_launches(rows, key):
-    """Group per-dispatch rows into decode moe_ffn_slots launches: each anchor
-    (the bf16 decode gate/up kernel) with the closest earlier k_group and the
-    closest later k_down and k_reduce by dispatch id.  Returns a list of
-    {kernel short name: row}."""
+    """Group per-dispatch rows into decode moe_ffn_slots launches: each
+    dispatch of the gate/up kernel FFN_SEQ[1] with the closest earlier
+    FFN_SEQ[0] and the closest later FFN_SEQ[2:] by dispatch id.  Returns a
+    list of {kernel short name: row}."""
     by_id = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     names = [_short(r["Kernel_Name"]) for r in by_id]
     launches = []
     for i, nm in enumerate(names):
-        if nm != FFN_ANCHOR:
+        if nm != FFN_SEQ[1]:
             continue
         got = {nm: by_id[i]}
         for j in range(i - 1, max(-1, i - 50), -1):
-            if names[j] == "k_group":
-                got["k_group"] = by_id[j]
+            if names[j] == FFN_SEQ[0]:
+                got[FFN_SEQ[0]] = by_id[j]
                 break
-        for want in ("k_down", "k_reduce"):
+        for want in FFN_SEQ[2:]:
             for j in range(i + 1, min(len(names), i + 50)):
-                if names[j].split("<")[0] == want:
-                    got[names[j]] = by_id[j]
+                if names[j] == want:
+                    got[want] = by_id[j]
                     break
-        if len(got) == 4:
+        if len(got) == len(FFN_SEQ):
             launches.append(got)
     return launches
 
@@ -646,8 +646,8 @@ def summarize(args):
     for L in launches:
         for nm, r in L.items():
             per_k.setdefault(nm, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
-    lines.append(f"decode moe_ffn_slots launches found in the trace: {len(launches)} (each: k_group, {FFN_ANCHOR}, "
-                 f"its k_down and k_reduce, by dispatch id)")
+    lines.append(f"decode moe_ffn_slots launches found in the trace: {len(launches)} (each: "
+                 f"{', '.join(FFN_SEQ)}, matched by dispatch id)")
     ffn_avg = 0.0
     for nm, v in per_k.items():
         lines.append(f"  {nm:<34}{np.mean(v):>10.2f} us")

@@ -213,18 +213,17 @@ __device__ __forceinline__ int wave_slot_rank(int s, bool valid, int nbits, int*
     return __popcll(mask & lt);
 }
 
-// Tiles of the grouped GEMM: ceil(cnt / MOE_PF_MT) per slot, slots in
-// ascending order.  Called by the whole workgroup (thread s holds slot s's
-// pick count and offset; S <= blockDim.x); tiles == NULL writes nothing.
-__device__ __forceinline__ void write_pf_tiles(int cnt, int off, int S, int* scratch, moe_pf_tile* tiles,
+// Tiles of the grouped GEMM: ceil(cnt / mt) per slot, slots in ascending
+// order.  Called by the whole workgroup (thread s holds slot s's pick count
+// and offset; S <= blockDim.x); tiles == NULL writes nothing.
+__device__ __forceinline__ void write_pf_tiles(int cnt, int off, int S, int mt, int* scratch, moe_pf_tile* tiles,
                                                int32_t* n_tiles) {
     if (!tiles) return;
     const int s = threadIdx.x;
-    const int nc = (s < S) ? (cnt + MOE_PF_MT - 1) / MOE_PF_MT : 0;
+    const int nc = (s < S) ? (cnt + mt - 1) / mt : 0;
     int tot;
     const int toff = moe::block_exclusive_scan(nc, scratch, &tot);
-    for (int c = 0; c < nc; ++c)
-        tiles[toff + c] = moe_pf_tile{off + c * MOE_PF_MT, min(MOE_PF_MT, cnt - c * MOE_PF_MT), s, 0};
+    for (int c = 0; c < nc; ++c) tiles[toff + c] = moe_pf_tile{off + c * mt, min(mt, cnt - c * mt), s, 0};
     if (threadIdx.x == 0) *n_tiles = tot;
 }
 
@@ -236,7 +235,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
                                                          int32_t* __restrict__ slot_off, int32_t* __restrict__ pair_list,
                                                          int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                          moe_pf_tile* __restrict__ pf_tiles,
-                                                         int32_t* __restrict__ pf_n_tiles) {
+                                                         int32_t* __restrict__ pf_n_tiles, int pf_mt) {
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
     __shared__ int ctot[MOE_MAX_S];
@@ -289,7 +288,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             const int apos = moe::block_exclusive_scan(flag, scratch, &na);
             if (flag) active[apos] = tid;
             if (tid == 0) *n_active = na;
-            write_pf_tiles(cnt, off, S, scratch, pf_tiles, pf_n_tiles);
+            write_pf_tiles(cnt, off, S, pf_mt, scratch, pf_tiles, pf_n_tiles);
             __syncthreads();
         }
     }
@@ -320,7 +319,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
                                                                int32_t* __restrict__ active,
                                                                int32_t* __restrict__ n_active,
                                                                moe_pf_tile* __restrict__ pf_tiles,
-                                                               int32_t* __restrict__ pf_n_tiles) {
+                                                               int32_t* __restrict__ pf_n_tiles, int pf_mt) {
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
     __shared__ int scratch[GROUP_THREADS / 64 + 1];
@@ -344,7 +343,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
         const int apos = moe::block_exclusive_scan(flag, scratch, &na);
         if (flag) active[apos] = tid;
         if (tid == 0) *n_active = na;
-        write_pf_tiles(tot, off, S, scratch, pf_tiles, pf_n_tiles);
+        write_pf_tiles(tot, off, S, pf_mt, scratch, pf_tiles, pf_n_tiles);
     }
     for (int i = tid; i < (GROUP_THREADS / 64) * S; i += GROUP_THREADS) wtab[i / S][i % S] = 0;
     __syncthreads();
@@ -817,11 +816,11 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt);
         if ((rc = moe_check_launch("moe_ffn_slots/group_hist"))) return rc;
         hipLaunchKernelGGL(k_group_place, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt, nch, slot_off,
-                           pair_list, active, n_active, pf_tiles, pf_n_tiles);
+                           pair_list, active, n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k));
         if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
     } else {
         hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
-                           n_active, pf_tiles, pf_n_tiles);
+                           n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k));
         if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
     }
 

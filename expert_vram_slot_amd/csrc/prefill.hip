@@ -37,7 +37,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 using v4u = uint32_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_THREADS = 256;
-constexpr int PF_MT = MOE_PF_MT;   // token rows per tile
+constexpr int PF_MT = 128;         // token rows per prefill-shaped tile
 constexpr int PF_NT = 128;         // weight rows per tile
 constexpr int PF_KT = 64;          // k per step (128 bytes of bf16 per row)
 constexpr int PF_ROWB = PF_KT * 2; // bytes of one row of a k-step
@@ -45,7 +45,9 @@ constexpr int PF_TILE_BYTES = PF_MT * PF_ROWB;  // 16 KiB: the A tile of one k-s
 // LDS of a workgroup whose B tile has NB blocks of 32 weight rows: two buffers of A and B
 constexpr int pf_lds_bytes(int NB) { return 2 * (PF_TILE_BYTES + NB * 32 * PF_ROWB); }
 constexpr int PF_XCD = 8;
-constexpr int PF_BIG_P = 4096;  // picks from which the weight tiles are full height
+constexpr int PF_BIG_P = 4096;  // picks from which prefill-shaped tiles are used
+constexpr int DEC_MT = 32;      // token rows of a decode-shaped tile
+constexpr int DEC_NW = 4;       // waves of a decode-shaped workgroup (32 weight rows each)
 
 enum { PF_GU = 0, PF_DOWN = 1 };
 
@@ -232,6 +234,167 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     }
 }
 
+// Decode-shaped tile: DEC_MT = 32 token rows (a slot holds a few picks at
+// decode batch sizes) x 32 * NW weight rows; wave w owns weight rows
+// [32 w, 32 w + 32) and all 32 token rows, so every wave has MFMA work and
+// the A tile is small.  Gate/up: weight block w holds gate rows of 16 h
+// columns followed by the up rows of the same columns, so output column c <
+// 16 (gate) and c + 16 (up) of one wave pair up through one lane exchange.
+// The k-loop is the grouped GEMM's: two register sets ahead of two LDS
+// buffers, XOR-swizzled 16-byte chunks.
+template <int MODE, int NW>
+__global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
+    constexpr int NTH = 64 * NW;
+    constexpr int WR = 32 * NW;                  // weight rows per tile
+    constexpr int A_BYTES = DEC_MT * PF_ROWB;     // 4 KiB per k-step
+    constexpr int B_BYTES = WR * PF_ROWB;
+    constexpr int NA = DEC_MT * 8 / NTH;          // A chunks per thread and k-step
+    constexpr int NBU = WR * 8 / NTH;             // B chunks per thread and k-step (4)
+    static_assert(NA >= 1 && NBU >= 1, "tile shape");
+    extern __shared__ __attribute__((aligned(16))) unsigned char dec_lds[];
+    const int b = blockIdx.x;
+    const int xcd = b % PF_XCD, i = b / PF_XCD;
+    const int e = xcd + PF_XCD * (i / g.ntiles_n);
+    const int jn = i % g.ntiles_n;
+    if (e >= *g.n_tiles) return;
+    const PfTile tl = g.tiles[e];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
+    const size_t row_bytes = (size_t)g.K * 2;
+
+    const unsigned char* arow[NA];
+    int aso[NA];
+#pragma unroll
+    for (int q = 0; q < NA; ++q) {
+        const int u = q * NTH + tid, r = u >> 3, ch = u & 7;
+        const int pos = tl.p0 + min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
+        int idx;
+        if constexpr (MODE == PF_GU) idx = g.pair_list[pos] / g.k;
+        else idx = pos;
+        arow[q] = g.act + (size_t)idx * row_bytes + ch * 16;
+        aso[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
+    }
+    const unsigned char* brow[NBU];
+    int bso[NBU];
+#pragma unroll
+    for (int q = 0; q < NBU; ++q) {
+        const int u = q * NTH + tid, r = u >> 3, ch = u & 7;
+        int64_t plane;
+        int wr;
+        if constexpr (MODE == PF_GU) {
+            const int blk = r >> 5, c = r & 31;
+            plane = c < 16 ? g.w0 : g.w1;
+            wr = jn * (16 * NW) + blk * 16 + (c & 15);
+        } else {
+            plane = g.w0;
+            wr = jn * WR + r;
+        }
+        brow[q] = slab + plane + (size_t)wr * row_bytes + ch * 16;
+        bso[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
+    }
+    const int khalf = lane >> 5, ar = lane & 31, br = wv * 32 + (lane & 31);
+    int a_off[4], b_off[4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+        a_off[ks] = ar * PF_ROWB + (((ks * 2 + khalf) ^ swz(ar)) * 16);
+        b_off[ks] = br * PF_ROWB + (((ks * 2 + khalf) ^ swz(br)) * 16);
+    }
+    f32x16 acc;
+#pragma unroll
+    for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
+
+    const int nk = g.K / PF_KT;
+    v4u ra[2][NA], rb[2][NBU];
+    auto fetch = [&](v4u (&a)[NA], v4u (&w)[NBU], int kt) {
+        const size_t ko = (size_t)kt * PF_ROWB;
+#pragma unroll
+        for (int q = 0; q < NA; ++q) a[q] = ld16(arow[q] + ko);
+#pragma unroll
+        for (int q = 0; q < NBU; ++q) w[q] = ld16_nt(brow[q] + ko);
+    };
+    auto stash = [&](const v4u (&a)[NA], const v4u (&w)[NBU], int buf) {
+        unsigned char* A = dec_lds + buf * (A_BYTES + B_BYTES);
+        unsigned char* B = A + A_BYTES;
+#pragma unroll
+        for (int q = 0; q < NA; ++q) *reinterpret_cast<v4u*>(A + aso[q]) = a[q];
+#pragma unroll
+        for (int q = 0; q < NBU; ++q) *reinterpret_cast<v4u*>(B + bso[q]) = w[q];
+    };
+    auto compute = [&](int buf) {
+        const unsigned char* A = dec_lds + buf * (A_BYTES + B_BYTES);
+        const unsigned char* B = A + A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(A + a_off[ks]));
+            const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(B + b_off[ks]));
+            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+        }
+    };
+    fetch(ra[0], rb[0], 0);
+    fetch(ra[1], rb[1], 1);
+    stash(ra[0], rb[0], 0);
+    __syncthreads();
+    for (int kt = 0; kt + 2 < nk; kt += 2) {
+        fetch(ra[0], rb[0], kt + 2);
+        compute(0);
+        stash(ra[1], rb[1], 1);
+        __syncthreads();
+        fetch(ra[1], rb[1], kt + 3);
+        compute(1);
+        stash(ra[0], rb[0], 0);
+        __syncthreads();
+    }
+    compute(0);
+    stash(ra[1], rb[1], 1);
+    __syncthreads();
+    compute(1);
+
+    // accumulator element x of lane l: column l % 32 of this wave's block, row (x/4)*8 + (l/32)*4 + x%4
+    const int col = lane & 31;
+    if constexpr (MODE == PF_GU) {
+        uint16_t* h = reinterpret_cast<uint16_t*>(g.out);
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const float up = __shfl_xor(acc[x], 16, 64);  // every lane takes part
+            const int r = (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
+            if (r < tl.rows && col < 16) {
+                const float gv = acc[x];
+                const float hv = gv / (1.0f + expf(-gv)) * up;
+                h[(size_t)(tl.p0 + r) * g.N + jn * (16 * NW) + wv * 16 + col] = moe::f32_to_bf16(hv);
+            }
+        }
+    } else {
+        float* part = reinterpret_cast<float*>(g.out);
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int r = (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
+            if (r >= tl.rows) continue;
+            const int pk = g.pair_list[tl.p0 + r];
+            part[(size_t)pk * g.N + jn * WR + wv * 32 + col] = g.wts[pk] * acc[x];
+        }
+    }
+}
+
+template <int NW>
+int dec_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
+               const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
+               int max_tiles, void* hbuf, float* part, hipStream_t st) {
+    const int lds = 2 * (DEC_MT + 32 * NW) * PF_ROWB;
+    const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
+    PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
+              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / (16 * NW)};
+    hipLaunchKernelGGL((k_dec_gemm<PF_GU, NW>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)), dim3(64 * NW),
+                       lds, st, gu);
+    int rc;
+    if ((rc = moe_check_launch("moe_ffn_slots/decode_gate_up"))) return rc;
+    PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
+              reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k,
+              H / (32 * NW)};
+    hipLaunchKernelGGL((k_dec_gemm<PF_DOWN, NW>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+                       dim3(64 * NW), lds, st, dn);
+    return moe_check_launch("moe_ffn_slots/decode_down");
+}
+
 template <int NB>
 int pf_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
               const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
@@ -270,9 +433,11 @@ bool moe_pf_supported(int w_type, int H, int I) {
     return w_type == MOE_W_BF16 && H % 128 == 0 && I % 128 == 0;
 }
 
+int moe_pf_tile_rows(int T, int k) { return T * k < PF_BIG_P ? DEC_MT : PF_MT; }
+
 int moe_pf_max_tiles(int T, int k, int S) {
     const int P = T * k;
-    return (S < P ? S : P) + P / PF_MT + 1;  // bounds the sum over slots of ceil(n_s / PF_MT)
+    return (S < P ? S : P) + P / moe_pf_tile_rows(T, k) + 1;  // bounds the sum over slots of ceil(n_s / rows)
 }
 
 size_t moe_pf_tiles_bytes(int T, int k, int S) { return (size_t)moe_pf_max_tiles(T, k, S) * sizeof(PfTile) + 16; }
@@ -286,9 +451,9 @@ int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_sto
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(reinterpret_cast<unsigned char*>(tiles_ws) +
                                                               (size_t)max_tiles * sizeof(PfTile));
 
-    // decode-sized batches: half-height weight tiles (twice the workgroups, 3 per CU)
-    return P < PF_BIG_P ? pf_launch<2>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
-                                       max_tiles, hbuf, part, st)
+    // decode-sized batches (a few picks per slot): 32-row token tiles
+    return P < PF_BIG_P ? dec_launch<DEC_NW>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
+                                             max_tiles, hbuf, part, st)
                         : pf_launch<4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
                                        max_tiles, hbuf, part, st);
 }

@@ -3,12 +3,12 @@
 
 #include "common.hpp"
 
-// A token tile of the grouped GEMM: up to MOE_PF_MT consecutive picks of one
-// slot in the slot-sorted pick list.  Written by the pick-sorting kernels.
-constexpr int MOE_PF_MT = 128;
+// A token tile of the grouped GEMM: up to moe_pf_tile_rows() consecutive
+// picks of one slot in the slot-sorted pick list.  Written by the
+// pick-sorting kernels.
 struct moe_pf_tile {
     int p0;    // first position in the slot-sorted pick list
-    int rows;  // picks of the tile (1..MOE_PF_MT)
+    int rows;  // picks of the tile (1 .. tile rows)
     int slot;
     int pad;
 };
@@ -18,6 +18,9 @@ bool moe_pf_supported(int w_type, int H, int I);
 // Workspace bytes of the tile list for T*k picks over S slots (the list,
 // then its length as one int32).
 size_t moe_pf_tiles_bytes(int T, int k, int S);
+// Token rows per tile for a batch of T*k picks: 32 for decode-sized batches
+// (a few picks per slot), 128 for prefill-sized ones.
+int moe_pf_tile_rows(int T, int k);
 // Largest number of tiles T*k picks over S slots can need.
 int moe_pf_max_tiles(int T, int k, int S);
 // Gate/up and down grouped GEMMs over the slot-sorted picks (pair_list and
