@@ -49,8 +49,8 @@ HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 
 # kernels launched, in order, by one moe_ffn_slots call on the bf16 decode batch of 64 tokens (512 picks):
-# the pick sort, the MFMA gate/up and down grouped GEMMs with half-height weight tiles, the reduction
-FFN_SEQ = ("k_group", "k_pf_gemm<0, 2>", "k_pf_gemm<1, 2>", "k_reduce")
+# the pick sort, the MFMA gate/up and down grouped GEMMs on decode-shaped tiles, the reduction
+FFN_SEQ = ("k_group", "k_dec_gemm<0, 4>", "k_dec_gemm<1, 4>", "k_reduce")
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
                "expert_vram_slot_amd/csrc/prefill.hpp", "expert_vram_slot_amd/csrc/common.hpp")
@@ -564,7 +564,7 @@ def _short(name):
     n = name.split("(")[0] if "::" not in name else name
     for k in ("k_group_hist", "k_group_place", "k_group", "k_gu", "k_down", "k_reduce", "k_route", "k_logits",
               "k_topk", "k_manage", "k_gather", "k_combine", "k_quant_rows", "k_block_sums", "k_pick_static",
-              "k_bias_table", "k_cache_init", "k_pf_gemm", "k_pf_tiles", "k_residual_bf16", "k_residual_f32"):
+              "k_bias_table", "k_cache_init", "k_pf_gemm", "k_dec_gemm", "k_pf_tiles", "k_residual_bf16", "k_residual_f32"):
         if f"::{k}<" in name or f"::{k}(" in name:
             i = name.index(k)
             j = name.find("(", i)

@@ -13,12 +13,15 @@
 //                   SwiGLU epilogue, h (bf16, RNE) stored in sorted-pick order
 //   k_pf_gemm<DOWN> O = H_s W_d^T per tile of 128 output columns,
 //                   part[pick] = w * O (fp32)
+//   k_dec_gemm<GU|DOWN>  the same two GEMMs on decode-shaped tiles
 //   k_reduce     y[t] = sum over resident picks in top-k order (decode path's)
 //
-// A workgroup owns PF_MT = 128 token rows x NB * 32 weight rows (NB = 4 for
-// large batches; NB = 2 for decode-sized ones, which gives twice the
-// workgroups and three of them per CU) and walks K in steps of 64.  Each k-step is fetched into registers two steps ahead and
-// stored to one of two LDS buffers; 16-byte chunks are XOR-swizzled per row
+// Prefill-sized batches (4096 picks and more): a workgroup owns PF_MT = 128
+// token rows x NB * 32 weight rows (NB = 4) and walks K in steps of 64.
+// Decode-sized batches (a few picks per slot) use k_dec_gemm below: 32 token
+// rows, each wave a 32-row weight block.  Each k-step is fetched into
+// registers two steps ahead and stored to one of two LDS buffers; 16-byte
+// chunks are XOR-swizzled per row
 // so that both the stores and the MFMA operand reads are free of bank
 // conflicts.  Each wave owns 32 of the token rows; a wave whose rows are all
 // past the tile's picks skips its MFMAs.  Workgroups that share a tile's
