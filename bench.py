@@ -252,7 +252,7 @@ def main():
     if not args.no_prefill:
         out["prefill"] = bench_prefill(m, torch, synth, SlotLayer)
     if not args.no_dynamic:
-        out["dynamic"] = bench_dynamic(m, torch, synth, SlotLayer, nthreads, link)
+        out["dynamic"] = bench_dynamic(m, torch, synth, SlotLayer, NativeStack, nthreads, link)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, T)
     print(json.dumps(out), flush=True)
@@ -320,51 +320,61 @@ def bench_prefill(m, torch, synth, SlotLayer, steps=10, warmup=2):
     return out
 
 
-def bench_dynamic(m, torch, synth, SlotLayer, nthreads, link_gbs, steps=256, warmup=8):
+def bench_dynamic(m, torch, synth, SlotLayer, NativeStack, nthreads, link_gbs, steps=256, warmup=8):
     """128-expert W8A8 layer, Zipf(0.8) routing ids (permutation per layer),
-    32 LRU slots starting empty, 256 steps of 16 tokens; x fresh per step."""
+    32 LRU slots starting empty, 256 steps of 16 tokens; x fresh per step.
+    Timed with the native driver; the same steps are then replayed from
+    Python from an empty cache again (the cache evolves identically) with HIP
+    events around every cache_gather and moe_ffn_slots."""
     c = synth.CONFIGS["c3"]
     E, k, H, I, S, T = c["E"], c["k"], c["H"], c["I"], c["S"], c["T"]
     base = synth.config_seed("c3")
     slab = synth.slab_bytes(synth.W_W8A8, H, I)
     store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
     synth.slabs_into(store.data_ptr(), synth.W_W8A8, base, 0, 0, E, H, I, c["sigma_w"], slab)
-    slots = torch.empty((S, slab), dtype=torch.uint8, device="cuda")
     G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
     ids_all = synth.zipf_ids(synth.key(base, synth.TAG_ZIPF_PERM), synth.key(base, synth.TAG_ZIPF_DRAW),
                              (warmup + steps) * T, E, k, c["zipf_s"])
     ids_all = torch.from_numpy(ids_all).cuda().reshape(warmup + steps, T * k)
     xs = torch.from_numpy(np.stack([synth.normal(synth.key(base, synth.TAG_X, 0, st), (T, H), 1.0, 1)
                                     for st in range(warmup + steps)]).view(np.int16)).cuda()
-    L = SlotLayer(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_W8A8, T_max=T, policy="lru", host_store=store,
-                  slot_store=slots, G=G, n_threads=nthreads)
-    acc = torch.zeros(4, dtype=torch.int64, device="cuda")
-    gev, fev = [], []
+    spec = dict(host_store=store, slot_store=torch.empty((S, slab), dtype=torch.uint8, device="cuda"), G=G,
+                bias=None, resident=None, policy="lru")
+    elapsed = None
     for phase in ("warmup", "timed"):
-        L.init_cache(None)  # empty cache
+        native = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_W8A8, T_max=T, layers=[spec],
+                             n_threads=nthreads)  # a fresh, empty cache
         n = warmup if phase == "warmup" else steps
         off = 0 if phase == "warmup" else warmup
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(n):
-            timed = phase == "timed"
-            if timed:
-                L.gather_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                L.ffn_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-            L.step(xs[off + i], T, ids_in=ids_all[off + i])
-            if timed:
-                acc += L.stats
-                gev.append(L.gather_events)
-                fev.append(L.ffn_events)
+            native.layer_step(0, xs[off + i], T, ids_in=ids_all[off + i])
         torch.cuda.synchronize()
         elapsed = time.perf_counter() - t0
+        hits, distinct, gathered, host = native.stats()
+        native.close()
+    # replay with events
+    L = SlotLayer(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_W8A8, T_max=T, policy="lru", host_store=store,
+                  slot_store=torch.empty((S, slab), dtype=torch.uint8, device="cuda"), G=G, n_threads=nthreads)
+    L.init_cache(None)
+    acc = torch.zeros(4, dtype=torch.int64, device="cuda")
+    gev, fev = [], []
+    for i in range(steps):
+        L.gather_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        L.ffn_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        L.step(xs[warmup + i], T, ids_in=ids_all[warmup + i])
+        acc += L.stats
+        gev.append(L.gather_events)
+        fev.append(L.ffn_events)
+    torch.cuda.synchronize()
     L.gather_events = L.ffn_events = None
-    hits, distinct, gathered, host = (int(v) for v in acc.cpu())
+    assert [int(v) for v in acc.cpu()] == [hits, distinct, gathered, host], "replay differs from the timed run"
     g_ms = float(np.sum([a.elapsed_time(b) for a, b in gev]))
     g_bytes = gathered * slab
     g_gbs = g_bytes / (g_ms * 1e-3) / 1e9 if g_ms > 0 else None
     out = {"workload": "128-expert W8A8 MoE layer, H=2048 I=768 top-8, Zipf(0.8) ids, 32 LRU slots from empty, "
-                       f"{steps} steps x {T} tokens, host pass on {nthreads} threads",
+                       f"{steps} steps x {T} tokens, host pass on {nthreads} threads, native moe_layer_step",
            "tokens_per_s": round(T * steps / elapsed, 1), "ms_per_step": round(elapsed / steps * 1e3, 4),
            "hit_rate": round(hits / (steps * T * k), 4), "distinct_per_step": round(distinct / steps, 2),
            "gathered_per_step": round(gathered / steps, 2), "host_experts_per_step": round(host / steps, 2),

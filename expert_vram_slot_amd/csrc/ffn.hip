@@ -41,8 +41,6 @@ constexpr int NTMAX = 4;       // tokens of one slot handled per pass
 constexpr int RPW_GU = 1;      // gate rows (and as many up rows) per wave
 constexpr int RPW_DN = 4;      // down rows per wave
 constexpr int GROUP_THREADS = 1024;
-constexpr int GU_REP = 1;  // row tiles per gate/up workgroup (taken one after the other)
-constexpr int DN_REP = 1;  // row tiles per down workgroup
 constexpr bool X_PREFETCH = true;  // activation granules one chunk ahead (16-byte activation granules)
 constexpr int GROUP_MULTI_P = 4096;  // larger batches sort with one workgroup per 1024 picks
 // bf16 batches with at least this many picks take the MFMA grouped-GEMM path
@@ -54,24 +52,28 @@ template <int F>
 struct Fmt;
 template <>
 struct Fmt<MOE_W_F32> {
+    static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
     static constexpr int EPG = 4;       // weights per 16-byte granule
     static constexpr int ABYTES = 4;    // bytes per activation element in LDS
     using Acc = float;
 };
 template <>
 struct Fmt<MOE_W_BF16> {
+    static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
     static constexpr int EPG = 8;
     static constexpr int ABYTES = 2;
     using Acc = float;
 };
 template <>
 struct Fmt<MOE_W_W8A8> {
+    static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
     static constexpr int EPG = 16;
     static constexpr int ABYTES = 1;
     using Acc = int;
 };
 template <>
 struct Fmt<MOE_W_Q4B32> {
+    static constexpr int REP = 2;  // row tiles per GEMV workgroup, taken one after the other
     static constexpr int EPG = 32;
     static constexpr int ABYTES = 2;
     using Acc = float;
@@ -643,13 +645,13 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
                                                     const int32_t* __restrict__ n_active, void* __restrict__ hbuf,
                                                     int tiles) {
     constexpr int ROWS = 2 * RPW_GU;
-    const int tiles_l = (tiles + GU_REP - 1) / GU_REP;  // workgroups per slot
+    const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
     if (a >= *n_active) return;
     const int s = active[a];
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
 #pragma unroll
-    for (int rep = 0; rep < GU_REP; ++rep) {
+    for (int rep = 0; rep < Fmt<F>::REP; ++rep) {
     const int tile = blockIdx.x % tiles_l + rep * tiles_l;
     if (tile >= tiles) break;
     const int r_base = tile * (4 * RPW_GU) + (threadIdx.x >> 6) * RPW_GU;
@@ -720,13 +722,13 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, float* __restrict__ part,
                                                       int tiles) {
-    const int tiles_l = (tiles + DN_REP - 1) / DN_REP;  // workgroups per slot
+    const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
     if (a >= *n_active) return;
     const int s = active[a];
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
 #pragma unroll
-    for (int rep = 0; rep < DN_REP; ++rep) {
+    for (int rep = 0; rep < Fmt<F>::REP; ++rep) {
     const int tile = blockIdx.x % tiles_l + rep * tiles_l;
     if (tile >= tiles) break;
     const int r_base = tile * (4 * RPW_DN) + (threadIdx.x >> 6) * RPW_DN;
@@ -857,7 +859,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
     const int tiles_gu = (I + 4 * RPW_GU - 1) / (4 * RPW_GU);
 #define MOE_LAUNCH_GU(G)                                                                                       \
-    hipLaunchKernelGGL((k_gu<F, G>), dim3(S * ((tiles_gu + GU_REP - 1) / GU_REP)), dim3(FFN_THREADS), 0, st, gv,    \
+    hipLaunchKernelGGL((k_gu<F, G>), dim3(S * ((tiles_gu + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, gv,    \
                        gu_act, xscale, xbsum, H,                                                                    \
                        I, k, slot_off, pair_list, active, n_active, hbuf, tiles_gu)
     MOE_NCHG_DISPATCH(H / Fmt<F>::EPG, MOE_LAUNCH_GU);
@@ -886,7 +888,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
     const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
 #define MOE_LAUNCH_DN(G, LP)                                                                                 \
-    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(S * ((tiles_dn + DN_REP - 1) / DN_REP)), dim3(FFN_THREADS), 0, st, \
+    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(S * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, \
                        dv, dn_act, hscale, hbsum,                                                                   \
                        w, H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
     MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
