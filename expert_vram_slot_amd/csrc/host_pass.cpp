@@ -148,15 +148,44 @@ inline uint16_t f2bf(float f) {
 
 inline float half_to_float(uint16_t h) { return _cvtsh_ss(h); }
 
-// dot of a bf16 weight row with a bf16 activation row, n a multiple of 32
-__attribute__((target("avx512f,avx512bf16"))) float dot_bf16_avx512(const uint16_t* w, const uint16_t* x, int n) {
-    __m512 acc = _mm512_setzero_ps();
-    for (int i = 0; i < n; i += 32) {
-        const __m512i wv = _mm512_loadu_si512(reinterpret_cast<const void*>(w + i));
-        const __m512i xv = _mm512_loadu_si512(reinterpret_cast<const void*>(x + i));
-        acc = _mm512_dpbf16_ps(acc, (__m512bh)wv, (__m512bh)xv);
+// one bf16 weight row against NT <= 4 bf16 activation rows, n % 32 == 0:
+// the row is loaded once per 32 inputs for all NT rows, and each activation
+// row keeps four accumulators (32-input chunk j goes to accumulator j mod 4),
+// so a row's sum runs in the same order whatever NT is
+template <int NT>
+__attribute__((target("avx512f,avx512bf16"))) void dot_bf16x(const uint16_t* w, const uint16_t* const* x, int n,
+                                                              float* out) {
+    __m512 acc[NT][4];
+    for (int t = 0; t < NT; ++t)
+        for (int a = 0; a < 4; ++a) acc[t][a] = _mm512_setzero_ps();
+    int i = 0;
+    for (; i + 128 <= n; i += 128) {
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+            const __m512i wv = _mm512_loadu_si512(reinterpret_cast<const void*>(w + i + 32 * a));
+#pragma unroll
+            for (int t = 0; t < NT; ++t)
+                acc[t][a] = _mm512_dpbf16_ps(acc[t][a], (__m512bh)wv,
+                                             (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(x[t] + i + 32 * a)));
+        }
     }
-    return _mm512_reduce_add_ps(acc);
+    for (int a = 0; i < n; i += 32, ++a) {
+        const __m512i wv = _mm512_loadu_si512(reinterpret_cast<const void*>(w + i));
+        for (int t = 0; t < NT; ++t)
+            acc[t][a] = _mm512_dpbf16_ps(acc[t][a], (__m512bh)wv,
+                                         (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(x[t] + i)));
+    }
+    for (int t = 0; t < NT; ++t)
+        out[t] = _mm512_reduce_add_ps(_mm512_add_ps(_mm512_add_ps(acc[t][0], acc[t][1]), _mm512_add_ps(acc[t][2], acc[t][3])));
+}
+
+void dot_bf16x_rows(int nt, const uint16_t* w, const uint16_t* const* x, int n, float* out) {
+    switch (nt) {
+        case 1: dot_bf16x<1>(w, x, n, out); break;
+        case 2: dot_bf16x<2>(w, x, n, out); break;
+        case 3: dot_bf16x<3>(w, x, n, out); break;
+        default: dot_bf16x<4>(w, x, n, out); break;
+    }
 }
 
 float dot_bf16_plain(const uint16_t* w, const uint16_t* x, int n) {
@@ -187,16 +216,42 @@ int32_t dot_i8(const int8_t* w, const int8_t* x, int n) {
     return acc;
 }
 
-// Same exact integer dot with AVX-512BW: int8 widened to int16, pairwise
-// products summed into int32 (|acc| stays far below 2^31), n % 32 == 0.
-__attribute__((target("avx512f,avx512bw"))) int32_t dot_i8_avx512(const int8_t* w, const int8_t* x, int n) {
-    __m512i acc = _mm512_setzero_si512();
-    for (int i = 0; i < n; i += 32) {
-        const __m512i wv = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + i)));
-        const __m512i xv = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(x + i)));
-        acc = _mm512_add_epi32(acc, _mm512_madd_epi16(wv, xv));
+// one int8 weight row against NT <= 4 int8 activation rows held widened to
+// int16, n % 32 == 0: the row is widened once per 32 inputs for all NT rows;
+// exact int32 sums, so the grouping cannot change a result
+template <int NT>
+__attribute__((target("avx512f,avx512bw"))) void dot_i8x(const int8_t* w, const int16_t* const* x, int n,
+                                                          int32_t* out) {
+    __m512i acc[NT][2];
+    for (int t = 0; t < NT; ++t) acc[t][0] = acc[t][1] = _mm512_setzero_si512();
+    int i = 0;
+    for (; i + 64 <= n; i += 64) {
+        const __m512i w0 = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + i)));
+        const __m512i w1 = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + i + 32)));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            acc[t][0] = _mm512_add_epi32(
+                acc[t][0], _mm512_madd_epi16(w0, _mm512_loadu_si512(reinterpret_cast<const void*>(x[t] + i))));
+            acc[t][1] = _mm512_add_epi32(
+                acc[t][1], _mm512_madd_epi16(w1, _mm512_loadu_si512(reinterpret_cast<const void*>(x[t] + i + 32))));
+        }
     }
-    return _mm512_reduce_add_epi32(acc);
+    if (i < n) {
+        const __m512i w0 = _mm512_cvtepi8_epi16(_mm256_loadu_si256(reinterpret_cast<const __m256i*>(w + i)));
+        for (int t = 0; t < NT; ++t)
+            acc[t][0] = _mm512_add_epi32(
+                acc[t][0], _mm512_madd_epi16(w0, _mm512_loadu_si512(reinterpret_cast<const void*>(x[t] + i))));
+    }
+    for (int t = 0; t < NT; ++t) out[t] = _mm512_reduce_add_epi32(_mm512_add_epi32(acc[t][0], acc[t][1]));
+}
+
+void dot_i8x_rows(int nt, const int8_t* w, const int16_t* const* x, int n, int32_t* out) {
+    switch (nt) {
+        case 1: dot_i8x<1>(w, x, n, out); break;
+        case 2: dot_i8x<2>(w, x, n, out); break;
+        case 3: dot_i8x<3>(w, x, n, out); break;
+        default: dot_i8x<4>(w, x, n, out); break;
+    }
 }
 
 bool have_avx512bw() {
@@ -268,6 +323,73 @@ __attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) float dot_q4_avx
         tail += s * xsum[b0];
     }
     return _mm512_reduce_add_ps(_mm512_add_ps(acc0, acc1)) - 136.0f * (_mm512_reduce_add_ps(corr) + tail);
+}
+
+// The same 4-bit dot, four blocks (128 weights) per step: the 64 code bytes
+// of four blocks fill one 512-bit register, one block per 128-bit lane, and
+// byte interleaves with 0x43 turn the nibbles into the bf16 values 128 + q in
+// place.  An interleave stays inside its 128-bit lane, so the activations are
+// stored to match (q4x_order), and every fp32 lane of a product belongs to
+// one block and takes that block's scale.  NT activation rows share each
+// decoded group; each row's sum runs in the same order whatever NT is.
+// n % 128 == 0.
+void q4x_order(const uint16_t* x, int n, uint16_t* xp) {
+    // group g (blocks 4g..4g+3), part c (inputs 8c..8c+7 of a block), block L, input i
+    for (int g = 0; g < n / 128; ++g)
+        for (int c = 0; c < 4; ++c)
+            for (int L = 0; L < 4; ++L)
+                for (int i = 0; i < 8; ++i) xp[128 * g + 32 * c + 8 * L + i] = x[32 * (4 * g + L) + 8 * c + i];
+}
+
+template <int NT>
+__attribute__((target("avx512f,avx512bw,avx512bf16,avx512vl"))) void dot_q4x(const uint8_t* q, const uint16_t* sc,
+                                                                                const uint16_t* const* xp,
+                                                                                const float* const* xsum, int n,
+                                                                                float* out) {
+    __m512 acc[NT];
+    __m128 corr[NT];
+    for (int t = 0; t < NT; ++t) {
+        acc[t] = _mm512_setzero_ps();
+        corr[t] = _mm_setzero_ps();
+    }
+    const __m512i m4 = _mm512_set1_epi8(0x0F), c43 = _mm512_set1_epi8(0x43);
+    const __m512i lane_block = _mm512_set_epi32(3, 3, 3, 3, 2, 2, 2, 2, 1, 1, 1, 1, 0, 0, 0, 0);
+    for (int g = 0; g < n / 128; ++g) {
+        const __m512i v = _mm512_loadu_si512(reinterpret_cast<const void*>(q + 64 * g));
+        const __m512i lo = _mm512_and_si512(v, m4), hi = _mm512_and_si512(_mm512_srli_epi16(v, 4), m4);
+        const __m512i w0 = _mm512_unpacklo_epi8(lo, c43), w1 = _mm512_unpackhi_epi8(lo, c43);
+        const __m512i w2 = _mm512_unpacklo_epi8(hi, c43), w3 = _mm512_unpackhi_epi8(hi, c43);
+        const __m128 s4 = _mm_cvtph_ps(_mm_loadl_epi64(reinterpret_cast<const __m128i*>(sc + 4 * g)));
+        const __m512 S = _mm512_permutexvar_ps(lane_block, _mm512_castps128_ps512(s4));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const uint16_t* p = xp[t] + 128 * g;
+            __m512 d = _mm512_dpbf16_ps(_mm512_setzero_ps(), (__m512bh)w0,
+                                        (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(p)));
+            d = _mm512_dpbf16_ps(d, (__m512bh)w1, (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(p + 32)));
+            d = _mm512_dpbf16_ps(d, (__m512bh)w2, (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(p + 64)));
+            d = _mm512_dpbf16_ps(d, (__m512bh)w3, (__m512bh)_mm512_loadu_si512(reinterpret_cast<const void*>(p + 96)));
+            acc[t] = _mm512_fmadd_ps(S, d, acc[t]);
+            corr[t] = _mm_fmadd_ps(s4, _mm_loadu_ps(xsum[t] + 4 * g), corr[t]);
+        }
+    }
+    for (int t = 0; t < NT; ++t) {
+        __m128 c = corr[t];
+        c = _mm_add_ps(c, _mm_movehl_ps(c, c));
+        c = _mm_add_ss(c, _mm_movehdup_ps(c));
+        out[t] = _mm512_reduce_add_ps(acc[t]) - 136.0f * _mm_cvtss_f32(c);
+    }
+}
+
+// one 4-bit row against nt <= 4 activation rows
+void dot_q4x_rows(int nt, const uint8_t* q, const uint16_t* sc, const uint16_t* const* xp, const float* const* xsum,
+                  int n, float* out) {
+    switch (nt) {
+        case 1: dot_q4x<1>(q, sc, xp, xsum, n, out); break;
+        case 2: dot_q4x<2>(q, sc, xp, xsum, n, out); break;
+        case 3: dot_q4x<3>(q, sc, xp, xsum, n, out); break;
+        default: dot_q4x<4>(q, sc, xp, xsum, n, out); break;
+    }
 }
 
 // per-block (32 inputs) sums of bf16 rows, fp32 in input order
@@ -352,6 +474,20 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
             for (int t = 0; t < T; ++t) xs[t] = quant_row(&xf[(size_t)t * H], H, &xq[(size_t)t * H]);
         }
     }
+    std::vector<int16_t> xw;  // W8A8: int8 activations widened once
+    if (i8_fast) {
+        xw.resize((size_t)T * H);
+        for (size_t i = 0; i < (size_t)T * H; ++i) xw[i] = xq[i];
+    }
+
+    // 4-bit with H and I in whole groups of four blocks: activations in the
+    // grouped order, up to four picks of an expert per decoded row
+    const bool q4x = q4_fast && H % 128 == 0 && I % 128 == 0;
+    std::vector<uint16_t> xp;
+    if (q4x) {
+        xp.resize((size_t)T * H);
+        for (int t = 0; t < T; ++t) q4x_order(xb + (size_t)t * H, H, &xp[(size_t)t * H]);
+    }
 
     // phase 1: gate/up rows, blocks of RB rows per work item
     const int RB = 32;
@@ -361,6 +497,70 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     parallel(n_threads, NE * nrb, [&](int item) {
         const int e = experts[item / nrb], r0 = (item % nrb) * RB, r1 = std::min(I, r0 + RB);
         const unsigned char* slab = store + (size_t)e * slab_bytes;
+        if (q4x) {
+            const uint8_t* qg = slab + lay.w[0];
+            const uint8_t* qu = slab + lay.w[1];
+            const uint16_t* sg = reinterpret_cast<const uint16_t*>(slab + lay.s[0]);
+            const uint16_t* su = reinterpret_cast<const uint16_t*>(slab + lay.s[1]);
+            for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
+                const int nt = std::min(4, cnt[e + 1] - c0);
+                const uint16_t* xr[4];
+                const float* bs[4];
+                for (int i = 0; i < nt; ++i) {
+                    const int t = order[c0 + i] / k;
+                    xr[i] = &xp[(size_t)t * H];
+                    bs[i] = &xbs[(size_t)t * (H / 32)];
+                }
+                for (int r = r0; r < r1; ++r) {
+                    float g[4], u[4];
+                    dot_q4x_rows(nt, qg + (size_t)r * (H / 2), sg + (size_t)r * (H / 32), xr, bs, H, g);
+                    dot_q4x_rows(nt, qu + (size_t)r * (H / 2), su + (size_t)r * (H / 32), xr, bs, H, u);
+                    for (int i = 0; i < nt; ++i)
+                        hf[(size_t)order[c0 + i] * I + r] = bf16f(f2bf(g[i] / (1.0f + expf(-g[i])) * u[i]));
+                }
+            }
+            return;
+        }
+        if (i8_fast) {
+            const int8_t* wg = reinterpret_cast<const int8_t*>(slab + lay.w[0]);
+            const int8_t* wu = reinterpret_cast<const int8_t*>(slab + lay.w[1]);
+            const float* sg = reinterpret_cast<const float*>(slab + lay.s[0]);
+            const float* su = reinterpret_cast<const float*>(slab + lay.s[1]);
+            for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
+                const int nt = std::min(4, cnt[e + 1] - c0);
+                const int16_t* xr[4];
+                for (int i = 0; i < nt; ++i) xr[i] = &xw[(size_t)(order[c0 + i] / k) * H];
+                for (int r = r0; r < r1; ++r) {
+                    int32_t dg[4], du[4];
+                    dot_i8x_rows(nt, wg + (size_t)r * H, xr, H, dg);
+                    dot_i8x_rows(nt, wu + (size_t)r * H, xr, H, du);
+                    for (int i = 0; i < nt; ++i) {
+                        const int p = order[c0 + i], t = p / k;
+                        const float g = ((float)dg[i] * xs[t]) * sg[r];
+                        const float u = ((float)du[i] * xs[t]) * su[r];
+                        hf[(size_t)p * I + r] = (float)(((double)g / (1.0 + exp(-(double)g))) * (double)u);
+                    }
+                }
+            }
+            return;
+        }
+        if (bf16_fast) {
+            const uint16_t* wg = reinterpret_cast<const uint16_t*>(slab + lay.w[0]);
+            const uint16_t* wu = reinterpret_cast<const uint16_t*>(slab + lay.w[1]);
+            for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
+                const int nt = std::min(4, cnt[e + 1] - c0);
+                const uint16_t* xr[4];
+                for (int i = 0; i < nt; ++i) xr[i] = xb + (size_t)(order[c0 + i] / k) * H;
+                for (int r = r0; r < r1; ++r) {
+                    float g[4], u[4];
+                    dot_bf16x_rows(nt, wg + (size_t)r * H, xr, H, g);
+                    dot_bf16x_rows(nt, wu + (size_t)r * H, xr, H, u);
+                    for (int i = 0; i < nt; ++i)
+                        hf[(size_t)order[c0 + i] * I + r] = bf16f(f2bf(g[i] / (1.0f + expf(-g[i])) * u[i]));
+                }
+            }
+            return;
+        }
         for (int r = r0; r < r1; ++r) {
             for (int q = cnt[e]; q < cnt[e + 1]; ++q) {
                 const int p = order[q], t = p / k;
@@ -376,8 +576,8 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                         const uint16_t* wg = reinterpret_cast<const uint16_t*>(slab + lay.w[0]) + (size_t)r * H;
                         const uint16_t* wu = reinterpret_cast<const uint16_t*>(slab + lay.w[1]) + (size_t)r * H;
                         const uint16_t* xr = xb + (size_t)t * H;
-                        g = bf16_fast ? dot_bf16_avx512(wg, xr, H) : dot_bf16_plain(wg, xr, H);
-                        u = bf16_fast ? dot_bf16_avx512(wu, xr, H) : dot_bf16_plain(wu, xr, H);
+                        g = dot_bf16_plain(wg, xr, H);
+                        u = dot_bf16_plain(wu, xr, H);
                     } break;
                     case MOE_W_W8A8: {
                         const int8_t* wg = reinterpret_cast<const int8_t*>(slab + lay.w[0]) + (size_t)r * H;
@@ -385,8 +585,8 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                         const float sg = reinterpret_cast<const float*>(slab + lay.s[0])[r];
                         const float su = reinterpret_cast<const float*>(slab + lay.s[1])[r];
                         const int8_t* xr = &xq[(size_t)t * H];
-                        g = ((float)(i8_fast ? dot_i8_avx512(wg, xr, H) : dot_i8(wg, xr, H)) * xs[t]) * sg;
-                        u = ((float)(i8_fast ? dot_i8_avx512(wu, xr, H) : dot_i8(wu, xr, H)) * xs[t]) * su;
+                        g = ((float)dot_i8(wg, xr, H) * xs[t]) * sg;
+                        u = ((float)dot_i8(wu, xr, H) * xs[t]) * su;
                     } break;
                     default: {
                         const uint8_t* qg = slab + lay.w[0] + (size_t)r * (H / 2);
@@ -420,6 +620,12 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
         hs.resize(P);
         for (int p : order) hs[p] = quant_row(&hf[(size_t)p * I], I, &hq[(size_t)p * I]);
     }
+    std::vector<int16_t> hw;  // W8A8: int8 h widened once
+    if (i8_fast) {
+        hw.resize((size_t)P * I);
+        for (int p : order)
+            for (int i = 0; i < I; ++i) hw[(size_t)p * I + i] = hq[(size_t)p * I + i];
+    }
     std::vector<uint16_t> hb;
     std::vector<float> hbs;  // 4-bit: per-block sums of h
     if ((w_type == MOE_W_BF16 && bf16_fast) || q4_fast) {
@@ -431,6 +637,11 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
         hbs.resize((size_t)P * (I / 32));
         for (int p : order) block_sums(&hb[(size_t)p * I], I, &hbs[(size_t)p * (I / 32)]);
     }
+    std::vector<uint16_t> hp;
+    if (q4x) {
+        hp.resize((size_t)P * I);
+        for (int p : order) q4x_order(&hb[(size_t)p * I], I, &hp[(size_t)p * I]);
+    }
 
     // phase 2: down rows -> part[p][m] = w * o
     const int RD = 64;
@@ -439,6 +650,63 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     parallel(n_threads, NE * nrd, [&](int item) {
         const int e = experts[item / nrd], m0 = (item % nrd) * RD, m1 = std::min(H, m0 + RD);
         const unsigned char* slab = store + (size_t)e * slab_bytes;
+        if (q4x) {
+            const uint8_t* qd = slab + lay.w[2];
+            const uint16_t* sd = reinterpret_cast<const uint16_t*>(slab + lay.s[2]);
+            for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
+                const int nt = std::min(4, cnt[e + 1] - c0);
+                const uint16_t* hr[4];
+                const float* bs[4];
+                for (int i = 0; i < nt; ++i) {
+                    hr[i] = &hp[(size_t)order[c0 + i] * I];
+                    bs[i] = &hbs[(size_t)order[c0 + i] * (I / 32)];
+                }
+                for (int m = m0; m < m1; ++m) {
+                    float o[4];
+                    dot_q4x_rows(nt, qd + (size_t)m * (I / 2), sd + (size_t)m * (I / 32), hr, bs, I, o);
+                    for (int i = 0; i < nt; ++i) {
+                        const int p = order[c0 + i];
+                        part[(size_t)p * H + m] = w_h[p] * o[i];
+                    }
+                }
+            }
+            return;
+        }
+        if (i8_fast) {
+            const int8_t* wd = reinterpret_cast<const int8_t*>(slab + lay.w[2]);
+            const float* sd = reinterpret_cast<const float*>(slab + lay.s[2]);
+            for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
+                const int nt = std::min(4, cnt[e + 1] - c0);
+                const int16_t* hr[4];
+                for (int i = 0; i < nt; ++i) hr[i] = &hw[(size_t)order[c0 + i] * I];
+                for (int m = m0; m < m1; ++m) {
+                    int32_t d[4];
+                    dot_i8x_rows(nt, wd + (size_t)m * I, hr, I, d);
+                    for (int i = 0; i < nt; ++i) {
+                        const int p = order[c0 + i];
+                        part[(size_t)p * H + m] = w_h[p] * (((float)d[i] * hs[p]) * sd[m]);
+                    }
+                }
+            }
+            return;
+        }
+        if (bf16_fast) {
+            const uint16_t* wd = reinterpret_cast<const uint16_t*>(slab + lay.w[2]);
+            for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
+                const int nt = std::min(4, cnt[e + 1] - c0);
+                const uint16_t* hr[4];
+                for (int i = 0; i < nt; ++i) hr[i] = &hb[(size_t)order[c0 + i] * I];
+                for (int m = m0; m < m1; ++m) {
+                    float o[4];
+                    dot_bf16x_rows(nt, wd + (size_t)m * I, hr, I, o);
+                    for (int i = 0; i < nt; ++i) {
+                        const int p = order[c0 + i];
+                        part[(size_t)p * H + m] = w_h[p] * o[i];
+                    }
+                }
+            }
+            return;
+        }
         for (int m = m0; m < m1; ++m) {
             for (int q = cnt[e]; q < cnt[e + 1]; ++q) {
                 const int p = order[q];
@@ -449,19 +717,15 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                         break;
                     case MOE_W_BF16: {
                         const uint16_t* wd = reinterpret_cast<const uint16_t*>(slab + lay.w[2]) + (size_t)m * I;
-                        if (bf16_fast) {
-                            o = dot_bf16_avx512(wd, &hb[(size_t)p * I], I);
-                        } else {
-                            float a = 0.0f;
-                            for (int i = 0; i < I; ++i) a += bf16f(wd[i]) * hf[(size_t)p * I + i];
-                            o = a;
-                        }
+                        float a = 0.0f;
+                        for (int i = 0; i < I; ++i) a += bf16f(wd[i]) * hf[(size_t)p * I + i];
+                        o = a;
                     } break;
                     case MOE_W_W8A8: {
                         const int8_t* wd = reinterpret_cast<const int8_t*>(slab + lay.w[2]) + (size_t)m * I;
                         const float sd = reinterpret_cast<const float*>(slab + lay.s[2])[m];
                         const int8_t* hr = &hq[(size_t)p * I];
-                        o = ((float)(i8_fast ? dot_i8_avx512(wd, hr, I) : dot_i8(wd, hr, I)) * hs[p]) * sd;
+                        o = ((float)dot_i8(wd, hr, I) * hs[p]) * sd;
                     } break;
                     default: {
                         const uint8_t* qd = slab + lay.w[2] + (size_t)m * (I / 2);

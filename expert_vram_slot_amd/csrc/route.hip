@@ -83,30 +83,31 @@ __device__ __forceinline__ void widen(const v4u& g, double (&d)[XD == MOE_X_F32 
     }
 }
 
-// Top-k of one token's selection scores fl32(z + bias) on (score desc, id
-// asc) by one wave: k rounds of a wave arg-max over the experts not yet
-// taken; lane j < k ends up holding the j-th pick.  Then the softmax of the
-// raw logits over the picks, in double.  Given picks (ids_in) are trusted to
-// lie in [0, E) and clamped only to keep the read in bounds.
-__device__ __forceinline__ void topk_softmax(const float* z, const float* __restrict__ bias,
-                                             const int32_t* __restrict__ ids_in, int E, int k, int t,
-                                             int32_t* __restrict__ ids, float* __restrict__ w) {
+// Top-k of one token's selection scores sc[e] = fl32(z[e] + bias[e]) on
+// (score desc, id asc) by one wave: k rounds of a wave arg-max over the
+// experts not yet taken; lane j < k ends up holding the j-th pick.  The scores
+// sit in LDS, staged once, so a round reads no global memory.  Then the
+// softmax of the raw logits zr over the picks, in double.  Given picks
+// (ids_in) are trusted to lie in [0, E) and clamped only to keep the read in
+// bounds.
+__device__ __forceinline__ void topk_softmax(const float* sc, const float* zr, const int32_t* __restrict__ ids_in,
+                                             int E, int k, int t, int32_t* __restrict__ ids, float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
     int32_t pick = -1;
     if (ids_in) {
         if (lane < k) pick = ids_in[(int64_t)t * k + lane];
     } else {
         uint64_t taken = 0;  // bit j: expert lane + 64 j already picked (E <= 4096)
+        const int nj = (E - lane + 63) >> 6;
         for (int r = 0; r < k; ++r) {
             float best = -INFINITY;
             int be = 0x7FFFFFFF;
-            for (int j = 0; lane + 64 * j < E; ++j) {
-                if (taken >> j & 1) continue;
+            for (int j = 0; j < nj; ++j) {
                 const int e = lane + 64 * j;
-                float sc = z[e];
-                if (bias) sc = sc + bias[e];
-                if (sc > best || (sc == best && e < be)) {
-                    best = sc;
+                const float s = sc[e];
+                const bool better = s > best || (s == best && e < be);
+                if (!(taken >> j & 1) && better) {
+                    best = s;
                     be = e;
                 }
             }
@@ -124,7 +125,7 @@ __device__ __forceinline__ void topk_softmax(const float* z, const float* __rest
         }
         if (lane < k) ids[(int64_t)t * k + lane] = pick;
     }
-    const double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
+    const double zj = lane < k ? (double)zr[min(max(pick, 0), E - 1)] : -INFINITY;
     double m = zj;
 #pragma unroll
     for (int sft = 32; sft >= 1; sft >>= 1) m = fmax(m, __shfl_xor(m, sft, 64));
@@ -151,7 +152,8 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
     constexpr int ROUTE_RW = route_rows<TB>();
     constexpr int V = ROUTE_RW * TB;
     double* xd = reinterpret_cast<double*>(smem);               // [TB][H]
-    float* zl = reinterpret_cast<float*>(xd + (size_t)TB * H);  // [TB][E]
+    float* zl = reinterpret_cast<float*>(xd + (size_t)TB * H);  // [TB][E] raw logits
+    float* sl = bias ? zl + (size_t)TB * E : zl;                 // [TB][E] selection scores
 
     const int t0 = blockIdx.x * TB;
     const int nt = min(TB, T - t0);
@@ -213,9 +215,13 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
     if (logits) {
         for (int i = threadIdx.x; i < nt * E; i += ROUTE_THREADS) logits[(int64_t)t0 * E + i] = zl[i];
     }
+    if (bias && !ids_in) {
+        for (int i = threadIdx.x; i < nt * E; i += ROUTE_THREADS) sl[i] = zl[i] + bias[i % E];
+        __syncthreads();
+    }
 
     // one wave per token
-    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax(zl + t * E, bias, ids_in, E, k, t0 + t, ids, w);
+    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax(sl + t * E, zl + t * E, ids_in, E, k, t0 + t, ids, w);
 }
 
 // ----------------------------------------------------- two-kernel router
@@ -289,8 +295,9 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_logits(const void* __restrict
     (void)XB;
 }
 
-// Top-k and weights from z[T][E], one wave per token; the token's logits are
-// staged in LDS first (k rounds read them).
+// Top-k and weights from z[T][E], one wave per token; the token's selection
+// scores z + bias are staged in LDS first (k rounds read them), the softmax
+// reads the k raw logits of the picks from z.
 __global__ void __launch_bounds__(ROUTE_THREADS) k_topk(const float* __restrict__ z, const float* __restrict__ bias,
                                                         const int32_t* __restrict__ ids_in, int T, int E, int k,
                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
@@ -298,9 +305,15 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_topk(const float* __restrict_
     const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int t = blockIdx.x * ROUTE_KSPLIT + wv;
     if (t >= T) return;
-    float* zl = reinterpret_cast<float*>(smem) + (size_t)wv * E;
-    for (int e = lane; e < E; e += 64) zl[e] = z[(int64_t)t * E + e];
-    topk_softmax(zl, bias, ids_in, E, k, t, ids, w);
+    const float* zt = z + (int64_t)t * E;
+    float* sl = reinterpret_cast<float*>(smem) + (size_t)wv * E;
+    if (!ids_in) {
+        if (bias)
+            for (int e = lane; e < E; e += 64) sl[e] = zt[e] + bias[e];
+        else
+            for (int e = lane; e < E; e += 64) sl[e] = zt[e];
+    }
+    topk_softmax(sl, zt, ids_in, E, k, t, ids, w);
 }
 
 template <int XD, int TB>
@@ -337,7 +350,7 @@ int route_split(const void* x, const void* G, const float* bias, const int32_t* 
 template <int XD, int TB>
 int launch_route(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
                  int32_t* ids, float* w, float* logits, hipStream_t s) {
-    const size_t lds = sizeof(double) * TB * H + sizeof(float) * TB * E;
+    const size_t lds = sizeof(double) * TB * H + sizeof(float) * TB * E * (bias ? 2 : 1);
     if (lds > 160 * 1024) return moe_fail(MOE_E_SHAPE, "moe_route: H=%d E=%d need %zu B of LDS", H, E, lds);
     const int grid = (T + TB - 1) / TB;
     if (lds > 64 * 1024) {
@@ -362,7 +375,7 @@ int route_dispatch(const void* x, const void* G, const float* bias, const int32_
     // small batches: one token per workgroup (more workgroups, lower latency);
     // large batches: several tokens share each read of G
     int tb = T <= 64 ? 1 : 4;
-    while (tb > 1 && sizeof(double) * tb * H + sizeof(float) * tb * E > 80 * 1024) tb >>= 1;
+    while (tb > 1 && sizeof(double) * tb * H + sizeof(float) * tb * E * (bias ? 2 : 1) > 80 * 1024) tb >>= 1;
     switch (tb) {
         case 4: return launch_route<XD, 4>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
         case 2: return launch_route<XD, 2>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);

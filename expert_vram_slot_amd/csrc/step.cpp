@@ -183,6 +183,12 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
                            h->meta + 3 * Pm, s0)))
         return rc;
     if ((e = hipEventRecord(h->ev_manage, s0)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+    if (host_pass) {  // picks, slots and weights to pinned memory in one copy, before the FFN is queued
+        if ((e = hipStreamWaitEvent(s_copy, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
+        if ((e = hipMemcpyAsync(h->h_meta, h->meta, (size_t)12 * Pm + 16, hipMemcpyDeviceToHost, s_copy)) != hipSuccess)
+            return hip_fail("moe_layer_step: picks to host", e);
+        if ((e = hipEventRecord(h->ev_copy, s_copy)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+    }
     if (L->policy != MOE_STATIC && h->S > 0) {
         if ((e = hipStreamWaitEvent(s_side, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
         if ((rc = cache_gather(h->miss, h->n_miss, h->S, L->host_store, L->slot_store, L->slab_bytes, s_side)))
@@ -194,11 +200,7 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
                             h->w_type, h->H, h->I, y, h->ffn_ws, h->ffn_ws_bytes, s0)))
         return rc;
     if (!host_pass) return moe_ok();
-    // picks, slots and weights to pinned memory in one copy, then the host pass on this thread
-    if ((e = hipStreamWaitEvent(s_copy, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
-    if ((e = hipMemcpyAsync(h->h_meta, h->meta, (size_t)12 * Pm + 16, hipMemcpyDeviceToHost, s_copy)) != hipSuccess)
-        return hip_fail("moe_layer_step: picks to host", e);
-    if ((e = hipEventRecord(h->ev_copy, s_copy)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+    // the host pass on this thread, while the GPU runs the FFN
     if ((e = hipEventSynchronize(h->ev_copy)) != hipSuccess) return hip_fail("moe_layer_step: wait for picks", e);
     const int32_t* h_ids = h->h_meta;
     const int32_t* h_slot = h->h_meta + Pm;

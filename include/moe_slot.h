@@ -309,9 +309,10 @@ int moe_step_stats(moe_step* h, int64_t* out, int reset);
 /* One layer step for T tokens of x (device [T][H], activation format):
  * moe_route (ids_in: given device picks [T][k] or NULL) -> cache_manage ->
  * cache_gather on s_side (dynamic caches) -> moe_ffn_slots on s0, and with
- * host_pass != 0: x and the picks go to pinned memory on s_copy, this thread
- * waits for them and runs moe_ffn_host_misses on n_threads threads, the
- * result is added on s0 (moe_combine).  y_out: device float[T][H] out, or
+ * host_pass != 0: x and the picks go to pinned memory on s_copy (the picks
+ * right after cache_manage), this thread waits for them and runs
+ * moe_ffn_host_misses on n_threads threads while the GPU runs the FFN, and
+ * the result is added on s0 (moe_combine).  y_out: device float[T][H] out, or
  * NULL for the driver's own buffer (moe_step_output); final in s0's order
  * when the call returns.  The three streams must be distinct streams of one
  * device.  Errors: those of the entry points it calls; SHAPE when the layer

@@ -170,6 +170,37 @@ def test_host_pass_thread_count_does_not_change_bits(mlib):
     np.testing.assert_array_equal(a, b)
 
 
+@pytest.mark.parametrize("cfg,T,S,E", [("c4", 12, 8, 32), ("c2", 16, 4, 16), ("c3", 16, 4, 16)])
+def test_host_pass_many_picks_per_expert(mlib, cfg, T, S, E):
+    # most experts carry several picks, so each weight row is read (and for
+    # 4-bit decoded) once for groups of up to four picks, and more than four
+    # spill into a second group; bits must not depend on the thread count
+    li, ids, w, sl, yg, yh = _host_case(cfg, T, S, 4, E=E)
+    counts = np.bincount(ids[sl < 0], minlength=E)
+    assert counts.max() > 4
+    a = _run_host(mlib, li, ids, w, sl, 1)
+    _assert_close(a, yh, li.w_type)
+    np.testing.assert_array_equal(a, _run_host(mlib, li, ids, w, sl, 5))
+
+
+def test_host_pass_q4_rows_not_in_whole_groups(mlib):
+    # H = 96, I = 160: 32-weight blocks but not whole groups of four blocks
+    E, k, H, I, T = 6, 2, 96, 160, 5
+    base = synth.config_seed("c4")
+    x = synth.normal(synth.key(base, synth.TAG_X, 3, 0), (T, H), 1.0, synth.X_BF16)
+    G = synth.normal(synth.key(base, synth.TAG_G, 3, 0), (E, H), 0.5, synth.X_BF16)
+    store = synth.slabs(synth.W_Q4B32, base, 3, 0, E, H, I, 0.05)
+    z = oracle.logits(x, synth.X_BF16, G)
+    ids = oracle.topk(z, k)
+    w = oracle.route_weights(z, ids)
+    sl = np.where(ids % 2 == 0, -1, 0).astype(np.int32)
+    _, _, yh = oracle.layer(synth.W_Q4B32, store, E, H, I, x, synth.X_BF16, ids, w, sl)
+    y = np.full((T, H), np.nan, np.float32)
+    mlib.moe_ffn_host_misses(x, synth.X_BF16, ids, sl, w, T, k, store, synth.slab_bytes(synth.W_Q4B32, H, I), E,
+                             synth.W_Q4B32, H, I, y, 3)
+    _assert_close(y, yh, synth.W_Q4B32)
+
+
 def test_host_pass_all_miss_is_the_whole_layer(mlib):
     li = synth.LayerInputs("c1")
     z = oracle.logits(li.x, 0, li.G)
