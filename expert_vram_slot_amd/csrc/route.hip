@@ -83,55 +83,116 @@ __device__ __forceinline__ void widen(const v4u& g, double (&d)[XD == MOE_X_F32 
     }
 }
 
-// Top-k of one token's selection scores sc[e] = fl32(z[e] + bias[e]) on
-// (score desc, id asc) by one wave: k rounds of a wave arg-max over the
-// experts not yet taken; lane j < k ends up holding the j-th pick.  The scores
-// sit in LDS, staged once, so a round reads no global memory.  Then the
-// softmax of the raw logits zr over the picks, in double.  Given picks
-// (ids_in) are trusted to lie in [0, E) and clamped only to keep the read in
-// bounds.
-__device__ __forceinline__ void topk_softmax(const float* sc, const float* zr, const int32_t* __restrict__ ids_in,
-                                             int E, int k, int t, int32_t* __restrict__ ids, float* __restrict__ w) {
+// Order-preserving code of a selection score: larger score, larger code;
+// -0 and +0 share one code (they compare equal); every code is >= 1, and a
+// NaN gets 1 (it never beats a number).  0 marks "absent or taken".
+__device__ __forceinline__ uint32_t score_code(float f) {
+    if (f != f) return 1u;
+    if (f == 0.0f) return 0x80000000u;
+    const uint32_t u = __float_as_uint(f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+template <int CTRL>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
+    return ((uint64_t)(uint32_t)hi << 32) | (uint32_t)lo;
+}
+
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    return __longlong_as_double((long long)readlane_u64((uint64_t)__double_as_longlong(v), lane));
+}
+
+// Maximum of v over the 64 lanes of a wave (every lane active), the same on
+// every lane: within each row of 16 lanes by DPP rotations by 8 and 4 and
+// swaps within quads, then the four row maxima read out by lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+    uint64_t o = dpp_u64<0x128>(v);  // row_ror:8
+    v = o > v ? o : v;
+    o = dpp_u64<0x124>(v);  // row_ror:4
+    v = o > v ? o : v;
+    o = dpp_u64<0x4E>(v);  // quad_perm [2,3,0,1]
+    v = o > v ? o : v;
+    o = dpp_u64<0xB1>(v);  // quad_perm [1,0,3,2]
+    v = o > v ? o : v;
+    uint64_t m = readlane_u64(v, 0);
+    o = readlane_u64(v, 16);
+    m = o > m ? o : m;
+    o = readlane_u64(v, 32);
+    m = o > m ? o : m;
+    o = readlane_u64(v, 48);
+    return o > m ? o : m;
+}
+
+// Top-k of one token's selection scores fl32(z[e] + bias[e]) on (score desc,
+// id asc) by one wave, then the softmax of the raw logits z over the picks
+// in double; lane j < k ends up holding the j-th pick.  Lane l keeps the
+// codes of experts l, l + 64, ... in registers (JM >= ceil(E / 64) of them),
+// read once; each of the k rounds takes the lane's best code (the lowest
+// expert on equal codes), a wave maximum of (code, ~expert), and clears the
+// winner's code.  z and bias may be global or LDS.  Given picks (ids_in) are
+// trusted to lie in [0, E) and clamped only to keep the read in bounds.
+template <int JM>
+__device__ __forceinline__ void topk_softmax(const float* z, const float* __restrict__ bias,
+                                             const int32_t* __restrict__ ids_in, int E, int k, int t,
+                                             int32_t* __restrict__ ids, float* __restrict__ w) {
     const int lane = threadIdx.x & 63;
     int32_t pick = -1;
     if (ids_in) {
         if (lane < k) pick = ids_in[(int64_t)t * k + lane];
     } else {
-        uint64_t taken = 0;  // bit j: expert lane + 64 j already picked (E <= 4096)
-        const int nj = (E - lane + 63) >> 6;
-        for (int r = 0; r < k; ++r) {
-            float best = -INFINITY;
-            int be = 0x7FFFFFFF;
-            for (int j = 0; j < nj; ++j) {
-                const int e = lane + 64 * j;
-                const float s = sc[e];
-                const bool better = s > best || (s == best && e < be);
-                if (!(taken >> j & 1) && better) {
-                    best = s;
-                    be = e;
-                }
-            }
+        uint32_t code[JM];
 #pragma unroll
-            for (int sft = 32; sft >= 1; sft >>= 1) {
-                const float ob = __shfl_xor(best, sft, 64);
-                const int oe = __shfl_xor(be, sft, 64);
-                if (ob > best || (ob == best && oe < be)) {
-                    best = ob;
-                    be = oe;
+        for (int j = 0; j < JM; ++j) {
+            const int e = lane + 64 * j;
+            float sc = 0.0f;
+            if (e < E) sc = bias ? z[e] + bias[e] : z[e];
+            code[j] = e < E ? score_code(sc) : 0u;
+        }
+        for (int r = 0; r < k; ++r) {
+            uint32_t bc = 0u;
+            int bj = 0;
+#pragma unroll
+            for (int j = 0; j < JM; ++j) {
+                if (code[j] > bc) {
+                    bc = code[j];
+                    bj = j;
                 }
             }
-            if (lane == (be & 63)) taken |= 1ull << (be >> 6);
-            if (lane == r) pick = be;
+            const uint64_t mine = bc ? ((uint64_t)bc << 32) | (uint32_t)~(uint32_t)(lane + 64 * bj) : 0ull;
+            const int e = (int)~(uint32_t)wave_max_u64(mine);
+            if (lane == (e & 63)) {
+#pragma unroll
+                for (int j = 0; j < JM; ++j)
+                    if (j == (e >> 6)) code[j] = 0u;
+            }
+            if (lane == r) pick = e;
         }
         if (lane < k) ids[(int64_t)t * k + lane] = pick;
     }
-    const double zj = lane < k ? (double)zr[min(max(pick, 0), E - 1)] : -INFINITY;
-    double m = zj;
-#pragma unroll
-    for (int sft = 32; sft >= 1; sft >>= 1) m = fmax(m, __shfl_xor(m, sft, 64));
+    const double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
+    double m = -INFINITY;
+    for (int j = 0; j < k; ++j) m = fmax(m, readlane_f64(zj, j));
     const double ej = lane < k ? exp(zj - m) : 0.0;
-    const double sum = moe::wave_sum(ej);
+    double sum = 0.0;
+    for (int j = 0; j < k; ++j) sum += readlane_f64(ej, j);
     if (lane < k) w[(int64_t)t * k + lane] = (float)(ej / sum);
+}
+
+// topk_softmax with the register count picked for E at run time
+__device__ __forceinline__ void topk_softmax_any(const float* z, const float* __restrict__ bias,
+                                                 const int32_t* __restrict__ ids_in, int E, int k, int t,
+                                                 int32_t* __restrict__ ids, float* __restrict__ w) {
+    if (E <= 256) topk_softmax<4>(z, bias, ids_in, E, k, t, ids, w);
+    else if (E <= 1024) topk_softmax<16>(z, bias, ids_in, E, k, t, ids, w);
+    else topk_softmax<64>(z, bias, ids_in, E, k, t, ids, w);
 }
 
 // One workgroup routes TB consecutive tokens.  Logits: G is [E][H]; each wave
@@ -152,8 +213,7 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
     constexpr int ROUTE_RW = route_rows<TB>();
     constexpr int V = ROUTE_RW * TB;
     double* xd = reinterpret_cast<double*>(smem);               // [TB][H]
-    float* zl = reinterpret_cast<float*>(xd + (size_t)TB * H);  // [TB][E] raw logits
-    float* sl = bias ? zl + (size_t)TB * E : zl;                 // [TB][E] selection scores
+    float* zl = reinterpret_cast<float*>(xd + (size_t)TB * H);  // [TB][E]
 
     const int t0 = blockIdx.x * TB;
     const int nt = min(TB, T - t0);
@@ -215,13 +275,9 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
     if (logits) {
         for (int i = threadIdx.x; i < nt * E; i += ROUTE_THREADS) logits[(int64_t)t0 * E + i] = zl[i];
     }
-    if (bias && !ids_in) {
-        for (int i = threadIdx.x; i < nt * E; i += ROUTE_THREADS) sl[i] = zl[i] + bias[i % E];
-        __syncthreads();
-    }
 
     // one wave per token
-    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax(sl + t * E, zl + t * E, ids_in, E, k, t0 + t, ids, w);
+    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax_any(zl + t * E, bias, ids_in, E, k, t0 + t, ids, w);
 }
 
 // ----------------------------------------------------- two-kernel router
@@ -295,25 +351,15 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_logits(const void* __restrict
     (void)XB;
 }
 
-// Top-k and weights from z[T][E], one wave per token; the token's selection
-// scores z + bias are staged in LDS first (k rounds read them), the softmax
-// reads the k raw logits of the picks from z.
+// Top-k and weights from z[T][E], one wave per token, the token's scores
+// read straight into registers.
+template <int JM>
 __global__ void __launch_bounds__(ROUTE_THREADS) k_topk(const float* __restrict__ z, const float* __restrict__ bias,
                                                         const int32_t* __restrict__ ids_in, int T, int E, int k,
                                                         int32_t* __restrict__ ids, float* __restrict__ w) {
-    extern __shared__ __align__(16) unsigned char smem[];
-    const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int t = blockIdx.x * ROUTE_KSPLIT + wv;
+    const int t = blockIdx.x * ROUTE_KSPLIT + (int)(threadIdx.x >> 6);
     if (t >= T) return;
-    const float* zt = z + (int64_t)t * E;
-    float* sl = reinterpret_cast<float*>(smem) + (size_t)wv * E;
-    if (!ids_in) {
-        if (bias)
-            for (int e = lane; e < E; e += 64) sl[e] = zt[e] + bias[e];
-        else
-            for (int e = lane; e < E; e += 64) sl[e] = zt[e];
-    }
-    topk_softmax(sl, zt, ids_in, E, k, t, ids, w);
+    topk_softmax<JM>(z + (int64_t)t * E, bias, ids_in, E, k, t, ids, w);
 }
 
 template <int XD, int TB>
@@ -341,16 +387,20 @@ int route_split(const void* x, const void* G, const float* bias, const int32_t* 
         default: rc = launch_logits<XD, 1>(x, G, T, H, E, logits, s); break;
     }
     if (rc) return rc;
-    const size_t lds = (size_t)ROUTE_KSPLIT * E * sizeof(float);
-    hipLaunchKernelGGL(k_topk, dim3((T + ROUTE_KSPLIT - 1) / ROUTE_KSPLIT), dim3(ROUTE_THREADS), lds, s, logits, bias,
-                       ids_in, T, E, k, ids, w);
+    const dim3 grid((T + ROUTE_KSPLIT - 1) / ROUTE_KSPLIT);
+    const int nj = (E + 63) / 64;
+    if (nj <= 2) hipLaunchKernelGGL(k_topk<2>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
+    else if (nj <= 4) hipLaunchKernelGGL(k_topk<4>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
+    else if (nj <= 8) hipLaunchKernelGGL(k_topk<8>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
+    else if (nj <= 16) hipLaunchKernelGGL(k_topk<16>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
+    else hipLaunchKernelGGL(k_topk<64>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
     return moe_check_launch("moe_route/topk");
 }
 
 template <int XD, int TB>
 int launch_route(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
                  int32_t* ids, float* w, float* logits, hipStream_t s) {
-    const size_t lds = sizeof(double) * TB * H + sizeof(float) * TB * E * (bias ? 2 : 1);
+    const size_t lds = sizeof(double) * TB * H + sizeof(float) * TB * E;
     if (lds > 160 * 1024) return moe_fail(MOE_E_SHAPE, "moe_route: H=%d E=%d need %zu B of LDS", H, E, lds);
     const int grid = (T + TB - 1) / TB;
     if (lds > 64 * 1024) {
@@ -375,7 +425,7 @@ int route_dispatch(const void* x, const void* G, const float* bias, const int32_
     // small batches: one token per workgroup (more workgroups, lower latency);
     // large batches: several tokens share each read of G
     int tb = T <= 64 ? 1 : 4;
-    while (tb > 1 && sizeof(double) * tb * H + sizeof(float) * tb * E * (bias ? 2 : 1) > 80 * 1024) tb >>= 1;
+    while (tb > 1 && sizeof(double) * tb * H + sizeof(float) * tb * E > 80 * 1024) tb >>= 1;
     switch (tb) {
         case 4: return launch_route<XD, 4>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
         case 2: return launch_route<XD, 2>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
