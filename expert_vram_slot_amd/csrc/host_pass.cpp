@@ -13,6 +13,7 @@
 
 #include <algorithm>
 #include <atomic>
+#include <chrono>
 #include <condition_variable>
 #include <functional>
 #include <mutex>
@@ -33,8 +34,9 @@ class Pool {
    public:
     // Run fn(item) for item in [0, n) on `threads` threads (the caller
     // included).  Items are handed out dynamically; each runs exactly once.
-    // Idle workers spin for a short while before they sleep, so the phases
-    // of one call, and calls that follow each other closely, start without a
+    // Idle workers spin for up to kSpinNs before they sleep, so the phases of
+    // one call, and calls that follow each other closely (the layers of a
+    // decode step, with only the GPU router between them), start without a
     // wake-up delay.
     void run(int threads, int n, const std::function<void(int)>& fn) {
         if (n <= 0) return;
@@ -60,7 +62,7 @@ class Pool {
         }
         cv_.notify_all();
         work();
-        for (int i = 0; i < kSpin && pending_.load(std::memory_order_acquire) != 0; ++i) _mm_pause();
+        for (Spin sp; pending_.load(std::memory_order_acquire) != 0 && sp.more();) _mm_pause();
         if (pending_.load(std::memory_order_acquire) != 0) {
             std::unique_lock<std::mutex> lk(mu_);
             done_cv_.wait(lk, [&] { return pending_.load(std::memory_order_acquire) == 0; });
@@ -79,7 +81,18 @@ class Pool {
     }
 
    private:
-    static constexpr int kSpin = 1000;  // pause instructions (tens of microseconds)
+    static constexpr int64_t kSpinNs = 250000;
+
+    // spin budget: true until kSpinNs have passed (the clock is read every 64 calls)
+    struct Spin {
+        std::chrono::steady_clock::time_point t0 = std::chrono::steady_clock::now();
+        int n = 0;
+        bool more() {
+            if (++n & 63) return true;
+            return std::chrono::duration_cast<std::chrono::nanoseconds>(std::chrono::steady_clock::now() - t0).count() <
+                   kSpinNs;
+        }
+    };
 
     void work() {
         for (;;) {
@@ -92,7 +105,7 @@ class Pool {
         uint64_t seen = 0;
         for (;;) {
             uint64_t w = word_.load(std::memory_order_acquire);
-            for (int i = 0; (w >> 8) == (seen >> 8) && i < kSpin; ++i) {
+            for (Spin sp; (w >> 8) == (seen >> 8) && sp.more();) {
                 _mm_pause();
                 w = word_.load(std::memory_order_acquire);
             }
