@@ -405,6 +405,23 @@ void dot_q4x_rows(int nt, const uint8_t* q, const uint16_t* sc, const uint16_t* 
     }
 }
 
+// Software prefetch of the weight row `ahead` rows past row r (each stream
+// about 4 KiB ahead).  Pinned host memory comes in 4 KiB pages, and hardware
+// prefetchers stop at page boundaries; a prefetch instruction does not.
+struct RowPrefetch {
+    const unsigned char* base;
+    size_t row_bytes;
+    int rows, ahead;
+    RowPrefetch(const void* b, size_t rb, int n)
+        : base(reinterpret_cast<const unsigned char*>(b)), row_bytes(rb), rows(n),
+          ahead((int)std::max<size_t>(1, 4096 / rb)) {}
+    void operator()(int r) const {
+        if (r + ahead >= rows) return;
+        const unsigned char* p = base + (size_t)(r + ahead) * row_bytes;
+        for (size_t o = 0; o < row_bytes; o += 64) _mm_prefetch(reinterpret_cast<const char*>(p + o), _MM_HINT_T0);
+    }
+};
+
 // per-block (32 inputs) sums of bf16 rows, fp32 in input order
 void block_sums(const uint16_t* x, int n, float* out) {
     for (int b = 0; b < n / 32; ++b) {
@@ -464,42 +481,38 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     const int NE = (int)experts.size();
     const unsigned char* store = reinterpret_cast<const unsigned char*>(host_store);
 
-    // activations as fp32 (fp32 / 4-bit), bf16 bits (bf16) or int8 (W8A8)
-    std::vector<float> xf;
-    std::vector<int8_t> xq;
-    std::vector<float> xs;
+    // per-token activation forms, one token per work item: bf16 bits as given
+    // (bf16, 4-bit), fp32 (fp32 as given; 4-bit scalar path and W8A8), int8
+    // with its scale and widened to int16 (W8A8), and for 4-bit the block sums
+    // and, with H and I in whole groups of four blocks, the grouped order
     const uint16_t* xb = reinterpret_cast<const uint16_t*>(x_h);
     const bool q4_fast = w_type == MOE_W_Q4B32 && have_avx512bf16() && have_avx512bw() && have_avx512vl();
-    const bool i8_fast = w_type == MOE_W_W8A8 && have_avx512bw() && H % 32 == 0 && I % 32 == 0;
-    std::vector<float> xbs;  // 4-bit: per-block sums of x
-    if (q4_fast) {
-        xbs.resize((size_t)T * (H / 32));
-        for (int t = 0; t < T; ++t) block_sums(xb + (size_t)t * H, H, &xbs[(size_t)t * (H / 32)]);
-    }
-    if (w_type == MOE_W_F32) {
-        xf.assign(reinterpret_cast<const float*>(x_h), reinterpret_cast<const float*>(x_h) + (size_t)T * H);
-    } else if (w_type == MOE_W_Q4B32 || w_type == MOE_W_W8A8) {
-        xf.resize((size_t)T * H);
-        for (size_t i = 0; i < (size_t)T * H; ++i) xf[i] = bf16f(xb[i]);
-        if (w_type == MOE_W_W8A8) {
-            xq.resize((size_t)T * H);
-            xs.resize(T);
-            for (int t = 0; t < T; ++t) xs[t] = quant_row(&xf[(size_t)t * H], H, &xq[(size_t)t * H]);
-        }
-    }
-    std::vector<int16_t> xw;  // W8A8: int8 activations widened once
-    if (i8_fast) {
-        xw.resize((size_t)T * H);
-        for (size_t i = 0; i < (size_t)T * H; ++i) xw[i] = xq[i];
-    }
-
-    // 4-bit with H and I in whole groups of four blocks: activations in the
-    // grouped order, up to four picks of an expert per decoded row
     const bool q4x = q4_fast && H % 128 == 0 && I % 128 == 0;
-    std::vector<uint16_t> xp;
-    if (q4x) {
-        xp.resize((size_t)T * H);
-        for (int t = 0; t < T; ++t) q4x_order(xb + (size_t)t * H, H, &xp[(size_t)t * H]);
+    const bool i8_fast = w_type == MOE_W_W8A8 && have_avx512bw() && H % 32 == 0 && I % 32 == 0;
+    const bool need_xf = w_type == MOE_W_W8A8 || (w_type == MOE_W_Q4B32 && !q4_fast);
+    std::vector<float> xf(need_xf ? (size_t)T * H : 0);
+    const float* xfp = w_type == MOE_W_F32 ? reinterpret_cast<const float*>(x_h) : xf.data();
+    std::vector<int8_t> xq(w_type == MOE_W_W8A8 ? (size_t)T * H : 0);
+    std::vector<float> xs(w_type == MOE_W_W8A8 ? T : 0);
+    std::vector<int16_t> xw(i8_fast ? (size_t)T * H : 0);  // W8A8: int8 activations widened once
+    std::vector<float> xbs(q4_fast ? (size_t)T * (H / 32) : 0);  // 4-bit: per-block sums of x
+    std::vector<uint16_t> xp(q4x ? (size_t)T * H : 0);          // 4-bit: grouped order
+    const std::function<void(int)> prep_token = [&](int t) {
+        const uint16_t* xr = xb + (size_t)t * H;
+        if (need_xf)
+            for (int i = 0; i < H; ++i) xf[(size_t)t * H + i] = bf16f(xr[i]);
+        if (w_type == MOE_W_W8A8) {
+            xs[t] = quant_row(&xf[(size_t)t * H], H, &xq[(size_t)t * H]);
+            if (i8_fast)
+                for (int i = 0; i < H; ++i) xw[(size_t)t * H + i] = xq[(size_t)t * H + i];
+        }
+        if (q4_fast) block_sums(xr, H, &xbs[(size_t)t * (H / 32)]);
+        if (q4x) q4x_order(xr, H, &xp[(size_t)t * H]);
+    };
+    if (w_type != MOE_W_F32 && w_type != MOE_W_BF16) {
+        if (T >= 8) parallel(n_threads, T, prep_token);
+        else
+            for (int t = 0; t < T; ++t) prep_token(t);
     }
 
     // phase 1: gate/up rows, blocks of RB rows per work item
@@ -524,7 +537,9 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                     xr[i] = &xp[(size_t)t * H];
                     bs[i] = &xbs[(size_t)t * (H / 32)];
                 }
+                const RowPrefetch pq_g(qg, H / 2, I), pq_u(qu, H / 2, I), ps_g(sg, H / 16, I), ps_u(su, H / 16, I);
                 for (int r = r0; r < r1; ++r) {
+                    pq_g(r), pq_u(r), ps_g(r), ps_u(r);
                     float g[4], u[4];
                     dot_q4x_rows(nt, qg + (size_t)r * (H / 2), sg + (size_t)r * (H / 32), xr, bs, H, g);
                     dot_q4x_rows(nt, qu + (size_t)r * (H / 2), su + (size_t)r * (H / 32), xr, bs, H, u);
@@ -543,7 +558,9 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                 const int nt = std::min(4, cnt[e + 1] - c0);
                 const int16_t* xr[4];
                 for (int i = 0; i < nt; ++i) xr[i] = &xw[(size_t)(order[c0 + i] / k) * H];
+                const RowPrefetch p_g(wg, H, I), p_u(wu, H, I);
                 for (int r = r0; r < r1; ++r) {
+                    p_g(r), p_u(r);
                     int32_t dg[4], du[4];
                     dot_i8x_rows(nt, wg + (size_t)r * H, xr, H, dg);
                     dot_i8x_rows(nt, wu + (size_t)r * H, xr, H, du);
@@ -564,7 +581,9 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                 const int nt = std::min(4, cnt[e + 1] - c0);
                 const uint16_t* xr[4];
                 for (int i = 0; i < nt; ++i) xr[i] = xb + (size_t)(order[c0 + i] / k) * H;
+                const RowPrefetch p_g(wg, (size_t)H * 2, I), p_u(wu, (size_t)H * 2, I);
                 for (int r = r0; r < r1; ++r) {
+                    p_g(r), p_u(r);
                     float g[4], u[4];
                     dot_bf16x_rows(nt, wg + (size_t)r * H, xr, H, g);
                     dot_bf16x_rows(nt, wu + (size_t)r * H, xr, H, u);
@@ -582,8 +601,8 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                     case MOE_W_F32: {
                         const float* wg = reinterpret_cast<const float*>(slab + lay.w[0]) + (size_t)r * H;
                         const float* wu = reinterpret_cast<const float*>(slab + lay.w[1]) + (size_t)r * H;
-                        g = dot_f32(wg, &xf[(size_t)t * H], H);
-                        u = dot_f32(wu, &xf[(size_t)t * H], H);
+                        g = dot_f32(wg, xfp + (size_t)t * H, H);
+                        u = dot_f32(wu, xfp + (size_t)t * H, H);
                     } break;
                     case MOE_W_BF16: {
                         const uint16_t* wg = reinterpret_cast<const uint16_t*>(slab + lay.w[0]) + (size_t)r * H;
@@ -611,8 +630,8 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                             g = dot_q4_avx512(qg, sg, xb + (size_t)t * H, bs, H);
                             u = dot_q4_avx512(qu, su, xb + (size_t)t * H, bs, H);
                         } else {
-                            g = dot_q4(qg, sg, &xf[(size_t)t * H], H);
-                            u = dot_q4(qu, su, &xf[(size_t)t * H], H);
+                            g = dot_q4(qg, sg, xfp + (size_t)t * H, H);
+                            u = dot_q4(qu, su, xfp + (size_t)t * H, H);
                         }
                     } break;
                 }
@@ -625,35 +644,34 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
         }
     });
 
-    // W8A8: h quantised per pick
-    std::vector<int8_t> hq;
-    std::vector<float> hs;
-    if (w_type == MOE_W_W8A8) {
-        hq.resize((size_t)P * I);
-        hs.resize(P);
-        for (int p : order) hs[p] = quant_row(&hf[(size_t)p * I], I, &hq[(size_t)p * I]);
-    }
-    std::vector<int16_t> hw;  // W8A8: int8 h widened once
-    if (i8_fast) {
-        hw.resize((size_t)P * I);
-        for (int p : order)
-            for (int i = 0; i < I; ++i) hw[(size_t)p * I + i] = hq[(size_t)p * I + i];
-    }
-    std::vector<uint16_t> hb;
-    std::vector<float> hbs;  // 4-bit: per-block sums of h
-    if ((w_type == MOE_W_BF16 && bf16_fast) || q4_fast) {
-        hb.resize((size_t)P * I);
-        for (int p : order)
-            for (int i = 0; i < I; ++i) hb[(size_t)p * I + i] = f2bf(hf[(size_t)p * I + i]);
-    }
-    if (q4_fast) {
-        hbs.resize((size_t)P * (I / 32));
-        for (int p : order) block_sums(&hb[(size_t)p * I], I, &hbs[(size_t)p * (I / 32)]);
-    }
-    std::vector<uint16_t> hp;
-    if (q4x) {
-        hp.resize((size_t)P * I);
-        for (int p : order) q4x_order(&hb[(size_t)p * I], I, &hp[(size_t)p * I]);
+    // per-pick forms of h, one pick per work item: int8 with its scale and
+    // widened (W8A8), bf16 bits (bf16, 4-bit), and for 4-bit the block sums
+    // and the grouped order
+    const bool need_hb = (w_type == MOE_W_BF16 && bf16_fast) || q4_fast;
+    std::vector<int8_t> hq(w_type == MOE_W_W8A8 ? (size_t)P * I : 0);
+    std::vector<float> hs(w_type == MOE_W_W8A8 ? P : 0);
+    std::vector<int16_t> hw(i8_fast ? (size_t)P * I : 0);  // W8A8: int8 h widened once
+    std::vector<uint16_t> hb(need_hb ? (size_t)P * I : 0);
+    std::vector<float> hbs(q4_fast ? (size_t)P * (I / 32) : 0);  // 4-bit: per-block sums of h
+    std::vector<uint16_t> hp(q4x ? (size_t)P * I : 0);          // 4-bit: grouped order
+    const std::function<void(int)> prep_pick = [&](int q) {
+        const int p = order[q];
+        const float* hr = &hf[(size_t)p * I];
+        if (w_type == MOE_W_W8A8) {
+            hs[p] = quant_row(hr, I, &hq[(size_t)p * I]);
+            if (i8_fast)
+                for (int i = 0; i < I; ++i) hw[(size_t)p * I + i] = hq[(size_t)p * I + i];
+        }
+        if (need_hb)
+            for (int i = 0; i < I; ++i) hb[(size_t)p * I + i] = f2bf(hr[i]);
+        if (q4_fast) block_sums(&hb[(size_t)p * I], I, &hbs[(size_t)p * (I / 32)]);
+        if (q4x) q4x_order(&hb[(size_t)p * I], I, &hp[(size_t)p * I]);
+    };
+    if (w_type != MOE_W_F32) {
+        const int nq = (int)order.size();
+        if (nq >= 8) parallel(n_threads, nq, prep_pick);
+        else
+            for (int q = 0; q < nq; ++q) prep_pick(q);
     }
 
     // phase 2: down rows -> part[p][m] = w * o
@@ -674,7 +692,9 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                     hr[i] = &hp[(size_t)order[c0 + i] * I];
                     bs[i] = &hbs[(size_t)order[c0 + i] * (I / 32)];
                 }
+                const RowPrefetch pq(qd, I / 2, H), ps(sd, I / 16, H);
                 for (int m = m0; m < m1; ++m) {
+                    pq(m), ps(m);
                     float o[4];
                     dot_q4x_rows(nt, qd + (size_t)m * (I / 2), sd + (size_t)m * (I / 32), hr, bs, I, o);
                     for (int i = 0; i < nt; ++i) {
@@ -692,7 +712,9 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                 const int nt = std::min(4, cnt[e + 1] - c0);
                 const int16_t* hr[4];
                 for (int i = 0; i < nt; ++i) hr[i] = &hw[(size_t)order[c0 + i] * I];
+                const RowPrefetch pw(wd, I, H);
                 for (int m = m0; m < m1; ++m) {
+                    pw(m);
                     int32_t d[4];
                     dot_i8x_rows(nt, wd + (size_t)m * I, hr, I, d);
                     for (int i = 0; i < nt; ++i) {
@@ -709,7 +731,9 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
                 const int nt = std::min(4, cnt[e + 1] - c0);
                 const uint16_t* hr[4];
                 for (int i = 0; i < nt; ++i) hr[i] = &hb[(size_t)order[c0 + i] * I];
+                const RowPrefetch pw(wd, (size_t)I * 2, H);
                 for (int m = m0; m < m1; ++m) {
+                    pw(m);
                     float o[4];
                     dot_bf16x_rows(nt, wd + (size_t)m * I, hr, I, o);
                     for (int i = 0; i < nt; ++i) {

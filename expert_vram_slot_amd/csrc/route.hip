@@ -148,14 +148,20 @@ __device__ __forceinline__ void topk_softmax(const float* z, const float* __rest
     if (ids_in) {
         if (lane < k) pick = ids_in[(int64_t)t * k + lane];
     } else {
+        // all loads issued before any is used (addresses clamped, not branched)
+        float sc[JM];
+#pragma unroll
+        for (int j = 0; j < JM; ++j) sc[j] = z[min(lane + 64 * j, E - 1)];
+        if (bias) {
+            float bv[JM];
+#pragma unroll
+            for (int j = 0; j < JM; ++j) bv[j] = bias[min(lane + 64 * j, E - 1)];
+#pragma unroll
+            for (int j = 0; j < JM; ++j) sc[j] = sc[j] + bv[j];
+        }
         uint32_t code[JM];
 #pragma unroll
-        for (int j = 0; j < JM; ++j) {
-            const int e = lane + 64 * j;
-            float sc = 0.0f;
-            if (e < E) sc = bias ? z[e] + bias[e] : z[e];
-            code[j] = e < E ? score_code(sc) : 0u;
-        }
+        for (int j = 0; j < JM; ++j) code[j] = lane + 64 * j < E ? score_code(sc[j]) : 0u;
         for (int r = 0; r < k; ++r) {
             uint32_t bc = 0u;
             int bj = 0;
@@ -315,29 +321,41 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_logits(const void* __restrict
     double acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0.0;
-    for (int g0 = 0; g0 < KG; g0 += 64) {
-        const int g = g0 + lane;
-        const bool on = g < KG;
-        const int gc = on ? g : KG - 1;
-        v4u gr[RW];
+    // U passes of 64 granules per chunk: every load of a chunk is issued
+    // before the first is used; granules past the row are read clamped and
+    // enter as zeros (adding +0 changes no sum); the sums still run pass by
+    // pass, lane by lane
+    constexpr int U = 4;
+    for (int g0 = 0; g0 < KG; g0 += 64 * U) {
+        v4u gr[U][RW];
 #pragma unroll
-        for (int r = 0; r < RW; ++r) {
-            const int e = min(ebase + r, E - 1);  // rows past E are computed on a valid row and dropped
-            gr[r] = *reinterpret_cast<const v4u*>(Gb + e * row_bytes + (size_t)gc * 16);
-            if (!on) gr[r] = v4u{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int t = 0; t < TB; ++t) {
-            double xv[EPG];
-            widen<XD>(*reinterpret_cast<const v4u*>(smem + (size_t)t * row_bytes + (size_t)gc * 16), xv);
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + 64 * u + lane;
+            const int gc = g < KG ? g : KG - 1;
 #pragma unroll
             for (int r = 0; r < RW; ++r) {
-                double gd[EPG];
-                widen<XD>(gr[r], gd);
-                double a = acc[r * TB + t];
+                const int e = min(ebase + r, E - 1);  // rows past E are computed on a valid row and dropped
+                gr[u][r] = *reinterpret_cast<const v4u*>(Gb + e * row_bytes + (size_t)gc * 16);
+            }
+        }
 #pragma unroll
-                for (int i = 0; i < EPG; ++i) a = fma(xv[i], gd[i], a);
-                acc[r * TB + t] = a;
+        for (int u = 0; u < U; ++u) {
+            const int g = g0 + 64 * u + lane;
+            const bool on = g < KG;
+            const int gc = on ? g : KG - 1;
+#pragma unroll
+            for (int t = 0; t < TB; ++t) {
+                double xv[EPG];
+                widen<XD>(*reinterpret_cast<const v4u*>(smem + (size_t)t * row_bytes + (size_t)gc * 16), xv);
+#pragma unroll
+                for (int r = 0; r < RW; ++r) {
+                    double gd[EPG];
+                    widen<XD>(on ? gr[u][r] : v4u{0u, 0u, 0u, 0u}, gd);
+                    double a = acc[r * TB + t];
+#pragma unroll
+                    for (int i = 0; i < EPG; ++i) a = fma(xv[i], gd[i], a);
+                    acc[r * TB + t] = a;
+                }
             }
         }
     }
