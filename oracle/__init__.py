@@ -48,6 +48,9 @@ def lib():
         L.oracle_bias_table.argtypes = [vp, i32, i32, f32, vp]
         L.oracle_topk.argtypes = [vp, vp, i32, i32, i32, vp]
         L.oracle_route_weights.argtypes = [vp, vp, i32, i32, i32, vp]
+        L.oracle_bias_flat.argtypes = [vp, i32, i32, f32, vp]
+        L.oracle_bias_affinity.argtypes = [vp, vp, i32, f32, vp]
+        L.oracle_route_weights_damped.argtypes = [vp, vp, vp, i32, i32, i32, vp]
         L.oracle_expert.argtypes = [i32, vp, i32, i32, vp, i32, vp]
         L.oracle_layer.argtypes = [i32, vp, i64, i32, i32, i32, vp, i32, vp, vp, vp, i32, i32, vp, vp, vp]
         L.oracle_manage.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
@@ -56,7 +59,8 @@ def lib():
         L.oracle_residual.argtypes = [vp, i32, vp, i32, i32, vp]
         for f in ("oracle_decode_expert", "oracle_logits", "oracle_bias_table", "oracle_topk",
                   "oracle_route_weights", "oracle_expert", "oracle_layer", "oracle_manage", "oracle_gather",
-                  "oracle_pick_static", "oracle_residual"):
+                  "oracle_pick_static", "oracle_residual", "oracle_bias_flat", "oracle_bias_affinity",
+                  "oracle_route_weights_damped"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -126,6 +130,35 @@ def route_weights(z, ids):
     k = ids.shape[1]
     w = np.empty((T, k), np.float32)
     _check(lib().oracle_route_weights(_p(z), _p(ids), T, E, k, _p(w)), "route_weights")
+    return w
+
+
+def bias_flat(b, n_hot, value):
+    """0 for the n_hot brightest experts, `value` for every other (-inf: hard mask)."""
+    b = _c(b, np.float64)
+    out = np.empty(b.shape[0], np.float32)
+    _check(lib().oracle_bias_flat(_p(b), b.shape[0], n_hot, value, _p(out)), "bias_flat")
+    return out
+
+
+def bias_affinity(e2s, lam, base=None):
+    """base (or 0) plus lam for every expert with e2s[e] >= 0, one fp32 add."""
+    e2s = _c(e2s, np.int32)
+    base = None if base is None else _c(base, np.float32)
+    out = np.empty(e2s.shape[0], np.float32)
+    _check(lib().oracle_bias_affinity(_p(e2s), _p(base), e2s.shape[0], lam, _p(out)), "bias_affinity")
+    return out
+
+
+def route_weights_damped(z, bias, ids):
+    """Softmax of the biased scores fl32(z + bias) over the picks."""
+    z = _c(z, np.float32)
+    ids = _c(ids, np.int32)
+    bias = None if bias is None else _c(bias, np.float32)
+    T, E = z.shape
+    k = ids.shape[1]
+    w = np.empty((T, k), np.float32)
+    _check(lib().oracle_route_weights_damped(_p(z), _p(bias), _p(ids), T, E, k, _p(w)), "route_weights_damped")
     return w
 
 

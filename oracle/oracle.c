@@ -239,6 +239,59 @@ int oracle_route_weights(const float* z, const int32_t* ids, int T, int E, int k
     return 0;
 }
 
+/* Flat soft bias and hard mask, [PGO] "Experts that don't fit": the hot set
+ * (the same n_hot brightest experts as the graded table, ties to the lower
+ * id) gets 0, every other expert the one number `value`; value = -inf is the
+ * hard mask (a cold expert can never beat a hot one). */
+int oracle_bias_flat(const double* b, int E, int n_hot, float value, float* bias) {
+    if (E <= 0 || n_hot < 1 || value != value || value > 0.0f) return -1;
+    for (int e = 0; e < E; ++e) {
+        int rank = 0;
+        for (int o = 0; o < E; ++o)
+            if (b[o] > b[e] || (b[o] == b[e] && o < e)) ++rank;
+        bias[e] = rank < n_hot ? 0.0f : value;
+    }
+    return 0;
+}
+
+/* Live-cache affinity, [PGO] "Then Maya's own knob beat ours": every expert
+ * that is in VRAM right now (e2s[e] >= 0 in the cache state) has lambda added
+ * to its selection score; on top of an optional static table, one fp32 add. */
+int oracle_bias_affinity(const int32_t* e2s, const float* base, int E, float lambda, float* bias) {
+    if (E <= 0 || !(lambda - lambda == 0.0f)) return -1;
+    for (int e = 0; e < E; ++e) {
+        float v = base ? base[e] : 0.0f;
+        if (e2s[e] >= 0) v = v + lambda;
+        bias[e] = v;
+    }
+    return 0;
+}
+
+/* Damped weights, [PGO] "Qwen on Strata: the bias as a quality dial": the
+ * alternative to selection-only in which the weights are the softmax of the
+ * biased scores s = fl32(z + bias) over the picked k, in double, as fp32. */
+int oracle_route_weights_damped(const float* z, const float* bias, const int32_t* ids, int T, int E, int k, float* w) {
+    if (k < 1) return -1;
+    for (int t = 0; t < T; ++t) {
+        const int32_t* id = ids + (int64_t)t * k;
+        double s[64];
+        if (k > 64) return -1;
+        for (int j = 0; j < k; ++j) {
+            if (id[j] < 0 || id[j] >= E) return -1;
+            float v = z[(int64_t)t * E + id[j]];
+            if (bias) v = v + bias[id[j]];
+            s[j] = v;
+        }
+        double m = -INFINITY;
+        for (int j = 0; j < k; ++j)
+            if (s[j] > m) m = s[j];
+        double sum = 0.0;
+        for (int j = 0; j < k; ++j) sum += exp(s[j] - m);
+        for (int j = 0; j < k; ++j) w[(int64_t)t * k + j] = (float)(exp(s[j] - m) / sum);
+    }
+    return 0;
+}
+
 /* -------------------------------------------------------- expert FFN */
 
 static double silu(double v) { return v / (1.0 + exp(-v)); }

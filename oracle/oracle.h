@@ -10,7 +10,10 @@
  *
  * Sources (web pages, cited by title and section):
  *   [PGO]  "Nudge, don't cut" (oois.ee/pgo-sgb): "The method in five lines",
- *          "PGO-SGB in two pictures".
+ *          "PGO-SGB in two pictures", "Experts that don't fit" (hard mask,
+ *          flat soft bias), "Qwen on Strata: the bias as a quality dial"
+ *          (damped weights), "Then Maya's own knob beat ours" (live-cache
+ *          affinity).
  *   [VEC]  "Porting vllm-expert-cache to NVIDIA GPUs" (davetha/vllm-expert-cache
  *          docs/porting-nvidia.md): "What this package does", "Prove it is
  *          correct before measuring", "Measuring, without fooling yourself".
@@ -46,6 +49,9 @@ int oracle_topk(const float* z, const float* bias, int T, int E, int k, int32_t*
 
 /* softmax of the raw logits restricted to the picked k (double -> fp32). */
 int oracle_route_weights(const float* z, const int32_t* ids, int T, int E, int k, float* w);
+int oracle_bias_flat(const double* b, int E, int n_hot, float value, float* bias);
+int oracle_bias_affinity(const int32_t* e2s, const float* base, int E, float lambda, float* bias);
+int oracle_route_weights_damped(const float* z, const float* bias, const int32_t* ids, int T, int E, int k, float* w);
 
 /* One expert's down-projection output for one token, o = Wd h, before the
  * routing weight (double). */

@@ -254,6 +254,89 @@ def test_bias_table_edge_tail_cap_and_hot():
     assert bias.nbytes * 48 == 98_304
 
 
+def test_bias_flat_hot_set_value_and_hard_mask():
+    """'Nudge, don't cut' / 'Experts that don't fit': the hot set is kept at 0,
+    every other expert gets one flat number; -inf is the hard mask, under
+    which the picks are the plain top-k of the hot experts alone."""
+    E, n_hot, k = 512, 192, 10
+    b = synth.dirichlet(synth.key(11, synth.TAG_B), E, 0.3)
+    order = np.lexsort((np.arange(E), -b))
+    hot = np.sort(order[:n_hot])
+    for v in (-0.5, -0.75, -1.0):
+        bias = oracle.bias_flat(b, n_hot, v)
+        assert np.all(bias[hot] == 0.0)
+        assert np.sum(bias == np.float32(v)) == E - n_hot
+        # the same hot set as the graded table (its zeros)
+        np.testing.assert_array_equal(np.flatnonzero(oracle.bias_table(b, n_hot, -1.0) == 0.0), hot)
+    mask = oracle.bias_flat(b, n_hot, -np.inf)
+    z = rng.normal(0, 2.3, (40, E)).astype(np.float32)
+    ids = oracle.topk(z, k, mask)
+    for t in range(40):
+        sub = np.lexsort((hot, -z[t, hot].astype(np.float64)))
+        assert list(ids[t]) == list(hot[sub[:k]])
+    # value 0 is no bias at all, bit for bit
+    np.testing.assert_array_equal(oracle.topk(z, k, oracle.bias_flat(b, n_hot, 0.0)), oracle.topk(z, k))
+
+
+def test_bias_affinity_values_zero_lambda_and_monotone_hits():
+    """'Then Maya's own knob beat ours': lambda is added to the score of every
+    expert resident now.  lambda = 0 changes nothing; a larger lambda never
+    lowers the number of resident picks of a token; a lambda above the logit
+    range makes the picks the top-k of the resident experts alone."""
+    E, S, k = 128, 32, 8
+    e2s = np.full(E, -1, np.int32)
+    res = np.sort(rng.choice(E, S, replace=False))
+    e2s[res] = np.arange(S)
+    base = -rng.uniform(0, 1, E).astype(np.float32)
+    a = oracle.bias_affinity(e2s, 0.25)
+    assert np.all(a[res] == np.float32(0.25)) and np.sum(a == 0.0) == E - S
+    np.testing.assert_array_equal(oracle.bias_affinity(e2s, 0.0, base), base)
+    ab = oracle.bias_affinity(e2s, 0.25, base)
+    ref = base.copy()
+    ref[res] = base[res] + np.float32(0.25)  # one fp32 add
+    np.testing.assert_array_equal(ab, ref)
+    z = rng.normal(0, 2.3, (200, E)).astype(np.float32)
+    prev = None
+    for lam in (0.0, 0.125, 0.25, 0.5, 1.0, 2.0):
+        ids = oracle.topk(z, k, oracle.bias_affinity(e2s, lam))
+        hits = (e2s[ids] >= 0).sum(1)
+        if prev is not None:
+            assert np.all(hits >= prev)
+        prev = hits
+    big = np.float32(2.0 * (z.max() - z.min()) + 1.0)
+    ids = oracle.topk(z, k, oracle.bias_affinity(e2s, big))
+    for t in range(200):
+        assert np.all(e2s[ids[t]] >= 0)
+        sub = np.lexsort((res, -(z[t, res] + big).astype(np.float64)))
+        assert list(ids[t]) == list(res[sub[:k]])
+
+
+def test_route_weights_damped_closed_form():
+    """'Qwen on Strata': damped weights are the softmax of the biased scores
+    fl32(z + bias); with no bias (or one bias for all picks) they are the
+    selection-only weights."""
+    E = 256
+    z = rng.normal(0, 2.3, (100, E)).astype(np.float32)
+    bias = np.where(rng.uniform(size=E) < 0.5, -0.75, 0.0).astype(np.float32)
+    ids2 = oracle.topk(z, 2, bias)
+    w = oracle.route_weights_damped(z, bias, ids2)
+    s = (z + bias).astype(np.float32)
+    s0 = s[np.arange(100), ids2[:, 0]].astype(np.float64)
+    s1 = s[np.arange(100), ids2[:, 1]].astype(np.float64)
+    np.testing.assert_allclose(w[:, 0], 1.0 / (1.0 + np.exp(s1 - s0)), rtol=2 ** -23)
+    ids = oracle.topk(z, 8, bias)
+    wd = oracle.route_weights_damped(z, bias, ids)
+    assert np.all(np.abs(wd.astype(np.float64).sum(1) - 1.0) <= 8 * 2.0 ** -24)
+    np.testing.assert_array_equal(oracle.route_weights_damped(z, None, ids), oracle.route_weights(z, ids))
+    same = np.full(E, -0.75, np.float32)  # one shift for every pick: the softmax does not move
+    np.testing.assert_allclose(oracle.route_weights_damped(z, same, ids), oracle.route_weights(z, ids), rtol=2e-6)
+    # a pick that carries the penalty weighs less than it would selection-only
+    ws = oracle.route_weights(z, ids)
+    pen = bias[ids] < 0
+    mixed = pen.any(1) & ~pen.all(1)
+    assert np.all(wd[mixed][pen[mixed]] < ws[mixed][pen[mixed]])
+
+
 def test_bias_table_hand_values():
     # b_edge = 0.2 (weakest of the two hot experts)
     b = np.array([0.4, 0.2, 0.2, 0.2 * math.exp(-0.5), 0.2 * math.exp(-3), 0.0])
