@@ -30,7 +30,9 @@ line carries two more workloads of the layer:
            routing id, experts gathered per step, gather GB/s against the
            measured host link, layer tokens/s with the host pass
 
-`--workload stack` runs the 48-layer, 512-expert 4-bit stack instead.
+`--workload stack` runs the 48-layer, 512-expert 4-bit stack instead, and
+`--workload bias` the routing-bias variants (flat bias, hard mask, graded
+table, damped weights; live-cache affinity on a dynamic cache).
 """
 from __future__ import annotations
 
@@ -70,7 +72,7 @@ def parse():
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
-    ap.add_argument("--workload", choices=["decode", "stack"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "stack", "bias"], default="decode")
     ap.add_argument("--stack-steps", type=int, default=20, help="timed 48-layer steps at T=1 (half at T=32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
@@ -111,6 +113,10 @@ def main():
 
     if args.workload == "stack":
         out = bench_stack(m, torch, synth, SlotStack, NativeStack, args.threads or host_threads(), args)
+        print(json.dumps(out), flush=True)
+        return
+    if args.workload == "bias":
+        out = bench_bias(m, torch, synth, SlotLayer, NativeStack, args.threads or host_threads())
         print(json.dumps(out), flush=True)
         return
 
@@ -468,6 +474,157 @@ def bench_stack(m, torch, synth, SlotStack, NativeStack, nthreads, args, n_base=
                         "resident_experts_per_layer": round(resident_slabs / (steps * NL), 2),
                         "host_experts_per_layer": round(host / (steps * NL), 2)}
     native.close()
+    return out
+
+
+def _drift(y, y0):
+    """Relative L2 distance of a layer output from the unbiased layer's output."""
+    return float((y - y0).double().norm()) / max(float(y0.double().norm()), 1e-30)
+
+
+def bench_bias(m, torch, synth, SlotLayer, NativeStack, nthreads, steps=48, warmup=4):
+    """Routing-bias variants of "Nudge, don't cut" on the same router.
+
+    static: the 512-expert top-10 4-bit layer (hidden 2048, intermediate 512)
+    with the 192 brightest experts of a Dirichlet(0.3) profile resident, 32
+    tokens per step.  Variants: no bias; graded table (cap -1, -0.5); flat
+    bias (-1, -0.75, -0.5); hard mask; graded cap -1 with damped weights.
+    live: the 128-expert W8A8 layer (hidden 2048, intermediate 768, top-8)
+    routed by its own router (gate ~N(0, 0.05)) through a 32-slot LRU cache
+    from empty, 16 tokens per step, with live-cache affinity lambda in
+    {0, 0.25, 0.5, 1}: the bias is rebuilt from the cache state before every
+    step (moe_bias_affinity on the compute stream).
+    Per variant: hit rate per routing id, experts served by the host per
+    step (and gathered, live cache), layer tokens/s with the host pass on the
+    native driver, and the layer-output drift: relative L2 distance of the
+    variant's output from the unbiased layer's on the same tokens (the
+    layer's output does not depend on what is cached, so the unbiased
+    output is the same for every cache)."""
+    out = {"workload": "routing-bias variants: static 512-expert top-10 4-bit layer, 192 hot resident, T=32; "
+                       "live-cache affinity on a 128-expert W8A8 layer, 32 LRU slots, T=16",
+           "data": "synthetic", "steps": steps}
+
+    # ---------------------------------------------------------------- static cache
+    c = synth.CONFIGS["c4"]
+    E, k, H, I, S = c["E"], c["k"], c["H"], c["I"], c["S"]
+    T = 32
+    base = synth.config_seed("c4")
+    slab = synth.slab_bytes(synth.W_Q4B32, H, I)
+    store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
+    synth.slabs_into(store.data_ptr(), synth.W_Q4B32, base, 0, 0, E, H, I, c["sigma_w"], slab)
+    b = synth.dirichlet(synth.key(base, synth.TAG_B, 0), E, 0.3)
+    resident = np.lexsort((np.arange(E), -b))[:S].astype(np.int32)
+    res_t = torch.from_numpy(resident).cuda()
+    slots = store[torch.from_numpy(resident.astype(np.int64))].cuda()
+    G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
+    b_t = torch.from_numpy(b).cuda()
+    xs = torch.from_numpy(np.stack([synth.normal(synth.key(base, synth.TAG_X, 0, 100 + i), (T, H), 1.0, 1)
+                                    for i in range(warmup + steps)]).view(np.int16)).cuda()
+
+    def table(kind, val):
+        t = torch.empty(E, dtype=torch.float32, device="cuda")
+        if kind == "graded":
+            m.moe_bias_table(b_t, E, S, val, t)
+        else:
+            m.moe_bias_flat(b_t, E, S, val, t)
+        return t
+
+    variants = [("none", None, 0), ("graded cap -1", table("graded", -1.0), 0),
+                ("graded cap -0.5", table("graded", -0.5), 0), ("flat -1", table("flat", -1.0), 0),
+                ("flat -0.75", table("flat", -0.75), 0), ("flat -0.5", table("flat", -0.5), 0),
+                ("hard mask", table("flat", -float("inf")), 0),
+                ("graded cap -1, damped weights", table("graded", -1.0), m.MOE_ROUTE_DAMPED)]
+    res_mask = torch.zeros(E, dtype=torch.bool, device="cuda")
+    res_mask[res_t.long()] = True
+    L = SlotLayer(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_Q4B32, T_max=T, policy="static", host_store=store,
+                  slot_store=slots, G=G, n_threads=nthreads)
+    L.init_cache(res_t)
+    y0 = []
+    rows = []
+    for name, bias, flags in variants:
+        # analysis pass: picks, hits and outputs through the Python-driven layer
+        L.bias, L.route_flags = bias, flags
+        hits, host_e, drift = 0, 0, []
+        for i in range(steps):
+            y = L.step(xs[warmup + i], T).clone()
+            ids = L.ids[:T * k].long()
+            hits += int(res_mask[ids].sum())
+            host_e += int(torch.unique(ids[~res_mask[ids]]).numel())
+            if name == "none":
+                y0.append(y)
+            else:
+                drift.append(_drift(y, y0[i]))
+        row = {"variant": name, "hit_rate": round(hits / (steps * T * k), 4),
+               "host_experts_per_step": round(host_e / steps, 2),
+               "output_drift": round(float(np.mean(drift)), 4) if drift else 0.0}
+        if flags == 0:  # timing on the native driver (damped weights change no pick: the same work)
+            nat = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_Q4B32, T_max=T, n_threads=nthreads,
+                              layers=[dict(host_store=store, slot_store=slots, G=G, bias=bias, resident=res_t)])
+            for i in range(warmup):
+                nat.layer_step(0, xs[i], T)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                nat.layer_step(0, xs[warmup + i], T)
+            torch.cuda.synchronize()
+            row["tokens_per_s"] = round(T * steps / (time.perf_counter() - t0), 1)
+            nat.close()
+        rows.append(row)
+    out["static"] = rows
+    del L, slots, store
+
+    # ---------------------------------------------------------------- live-cache affinity
+    c = synth.CONFIGS["c3"]
+    E, k, H, I, S = c["E"], c["k"], c["H"], c["I"], c["S"]
+    T = c["T"]
+    base = synth.config_seed("c3")
+    slab = synth.slab_bytes(synth.W_W8A8, H, I)
+    store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
+    synth.slabs_into(store.data_ptr(), synth.W_W8A8, base, 0, 0, E, H, I, c["sigma_w"], slab)
+    G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
+    xs = torch.from_numpy(np.stack([synth.normal(synth.key(base, synth.TAG_X, 0, 100 + i), (T, H), 1.0, 1)
+                                    for i in range(warmup + steps)]).view(np.int16)).cuda()
+    rows = []
+    y0 = []
+    for lam in (0.0, 0.25, 0.5, 1.0):
+        bias = torch.zeros(E, dtype=torch.float32, device="cuda")
+        L = SlotLayer(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_W8A8, T_max=T, policy="lru", host_store=store,
+                      slot_store=torch.empty((S, slab), dtype=torch.uint8, device="cuda"), G=G, bias=bias,
+                      n_threads=nthreads)
+        L.init_cache(None)
+        acc = torch.zeros(4, dtype=torch.int64, device="cuda")
+        drift = []
+        for i in range(warmup + steps):
+            m.moe_bias_affinity(L.e2s, None, E, lam, bias)
+            y = L.step(xs[i], T).clone()
+            if i >= warmup:
+                acc += L.stats
+                if lam == 0.0:
+                    y0.append(y)
+                else:
+                    drift.append(_drift(y, y0[i - warmup]))
+        hits, distinct, gathered, host = [int(v) for v in acc.cpu()]
+        row = {"lambda": lam, "hit_rate": round(hits / (steps * T * k), 4),
+               "gathered_per_step": round(gathered / steps, 2), "host_experts_per_step": round(host / steps, 2),
+               "output_drift": round(float(np.mean(drift)), 4) if drift else 0.0}
+        # timing on the native driver, the affinity table rebuilt before each step on the same stream
+        spec = dict(host_store=store, slot_store=torch.empty((S, slab), dtype=torch.uint8, device="cuda"), G=G,
+                    bias=bias, resident=None, policy="lru")
+        nat = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_W8A8, T_max=T, layers=[spec], n_threads=nthreads)
+        for i in range(warmup):
+            m.moe_bias_affinity(nat.e2s(0), None, E, lam, bias)
+            nat.layer_step(0, xs[i], T)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            m.moe_bias_affinity(nat.e2s(0), None, E, lam, bias)
+            nat.layer_step(0, xs[warmup + i], T)
+        torch.cuda.synchronize()
+        row["tokens_per_s"] = round(T * steps / (time.perf_counter() - t0), 1)
+        nat.close()
+        rows.append(row)
+        del L
+    out["live_affinity"] = rows
     return out
 
 

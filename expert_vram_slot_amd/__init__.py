@@ -21,6 +21,7 @@ MOE_X_F32, MOE_X_BF16 = 0, 1
 MOE_W_F32, MOE_W_BF16, MOE_W_W8A8, MOE_W_Q4B32 = 0, 1, 2, 3
 MOE_STATIC, MOE_LRU, MOE_LFU = 0, 1, 2
 MOE_MAX_E, MOE_MAX_S, MOE_MAX_K = 4096, 1024, 32
+MOE_ROUTE_DAMPED = 1
 POLICIES = {"static": MOE_STATIC, "lru": MOE_LRU, "lfu": MOE_LFU}
 
 
@@ -61,7 +62,10 @@ def lib():
             "moe_last_error": (ctypes.c_char_p, []),
             "moe_slab_layout": (i32, [i32, i32, i32, ctypes.POINTER(SlabLayout)]),
             "moe_bias_table": (i32, [vp, i32, i32, f32, vp, vp]),
+            "moe_bias_flat": (i32, [vp, i32, i32, f32, vp, vp]),
+            "moe_bias_affinity": (i32, [vp, vp, i32, f32, vp, vp]),
             "moe_route": (i32, [vp, i32, vp, vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]),
+            "moe_route_ex": (i32, [vp, i32, vp, vp, vp, i32, i32, i32, i32, i32, vp, vp, vp, vp]),
             "cache_init": (i32, [ctypes.POINTER(CacheState), vp, vp]),
             "cache_pick_static": (i32, [vp, i32, i32, i32, vp, vp]),
             "cache_manage": (i32, [ctypes.POINTER(CacheState), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
@@ -134,6 +138,19 @@ def moe_bias_table(b, E, n_hot, cap, bias, stream=None):
 def moe_route(x, x_dtype, G, bias, ids_in, T, H, E, k, ids, w, logits, stream=None):
     return _check("moe_route", lib().moe_route(_p(x), x_dtype, _p(G), _p(bias), _p(ids_in), T, H, E, k, _p(ids),
                                                _p(w), _p(logits), _stream(stream)))
+
+
+def moe_route_ex(x, x_dtype, G, bias, ids_in, T, H, E, k, flags, ids, w, logits, stream=None):
+    return _check("moe_route_ex", lib().moe_route_ex(_p(x), x_dtype, _p(G), _p(bias), _p(ids_in), T, H, E, k, flags,
+                                                     _p(ids), _p(w), _p(logits), _stream(stream)))
+
+
+def moe_bias_flat(b, E, n_hot, value, bias, stream=None):
+    return _check("moe_bias_flat", lib().moe_bias_flat(_p(b), E, n_hot, value, _p(bias), _stream(stream)))
+
+
+def moe_bias_affinity(e2s, base, E, lam, bias, stream=None):
+    return _check("moe_bias_affinity", lib().moe_bias_affinity(_p(e2s), _p(base), E, lam, _p(bias), _stream(stream)))
 
 
 def cache_state(e2s, s2e, last, freq, step, E, S) -> CacheState:

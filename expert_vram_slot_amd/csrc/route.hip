@@ -25,6 +25,8 @@ __device__ __forceinline__ float load_act(const void* p, int64_t i) {
 
 // ---------------------------------------------------------------- bias table
 
+// FLAT: every cold expert gets `cap` itself (flat bias; -inf is the hard mask)
+template <bool FLAT>
 __global__ void __launch_bounds__(1024) k_bias_table(const double* __restrict__ b, int E, int n_hot, float cap,
                                                      float* __restrict__ bias) {
     __shared__ double sb[MOE_MAX_E];
@@ -51,10 +53,24 @@ __global__ void __launch_bounds__(1024) k_bias_table(const double* __restrict__ 
             bias[e] = 0.0f;
             continue;
         }
+        if (FLAT) {
+            bias[e] = cap;
+            continue;
+        }
         const double be = sb[e];
         const double v = (be > 0.0 && b_edge > 0.0) ? log(be / b_edge) : -INFINITY;
         bias[e] = (float)(v > (double)cap ? v : (double)cap);
     }
+}
+
+// Live-cache affinity: base (or 0) plus lambda for every expert with a slot.
+__global__ void k_bias_affinity(const int32_t* __restrict__ e2s, const float* __restrict__ base, int E, float lambda,
+                                float* __restrict__ bias) {
+    const int e = blockIdx.x * blockDim.x + threadIdx.x;
+    if (e >= E) return;
+    float v = base ? base[e] : 0.0f;
+    if (e2s[e] >= 0) v = v + lambda;
+    bias[e] = v;
 }
 
 // ----------------------------------------------------------------- router
@@ -132,8 +148,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 }
 
 // Top-k of one token's selection scores fl32(z[e] + bias[e]) on (score desc,
-// id asc) by one wave, then the softmax of the raw logits z over the picks
-// in double; lane j < k ends up holding the j-th pick.  Lane l keeps the
+// id asc) by one wave, then the softmax over the picks, in double, of the
+// raw logits z (selection only) or, with `damped`, of the biased scores;
+// lane j < k ends up holding the j-th pick.  Lane l keeps the
 // codes of experts l, l + 64, ... in registers (JM >= ceil(E / 64) of them),
 // read once; each of the k rounds takes the lane's best code (the lowest
 // expert on equal codes), a wave maximum of (code, ~expert), and clears the
@@ -142,7 +159,7 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 template <int JM>
 __device__ __forceinline__ void topk_softmax(const float* z, const float* __restrict__ bias,
                                              const int32_t* __restrict__ ids_in, int E, int k, int t,
-                                             int32_t* __restrict__ ids, float* __restrict__ w) {
+                                             int32_t* __restrict__ ids, float* __restrict__ w, bool damped) {
     const int lane = threadIdx.x & 63;
     int32_t pick = -1;
     if (ids_in) {
@@ -183,7 +200,14 @@ __device__ __forceinline__ void topk_softmax(const float* z, const float* __rest
         }
         if (lane < k) ids[(int64_t)t * k + lane] = pick;
     }
-    const double zj = lane < k ? (double)z[min(max(pick, 0), E - 1)] : -INFINITY;
+    // the softmax input: the raw logit, or with `damped` the biased score
+    double zj = -INFINITY;
+    if (lane < k) {
+        const int pe = min(max(pick, 0), E - 1);
+        float v = z[pe];
+        if (damped && bias) v = v + bias[pe];
+        zj = (double)v;
+    }
     double m = -INFINITY;
     for (int j = 0; j < k; ++j) m = fmax(m, readlane_f64(zj, j));
     const double ej = lane < k ? exp(zj - m) : 0.0;
@@ -195,10 +219,10 @@ __device__ __forceinline__ void topk_softmax(const float* z, const float* __rest
 // topk_softmax with the register count picked for E at run time
 __device__ __forceinline__ void topk_softmax_any(const float* z, const float* __restrict__ bias,
                                                  const int32_t* __restrict__ ids_in, int E, int k, int t,
-                                                 int32_t* __restrict__ ids, float* __restrict__ w) {
-    if (E <= 256) topk_softmax<4>(z, bias, ids_in, E, k, t, ids, w);
-    else if (E <= 1024) topk_softmax<16>(z, bias, ids_in, E, k, t, ids, w);
-    else topk_softmax<64>(z, bias, ids_in, E, k, t, ids, w);
+                                                 int32_t* __restrict__ ids, float* __restrict__ w, bool damped) {
+    if (E <= 256) topk_softmax<4>(z, bias, ids_in, E, k, t, ids, w, damped);
+    else if (E <= 1024) topk_softmax<16>(z, bias, ids_in, E, k, t, ids, w, damped);
+    else topk_softmax<64>(z, bias, ids_in, E, k, t, ids, w, damped);
 }
 
 // One workgroup routes TB consecutive tokens.  Logits: G is [E][H]; each wave
@@ -213,7 +237,7 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
                                                          const float* __restrict__ bias,
                                                          const int32_t* __restrict__ ids_in, int T, int H, int E,
                                                          int k, int32_t* __restrict__ ids, float* __restrict__ w,
-                                                         float* __restrict__ logits) {
+                                                         float* __restrict__ logits, int damped) {
     extern __shared__ __align__(16) unsigned char smem[];
     constexpr int EPG = XD == MOE_X_F32 ? 4 : 8;  // elements per 16-byte granule
     constexpr int ROUTE_RW = route_rows<TB>();
@@ -283,7 +307,7 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_route(const void* __restrict_
     }
 
     // one wave per token
-    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax_any(zl + t * E, bias, ids_in, E, k, t0 + t, ids, w);
+    for (int t = wv; t < nt; t += ROUTE_KSPLIT) topk_softmax_any(zl + t * E, bias, ids_in, E, k, t0 + t, ids, w, damped != 0);
 }
 
 // ----------------------------------------------------- two-kernel router
@@ -374,10 +398,10 @@ __global__ void __launch_bounds__(ROUTE_THREADS) k_logits(const void* __restrict
 template <int JM>
 __global__ void __launch_bounds__(ROUTE_THREADS) k_topk(const float* __restrict__ z, const float* __restrict__ bias,
                                                         const int32_t* __restrict__ ids_in, int T, int E, int k,
-                                                        int32_t* __restrict__ ids, float* __restrict__ w) {
+                                                        int32_t* __restrict__ ids, float* __restrict__ w, int damped) {
     const int t = blockIdx.x * ROUTE_KSPLIT + (int)(threadIdx.x >> 6);
     if (t >= T) return;
-    topk_softmax<JM>(z + (int64_t)t * E, bias, ids_in, E, k, t, ids, w);
+    topk_softmax<JM>(z + (int64_t)t * E, bias, ids_in, E, k, t, ids, w, damped != 0);
 }
 
 template <int XD, int TB>
@@ -391,7 +415,7 @@ int launch_logits(const void* x, const void* G, int T, int H, int E, float* z, h
 
 template <int XD>
 int route_split(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
-                int32_t* ids, float* w, float* logits, hipStream_t s) {
+                int32_t* ids, float* w, float* logits, int damped, hipStream_t s) {
     // tokens per workgroup: more for larger batches (fewer reads of G), within 64 KiB of LDS
     const size_t xrow = (size_t)H * (XD == MOE_X_F32 ? 4 : 2);
     int tb = T >= 512 ? 8 : T >= 128 ? 4 : T >= 32 ? 2 : 1;
@@ -407,17 +431,17 @@ int route_split(const void* x, const void* G, const float* bias, const int32_t* 
     if (rc) return rc;
     const dim3 grid((T + ROUTE_KSPLIT - 1) / ROUTE_KSPLIT);
     const int nj = (E + 63) / 64;
-    if (nj <= 2) hipLaunchKernelGGL(k_topk<2>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
-    else if (nj <= 4) hipLaunchKernelGGL(k_topk<4>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
-    else if (nj <= 8) hipLaunchKernelGGL(k_topk<8>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
-    else if (nj <= 16) hipLaunchKernelGGL(k_topk<16>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
-    else hipLaunchKernelGGL(k_topk<64>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w);
+    if (nj <= 2) hipLaunchKernelGGL(k_topk<2>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w, damped);
+    else if (nj <= 4) hipLaunchKernelGGL(k_topk<4>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w, damped);
+    else if (nj <= 8) hipLaunchKernelGGL(k_topk<8>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w, damped);
+    else if (nj <= 16) hipLaunchKernelGGL(k_topk<16>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w, damped);
+    else hipLaunchKernelGGL(k_topk<64>, grid, dim3(ROUTE_THREADS), 0, s, logits, bias, ids_in, T, E, k, ids, w, damped);
     return moe_check_launch("moe_route/topk");
 }
 
 template <int XD, int TB>
 int launch_route(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
-                 int32_t* ids, float* w, float* logits, hipStream_t s) {
+                 int32_t* ids, float* w, float* logits, int damped, hipStream_t s) {
     const size_t lds = sizeof(double) * TB * H + sizeof(float) * TB * E;
     if (lds > 160 * 1024) return moe_fail(MOE_E_SHAPE, "moe_route: H=%d E=%d need %zu B of LDS", H, E, lds);
     const int grid = (T + TB - 1) / TB;
@@ -430,24 +454,24 @@ int launch_route(const void* x, const void* G, const float* bias, const int32_t*
         }
     }
     hipLaunchKernelGGL((k_route<XD, TB>), dim3(grid), dim3(ROUTE_THREADS), lds, s, x, G, bias, ids_in, T, H, E, k,
-                       ids, w, logits);
+                       ids, w, logits, damped);
     return moe_check_launch("moe_route");
 }
 
 template <int XD>
 int route_dispatch(const void* x, const void* G, const float* bias, const int32_t* ids_in, int T, int H, int E, int k,
-                   int32_t* ids, float* w, float* logits, hipStream_t s) {
+                   int32_t* ids, float* w, float* logits, int damped, hipStream_t s) {
     // with a logits buffer the logits and the top-k run as two kernels (many
     // workgroups share the gate); without one, one fused kernel per token block
-    if (logits) return route_split<XD>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
+    if (logits) return route_split<XD>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, damped, s);
     // small batches: one token per workgroup (more workgroups, lower latency);
     // large batches: several tokens share each read of G
     int tb = T <= 64 ? 1 : 4;
     while (tb > 1 && sizeof(double) * tb * H + sizeof(float) * tb * E > 80 * 1024) tb >>= 1;
     switch (tb) {
-        case 4: return launch_route<XD, 4>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
-        case 2: return launch_route<XD, 2>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
-        default: return launch_route<XD, 1>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, s);
+        case 4: return launch_route<XD, 4>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, damped, s);
+        case 2: return launch_route<XD, 2>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, damped, s);
+        default: return launch_route<XD, 1>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, damped, s);
     }
 }
 
@@ -461,25 +485,53 @@ int moe_bias_table(const double* b, int E, int n_hot, float cap, float* bias, hi
     MOE_REQUIRE(E <= MOE_MAX_E, MOE_E_SHAPE, "moe_bias_table: E=%d exceeds %d", E, MOE_MAX_E);
     MOE_REQUIRE(!(cap > 0.0f) && cap == cap, MOE_E_ARG, "moe_bias_table: cap=%g must be <= 0", (double)cap);
     if (n_hot > E) n_hot = E;
-    hipLaunchKernelGGL(k_bias_table, dim3(1), dim3(1024), 0, stream, b, E, n_hot, cap, bias);
+    hipLaunchKernelGGL(k_bias_table<false>, dim3(1), dim3(1024), 0, stream, b, E, n_hot, cap, bias);
     return moe_check_launch("moe_bias_table");
 }
 
-int moe_route(const void* x, int x_dtype, const void* G, const float* bias, const int32_t* ids_in, int T, int H,
-              int E, int k, int32_t* ids, float* w, float* logits, hipStream_t stream) {
+int moe_bias_flat(const double* b, int E, int n_hot, float value, float* bias, hipStream_t stream) {
+    MOE_REQUIRE(b && bias, MOE_E_ARG, "moe_bias_flat: b and bias must be non-NULL");
+    MOE_REQUIRE(E >= 1 && n_hot >= 1, MOE_E_ARG, "moe_bias_flat: E=%d and n_hot=%d must be >= 1", E, n_hot);
+    MOE_REQUIRE(E <= MOE_MAX_E, MOE_E_SHAPE, "moe_bias_flat: E=%d exceeds %d", E, MOE_MAX_E);
+    MOE_REQUIRE(!(value > 0.0f) && value == value, MOE_E_ARG, "moe_bias_flat: value=%g must be <= 0", (double)value);
+    if (n_hot > E) n_hot = E;
+    hipLaunchKernelGGL(k_bias_table<true>, dim3(1), dim3(1024), 0, stream, b, E, n_hot, value, bias);
+    return moe_check_launch("moe_bias_flat");
+}
+
+int moe_bias_affinity(const int32_t* e2s, const float* base, int E, float lambda, float* bias, hipStream_t stream) {
+    MOE_REQUIRE(e2s && bias, MOE_E_ARG, "moe_bias_affinity: e2s and bias must be non-NULL");
+    MOE_REQUIRE(E >= 1, MOE_E_ARG, "moe_bias_affinity: E=%d must be >= 1", E);
+    MOE_REQUIRE(E <= MOE_MAX_E, MOE_E_SHAPE, "moe_bias_affinity: E=%d exceeds %d", E, MOE_MAX_E);
+    MOE_REQUIRE(lambda - lambda == 0.0f, MOE_E_ARG, "moe_bias_affinity: lambda=%g must be finite", (double)lambda);
+    hipLaunchKernelGGL(k_bias_affinity, dim3((E + 255) / 256), dim3(256), 0, stream, e2s, base, E, lambda, bias);
+    return moe_check_launch("moe_bias_affinity");
+}
+
+int moe_route_ex(const void* x, int x_dtype, const void* G, const float* bias, const int32_t* ids_in, int T, int H,
+                 int E, int k, int flags, int32_t* ids, float* w, float* logits, hipStream_t stream) {
     MOE_REQUIRE(x && G && w, MOE_E_ARG, "moe_route: x, G and w must be non-NULL");
     MOE_REQUIRE(ids_in || ids, MOE_E_ARG, "moe_route: ids must be non-NULL when ids_in is NULL");
     MOE_REQUIRE(T >= 0 && H >= 1 && E >= 1 && k >= 1, MOE_E_ARG, "moe_route: T=%d H=%d E=%d k=%d out of range", T, H,
                 E, k);
+    MOE_REQUIRE((flags & ~MOE_ROUTE_DAMPED) == 0, MOE_E_ARG, "moe_route: unknown flags 0x%x", flags);
     MOE_REQUIRE(k <= E && k <= MOE_MAX_K && E <= MOE_MAX_E, MOE_E_SHAPE,
                 "moe_route: need k=%d <= E=%d, k <= %d, E <= %d", k, E, MOE_MAX_K, MOE_MAX_E);
     if (T == 0) return moe_ok();
     MOE_REQUIRE(moe_aligned16(x) && moe_aligned16(G), MOE_E_ALIGN, "moe_route: x and G must be 16-byte aligned");
     MOE_REQUIRE(H % (x_dtype == MOE_X_F32 ? 4 : 8) == 0, MOE_E_ALIGN,
                 "moe_route: H=%d must fill whole 16-byte granules", H);
-    if (x_dtype == MOE_X_F32) return route_dispatch<MOE_X_F32>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, stream);
-    if (x_dtype == MOE_X_BF16) return route_dispatch<MOE_X_BF16>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, stream);
+    const int damped = (flags & MOE_ROUTE_DAMPED) ? 1 : 0;
+    if (x_dtype == MOE_X_F32)
+        return route_dispatch<MOE_X_F32>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, damped, stream);
+    if (x_dtype == MOE_X_BF16)
+        return route_dispatch<MOE_X_BF16>(x, G, bias, ids_in, T, H, E, k, ids, w, logits, damped, stream);
     return moe_fail(MOE_E_DTYPE, "moe_route: unknown activation format %d", x_dtype);
+}
+
+int moe_route(const void* x, int x_dtype, const void* G, const float* bias, const int32_t* ids_in, int T, int H,
+              int E, int k, int32_t* ids, float* w, float* logits, hipStream_t stream) {
+    return moe_route_ex(x, x_dtype, G, bias, ids_in, T, H, E, k, 0, ids, w, logits, stream);
 }
 
 }  // extern "C"

@@ -27,8 +27,8 @@ import torch
 
 from . import (MOE_W_F32, MOE_X_BF16, MOE_X_F32, POLICIES, LayerDesc, cache_gather, cache_init, cache_manage,
                cache_state, moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_layer_step,
-               moe_residual, moe_route, moe_slab_layout, moe_stack_step, moe_step_create, moe_step_destroy,
-               moe_step_stats)
+               moe_residual, moe_route_ex, moe_slab_layout, moe_stack_step, moe_step_create,
+               moe_step_destroy, moe_step_stats)
 
 
 def host_threads() -> int:
@@ -88,6 +88,7 @@ class SlotLayer:
         self.pool = cf.ThreadPoolExecutor(max_workers=1)
         self.ffn_events = None     # (start, end) torch events recorded around moe_ffn_slots when set
         self.gather_events = None  # (start, end) torch events recorded around cache_gather when set
+        self.route_flags = 0       # moe_route_ex flags (MOE_ROUTE_DAMPED)
 
     def init_cache(self, resident=None):
         cache_init(self.st, resident)
@@ -112,8 +113,8 @@ class SlotLayer:
             # given picks are copied into the packed block (the host pass reads them from there)
             self.ids[:P].copy_(ids_in.reshape(-1)[:P], non_blocking=True)
         # 1. router (picks, or weights of given picks)
-        moe_route(x, self.x_dtype, self.G, self.bias, None if ids_in is None else self.ids, T, self.H, self.E,
-                  self.k, self.ids, self.w, self.logits, cur)
+        moe_route_ex(x, self.x_dtype, self.G, self.bias, None if ids_in is None else self.ids, T, self.H, self.E,
+                     self.k, self.route_flags, self.ids, self.w, self.logits, cur)
         ids = self.ids
         # 2. cache step: victims, miss list, remap
         cache_manage(self.st, self.policy, ids, P, self.slot_ids, self.miss, self.n_miss, self.host_miss,

@@ -32,6 +32,10 @@
  *   [PGO] "Nudge, don't cut" -- "The method in five lines": bias[l][e] =
  *         max(cap, ln(b[l][e] / b_edge[l])), top-k by logit + bias, weights from
  *         the router's own softmax over the picked k; static table; opt-in.
+ *         "Experts that don't fit": the hard mask and the flat soft bias;
+ *         "Qwen on Strata: the bias as a quality dial": damped weights;
+ *         "Then Maya's own knob beat ours": live-cache affinity (a small lambda
+ *         on every expert in VRAM now, decode only).
  *
  * Conventions for every entry point
  *   - Return 0 on success or a negative MOE_E_* code; moe_last_error() then
@@ -144,6 +148,29 @@ int moe_slab_layout(int w_type, int H, int I, moe_slab_layout_t* out);
  * Errors: ARG (null, E < 1, n_hot < 1), SHAPE (E > MOE_MAX_E). */
 int moe_bias_table(const double* b, int E, int n_hot, float cap, float* bias, hipStream_t stream);
 
+/* Flat selection bias, or the hard mask, of one layer, [PGO] "Experts that
+ * don't fit".  The hot set is the one moe_bias_table uses.
+ *   b      device double[E]: brightness per expert
+ *   n_hot  the n_hot brightest experts (ties: lower id) get 0
+ *   value  every other expert gets this number; <= 0, not NaN.  -INFINITY is
+ *          the hard mask: a cold expert never outranks a hot one, so with at
+ *          least k hot experts no cold expert is picked.
+ *   bias   device float[E] out
+ * Errors: ARG (null, E < 1, n_hot < 1, value > 0 or NaN), SHAPE (E > MOE_MAX_E). */
+int moe_bias_flat(const double* b, int E, int n_hot, float value, float* bias, hipStream_t stream);
+
+/* Live-cache affinity, [PGO] "Then Maya's own knob beat ours": lambda added to
+ * the selection score of every expert that is in VRAM now.
+ *   e2s     device int32[E]: a cache state's expert -> slot map, read when the
+ *           kernel runs (so in stream order after the last cache_manage)
+ *   base    device float[E] or NULL: a static table to add to (NULL reads 0)
+ *   lambda  finite
+ *   bias    device float[E] out: fl32(base[e] + lambda) where e2s[e] >= 0,
+ *           else base[e]; pass it to moe_route as the bias.  The pages use it
+ *           at decode only; which calls get it is the caller's choice.
+ * Errors: ARG (null, E < 1, lambda not finite), SHAPE (E > MOE_MAX_E). */
+int moe_bias_affinity(const int32_t* e2s, const float* base, int E, float lambda, float* bias, hipStream_t stream);
+
 /* Router, [PGO] "The method in five lines".
  *   x       device [T][H] in x_dtype
  *   G       device [E][H] in x_dtype (one row per expert)
@@ -160,6 +187,16 @@ int moe_bias_table(const double* b, int E, int n_hot, float cap, float* bias, hi
  * Errors: ARG, DTYPE, SHAPE (k > E, k > MOE_MAX_K, E > MOE_MAX_E), HIP. */
 int moe_route(const void* x, int x_dtype, const void* G, const float* bias, const int32_t* ids_in, int T, int H,
               int E, int k, int32_t* ids, float* w, float* logits, hipStream_t stream);
+
+/* moe_route with options; flags = 0 is moe_route exactly.
+ *   MOE_ROUTE_DAMPED  w is the softmax over the k picks of the biased scores
+ *                     s = fl32(z + bias) ("damped weights", [PGO] "Qwen on
+ *                     Strata: the bias as a quality dial") instead of the raw
+ *                     logits; with bias NULL the two are the same.
+ * Errors: those of moe_route; ARG for an unknown flag. */
+#define MOE_ROUTE_DAMPED 1
+int moe_route_ex(const void* x, int x_dtype, const void* G, const float* bias, const int32_t* ids_in, int T, int H,
+                 int E, int k, int flags, int32_t* ids, float* w, float* logits, hipStream_t stream);
 
 /* Initialise a cache state.  resident: device int32[S] (slot s holds expert
  * resident[s]) or NULL for an empty cache.  Clears last/freq and step.

@@ -128,6 +128,59 @@ def test_route_with_graded_bias(m):
     assert np.any(ids != oracle.topk(z, li.k))
 
 
+@pytest.mark.parametrize("value", [-0.75, -np.inf])
+def test_flat_bias_and_hard_mask_match_oracle(m, value):
+    """Flat soft bias and hard mask tables, and the routing under them."""
+    li = synth.LayerInputs("c4", T=32, with_store=False, layer=5)
+    b = synth.dirichlet(synth.key(li.base, synth.TAG_B, 5), li.E, 0.3)
+    bias_o = oracle.bias_flat(b, 192, value)
+    bias_g = torch.empty(li.E, dtype=torch.float32, device="cuda")
+    m.moe_bias_flat(dev(b), li.E, 192, value, bias_g)
+    np.testing.assert_array_equal(host(bias_g), bias_o)
+    ids, w, z = check_route(m, li, bias_o)
+    if value == -np.inf:
+        assert np.all(bias_o[ids] == 0.0)  # only hot experts are picked
+
+
+def test_affinity_bias_follows_the_live_cache(m):
+    """The affinity table is read from the cache state on the device: after a
+    manage step it adds lambda exactly to the experts that now have a slot."""
+    E, S, k, T = 128, 32, 8, 16
+    li = synth.LayerInputs("c2", T=T, with_store=False, layer=2)
+    c = GpuCache(m, E, S)
+    ids0 = synth.zipf_ids(synth.key(li.base, synth.TAG_ZIPF_PERM, 2), synth.key(li.base, synth.TAG_ZIPF_DRAW, 2), T, E,
+                          k, 0.8)
+    c.manage("lru", ids0)
+    e2s = host(c.e2s)
+    base_o = oracle.bias_flat(synth.dirichlet(synth.key(li.base, synth.TAG_B, 2), E, 0.3), 48, -0.5)
+    for base in (None, base_o):
+        aff_o = oracle.bias_affinity(e2s, 0.25, base)
+        aff_g = torch.empty(E, dtype=torch.float32, device="cuda")
+        m.moe_bias_affinity(c.e2s, None if base is None else dev(base), E, 0.25, aff_g)
+        np.testing.assert_array_equal(host(aff_g), aff_o)
+        ids, w, z = check_route(m, li, aff_o)
+    assert (e2s >= 0).sum() > 0
+
+
+def test_route_damped_weights_match_oracle(m):
+    li = synth.LayerInputs("c4", T=32, with_store=False, layer=6)
+    b = synth.dirichlet(synth.key(li.base, synth.TAG_B, 6), li.E, 0.3)
+    bias = oracle.bias_table(b, 192, -1.0)
+    x = dev(li.x.view(np.int16)); G = dev(li.G.view(np.int16))
+    for with_logits in (True, False):
+        ids = torch.empty((li.T, li.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((li.T, li.k), dtype=torch.float32, device="cuda")
+        z = torch.empty((li.T, li.E), dtype=torch.float32, device="cuda") if with_logits else None
+        m.moe_route_ex(x, li.x_dtype, G, dev(bias), None, li.T, li.H, li.E, li.k, m.MOE_ROUTE_DAMPED, ids, w, z)
+        zo = oracle.logits(li.x, li.x_dtype, li.G)
+        ids_o = oracle.topk(zo, li.k, bias)
+        np.testing.assert_array_equal(host(ids), ids_o)
+        np.testing.assert_allclose(host(w), oracle.route_weights_damped(zo, bias, ids_o), rtol=4e-6, atol=1e-9)
+    # flags 0 is moe_route; an unknown flag is refused
+    with pytest.raises(m.MoeError):
+        m.moe_route_ex(x, li.x_dtype, G, dev(bias), None, li.T, li.H, li.E, li.k, 2, ids, w, None)
+
+
 def test_route_given_ids_only_weights(m):
     li = synth.LayerInputs("c3", T=16, with_store=False)
     ids_in = synth.zipf_ids(synth.key(li.base, synth.TAG_ZIPF_PERM), synth.key(li.base, synth.TAG_ZIPF_DRAW), 16,
