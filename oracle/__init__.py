@@ -56,11 +56,12 @@ def lib():
         L.oracle_manage.argtypes = [i32, i32, i32, vp, vp, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, vp]
         L.oracle_gather.argtypes = [vp, i32, vp, vp, i64]
         L.oracle_pick_static.argtypes = [vp, i32, i32, i32, vp]
+        L.oracle_repick.argtypes = [i32, i32, vp, vp, vp, vp, vp, vp, vp, vp]
         L.oracle_residual.argtypes = [vp, i32, vp, i32, i32, vp]
         for f in ("oracle_decode_expert", "oracle_logits", "oracle_bias_table", "oracle_topk",
                   "oracle_route_weights", "oracle_expert", "oracle_layer", "oracle_manage", "oracle_gather",
                   "oracle_pick_static", "oracle_residual", "oracle_bias_flat", "oracle_bias_affinity",
-                  "oracle_route_weights_damped"):
+                  "oracle_route_weights_damped", "oracle_repick"):
             getattr(L, f).restype = i32
         _lib = L
     return _lib
@@ -215,6 +216,17 @@ class Cache:
                                    _p(host), _p(n_host), _p(stats)), "manage")
         nm, nh = int(n_miss[0]), int(n_host[0])
         return dict(slot_ids=slot_ids, miss=miss[:2 * nm].reshape(nm, 2), host_miss=host[:nh], stats=stats)
+
+    def repick(self, want):
+        """Swap the resident set to the distinct valid experts of want (oracle_repick);
+        returns the (expert, slot) loads."""
+        want = _c(want, np.int32).reshape(-1)
+        assert want.shape[0] == self.S
+        miss = np.empty(2 * max(self.S, 1), np.int32)
+        n_miss = np.zeros(1, np.int32)
+        _check(lib().oracle_repick(self.E, self.S, _p(self.e2s), _p(self.s2e), _p(self.last), _p(self.freq),
+                                   _p(self.step), _p(want), _p(miss), _p(n_miss)), "repick")
+        return miss[:2 * int(n_miss[0])].reshape(-1, 2).copy()
 
 
 def gather(miss, host_store, slot_store):

@@ -553,6 +553,43 @@ int oracle_residual(const void* x, int x_dtype, const float* y, int T, int H, vo
     return 0;
 }
 
+/* Periodic repick, [RTX] "Full Transcript" (have another look every ~500
+ * tokens, swap out whatever has gone cold, then leave the set alone): the new
+ * set is the distinct valid experts of want[0..S) (a repeated or out-of-range
+ * entry is skipped).  Members of the new set that are resident keep their
+ * slots; the others are loaded, in ascending expert id, into the slots whose
+ * expert left the set (empty slots included), in ascending slot order; a
+ * slot not needed for a load keeps its expert.  miss[] lists the loads as
+ * (expert, slot) pairs for the gather; a loaded slot restarts with
+ * last = step, freq = 0.  step does not advance. */
+int oracle_repick(int E, int S, int32_t* e2s, int32_t* s2e, uint32_t* last, uint32_t* freq,
+                  const uint32_t* step, const int32_t* want, int32_t* miss, int32_t* n_miss) {
+    if (E <= 0 || S < 0 || S > E) return -1;
+    unsigned char* in_new = (unsigned char*)calloc((size_t)E, 1);
+    if (!in_new) return -2;
+    for (int i = 0; i < S; ++i)
+        if (want[i] >= 0 && want[i] < E) in_new[want[i]] = 1;
+    int nm = 0, s = 0;
+    for (int e = 0; e < E; ++e) {
+        if (!in_new[e] || e2s[e] >= 0) continue;
+        /* next slot whose expert is not in the new set */
+        while (s < S && s2e[s] >= 0 && in_new[s2e[s]]) ++s;
+        if (s >= S) break; /* cannot happen: there are at most S members */
+        if (s2e[s] >= 0) e2s[s2e[s]] = -1;
+        s2e[s] = e;
+        e2s[e] = s;
+        last[s] = *step;
+        freq[s] = 0;
+        miss[2 * nm] = e;
+        miss[2 * nm + 1] = s;
+        ++nm;
+        ++s;
+    }
+    *n_miss = nm;
+    free(in_new);
+    return 0;
+}
+
 /* Static resident set ([RTX] transcript: the set is chosen once before the
  * run from a profile of what the router picks, then never changes): count
  * picks per expert over a profile batch and keep the S most picked, ties to

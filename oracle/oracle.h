@@ -76,6 +76,8 @@ int oracle_residual(const void* x, int x_dtype, const float* y, int T, int H, vo
 
 /* Static resident set: the S most-picked experts of a profile batch. */
 int oracle_pick_static(const int32_t* ids, int n_ids, int E, int S, int32_t* resident);
+int oracle_repick(int E, int S, int32_t* e2s, int32_t* s2e, uint32_t* last, uint32_t* freq,
+                  const uint32_t* step, const int32_t* want, int32_t* miss, int32_t* n_miss);
 
 #ifdef __cplusplus
 }

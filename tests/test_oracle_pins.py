@@ -524,6 +524,57 @@ def test_manage_deterministic():
             np.testing.assert_array_equal(a[key], b[key])
 
 
+def test_repick_swaps_only_what_went_cold():
+    """[RTX] 'Full Transcript': every ~500 tokens have another look, swap out
+    whatever has gone cold and leave the rest alone.  Written independently:
+    the set after a repick is the new set; members already resident keep
+    their slots; exactly the new members are loaded, in ascending id, into the
+    freed slots in ascending order; a second repick to the same set loads
+    nothing."""
+    r = np.random.default_rng(77)
+    for _ in range(50):
+        E = int(r.integers(4, 40))
+        S = int(r.integers(1, E + 1))
+        old = r.choice(E, S, replace=False)
+        new = r.choice(E, S, replace=False)
+        c = oracle.Cache(E, S, "static", resident=old)
+        slots_before = c.e2s.copy()
+        loads = c.repick(new)
+        assert set(np.flatnonzero(c.e2s >= 0)) == set(new.tolist())
+        assert sorted(c.s2e.tolist()) == sorted(new.tolist())
+        assert np.all(c.e2s[c.s2e] == np.arange(S))
+        kept = set(old.tolist()) & set(new.tolist())
+        for e in kept:
+            assert c.e2s[e] == slots_before[e]
+        loaded = sorted(set(new.tolist()) - set(old.tolist()))
+        assert loads[:, 0].tolist() == loaded
+        freed = sorted(slots_before[e] for e in set(old.tolist()) - set(new.tolist()))
+        assert loads[:, 1].tolist() == freed
+        assert len(c.repick(c.s2e.copy())) == 0
+    # a repeated or out-of-range entry is skipped; an unneeded slot keeps its expert
+    c = oracle.Cache(10, 4, "static", resident=[1, 2, 3, 4])
+    loads = c.repick(np.array([3, 7, 7, 42], np.int32))
+    assert loads.tolist() == [[7, 0]]
+    assert c.s2e.tolist() == [7, 2, 3, 4]
+    # from an empty cache the new set fills slots 0.. in ascending id
+    c = oracle.Cache(10, 3, "static")
+    assert c.repick(np.array([9, 2, 5], np.int32)).tolist() == [[2, 0], [5, 1], [9, 2]]
+
+
+def test_best_fixed_set_is_the_most_picked():
+    """The perfect-foresight fixed set of [RTX] 'Full Transcript' (see the
+    whole run, pick the best fixed set before starting): over every subset of
+    S experts, none serves more routing ids of the trace than the S most
+    picked (pick_static over the whole trace)."""
+    r = np.random.default_rng(5)
+    E, S = 9, 3
+    for _ in range(10):
+        trace = r.choice(E, 200, p=r.dirichlet(np.ones(E) * 0.5)).astype(np.int32)
+        counts = np.bincount(trace, minlength=E)
+        best = max(counts[list(sub)].sum() for sub in itertools.combinations(range(E), S))
+        assert counts[oracle.pick_static(trace, E, S)].sum() == best
+
+
 def test_gather_bytes_equal_source_rows():
     E, S, sb = 10, 4, 96
     host = rng.integers(0, 256, (E, sb)).astype(np.uint8)
