@@ -30,9 +30,11 @@ line carries two more workloads of the layer:
            routing id, experts gathered per step, gather GB/s against the
            measured host link, layer tokens/s with the host pass
 
-`--workload stack` runs the 48-layer, 512-expert 4-bit stack instead, and
+`--workload stack` runs the 48-layer, 512-expert 4-bit stack instead,
 `--workload bias` the routing-bias variants (flat bias, hard mask, graded
-table, damped weights; live-cache affinity on a dynamic cache).
+table, damped weights; live-cache affinity on a dynamic cache), and
+`--workload replay` a routing trace replayed under the cache policies
+(static, LRU, LFU, periodic repick, the perfect-foresight fixed set).
 """
 from __future__ import annotations
 
@@ -72,7 +74,7 @@ def parse():
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
-    ap.add_argument("--workload", choices=["decode", "stack", "bias"], default="decode")
+    ap.add_argument("--workload", choices=["decode", "stack", "bias", "replay"], default="decode")
     ap.add_argument("--stack-steps", type=int, default=20, help="timed 48-layer steps at T=1 (half at T=32)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (known bytes, for scaling HBM counters)")
@@ -118,6 +120,9 @@ def main():
     if args.workload == "bias":
         out = bench_bias(m, torch, synth, SlotLayer, NativeStack, args.threads or host_threads())
         print(json.dumps(out), flush=True)
+        return
+    if args.workload == "replay":
+        print(json.dumps(bench_replay(m, torch, synth)), flush=True)
         return
 
     cfg = "c2"
@@ -626,6 +631,85 @@ def bench_bias(m, torch, synth, SlotLayer, NativeStack, nthreads, steps=48, warm
         del L
     out["live_affinity"] = rows
     return out
+
+
+def bench_replay(m, torch, synth, n_tok=4096, phase_len=256, every=500, s_zipf=0.8):
+    """A routing trace replayed one decode token per step through the cache
+    alone (cache_manage -> cache_gather, and for the repick policy
+    cache_pick_static -> cache_repick -> cache_gather every `every` tokens),
+    with real slab copies from the pinned store.  Layer shape and slab of the
+    128-expert W8A8 layer (4.73 MB per expert), 32 slots, top-8.  The trace's
+    popular handful changes: Zipf(0.8) over a permutation drawn anew for each
+    phase of 256 tokens.  Policies: a static set from the first 500 tokens'
+    picks; LRU and LFU from empty; the static set repicked every 500 tokens
+    from the last 500 tokens' picks; and the perfect-foresight fixed set (the
+    32 most-picked experts of the whole trace).  Reported per policy: hit
+    rate per routing id, experts and bytes fetched while running (the initial
+    upload of a static set is counted apart), and the GPU time of the replay."""
+    c = synth.CONFIGS["c3"]
+    E, k, H, I, S = c["E"], c["k"], c["H"], c["I"], c["S"]
+    base = synth.config_seed("c3")
+    slab = synth.slab_bytes(synth.W_W8A8, H, I)
+    store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)
+    synth.slabs_into(store.data_ptr(), synth.W_W8A8, base, 0, 0, E, H, I, c["sigma_w"], slab)
+    slots = torch.empty((S, slab), dtype=torch.uint8, device="cuda")
+    trace = np.concatenate([synth.zipf_ids(synth.key(base, synth.TAG_ZIPF_PERM, 1, ph),
+                                           synth.key(base, synth.TAG_ZIPF_DRAW, 1, ph),
+                                           min(phase_len, n_tok - ph * phase_len), E, k, s_zipf)
+                            for ph in range((n_tok + phase_len - 1) // phase_len)])
+    trace_d = torch.from_numpy(trace).cuda()
+    i32 = dict(dtype=torch.int32, device="cuda")
+    rows = []
+    for name in ("static (first 500 tokens)", "lru", "lfu", f"repick every {every} tokens",
+                 "perfect-foresight fixed set"):
+        st_t = [torch.empty(E, **i32), torch.empty(S, **i32), torch.empty(S, **i32), torch.empty(S, **i32),
+                torch.zeros(1, **i32)]
+        st = m.cache_state(*st_t, E, S)
+        policy = {"lru": m.MOE_LRU, "lfu": m.MOE_LFU}.get(name, m.MOE_STATIC)
+        want = torch.empty(S, **i32)
+        miss, n_miss = torch.empty(2 * S, **i32), torch.zeros(1, **i32)
+        host_miss, n_host = torch.empty(E, **i32), torch.zeros(1, **i32)
+        slot_ids = torch.empty(k, **i32)
+        stats = torch.zeros(4, **i32)
+        acc = torch.zeros(4, dtype=torch.int64, device="cuda")
+        loads = torch.zeros(1, dtype=torch.int64, device="cuda")
+        upload = 0
+        if policy == m.MOE_STATIC:
+            src = trace_d if name.startswith("perfect") else trace_d[:every]
+            m.cache_pick_static(src.reshape(-1), src.numel(), E, S, want)
+            m.cache_init(st, None)
+            m.cache_repick(st, want, miss, n_miss)  # the upload at load time
+            m.cache_gather(miss, n_miss, S, store, slots, slab)
+            upload = S
+        else:
+            m.cache_init(st, None)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for t in range(n_tok):
+            if name.startswith("repick") and t > 0 and t % every == 0:
+                m.cache_pick_static(trace_d[t - every:t].reshape(-1), every * k, E, S, want)
+                m.cache_repick(st, want, miss, n_miss)
+                m.cache_gather(miss, n_miss, S, store, slots, slab)
+                loads += n_miss
+            m.cache_manage(st, policy, trace_d[t], k, slot_ids, miss, n_miss, host_miss, n_host, stats)
+            if policy != m.MOE_STATIC:
+                m.cache_gather(miss, n_miss, S, store, slots, slab)
+            acc += stats
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        hits, distinct, gathered, host = [int(v) for v in acc.cpu()]
+        fetched = gathered + int(loads.item())
+        rows.append({"policy": name, "hit_rate": round(hits / (n_tok * k), 4), "experts_fetched": fetched,
+                     "gb_fetched": round(fetched * slab / 1e9, 3), "upload_experts": upload,
+                     "host_experts_per_token": round(host / n_tok, 3),
+                     "gpu_ms_per_token": round(e0.elapsed_time(e1) / n_tok, 4),
+                     "wall_ms_per_token": round(wall / n_tok * 1e3, 4)})
+    return {"workload": f"routing trace of {n_tok} decode tokens (Zipf {s_zipf} over a permutation redrawn every "
+                        f"{phase_len} tokens), 128 experts top-8, 32 slots of 4.73 MB (W8A8 slabs), cache only "
+                        "(manage + gather, real copies)", "data": "synthetic", "policies": rows}
 
 
 def measure_gather(m, torch, synth):

@@ -70,6 +70,7 @@ def lib():
             "cache_pick_static": (i32, [vp, i32, i32, i32, vp, vp]),
             "cache_manage": (i32, [ctypes.POINTER(CacheState), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
             "cache_gather": (i32, [vp, vp, i32, vp, vp, sz, vp]),
+            "cache_repick": (i32, [ctypes.POINTER(CacheState), vp, vp, vp, vp]),
             "moe_ffn_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
             "moe_ffn_slots": (i32, [vp, i32, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, vp, sz, vp]),
             "moe_ffn_host_misses": (i32, [vp, i32, vp, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, i32]),
@@ -168,6 +169,11 @@ def cache_pick_static(ids, n_ids, E, S, resident, stream=None):
 def cache_manage(st, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_host, stats=None, stream=None):
     return _check("cache_manage", lib().cache_manage(ctypes.byref(st), policy, _p(ids), n_ids, _p(slot_ids), _p(miss),
                                                      _p(n_miss), _p(host_miss), _p(n_host), _p(stats),
+                                                     _stream(stream)))
+
+
+def cache_repick(st, want, miss, n_miss, stream=None):
+    return _check("cache_repick", lib().cache_repick(ctypes.byref(st), _p(want), _p(miss), _p(n_miss),
                                                      _stream(stream)))
 
 

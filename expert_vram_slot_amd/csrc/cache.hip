@@ -191,6 +191,72 @@ __global__ void __launch_bounds__(MANAGE_THREADS) k_manage(int32_t* __restrict__
     }
 }
 
+// Periodic repick in one workgroup: the new set is the distinct valid
+// experts of want[0..S); its members already resident keep their slots, the
+// others take, in ascending expert id, the slots whose expert is not in the
+// new set (empty ones included), in ascending slot order.  The loads are the
+// miss list of the gather that follows.
+__global__ void __launch_bounds__(MANAGE_THREADS) k_repick(int32_t* __restrict__ e2s, int32_t* __restrict__ s2e,
+                                                           uint32_t* __restrict__ last, uint32_t* __restrict__ freq,
+                                                           const uint32_t* __restrict__ stepp, int E, int S,
+                                                           const int32_t* __restrict__ want,
+                                                           int32_t* __restrict__ miss, int32_t* __restrict__ n_miss) {
+    __shared__ int32_t me2s[MOE_MAX_E];
+    __shared__ unsigned char in_new[MOE_MAX_E];
+    __shared__ int32_t loads[MOE_MAX_S];
+    __shared__ int32_t victim[MOE_MAX_S];
+    __shared__ int scratch[MANAGE_THREADS / 64 + 1];
+    const int tid = threadIdx.x;
+    const uint32_t now = *stepp;
+    for (int e = tid; e < E; e += MANAGE_THREADS) {
+        me2s[e] = e2s[e];
+        in_new[e] = 0;
+    }
+    __syncthreads();
+    for (int i = tid; i < S; i += MANAGE_THREADS) {
+        const int e = want[i];
+        if (e >= 0 && e < E) in_new[e] = 1;  // every writer stores the same value
+    }
+    __syncthreads();
+    int n_load = 0;
+    for (int e0 = 0; e0 < E; e0 += MANAGE_THREADS) {
+        const int e = e0 + tid;
+        const bool ld = e < E && in_new[e] && me2s[e] < 0;
+        int cnt;
+        const int pos = moe::block_exclusive_scan(ld ? 1 : 0, scratch, &cnt);
+        if (ld) loads[n_load + pos] = e;  // at most S members, so at most S loads
+        n_load += cnt;
+    }
+    int n_vict = 0;
+    for (int s0 = 0; s0 < S; s0 += MANAGE_THREADS) {
+        const int s = s0 + tid;
+        bool v = false;
+        if (s < S) {
+            const int o = s2e[s];
+            v = o < 0 || !in_new[o];
+        }
+        int cnt;
+        const int pos = moe::block_exclusive_scan(v ? 1 : 0, scratch, &cnt);
+        if (v) victim[n_vict + pos] = s;
+        n_vict += cnt;
+    }
+    __syncthreads();
+    for (int i = tid; i < n_load; i += MANAGE_THREADS) {  // n_load <= n_vict
+        const int e = loads[i], s = victim[i];
+        const int old = s2e[s];
+        if (old >= 0) me2s[old] = -1;  // old experts are distinct and leave the set
+        me2s[e] = s;
+        s2e[s] = e;
+        last[s] = now;
+        freq[s] = 0;
+        miss[2 * i] = e;
+        miss[2 * i + 1] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += MANAGE_THREADS) e2s[e] = me2s[e];
+    if (tid == 0) *n_miss = n_load;
+}
+
 // Copy slabs host -> slot.  The flattened (miss, 16-byte granule) space is
 // walked grid-stride; each thread keeps UNROLL loads in flight so the host
 // link sees many outstanding reads.
@@ -269,6 +335,16 @@ int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int 
     hipLaunchKernelGGL(k_manage, dim3(1), dim3(MANAGE_THREADS), 0, stream, st->e2s, st->s2e, st->last, st->freq,
                        st->step, st->E, st->S, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_host, stats);
     return moe_check_launch("cache_manage");
+}
+
+int cache_repick(const moe_cache_state* st, const int32_t* want, int32_t* miss, int32_t* n_miss, hipStream_t stream) {
+    int rc = check_state(st, "cache_repick");
+    if (rc) return rc;
+    MOE_REQUIRE(want && miss && n_miss, MOE_E_ARG, "cache_repick: want, miss and n_miss must be non-NULL");
+    if (st->S == 0) return moe_ok();
+    hipLaunchKernelGGL(k_repick, dim3(1), dim3(MANAGE_THREADS), 0, stream, st->e2s, st->s2e, st->last, st->freq,
+                       st->step, st->E, st->S, want, miss, n_miss);
+    return moe_check_launch("cache_repick");
 }
 
 int cache_gather(const int32_t* miss, const int32_t* n_miss, int max_miss, const void* host_store, void* slot_store,

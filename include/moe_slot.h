@@ -235,6 +235,21 @@ int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int 
                  int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host, int32_t* stats,
                  hipStream_t stream);
 
+/* Periodic repick of the resident set, [RTX] "Full Transcript" (every ~500
+ * tokens have another look, swap out whatever has gone cold, then leave the
+ * set alone; a static set between repicks).
+ *   want    device int32[S]: the new set (e.g. cache_pick_static over the
+ *           last window's picks); a repeated or out-of-range entry is skipped
+ *   miss    device int32[2*S] out: (expert, slot) loads for cache_gather
+ *   n_miss  device int32 out: number of loads
+ * Members of the new set already resident keep their slots; the others are
+ * loaded, in ascending expert id, into the slots whose expert is not in the
+ * new set (empty slots included), in ascending slot order; a slot no load
+ * needs keeps its expert.  A loaded slot restarts with last = step, freq = 0;
+ * step does not advance.  Follow with cache_gather(miss, n_miss, S, ...).
+ * Errors: ARG, SHAPE (as cache_manage). */
+int cache_repick(const moe_cache_state* st, const int32_t* want, int32_t* miss, int32_t* n_miss, hipStream_t stream);
+
 /* Copy each missing expert's slab from pinned host memory into its slot,
  * [VEC] "What this package does" / "The port": the device itself reads the
  * host memory, in 16-byte units.  Launch it on a side stream and order the

@@ -232,6 +232,70 @@ class GpuCache:
                     host_miss=host(self.host_miss)[:nh], stats=host(self.stats))
 
 
+def phase_trace(base, n_tok, E, k, phase_len, s=0.8):
+    """Routing ids whose popular handful changes: Zipf(s) over a permutation
+    drawn anew for every phase of phase_len tokens."""
+    out = []
+    for ph in range((n_tok + phase_len - 1) // phase_len):
+        n = min(phase_len, n_tok - ph * phase_len)
+        out.append(synth.zipf_ids(synth.key(base, synth.TAG_ZIPF_PERM, 0, ph), synth.key(base, synth.TAG_ZIPF_DRAW, 0, ph),
+                                  n, E, k, s))
+    return np.concatenate(out)
+
+
+@pytest.mark.parametrize("policy", ["static", "lru", "lfu", "repick"])
+def test_policy_replay_matches_oracle(m, policy):
+    """Replay of a routing trace one token per step: static set from the
+    first window, LRU, LFU, and a static set repicked every `every` tokens
+    from the last window's picks (cache_pick_static -> cache_repick ->
+    cache_gather); stats, loads, state and slot contents equal the oracle's."""
+    E, S, k, n_tok, every = 64, 16, 4, 600, 100
+    trace = phase_trace(0xE55100AA, n_tok, E, k, 128)
+    slab = 64
+    store_h = np.arange(E * slab, dtype=np.uint32).astype(np.uint8).reshape(E, slab)
+    store = torch.from_numpy(store_h.copy()).pin_memory()
+    slots = torch.zeros((S, slab), dtype=torch.uint8, device="cuda")
+    first = oracle.pick_static(trace[:every], E, S)
+    pol = "static" if policy == "repick" else policy
+    res = first if pol == "static" else None
+    g = GpuCache(m, E, S, res)
+    o = oracle.Cache(E, S, pol, res)
+    if res is not None:
+        slots.copy_(torch.from_numpy(store_h[first]).cuda())
+    want = torch.empty(S, dtype=torch.int32, device="cuda")
+    acc_g = np.zeros(4, np.int64)
+    acc_o = np.zeros(4, np.int64)
+    loads_g = loads_o = 0
+    for t in range(n_tok):
+        if policy == "repick" and t > 0 and t % every == 0:
+            win = trace[t - every:t]
+            m.cache_pick_static(dev(win.reshape(-1)), every * k, E, S, want)
+            np.testing.assert_array_equal(host(want), oracle.pick_static(win, E, S))
+            m.cache_repick(g.st, want, g.miss, g.n_miss)
+            m.cache_gather(g.miss, g.n_miss, S, store, slots, slab)
+            ld = o.repick(oracle.pick_static(win, E, S))
+            nm = int(host(g.n_miss)[0])
+            np.testing.assert_array_equal(host(g.miss)[:2 * nm].reshape(-1, 2), ld)
+            loads_g += nm
+            loads_o += len(ld)
+        rg = g.manage(pol, trace[t])
+        ro = o.manage(trace[t])
+        if pol != "static":
+            m.cache_gather(g.miss, g.n_miss, S, store, slots, slab)
+        acc_g += rg["stats"]
+        acc_o += ro["stats"]
+    compare_state(g, o)
+    np.testing.assert_array_equal(acc_g, acc_o)
+    assert loads_g == loads_o
+    # every occupied slot holds its expert's bytes
+    s2e = host(g.s2e)[:S]
+    for s_, e in enumerate(s2e):
+        if e >= 0:
+            np.testing.assert_array_equal(host(slots[s_]), store_h[e])
+    if policy == "repick":
+        assert loads_g > 0
+
+
 def compare_state(g, o):
     np.testing.assert_array_equal(host(g.e2s), o.e2s)
     if o.S:
