@@ -41,7 +41,6 @@ using v4u = uint32_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_THREADS = 256;
 constexpr int PF_MT = 128;         // token rows per prefill-shaped tile
-constexpr int PF_NT = 128;         // weight rows per tile
 constexpr int PF_KT = 64;          // k per step (128 bytes of bf16 per row)
 constexpr int PF_ROWB = PF_KT * 2; // bytes of one row of a k-step
 constexpr int PF_TILE_BYTES = PF_MT * PF_ROWB;  // 16 KiB: the A tile of one k-step
@@ -51,6 +50,8 @@ constexpr int PF_XCD = 8;
 constexpr int PF_BIG_P = 4096;  // picks from which prefill-shaped tiles are used
 constexpr int DEC_MT = 32;      // token rows of a decode-shaped tile
 constexpr int DEC_NW = 4;       // waves of a decode-shaped workgroup (32 weight rows each)
+constexpr int DEC_NR_GU = 2;    // register sets of k-steps in flight per thread: gate/up
+constexpr int DEC_NR_DN = 2;    // and down
 
 enum { PF_GU = 0, PF_DOWN = 1 };
 
@@ -58,6 +59,14 @@ enum { PF_GU = 0, PF_DOWN = 1 };
 // 8 consecutive rows, and 16 consecutive rows taken with their parity, all
 // land on distinct chunks.
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// First k-step of this workgroup's walk over the contraction.  Weight rows
+// of 4 KiB (and other sizes whose steps line up across rows) read 128 B at a
+// time by workgroups in lockstep put every concurrent access at the same
+// offset within its row, which crowds a few HBM channels (a read probe:
+// 5.3 TB/s for 4 KiB rows, 6.5 TB/s once each workgroup starts elsewhere).
+// The sum over k is then taken in a rotated order, fixed per workgroup.
+__device__ __forceinline__ int k_rot(int nk) { return (int)(blockIdx.x % (unsigned)nk); }
 
 using PfTile = moe_pf_tile;
 
@@ -150,8 +159,11 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
 
     const int nk = g.K / PF_KT;
     v4u ra[2][4], rb[2][NB];
+    // each workgroup walks k from its own starting step (see k_rot)
+    const int rot = k_rot(nk);
     auto fetch = [&](v4u (&a)[4], v4u (&w)[NB], int kt) {
-        const size_t ko = (size_t)kt * PF_ROWB;
+        const int kr = kt + rot;
+        const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
             a[q] = ld16(arow[q] + ko);
@@ -245,7 +257,7 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
 // 16 (gate) and c + 16 (up) of one wave pair up through one lane exchange.
 // The k-loop is the grouped GEMM's: two register sets ahead of two LDS
 // buffers, XOR-swizzled 16-byte chunks.
-template <int MODE, int NW>
+template <int MODE, int NW, int NR>
 __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     constexpr int NTH = 64 * NW;
     constexpr int WR = 32 * NW;                  // weight rows per tile
@@ -307,9 +319,11 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
 
     const int nk = g.K / PF_KT;
-    v4u ra[2][NA], rb[2][NBU];
+    v4u ra[NR][NA], rb[NR][NBU];
+    const int rot = k_rot(nk);  // each workgroup walks k from its own starting step
     auto fetch = [&](v4u (&a)[NA], v4u (&w)[NBU], int kt) {
-        const size_t ko = (size_t)kt * PF_ROWB;
+        const int kr = kt + rot;
+        const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
 #pragma unroll
         for (int q = 0; q < NA; ++q) a[q] = ld16(arow[q] + ko);
 #pragma unroll
@@ -333,24 +347,30 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
         }
     };
-    fetch(ra[0], rb[0], 0);
-    fetch(ra[1], rb[1], 1);
+    // NR register sets in a ring ahead of the two LDS buffers: step t is
+    // fetched into set t % NR, stashed into buffer t % 2 one step before it
+    // is computed.  The main loop runs U = lcm(2, NR) steps per pass with no
+    // branch (fetches past the end re-read the last step and are never used),
+    // so every wait on outstanding loads is exact; the tail is guarded.
+    constexpr int U = NR % 2 == 0 ? NR : 2 * NR;
+#pragma unroll
+    for (int r = 0; r < NR; ++r) fetch(ra[r], rb[r], min(r, nk - 1));
     stash(ra[0], rb[0], 0);
     __syncthreads();
-    for (int kt = 0; kt + 2 < nk; kt += 2) {
-        fetch(ra[0], rb[0], kt + 2);
-        compute(0);
-        stash(ra[1], rb[1], 1);
+    auto step = [&](int j, int t) {  // j = t % U, static in every caller
+        fetch(ra[j % NR], rb[j % NR], min(t + NR, nk - 1));  // set j % NR went to LDS last step
+        compute(j % 2);
+        stash(ra[(j + 1) % NR], rb[(j + 1) % NR], (j + 1) % 2);
         __syncthreads();
-        fetch(ra[1], rb[1], kt + 3);
-        compute(1);
-        stash(ra[0], rb[0], 0);
-        __syncthreads();
+    };
+    int kt = 0;
+    for (; kt + U <= nk; kt += U) {
+#pragma unroll
+        for (int j = 0; j < U; ++j) step(j, kt + j);
     }
-    compute(0);
-    stash(ra[1], rb[1], 1);
-    __syncthreads();
-    compute(1);
+#pragma unroll
+    for (int j = 0; j < U; ++j)
+        if (kt + j < nk) step(j, kt + j);
 
     // accumulator element x of lane l: column l % 32 of this wave's block, row (x/4)*8 + (l/32)*4 + x%4
     const int col = lane & 31;
@@ -386,14 +406,14 @@ int dec_launch(const void* x, const float* w, int k, const void* slot_store, siz
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
     PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
               reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / (16 * NW)};
-    hipLaunchKernelGGL((k_dec_gemm<PF_GU, NW>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)), dim3(64 * NW),
-                       lds, st, gu);
+    hipLaunchKernelGGL((k_dec_gemm<PF_GU, NW, DEC_NR_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
+                       dim3(64 * NW), lds, st, gu);
     int rc;
     if ((rc = moe_check_launch("moe_ffn_slots/decode_gate_up"))) return rc;
     PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
               reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k,
               H / (32 * NW)};
-    hipLaunchKernelGGL((k_dec_gemm<PF_DOWN, NW>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+    hipLaunchKernelGGL((k_dec_gemm<PF_DOWN, NW, DEC_NR_DN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
                        dim3(64 * NW), lds, st, dn);
     return moe_check_launch("moe_ffn_slots/decode_down");
 }
