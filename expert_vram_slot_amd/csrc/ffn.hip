@@ -246,6 +246,44 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
     int nbits = 0;
     while ((1 << nbits) < S) ++nbits;
 
+    if (P <= GROUP_THREADS) {
+        // one chunk (every decode batch up to 1024 picks): counts, offsets
+        // and places from one read of the slot ids
+        for (int i = tid; i < (GROUP_THREADS / 64) * S; i += GROUP_THREADS) wtab[i / S][i % S] = 0;
+        __syncthreads();
+        const int p = tid;
+        int s = p < P ? slot_ids[p] : -1;
+        if (s >= S) s = -1;
+        const bool valid = s >= 0;
+        int cnt;
+        const int rank = wave_slot_rank(s, valid, nbits, &cnt);
+        if (valid && rank == 0) wtab[wid][s] = (uint16_t)cnt;
+        __syncthreads();
+        int tot_s = 0;
+        if (tid < S) {
+            for (int w = 0; w < GROUP_THREADS / 64; ++w) {
+                const int c = wtab[w][tid];
+                wtab[w][tid] = (uint16_t)tot_s;
+                tot_s += c;
+            }
+        }
+        int tot;
+        const int off = moe::block_exclusive_scan(tot_s, scratch, &tot);
+        if (tid < S) {
+            slot_off[tid] = off;
+            base[tid] = off;
+        }
+        if (tid == 0) slot_off[S] = tot;
+        const int flag = (tid < S && tot_s > 0) ? 1 : 0;
+        int na;
+        const int apos = moe::block_exclusive_scan(flag, scratch, &na);
+        if (flag) active[apos] = tid;
+        if (tid == 0) *n_active = na;
+        write_pf_tiles(tot_s, off, S, pf_mt, scratch, pf_tiles, pf_n_tiles);
+        __syncthreads();
+        if (valid) pair_list[base[s] + wtab[wid][s] + rank] = p;
+        return;
+    }
     for (int s = tid; s < S; s += GROUP_THREADS) base[s] = 0;
     __syncthreads();
     for (int pass = 0; pass < 2; ++pass) {
@@ -769,6 +807,9 @@ __global__ void __launch_bounds__(256) k_block_sums(const uint16_t* __restrict__
 }
 
 // y[t][m] = sum_j part[t*k+j][m] over resident picks, j ascending; +0.0 if none.
+// The picks' rows are loaded eight at a time before any is added (a row of a
+// non-resident pick is read from an in-bounds row and not added), so a
+// thread waits on one round of loads per eight picks, not on every pick.
 __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ part, const int32_t* __restrict__ slot_ids,
                                                 int T, int k, int S, int H, float* __restrict__ y) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
@@ -776,14 +817,26 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ part, 
     if (i >= (int64_t)T * h4) return;
     const int t = (int)(i / h4), m4 = (int)(i % h4);
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-        const int sl = slot_ids[t * k + j];
-        if (sl < 0 || sl >= S) continue;
-        const float4 v = reinterpret_cast<const float4*>(part + (int64_t)(t * k + j) * H)[m4];
-        acc.x += v.x;
-        acc.y += v.y;
-        acc.z += v.z;
-        acc.w += v.w;
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        float4 v[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            const int sl = j < k ? slot_ids[t * k + j] : -1;
+            ok[u] = sl >= 0 && sl < S;
+            const int64_t row = ok[u] ? (int64_t)(t * k + j) : (int64_t)t * k;
+            v[u] = reinterpret_cast<const float4*>(part + row * H)[m4];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (ok[u]) {
+                acc.x += v[u].x;
+                acc.y += v[u].y;
+                acc.z += v[u].z;
+                acc.w += v[u].w;
+            }
+        }
     }
     reinterpret_cast<float4*>(y + (int64_t)t * H)[m4] = acc;
 }
