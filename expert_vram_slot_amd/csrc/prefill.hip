@@ -66,7 +66,11 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // offset within its row, which crowds a few HBM channels (a read probe:
 // 5.3 TB/s for 4 KiB rows, 6.5 TB/s once each workgroup starts elsewhere).
 // The sum over k is then taken in a rotated order, fixed per workgroup.
-__device__ __forceinline__ int k_rot(int nk) { return (int)(blockIdx.x % (unsigned)nk); }
+// Rows whose length is not a multiple of 4 KiB spread by themselves (and the
+// down GEMM of the decode layer ran slower rotated), so they start at 0.
+__device__ __forceinline__ int k_rot(int nk) {
+    return (nk * PF_ROWB) % 4096 == 0 ? (int)(blockIdx.x % (unsigned)nk) : 0;
+}
 
 using PfTile = moe_pf_tile;
 
