@@ -71,6 +71,8 @@ def lib():
             "cache_manage": (i32, [ctypes.POINTER(CacheState), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp]),
             "cache_gather": (i32, [vp, vp, i32, vp, vp, sz, vp]),
             "cache_repick": (i32, [ctypes.POINTER(CacheState), vp, vp, vp, vp]),
+            "cache_manage_gather": (i32, [ctypes.POINTER(CacheState), i32, vp, i32, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                          sz, vp, i32, vp, vp, vp, vp, vp]),
             "moe_ffn_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
             "moe_ffn_slots": (i32, [vp, i32, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, vp, sz, vp]),
             "moe_ffn_host_misses": (i32, [vp, i32, vp, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, i32]),
@@ -170,6 +172,22 @@ def cache_manage(st, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_ho
     return _check("cache_manage", lib().cache_manage(ctypes.byref(st), policy, _p(ids), n_ids, _p(slot_ids), _p(miss),
                                                      _p(n_miss), _p(host_miss), _p(n_host), _p(stats),
                                                      _stream(stream)))
+
+
+class Doorbell(ctypes.Structure):
+    """moe_doorbell: written by cache_manage_gather into pinned host memory, seq last."""
+    _fields_ = [("seq", ctypes.c_int32), ("n_miss", ctypes.c_int32), ("n_host", ctypes.c_int32),
+                ("stats", ctypes.c_int32 * 4), ("err", ctypes.c_int32)]
+
+
+def cache_manage_gather(st, policy, ids, n_ids, w, slot_ids, miss, n_miss, host_miss, n_host, stats, host_store,
+                        slot_store, slab_bytes, sync, seq, bell=None, bell_ids=None, bell_slots=None, bell_w=None,
+                        stream=None):
+    return _check("cache_manage_gather",
+                  lib().cache_manage_gather(ctypes.byref(st), policy, _p(ids), n_ids, _p(w), _p(slot_ids), _p(miss),
+                                            _p(n_miss), _p(host_miss), _p(n_host), _p(stats), _p(host_store),
+                                            _p(slot_store), slab_bytes, _p(sync), seq, _p(bell), _p(bell_ids),
+                                            _p(bell_slots), _p(bell_w), _stream(stream)))
 
 
 def cache_repick(st, want, miss, n_miss, stream=None):

@@ -72,14 +72,13 @@ __device__ __forceinline__ bool victim_before(int policy, bool occ_a, uint32_t f
 }
 
 // One cache step in one workgroup of 1024 threads.
-__global__ void __launch_bounds__(MANAGE_THREADS) k_manage(int32_t* __restrict__ e2s, int32_t* __restrict__ s2e,
-                                                           uint32_t* __restrict__ last, uint32_t* __restrict__ freq,
-                                                           uint32_t* __restrict__ stepp, int E, int S, int policy,
-                                                           const int32_t* __restrict__ ids, int n_ids,
-                                                           int32_t* __restrict__ slot_ids, int32_t* __restrict__ miss,
-                                                           int32_t* __restrict__ n_miss,
-                                                           int32_t* __restrict__ host_miss,
-                                                           int32_t* __restrict__ n_host, int32_t* __restrict__ stats) {
+__device__ __forceinline__ void manage_core(int32_t* __restrict__ e2s, int32_t* __restrict__ s2e,
+                                            uint32_t* __restrict__ last, uint32_t* __restrict__ freq,
+                                            uint32_t* __restrict__ stepp, int E, int S, int policy,
+                                            const int32_t* __restrict__ ids, int n_ids,
+                                            int32_t* __restrict__ slot_ids, int32_t* __restrict__ miss,
+                                            int32_t* __restrict__ n_miss, int32_t* __restrict__ host_miss,
+                                            int32_t* __restrict__ n_host, int32_t* __restrict__ stats) {
     __shared__ int32_t me2s[MOE_MAX_E];
     __shared__ unsigned char need[MOE_MAX_E];
     __shared__ int32_t misses[MOE_MAX_E];
@@ -191,6 +190,18 @@ __global__ void __launch_bounds__(MANAGE_THREADS) k_manage(int32_t* __restrict__
     }
 }
 
+__global__ void __launch_bounds__(MANAGE_THREADS) k_manage(int32_t* __restrict__ e2s, int32_t* __restrict__ s2e,
+                                                           uint32_t* __restrict__ last, uint32_t* __restrict__ freq,
+                                                           uint32_t* __restrict__ stepp, int E, int S, int policy,
+                                                           const int32_t* __restrict__ ids, int n_ids,
+                                                           int32_t* __restrict__ slot_ids, int32_t* __restrict__ miss,
+                                                           int32_t* __restrict__ n_miss,
+                                                           int32_t* __restrict__ host_miss,
+                                                           int32_t* __restrict__ n_host, int32_t* __restrict__ stats) {
+    manage_core(e2s, s2e, last, freq, stepp, E, S, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_host,
+                stats);
+}
+
 // Periodic repick in one workgroup: the new set is the distinct valid
 // experts of want[0..S); its members already resident keep their slots, the
 // others take, in ascending expert id, the slots whose expert is not in the
@@ -292,6 +303,93 @@ __global__ void __launch_bounds__(GATHER_THREADS) k_gather(const int32_t* __rest
     }
 }
 
+// The copy loop of the gather over workgroups wg of nwg (blockDim threads each).
+__device__ __forceinline__ void gather_core(const int32_t* __restrict__ miss, int nm,
+                                            const unsigned char* __restrict__ host, unsigned char* __restrict__ slots,
+                                            uint64_t slab_bytes, int wg, int nwg) {
+    const uint64_t per = slab_bytes / 16;
+    const uint64_t total = (uint64_t)nm * per;
+    const uint64_t nth = blockDim.x;
+    const uint64_t stride = (uint64_t)nwg * nth * GATHER_UNROLL;
+    for (uint64_t base = (uint64_t)wg * nth * GATHER_UNROLL + threadIdx.x; base < total; base += stride) {
+        v4u v[GATHER_UNROLL];
+        uint64_t dst[GATHER_UNROLL];
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u) {
+            const uint64_t c = base + (uint64_t)u * nth;
+            dst[u] = ~0ull;
+            if (c < total) {
+                const uint64_t m = c / per, g = c - m * per;
+                const uint64_t e = (uint64_t)miss[2 * m], s = (uint64_t)miss[2 * m + 1];
+                v[u] = __builtin_nontemporal_load(reinterpret_cast<const v4u*>(host + e * slab_bytes) + g);
+                dst[u] = s * slab_bytes + g * 16;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < GATHER_UNROLL; ++u)
+            if (dst[u] != ~0ull) *reinterpret_cast<v4u*>(slots + dst[u]) = v[u];
+    }
+}
+
+constexpr uint32_t FUSED_SPIN_MAX = 1u << 22;  // polls of the hand-off word before a copying workgroup gives up
+
+// Fused cache step.  Workgroup 0 runs the cache step; its first wave then
+// mirrors the picks to pinned host memory and rings the doorbell (system-scope
+// release), and thread 0 releases the hand-off word (device scope).  The
+// other workgroups wait for the hand-off (a bounded number of polls) and all
+// of them copy the missing slabs.
+__global__ void __launch_bounds__(MANAGE_THREADS) k_manage_gather(
+    int32_t* __restrict__ e2s, int32_t* __restrict__ s2e, uint32_t* __restrict__ last, uint32_t* __restrict__ freq,
+    uint32_t* __restrict__ stepp, int E, int S, int policy, const int32_t* __restrict__ ids, int n_ids,
+    const float* __restrict__ w, int32_t* __restrict__ slot_ids, int32_t* __restrict__ miss,
+    int32_t* __restrict__ n_miss, int32_t* __restrict__ host_miss, int32_t* __restrict__ n_host,
+    int32_t* __restrict__ stats, const unsigned char* __restrict__ host, unsigned char* __restrict__ slots,
+    uint64_t slab_bytes, int32_t* __restrict__ sync, int32_t seq, moe_doorbell* __restrict__ bell,
+    int32_t* __restrict__ bell_ids, int32_t* __restrict__ bell_slots, float* __restrict__ bell_w) {
+    __shared__ int ok;
+    const int tid = threadIdx.x;
+    if (blockIdx.x == 0) {
+        manage_core(e2s, s2e, last, freq, stepp, E, S, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_host,
+                    stats);
+        __threadfence();  // every wave's results in device memory before the hand-off below
+        __syncthreads();
+        if (tid < 64) {  // the first wave: mirror, then the doorbell
+            if (bell_ids)
+                for (int i = tid; i < n_ids; i += 64) bell_ids[i] = ids[i];
+            if (bell_slots)
+                for (int i = tid; i < n_ids; i += 64) bell_slots[i] = slot_ids[i];
+            if (bell_w && w)
+                for (int i = tid; i < n_ids; i += 64) bell_w[i] = w[i];
+            if (bell) {
+                if (tid == 0) {
+                    bell->n_miss = *n_miss;
+                    bell->n_host = *n_host;
+                    for (int q = 0; q < 4; ++q) bell->stats[q] = stats ? stats[q] : 0;
+                    bell->err = 0;
+                }
+                __threadfence_system();  // every lane's mirror stores before the doorbell
+                if (tid == 0) __hip_atomic_store(&bell->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+            }
+        }
+        if (tid == 0) __hip_atomic_store(&sync[0], seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 1;
+    } else if (tid == 0) {
+        int v = 0;
+        uint32_t n = 0;
+        for (; n < FUSED_SPIN_MAX; ++n) {
+            v = __hip_atomic_load(&sync[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+            if (v == seq) break;
+            __builtin_amdgcn_s_sleep(2);
+        }
+        ok = v == seq;
+        if (!ok) atomicOr(&sync[1], 1);
+    }
+    __syncthreads();
+    if (!ok || policy == MOE_STATIC) return;
+    const int nm = min(max(__hip_atomic_load(n_miss, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT), 0), S);
+    gather_core(miss, nm, host, slots, slab_bytes, blockIdx.x, gridDim.x);
+}
+
 int check_state(const moe_cache_state* st, const char* who) {
     MOE_REQUIRE(st && st->e2s && st->s2e && st->last && st->freq && st->step, MOE_E_ARG,
                 "%s: cache state and its arrays must be non-NULL", who);
@@ -335,6 +433,61 @@ int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int 
     hipLaunchKernelGGL(k_manage, dim3(1), dim3(MANAGE_THREADS), 0, stream, st->e2s, st->s2e, st->last, st->freq,
                        st->step, st->E, st->S, policy, ids, n_ids, slot_ids, miss, n_miss, host_miss, n_host, stats);
     return moe_check_launch("cache_manage");
+}
+
+int cache_manage_gather(const moe_cache_state* st, int policy, const int32_t* ids, int n_ids, const float* w,
+                        int32_t* slot_ids, int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host,
+                        int32_t* stats, const void* host_store, void* slot_store, size_t slab_bytes, int32_t* sync,
+                        int32_t seq, moe_doorbell* bell, int32_t* bell_ids, int32_t* bell_slots, float* bell_w,
+                        hipStream_t stream) {
+    int rc = check_state(st, "cache_manage_gather");
+    if (rc) return rc;
+    MOE_REQUIRE(policy == MOE_STATIC || policy == MOE_LRU || policy == MOE_LFU, MOE_E_ARG,
+                "cache_manage_gather: unknown policy %d", policy);
+    MOE_REQUIRE(n_ids >= 0 && n_ids <= (1 << 24), MOE_E_SHAPE, "cache_manage_gather: n_ids=%d out of range", n_ids);
+    MOE_REQUIRE((ids && slot_ids) || n_ids == 0, MOE_E_ARG, "cache_manage_gather: ids and slot_ids must be non-NULL");
+    MOE_REQUIRE(miss && n_miss && host_miss && n_host && sync, MOE_E_ARG,
+                "cache_manage_gather: miss, n_miss, host_miss, n_host and sync must be non-NULL");
+    const unsigned char* dev_host = nullptr;
+    int nwg = 1;
+    if (policy != MOE_STATIC && st->S > 0) {
+        MOE_REQUIRE(host_store && slot_store, MOE_E_ARG, "cache_manage_gather: host_store and slot_store needed");
+        MOE_REQUIRE(slab_bytes > 0 && slab_bytes % 16 == 0 && moe_aligned16(host_store) && moe_aligned16(slot_store),
+                    MOE_E_ALIGN, "cache_manage_gather: slab_bytes=%zu and both stores must be 16-byte aligned",
+                    slab_bytes);
+        void* dev = nullptr;
+        hipError_t e = hipHostGetDevicePointer(&dev, const_cast<void*>(host_store), 0);
+        if (e != hipSuccess || !dev) {
+            (void)hipGetLastError();
+            return moe_fail(MOE_E_ARG, "cache_manage_gather: host_store is not pinned, device-visible host memory (%s)",
+                            hipGetErrorString(e));
+        }
+        dev_host = reinterpret_cast<const unsigned char*>(dev);
+        // copying workgroups: enough 16-byte loads in flight for the host link, and all co-resident
+        const uint64_t chunks = (uint64_t)st->S * (slab_bytes / 16);
+        const uint64_t want = (chunks + (uint64_t)MANAGE_THREADS * GATHER_UNROLL - 1) /
+                              ((uint64_t)MANAGE_THREADS * GATHER_UNROLL);
+        nwg = (int)(want < 1 ? 1 : want > 128 ? 128 : want);
+    }
+    // device addresses of the pinned doorbell and mirrors, looked up on every call
+    void* dptr[4] = {bell, bell_ids, bell_slots, bell_w};
+    for (void*& q : dptr) {
+        if (!q) continue;
+        void* d = nullptr;
+        hipError_t e = hipHostGetDevicePointer(&d, q, 0);
+        if (e != hipSuccess || !d) {
+            (void)hipGetLastError();
+            return moe_fail(MOE_E_ARG, "cache_manage_gather: doorbell and mirrors must be pinned host memory (%s)",
+                            hipGetErrorString(e));
+        }
+        q = d;
+    }
+    hipLaunchKernelGGL(k_manage_gather, dim3(nwg), dim3(MANAGE_THREADS), 0, stream, st->e2s, st->s2e, st->last,
+                       st->freq, st->step, st->E, st->S, policy, ids, n_ids, w, slot_ids, miss, n_miss, host_miss,
+                       n_host, stats, dev_host, reinterpret_cast<unsigned char*>(slot_store), (uint64_t)slab_bytes,
+                       sync, seq, reinterpret_cast<moe_doorbell*>(dptr[0]), reinterpret_cast<int32_t*>(dptr[1]),
+                       reinterpret_cast<int32_t*>(dptr[2]), reinterpret_cast<float*>(dptr[3]));
+    return moe_check_launch("cache_manage_gather");
 }
 
 int cache_repick(const moe_cache_state* st, const int32_t* want, int32_t* miss, int32_t* n_miss, hipStream_t stream) {

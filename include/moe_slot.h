@@ -15,12 +15,15 @@
  *                        resident; summed in with moe_combine
  *
  * Sources (web pages, by title and section):
+ *   [BEL] the Betelgeuse engine post: an in-stream kernel resolves expert hits
+ *         on the device and rings a mapped host doorbell only on a miss.
  *   [RTX] sozai.app transcript "rtx-3060-run-35b-llamacpp" -- "What the video
  *         covers", "Full Transcript": a fixed slot set chosen at load, missing
  *         experts return zeros on the GPU, a CPU pass over the RAM experts, one
  *         add to join them.
  *   [VEC] "Porting vllm-expert-cache to NVIDIA GPUs" -- "What this package does"
- *         (expert_cache_manage, expert_cache_gather, remap to slot space),
+ *         (expert_cache_manage, expert_cache_gather, remap to slot space;
+ *         expert_cache_fused, named in "The port"),
  *         "The port" (16-byte copy unit, build-time export check, binding by
  *         exported name), "Prove it is correct before measuring" (determinism:
  *         no atomics, no order-dependent reduction; the device reads pinned host
@@ -234,6 +237,47 @@ int cache_pick_static(const int32_t* ids, int n_ids, int E, int S, int32_t* resi
 int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int n_ids, int32_t* slot_ids,
                  int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host, int32_t* stats,
                  hipStream_t stream);
+
+/* Doorbell of a fused cache step in pinned host memory ([BEL]: the in-stream
+ * resolve rings a mapped host doorbell, so the host learns of misses without
+ * a stream synchronisation).  seq is written last, with system-scope release
+ * ordering: a host thread that reads seq == the call's seq (acquire) may read
+ * the other fields and the picks mirrored beside it.  n_host == 0 means no
+ * pick of the step needs the host pass. */
+typedef struct {
+    int32_t seq;
+    int32_t n_miss;
+    int32_t n_host;
+    int32_t stats[4];
+    int32_t err;
+} moe_doorbell;
+
+/* cache_manage and cache_gather in one launch ([VEC] "The port":
+ * expert_cache_fused), with an optional doorbell ([BEL] in-stream doorbell).
+ * Arguments as cache_manage and cache_gather (host_store pinned; STATIC
+ * caches copy nothing), plus:
+ *   w           device float[n_ids] or NULL: routing weights to mirror
+ *   sync        device int32[2], zeroed once by the caller, owned by this
+ *               call sequence (not shared by calls that may overlap): the
+ *               in-kernel hand-off from the managing workgroup to the copying
+ *               ones; sync[1] != 0 afterwards means a copying workgroup gave
+ *               up waiting (the gather is then incomplete; with co-resident
+ *               workgroups this does not happen)
+ *   seq         a number new for every call on this sync word and doorbell
+ *   bell        pinned host moe_doorbell or NULL
+ *   bell_ids, bell_slots, bell_w
+ *               pinned host int32/int32/float[n_ids] or NULL: ids, slot_ids
+ *               and w mirrored to the host before the doorbell rings
+ * One workgroup runs the cache step, mirrors the picks, rings the doorbell
+ * and releases the others, which wait for it (bounded) and then copy the
+ * missing slabs together with it.  Results equal cache_manage followed by
+ * cache_gather.
+ * Errors: those of cache_manage and cache_gather; ARG (sync NULL). */
+int cache_manage_gather(const moe_cache_state* st, int policy, const int32_t* ids, int n_ids, const float* w,
+                        int32_t* slot_ids, int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host,
+                        int32_t* stats, const void* host_store, void* slot_store, size_t slab_bytes, int32_t* sync,
+                        int32_t seq, moe_doorbell* bell, int32_t* bell_ids, int32_t* bell_slots, float* bell_w,
+                        hipStream_t stream);
 
 /* Periodic repick of the resident set, [RTX] "Full Transcript" (every ~500
  * tokens have another look, swap out whatever has gone cold, then leave the

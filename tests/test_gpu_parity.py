@@ -296,6 +296,54 @@ def test_policy_replay_matches_oracle(m, policy):
         assert loads_g > 0
 
 
+@pytest.mark.parametrize("policy,E,S,T,k", [("lru", 64, 16, 4, 4), ("lfu", 64, 16, 4, 4), ("static", 64, 16, 4, 4),
+                                             ("lru", 128, 32, 16, 8)])
+def test_fused_manage_gather_and_doorbell(m, policy, E, S, T, k):
+    """cache_manage_gather: the same state, lists and slot bytes as the
+    oracle's manage + gather, step after step; the doorbell and the mirrored
+    picks in pinned host memory match once seq has been written."""
+    slab = 256
+    store_h = (np.arange(E * slab, dtype=np.int64) * 7 % 251).astype(np.uint8).reshape(E, slab)
+    store = torch.from_numpy(store_h.copy()).pin_memory()
+    slots = torch.zeros((S, slab), dtype=torch.uint8, device="cuda")
+    res = list(range(0, 2 * S, 2))[:S] if policy == "static" else None
+    g = GpuCache(m, E, S, res)
+    o = oracle.Cache(E, S, policy, res)
+    if res is not None:
+        slots.copy_(torch.from_numpy(store_h[res]).cuda())
+    sync = torch.zeros(2, dtype=torch.int32, device="cuda")
+    bell = torch.zeros(8, dtype=torch.int32).pin_memory()
+    P = T * k
+    b_ids = torch.full((P,), -5, dtype=torch.int32).pin_memory()
+    b_slots = torch.full((P,), -5, dtype=torch.int32).pin_memory()
+    b_w = torch.zeros(P, dtype=torch.float32).pin_memory()
+    trace = phase_trace(0xE55100BB, 12 * T, E, k, 3 * T).reshape(12, P)
+    for step in range(12):
+        ids = dev(trace[step])
+        w = dev(np.linspace(0.1, 1.0, P).astype(np.float32))
+        slot_ids = torch.full((P,), -9, dtype=torch.int32, device="cuda")
+        seq = 1000 + step
+        m.cache_manage_gather(g.st, oracle.POLICIES[policy], ids, P, w, slot_ids, g.miss, g.n_miss, g.host_miss,
+                              g.n_host, g.stats, store, slots, slab, sync, seq, bell, b_ids, b_slots, b_w)
+        torch.cuda.synchronize()
+        ro = o.manage(trace[step])
+        np.testing.assert_array_equal(host(slot_ids), ro["slot_ids"])
+        nm = int(host(g.n_miss)[0])
+        np.testing.assert_array_equal(host(g.miss)[:2 * nm].reshape(-1, 2), ro["miss"])
+        np.testing.assert_array_equal(host(g.stats), ro["stats"])
+        b = bell.numpy()
+        assert b[0] == seq and b[1] == nm and b[2] == len(ro["host_miss"]) and list(b[3:7]) == list(ro["stats"])
+        np.testing.assert_array_equal(b_ids.numpy(), trace[step])
+        np.testing.assert_array_equal(b_slots.numpy(), ro["slot_ids"])
+        np.testing.assert_array_equal(b_w.numpy(), host(w))
+        assert int(host(sync)[1]) == 0
+        compare_state(g, o)
+    s2e = host(g.s2e)[:S]
+    for s_, e in enumerate(s2e):
+        if e >= 0:
+            np.testing.assert_array_equal(host(slots[s_]), store_h[e])
+
+
 def compare_state(g, o):
     np.testing.assert_array_equal(host(g.e2s), o.e2s)
     if o.S:
