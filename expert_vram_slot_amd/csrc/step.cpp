@@ -8,13 +8,18 @@
 // vllm-expert-cache to NVIDIA GPUs", "What this package does": manage, gather
 // and remap come before the expert FFN, which runs in slot space.
 //
-//   compute  [x -> host]  moe_route -> cache_manage -> (wait gather) -> moe_ffn_slots
+//   compute  [x -> host]  moe_route -> cache_manage_gather -> moe_ffn_slots
+//                                       (the cache step, the gather and the doorbell in one launch; a static
+//                                        cache without a host pass runs plain cache_manage)
 //                                                       -> y_host -> moe_combine [-> moe_residual]
-//   side                            `-> cache_gather (dynamic caches only)
-//   copy     x -> host (pinned);      picks | slots | weights -> host (pinned)
-//   caller's CPU thread               moe_ffn_host_misses once the picks are on the host
+//   copy     x -> host (pinned)
+//   caller's CPU thread               waits for the doorbell (the picks mirrored to pinned memory behind it),
+//                                     then moe_ffn_host_misses, only when the step has host misses
 #include <hip/hip_runtime.h>
+#include <immintrin.h>
 #include <string.h>
+
+#include <chrono>
 
 #include <new>
 
@@ -33,15 +38,20 @@ struct moe_step {
     void* ffn_ws;
     float *y, *y_host_dev;
     void* xbuf[2];  // residual stream of a stack
+    int32_t* sync;  // [2] hand-off word of the fused cache step
     // pinned host
     void* h_x;
-    int32_t* h_meta;
+    int32_t* h_meta;  // [3][T_max * k] picks, slots, weights mirrored by the fused cache step
     float* h_y;
-    hipEvent_t ev_x, ev_manage, ev_gather, ev_copy;
+    moe_doorbell* bell;
+    int32_t seq;  // sequence number of the last fused cache step
+    hipEvent_t ev_x, ev_copy;
     int64_t stats_sum[4];  // cache counters summed over host-pass steps
 };
 
 namespace {
+
+constexpr int kBellTimeoutS = 10;  // seconds a layer step waits for its cache step's doorbell
 
 int hip_fail(const char* what, hipError_t e) {
     (void)hipGetLastError();
@@ -51,13 +61,13 @@ int hip_fail(const char* what, hipError_t e) {
 void release(moe_step* h) {
     if (!h) return;
     void* dev[] = {h->meta, h->logits, h->miss, h->n_miss, h->host_miss, h->n_host, h->ffn_ws,
-                   h->y, h->y_host_dev, h->xbuf[0], h->xbuf[1]};
+                   h->y, h->y_host_dev, h->xbuf[0], h->xbuf[1], h->sync};
     for (void* p : dev)
         if (p) (void)hipFree(p);
-    void* host[] = {h->h_x, h->h_meta, h->h_y};
+    void* host[] = {h->h_x, h->h_meta, h->h_y, h->bell};
     for (void* p : host)
         if (p) (void)hipHostFree(p);
-    hipEvent_t evs[] = {h->ev_x, h->ev_manage, h->ev_gather, h->ev_copy};
+    hipEvent_t evs[] = {h->ev_x, h->ev_copy};
     for (hipEvent_t e : evs)
         if (e) (void)hipEventDestroy(e);
     delete h;
@@ -105,7 +115,8 @@ moe_step* moe_step_create(int T_max, int E, int k, int H, int I, int S, int w_ty
                {(void**)&h->y, 4 * (size_t)T_max * H},
                {(void**)&h->y_host_dev, 4 * (size_t)T_max * H},
                {&h->xbuf[0], xb * T_max * H},
-               {&h->xbuf[1], xb * T_max * H}};
+               {&h->xbuf[1], xb * T_max * H},
+               {(void**)&h->sync, 16}};
     for (auto& d : dev) {
         hipError_t e = hipMalloc(d.p, d.n);
         if (e != hipSuccess) {
@@ -117,7 +128,10 @@ moe_step* moe_step_create(int T_max, int E, int k, int H, int I, int S, int w_ty
     struct {
         void** p;
         size_t n;
-    } host[] = {{&h->h_x, xb * T_max * H}, {(void**)&h->h_meta, 12 * P + 16}, {(void**)&h->h_y, 4 * (size_t)T_max * H}};
+    } host[] = {{&h->h_x, xb * T_max * H},
+                {(void**)&h->h_meta, 12 * P + 16},
+                {(void**)&h->h_y, 4 * (size_t)T_max * H},
+                {(void**)&h->bell, sizeof(moe_doorbell)}};
     for (auto& d : host) {
         hipError_t e = hipHostMalloc(d.p, d.n, hipHostMallocDefault);
         if (e != hipSuccess) {
@@ -126,7 +140,15 @@ moe_step* moe_step_create(int T_max, int E, int k, int H, int I, int S, int w_ty
             return nullptr;
         }
     }
-    hipEvent_t* evs[] = {&h->ev_x, &h->ev_manage, &h->ev_gather, &h->ev_copy};
+    hipError_t me = hipMemset(h->sync, 0, 16);
+    if (me != hipSuccess) {
+        hip_fail("moe_step_create: hipMemset", me);
+        release(h);
+        return nullptr;
+    }
+    memset(h->bell, 0, sizeof(moe_doorbell));
+    h->seq = 0;
+    hipEvent_t* evs[] = {&h->ev_x, &h->ev_copy};
     for (hipEvent_t* e : evs) {
         hipError_t r = hipEventCreateWithFlags(e, hipEventDisableTiming);
         if (r != hipSuccess) {
@@ -152,6 +174,7 @@ int moe_step_stats(moe_step* h, int64_t* out, int reset) {
 
 int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, const int32_t* ids_in, int host_pass,
                    int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy) {
+    (void)s_side;  // the gather runs inside the fused cache step on s0
     if (!h || !L || !x) return moe_fail(MOE_E_ARG, "moe_layer_step: NULL argument");
     if (T < 0 || T > h->T_max) return moe_fail(MOE_E_SHAPE, "moe_layer_step: T=%d outside [0, %d]", T, h->T_max);
     if (L->state.E != h->E || L->state.S != h->S || L->slab_bytes < h->slab_bytes)
@@ -171,6 +194,7 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
         if ((e = hipStreamWaitEvent(s_copy, h->ev_x, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
         if ((e = hipMemcpyAsync(h->h_x, x, xbytes, hipMemcpyDeviceToHost, s_copy)) != hipSuccess)
             return hip_fail("moe_layer_step: x to host", e);
+        if ((e = hipEventRecord(h->ev_copy, s_copy)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
     }
     if (ids_in) {
         if ((e = hipMemcpyAsync(ids, ids_in, (size_t)P * 4, hipMemcpyDeviceToDevice, s0)) != hipSuccess)
@@ -179,36 +203,45 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
     if ((rc = moe_route(x, h->x_dtype, L->G, L->bias, ids_in ? ids : nullptr, T, h->H, h->E, h->k, ids, w, h->logits,
                         s0)))
         return rc;
-    if ((rc = cache_manage(&L->state, L->policy, ids, P, slot_ids, h->miss, h->n_miss, h->host_miss, h->n_host,
-                           h->meta + 3 * Pm, s0)))
-        return rc;
-    if ((e = hipEventRecord(h->ev_manage, s0)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
-    if (host_pass) {  // picks, slots and weights to pinned memory in one copy, before the FFN is queued
-        if ((e = hipStreamWaitEvent(s_copy, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
-        if ((e = hipMemcpyAsync(h->h_meta, h->meta, (size_t)12 * Pm + 16, hipMemcpyDeviceToHost, s_copy)) != hipSuccess)
-            return hip_fail("moe_layer_step: picks to host", e);
-        if ((e = hipEventRecord(h->ev_copy, s_copy)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
-    }
-    if (L->policy != MOE_STATIC && h->S > 0) {
-        if ((e = hipStreamWaitEvent(s_side, h->ev_manage, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
-        if ((rc = cache_gather(h->miss, h->n_miss, h->S, L->host_store, L->slot_store, L->slab_bytes, s_side)))
+    const bool dynamic = L->policy != MOE_STATIC && h->S > 0;
+    int32_t seq = 0;
+    if (host_pass || dynamic) {
+        // one launch: the cache step, the gather of the misses, and (host pass) the picks
+        // mirrored to pinned memory behind a doorbell
+        seq = ++h->seq;
+        int32_t* m_ids = host_pass ? h->h_meta : nullptr;
+        int32_t* m_slots = host_pass ? h->h_meta + Pm : nullptr;
+        float* m_w = host_pass ? reinterpret_cast<float*>(h->h_meta + 2 * Pm) : nullptr;
+        if ((rc = cache_manage_gather(&L->state, L->policy, ids, P, w, slot_ids, h->miss, h->n_miss, h->host_miss,
+                                      h->n_host, h->meta + 3 * Pm, L->host_store, L->slot_store, L->slab_bytes,
+                                      h->sync, seq, host_pass ? h->bell : nullptr, m_ids, m_slots, m_w, s0)))
             return rc;
-        if ((e = hipEventRecord(h->ev_gather, s_side)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
-        if ((e = hipStreamWaitEvent(s0, h->ev_gather, 0)) != hipSuccess) return hip_fail("moe_layer_step: wait", e);
+    } else if ((rc = cache_manage(&L->state, L->policy, ids, P, slot_ids, h->miss, h->n_miss, h->host_miss,
+                                  h->n_host, h->meta + 3 * Pm, s0))) {
+        return rc;
     }
     if ((rc = moe_ffn_slots(x, h->x_dtype, slot_ids, w, T, h->k, L->slot_store, L->slab_bytes, h->S > 0 ? h->S : 1,
                             h->w_type, h->H, h->I, y, h->ffn_ws, h->ffn_ws_bytes, s0)))
         return rc;
     if (!host_pass) return moe_ok();
+    // the doorbell: the picks are on the host once it shows this step's seq
+    const auto t0 = std::chrono::steady_clock::now();
+    for (int n = 0; __atomic_load_n(&h->bell->seq, __ATOMIC_ACQUIRE) != seq; ++n) {
+        _mm_pause();
+        if ((n & 1023) == 1023 &&
+            std::chrono::steady_clock::now() - t0 > std::chrono::seconds(kBellTimeoutS)) {
+            hipError_t pe = hipStreamQuery(s0);
+            return moe_fail(MOE_E_HIP, "moe_layer_step: no doorbell from the cache step after %d s (stream: %s)",
+                            kBellTimeoutS, hipGetErrorString(pe));
+        }
+    }
+    for (int i = 0; i < 4; ++i) h->stats_sum[i] += h->bell->stats[i];
+    if (h->bell->n_host == 0) return moe_ok();  // every pick resident: nothing to add
     // the host pass on this thread, while the GPU runs the FFN
-    if ((e = hipEventSynchronize(h->ev_copy)) != hipSuccess) return hip_fail("moe_layer_step: wait for picks", e);
+    if ((e = hipEventSynchronize(h->ev_copy)) != hipSuccess) return hip_fail("moe_layer_step: wait for x", e);
     const int32_t* h_ids = h->h_meta;
     const int32_t* h_slot = h->h_meta + Pm;
     const float* h_w = reinterpret_cast<const float*>(h->h_meta + 2 * Pm);
-    for (int i = 0; i < 4; ++i) h->stats_sum[i] += h->h_meta[3 * Pm + i];
-    int misses = 0;
-    for (int p = 0; p < P; ++p) misses += h_slot[p] < 0;
-    if (misses == 0) return moe_ok();  // every pick resident: nothing to add
     if ((rc = moe_ffn_host_misses(h->h_x, h->x_dtype, h_ids, h_slot, h_w, T, h->k, L->host_store, L->slab_bytes, h->E,
                                   h->w_type, h->H, h->I, h->h_y, n_threads)))
         return rc;

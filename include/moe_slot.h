@@ -403,16 +403,20 @@ const float* moe_step_output(const moe_step* h);
 int moe_step_stats(moe_step* h, int64_t* out, int reset);
 
 /* One layer step for T tokens of x (device [T][H], activation format):
- * moe_route (ids_in: given device picks [T][k] or NULL) -> cache_manage ->
- * cache_gather on s_side (dynamic caches) -> moe_ffn_slots on s0, and with
- * host_pass != 0: x and the picks go to pinned memory on s_copy (the picks
- * right after cache_manage), this thread waits for them and runs
- * moe_ffn_host_misses on n_threads threads while the GPU runs the FFN, and
- * the result is added on s0 (moe_combine).  y_out: device float[T][H] out, or
+ * moe_route (ids_in: given device picks [T][k] or NULL) -> the cache step ->
+ * moe_ffn_slots on s0.  The cache step is cache_manage_gather (one launch:
+ * cache step, gather of the misses, and with host_pass != 0 the picks
+ * mirrored to pinned memory behind a doorbell); a static cache without a
+ * host pass runs plain cache_manage.  With host_pass != 0, x goes to pinned
+ * memory on s_copy while the router runs; this thread waits for the
+ * doorbell and, only when the step has host misses, runs
+ * moe_ffn_host_misses on n_threads threads while the GPU runs the FFN; the
+ * result is added on s0 (moe_combine).  y_out: device float[T][H] out, or
  * NULL for the driver's own buffer (moe_step_output); final in s0's order
- * when the call returns.  The three streams must be distinct streams of one
- * device.  Errors: those of the entry points it calls; SHAPE when the layer
- * does not match the step. */
+ * when the call returns.  s_side is not used (kept for callers that pass
+ * three streams); s0 and s_copy must be distinct streams of one device.
+ * Errors: those of the entry points it calls; SHAPE when the layer does not
+ * match the step; HIP when the doorbell stays silent for 10 s. */
 int moe_layer_step(moe_step* h, const moe_layer_desc* layer, const void* x, int T, const int32_t* ids_in,
                    int host_pass, int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side,
                    hipStream_t s_copy);
