@@ -54,7 +54,7 @@ MFMA_BF16_PEAK_TFS = 2500.0
 
 # kernels launched, in order, by one moe_ffn_slots call on the bf16 decode batch of 64 tokens (512 picks):
 # the pick sort, the MFMA gate/up and down grouped GEMMs on decode-shaped tiles, the reduction
-FFN_SEQ = ("k_group", "k_dec_gemm<0, 4>", "k_dec_gemm<1, 4>", "k_reduce")
+FFN_SEQ = ("k_group", "k_dec_gemm<0, 4, 2>", "k_dec_gemm<1, 4, 2>", "k_reduce")
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
                "expert_vram_slot_amd/csrc/prefill.hpp", "expert_vram_slot_amd/csrc/common.hpp")

@@ -354,27 +354,28 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     // NR register sets in a ring ahead of the two LDS buffers: step t is
     // fetched into set t % NR, stashed into buffer t % 2 one step before it
     // is computed.  The main loop runs U = lcm(2, NR) steps per pass with no
-    // branch (fetches past the end re-read the last step and are never used),
-    // so every wait on outstanding loads is exact; the tail is guarded.
+    // branch, so every wait on outstanding loads is exact; the last steps
+    // (whose fetches would run past the end) are a guarded tail.
     constexpr int U = NR % 2 == 0 ? NR : 2 * NR;
 #pragma unroll
-    for (int r = 0; r < NR; ++r) fetch(ra[r], rb[r], min(r, nk - 1));
+    for (int r = 0; r < NR; ++r)
+        if (r < nk) fetch(ra[r], rb[r], r);
     stash(ra[0], rb[0], 0);
     __syncthreads();
-    auto step = [&](int j, int t) {  // j = t % U, static in every caller
-        fetch(ra[j % NR], rb[j % NR], min(t + NR, nk - 1));  // set j % NR went to LDS last step
+    auto step = [&](int j, int t, bool tail) {  // j = t % U, static in every caller
+        if (!tail || t + NR < nk) fetch(ra[j % NR], rb[j % NR], t + NR);  // set j % NR went to LDS last step
         compute(j % 2);
-        stash(ra[(j + 1) % NR], rb[(j + 1) % NR], (j + 1) % 2);
+        if (!tail || t + 1 < nk) stash(ra[(j + 1) % NR], rb[(j + 1) % NR], (j + 1) % 2);
         __syncthreads();
     };
     int kt = 0;
-    for (; kt + U <= nk; kt += U) {
+    for (; kt + U + NR <= nk; kt += U) {  // every fetch of these steps is in range
 #pragma unroll
-        for (int j = 0; j < U; ++j) step(j, kt + j);
+        for (int j = 0; j < U; ++j) step(j, kt + j, false);
     }
 #pragma unroll
-    for (int j = 0; j < U; ++j)
-        if (kt + j < nk) step(j, kt + j);
+    for (int j = 0; j < U + NR; ++j)
+        if (kt + j < nk) step(j % U, kt + j, true);
 
     // accumulator element x of lane l: column l % 32 of this wave's block, row (x/4)*8 + (l/32)*4 + x%4
     const int col = lane & 31;
