@@ -871,11 +871,11 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt);
         if ((rc = moe_check_launch("moe_ffn_slots/group_hist"))) return rc;
         hipLaunchKernelGGL(k_group_place, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt, nch, slot_off,
-                           pair_list, active, n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k));
+                           pair_list, active, n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k, S, H, I));
         if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
     } else {
         hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
-                           n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k));
+                           n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k, S, H, I));
         if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
     }
 

@@ -48,6 +48,7 @@ constexpr int PF_TILE_BYTES = PF_MT * PF_ROWB;  // 16 KiB: the A tile of one k-s
 constexpr int pf_lds_bytes(int NB) { return 2 * (PF_TILE_BYTES + NB * 32 * PF_ROWB); }
 constexpr int PF_XCD = 8;
 constexpr int PF_BIG_P = 4096;  // picks from which prefill-shaped tiles are used
+constexpr int PB_BIG_ROWS = 384;  // mean picks per slot from which 256-row tiles are used
 constexpr int DEC_MT = 32;      // token rows of a decode-shaped tile
 constexpr int DEC_NW = 4;       // waves of a decode-shaped workgroup (32 weight rows each)
 constexpr int DEC_NR_GU = 2;    // register sets of k-steps in flight per thread: gate/up
@@ -403,6 +404,205 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     }
 }
 
+// Large token groups (hundreds of picks per slot): 256 token rows x 256
+// weight rows per workgroup of 8 waves, wave (wr, wc) computing token rows
+// [64 wr, 64 wr + 64) against weight rows [128 wc, 128 wc + 128): 2 x 4
+// blocks of v_mfma_f32_32x32x16_bf16, so each LDS operand read feeds two or
+// four MFMAs, and every weight row is read once per 256 tokens.  Gate/up:
+// the 128 weight rows of a wave are 64 gate rows and the up rows of the same
+// 64 h columns.  One register set of the next k-step is in flight while the
+// current one is multiplied; two LDS buffers of 64 KiB.
+constexpr int PB_THREADS = 512;
+constexpr int PB_MT = 256;                           // token rows per tile
+constexpr int PB_NT = 256;                           // weight rows per tile
+constexpr int PB_A_BYTES = PB_MT * PF_ROWB;           // 32 KiB
+constexpr int PB_B_BYTES = PB_NT * PF_ROWB;           // 32 KiB
+constexpr int PB_LDS = 2 * (PB_A_BYTES + PB_B_BYTES);  // 128 KiB
+
+template <int MODE>
+__global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
+    extern __shared__ __attribute__((aligned(16))) unsigned char pb_lds[];
+    // workgroup -> (tile, column tile): each XCD takes a contiguous run of the
+    // tiles (the tiles of one slot are adjacent in the list) and walks them
+    // with the column tile fastest, so the token tiles of a slot read each
+    // weight tile at about the same time from the XCD's L2, and the column
+    // tiles of a token tile share its activations there
+    const int b = blockIdx.x;
+    const int xcd = b % PF_XCD, i = b / PF_XCD;
+    const int nt = *g.n_tiles;
+    const int per_xcd = (nt + PF_XCD - 1) / PF_XCD;
+    const int local = i / g.ntiles_n;
+    const int e = xcd * per_xcd + local;
+    const int jn = i % g.ntiles_n;
+    if (local >= per_xcd || e >= nt) return;
+    const PfTile tl = g.tiles[e];
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int wr = wv >> 1, wc = wv & 1;
+    const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
+    const size_t row_bytes = (size_t)g.K * 2;
+
+    // this thread's 4 A and 4 B chunks of a k-step: row u / 8, chunk u % 8 for u = q * 512 + tid
+    const unsigned char* arow[4];
+    const unsigned char* brow[4];
+    int soff[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const int u = q * PB_THREADS + tid, r = u >> 3, ch = u & 7;
+        const int pos = tl.p0 + min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
+        int idx;
+        if constexpr (MODE == PF_GU) idx = g.pair_list[pos] / g.k;
+        else idx = pos;
+        arow[q] = g.act + (size_t)idx * row_bytes + ch * 16;
+        soff[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
+        int64_t plane;
+        int w_row;
+        if constexpr (MODE == PF_GU) {
+            const int half = r >> 7, rr = r & 127;
+            plane = rr < 64 ? g.w0 : g.w1;
+            w_row = jn * 128 + half * 64 + (rr & 63);
+        } else {
+            plane = g.w0;
+            w_row = jn * PB_NT + r;
+        }
+        brow[q] = slab + plane + (size_t)w_row * row_bytes + ch * 16;
+    }
+    const int khalf = lane >> 5;
+    int a_off[4][2], b_off[4][4];
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+        for (int mb = 0; mb < 2; ++mb) {
+            const int r = wr * 64 + mb * 32 + (lane & 31);
+            a_off[ks][mb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
+        }
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb) {
+            const int r = wc * 128 + nb * 32 + (lane & 31);
+            b_off[ks][nb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
+        }
+    }
+    const bool active_wave = wr * 64 < tl.rows;
+    f32x16 acc[2][4];
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[mb][nb][x] = 0.0f;
+
+    const int nk = g.K / PF_KT;
+    const int rot = k_rot(nk);
+    v4u ra[4], rb[4];
+    auto fetch = [&](int kt) {
+        const int kr = kt + rot;
+        const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            ra[q] = ld16(arow[q] + ko);
+            rb[q] = ld16_nt(brow[q] + ko);
+        }
+    };
+    auto stash = [&](int buf) {
+        unsigned char* A = pb_lds + buf * (PB_A_BYTES + PB_B_BYTES);
+        unsigned char* B = A + PB_A_BYTES;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            *reinterpret_cast<v4u*>(A + soff[q]) = ra[q];
+            *reinterpret_cast<v4u*>(B + soff[q]) = rb[q];
+        }
+    };
+    auto compute = [&](int buf) {
+        if (!active_wave) return;
+        const unsigned char* A = pb_lds + buf * (PB_A_BYTES + PB_B_BYTES);
+        const unsigned char* B = A + PB_A_BYTES;
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks) {
+            bf16x8 av[2], bv[4];
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                av[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(A + a_off[ks][mb]));
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                bv[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(B + b_off[ks][nb]));
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb)
+                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+        }
+    };
+    // step t: the loads of t + 1 are in flight while t is multiplied out of buffer t % 2
+    fetch(0);
+    stash(0);
+    __syncthreads();
+    for (int kt = 0; kt + 2 <= nk; kt += 2) {  // nk is even
+        if (kt + 1 < nk) fetch(kt + 1);
+        compute(0);
+        stash(1);
+        __syncthreads();
+        if (kt + 2 < nk) fetch(kt + 2);
+        compute(1);
+        if (kt + 2 < nk) stash(0);
+        __syncthreads();
+    }
+
+    if (!active_wave) return;
+    const int col = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int r = wr * 64 + mb * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
+            if (r >= tl.rows) continue;
+            if constexpr (MODE == PF_GU) {
+                uint16_t* h = reinterpret_cast<uint16_t*>(g.out);
+                const size_t hrow = (size_t)(tl.p0 + r) * g.N + jn * 128 + wc * 64;
+#pragma unroll
+                for (int half = 0; half < 2; ++half) {
+                    const float gv = acc[mb][half][x], uv = acc[mb][2 + half][x];
+                    h[hrow + half * 32 + col] = moe::f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+                }
+            } else {
+                float* part = reinterpret_cast<float*>(g.out);
+                const int pk = g.pair_list[tl.p0 + r];
+                const float wt = g.wts[pk];
+                float* prow = part + (size_t)pk * g.N + jn * PB_NT + wc * 128;
+#pragma unroll
+                for (int nb = 0; nb < 4; ++nb) prow[nb * 32 + col] = wt * acc[mb][nb][x];
+            }
+        }
+    }
+}
+
+int pb_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
+              const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
+              int max_tiles, void* hbuf, float* part, hipStream_t st) {
+    static bool lds_set = false;
+    if (!lds_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_big<PF_GU>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, PB_LDS) != hipSuccess ||
+            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_big<PF_DOWN>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, PB_LDS) != hipSuccess) {
+            (void)hipGetLastError();
+            return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the large-group kernels",
+                            PB_LDS);
+        }
+        lds_set = true;
+    }
+    const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
+    PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
+              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / 128};
+    hipLaunchKernelGGL((k_pf_big<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)), dim3(PB_THREADS),
+                       PB_LDS, st, gu);
+    int rc;
+    if ((rc = moe_check_launch("moe_ffn_slots/large_gate_up"))) return rc;
+    PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
+              reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k, H / PB_NT};
+    hipLaunchKernelGGL((k_pf_big<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)), dim3(PB_THREADS),
+                       PB_LDS, st, dn);
+    return moe_check_launch("moe_ffn_slots/large_down");
+}
+
 template <int NW>
 int dec_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
                const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
@@ -463,6 +663,16 @@ bool moe_pf_supported(int w_type, int H, int I) {
 
 int moe_pf_tile_rows(int T, int k) { return T * k < PF_BIG_P ? DEC_MT : PF_MT; }
 
+bool moe_pf_big(int T, int k, int S, int H, int I) {
+    // hundreds of picks per slot on average, and whole 256-row / 128-column tiles
+    const int P = T * k;
+    return P >= PF_BIG_P && P / (S > 0 ? S : 1) >= PB_BIG_ROWS && H % PB_NT == 0 && I % 128 == 0;
+}
+
+int moe_pf_tile_rows(int T, int k, int S, int H, int I) {
+    return moe_pf_big(T, k, S, H, I) ? PB_MT : moe_pf_tile_rows(T, k);
+}
+
 int moe_pf_max_tiles(int T, int k, int S) {
     const int P = T * k;
     return (S < P ? S : P) + P / moe_pf_tile_rows(T, k) + 1;  // bounds the sum over slots of ceil(n_s / rows)
@@ -479,9 +689,13 @@ int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_sto
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(reinterpret_cast<unsigned char*>(tiles_ws) +
                                                               (size_t)max_tiles * sizeof(PfTile));
 
-    // decode-sized batches (a few picks per slot): 32-row token tiles
-    return P < PF_BIG_P ? dec_launch<DEC_NW>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
-                                             max_tiles, hbuf, part, st)
-                        : pf_launch<4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
-                                       max_tiles, hbuf, part, st);
+    // decode-sized batches (a few picks per slot): 32-row token tiles; large groups: 256-row tiles
+    if (P < PF_BIG_P)
+        return dec_launch<DEC_NW>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles,
+                                  hbuf, part, st);
+    if (moe_pf_big(T, k, S, H, I))
+        return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
+                         part, st);
+    return pf_launch<4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf, part,
+                        st);
 }

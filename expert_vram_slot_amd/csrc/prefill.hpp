@@ -21,6 +21,8 @@ size_t moe_pf_tiles_bytes(int T, int k, int S);
 // Token rows per tile for a batch of T*k picks: 32 for decode-sized batches
 // (a few picks per slot), 128 for prefill-sized ones.
 int moe_pf_tile_rows(int T, int k);
+int moe_pf_tile_rows(int T, int k, int S, int H, int I);
+bool moe_pf_big(int T, int k, int S, int H, int I);
 // Largest number of tiles T*k picks over S slots can need.
 int moe_pf_max_tiles(int T, int k, int S);
 // Gate/up and down grouped GEMMs over the slot-sorted picks (pair_list and

@@ -546,6 +546,31 @@ def test_ffn_prefill_grouped_gemm(m, T, S):
     assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
 
 
+@pytest.mark.parametrize("T,S,skew", [(1200, 6, False), (1100, 8, True)])
+def test_ffn_large_groups_256_row_tiles(m, T, S, skew):
+    """Hundreds of picks per slot run on 256 x 256 tiles of eight waves:
+    slots spanning several tiles with a ragged last one, a slot with few
+    picks (waves without token rows), non-resident experts."""
+    E, k, H, I = 8, 4, 256, 256
+    rng = np.random.default_rng(T + S)
+    x = synth.normal(synth.key(9, 1, T), (T, H), 1.0, 1)
+    store = synth.slabs(1, 556, 0, 0, E, H, I, 0.05)
+    p = np.array([0.3, 0.2, 0.2, 0.1, 0.1, 0.05, 0.04, 0.01]) if skew else np.ones(E) / E
+    ids = np.stack([rng.choice(E, k, replace=False, p=p) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    assert T * k >= 4096 and T * k // S >= 384
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(1, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 1, f"large groups T={T} S={S}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+
+
 @functools.lru_cache(maxsize=1)
 def prefill_inputs():
     """The 288-expert prefill layer's inputs (10.9 GB of slabs), made once per session."""
