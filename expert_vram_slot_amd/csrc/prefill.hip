@@ -405,19 +405,25 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
 }
 
 // Large token groups (hundreds of picks per slot): 256 token rows x 256
-// weight rows per workgroup of 8 waves, wave (wr, wc) computing token rows
-// [64 wr, 64 wr + 64) against weight rows [128 wc, 128 wc + 128): 2 x 4
-// blocks of v_mfma_f32_32x32x16_bf16, so each LDS operand read feeds two or
-// four MFMAs, and every weight row is read once per 256 tokens.  Gate/up:
-// the 128 weight rows of a wave are 64 gate rows and the up rows of the same
-// 64 h columns.  One register set of the next k-step is in flight while the
-// current one is multiplied; two LDS buffers of 64 KiB.
-constexpr int PB_THREADS = 512;
+// weight rows per workgroup of PB_WR x PB_WC waves, wave (wr, wc) computing
+// PB_MB x PB_NB blocks of v_mfma_f32_32x32x16_bf16 (token blocks from row
+// 32 PB_MB wr, weight blocks from row 32 PB_NB wc), so each LDS operand read
+// feeds several MFMAs, and every weight row is read once per 256 tokens.
+// Gate/up: the weight rows of a wave are gate rows of 16 PB_NB h columns,
+// then the up rows of the same columns.  One register set of the next
+// k-step is in flight while the current one is multiplied; two LDS buffers
+// of 64 KiB.
 constexpr int PB_MT = 256;                           // token rows per tile
 constexpr int PB_NT = 256;                           // weight rows per tile
 constexpr int PB_A_BYTES = PB_MT * PF_ROWB;           // 32 KiB
 constexpr int PB_B_BYTES = PB_NT * PF_ROWB;           // 32 KiB
 constexpr int PB_LDS = 2 * (PB_A_BYTES + PB_B_BYTES);  // 128 KiB
+// waves of a workgroup: PB_WR along the tokens x PB_WC along the weight rows
+constexpr int PB_WR = 4, PB_WC = 2;
+constexpr int PB_THREADS = 64 * PB_WR * PB_WC;
+constexpr int PB_MB = PB_MT / 32 / PB_WR;  // 32-row token blocks per wave
+constexpr int PB_NB = PB_NT / 32 / PB_WC;  // 32-row weight blocks per wave
+constexpr int PB_LD = PB_MT * 8 / PB_THREADS;  // 16-byte chunks per thread and k-step, of A and of B each
 
 template <int MODE>
 __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
@@ -437,16 +443,17 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
     if (local >= per_xcd || e >= nt) return;
     const PfTile tl = g.tiles[e];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wr = wv >> 1, wc = wv & 1;
+    const int wr = wv / PB_WC, wc = wv % PB_WC;
     const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
     const size_t row_bytes = (size_t)g.K * 2;
+    constexpr int HCW = PB_NB * 16;  // gate/up: h columns per wave (NB/2 gate blocks, NB/2 up blocks)
 
-    // this thread's 4 A and 4 B chunks of a k-step: row u / 8, chunk u % 8 for u = q * 512 + tid
-    const unsigned char* arow[4];
-    const unsigned char* brow[4];
-    int soff[4];
+    // this thread's A and B chunks of a k-step: row u / 8, chunk u % 8 for u = q * PB_THREADS + tid
+    const unsigned char* arow[PB_LD];
+    const unsigned char* brow[PB_LD];
+    int soff[PB_LD];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < PB_LD; ++q) {
         const int u = q * PB_THREADS + tid, r = u >> 3, ch = u & 7;
         const int pos = tl.p0 + min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
         int idx;
@@ -456,10 +463,10 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
         soff[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
         int64_t plane;
         int w_row;
-        if constexpr (MODE == PF_GU) {
-            const int half = r >> 7, rr = r & 127;
-            plane = rr < 64 ? g.w0 : g.w1;
-            w_row = jn * 128 + half * 64 + (rr & 63);
+        if constexpr (MODE == PF_GU) {  // wave column c: gate rows of HCW h columns, then their up rows
+            const int c = r / (32 * PB_NB), rr = r % (32 * PB_NB);
+            plane = rr < HCW ? g.w0 : g.w1;
+            w_row = jn * (HCW * PB_WC) + c * HCW + (rr % HCW);
         } else {
             plane = g.w0;
             w_row = jn * PB_NT + r;
@@ -467,37 +474,37 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
         brow[q] = slab + plane + (size_t)w_row * row_bytes + ch * 16;
     }
     const int khalf = lane >> 5;
-    int a_off[4][2], b_off[4][4];
+    int a_off[4][PB_MB], b_off[4][PB_NB];
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int r = wr * 64 + mb * 32 + (lane & 31);
+        for (int mb = 0; mb < PB_MB; ++mb) {
+            const int r = wr * (32 * PB_MB) + mb * 32 + (lane & 31);
             a_off[ks][mb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
         }
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb) {
-            const int r = wc * 128 + nb * 32 + (lane & 31);
+        for (int nb = 0; nb < PB_NB; ++nb) {
+            const int r = wc * (32 * PB_NB) + nb * 32 + (lane & 31);
             b_off[ks][nb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
         }
     }
-    const bool active_wave = wr * 64 < tl.rows;
-    f32x16 acc[2][4];
+    const bool active_wave = wr * (32 * PB_MB) < tl.rows;
+    f32x16 acc[PB_MB][PB_NB];
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb)
+    for (int mb = 0; mb < PB_MB; ++mb)
 #pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
+        for (int nb = 0; nb < PB_NB; ++nb)
 #pragma unroll
             for (int x = 0; x < 16; ++x) acc[mb][nb][x] = 0.0f;
 
     const int nk = g.K / PF_KT;
     const int rot = k_rot(nk);
-    v4u ra[4], rb[4];
+    v4u ra[PB_LD], rb[PB_LD];
     auto fetch = [&](int kt) {
         const int kr = kt + rot;
         const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < PB_LD; ++q) {
             ra[q] = ld16(arow[q] + ko);
             rb[q] = ld16_nt(brow[q] + ko);
         }
@@ -506,7 +513,7 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
         unsigned char* A = pb_lds + buf * (PB_A_BYTES + PB_B_BYTES);
         unsigned char* B = A + PB_A_BYTES;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
+        for (int q = 0; q < PB_LD; ++q) {
             *reinterpret_cast<v4u*>(A + soff[q]) = ra[q];
             *reinterpret_cast<v4u*>(B + soff[q]) = rb[q];
         }
@@ -517,17 +524,17 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
         const unsigned char* B = A + PB_A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 av[2], bv[4];
+            bf16x8 av[PB_MB], bv[PB_NB];
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < PB_MB; ++mb)
                 av[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(A + a_off[ks][mb]));
 #pragma unroll
-            for (int nb = 0; nb < 4; ++nb)
+            for (int nb = 0; nb < PB_NB; ++nb)
                 bv[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(B + b_off[ks][nb]));
 #pragma unroll
-            for (int mb = 0; mb < 2; ++mb)
+            for (int mb = 0; mb < PB_MB; ++mb)
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb)
+                for (int nb = 0; nb < PB_NB; ++nb)
                     acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
         }
     };
@@ -536,7 +543,7 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
     stash(0);
     __syncthreads();
     for (int kt = 0; kt + 2 <= nk; kt += 2) {  // nk is even
-        if (kt + 1 < nk) fetch(kt + 1);
+        fetch(kt + 1);
         compute(0);
         stash(1);
         __syncthreads();
@@ -549,10 +556,267 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
     if (!active_wave) return;
     const int col = lane & 31;
 #pragma unroll
-    for (int mb = 0; mb < 2; ++mb) {
+    for (int mb = 0; mb < PB_MB; ++mb) {
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-            const int r = wr * 64 + mb * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
+            const int r = wr * (32 * PB_MB) + mb * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
+            if (r >= tl.rows) continue;
+            if constexpr (MODE == PF_GU) {
+                uint16_t* h = reinterpret_cast<uint16_t*>(g.out);
+                const size_t hrow = (size_t)(tl.p0 + r) * g.N + jn * (HCW * PB_WC) + wc * HCW;
+#pragma unroll
+                for (int half = 0; half < PB_NB / 2; ++half) {
+                    const float gv = acc[mb][half][x], uv = acc[mb][PB_NB / 2 + half][x];
+                    h[hrow + half * 32 + col] = moe::f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+                }
+            } else {
+                float* part = reinterpret_cast<float*>(g.out);
+                const int pk = g.pair_list[tl.p0 + r];
+                const float wt = g.wts[pk];
+                float* prow = part + (size_t)pk * g.N + jn * PB_NT + wc * (32 * PB_NB);
+#pragma unroll
+                for (int nb = 0; nb < PB_NB; ++nb) prow[nb * 32 + col] = wt * acc[mb][nb][x];
+            }
+        }
+    }
+}
+
+// The same 256 x 256 tiles with the operands carried straight from memory
+// into LDS: four waves, wave (wr, wc) computing token rows [128 wr, 128 wr +
+// 128) against weight rows [128 wc, 128 wc + 128) as 4 x 4 blocks of
+// v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs), so one LDS operand read
+// feeds four MFMAs.  A k-step covers 64 k: whole 128-byte lines of every row
+// (row pieces of half a line halve the rate of the loads).  The 160 KiB of
+// LDS hold two k-steps of the token operand and three of the weight operand
+// (the one that misses in L2), so the loads of step t + 2 (tokens) and t + 3
+// (weights) go out while step t is multiplied.  The loads write LDS in lane
+// order (lane l of a load fills bytes 16 l of its 1 KiB), so the swizzle that
+// keeps the MFMA operand reads free of bank conflicts is applied on the memory
+// side: LDS chunk s of row r holds the row's 16-byte chunk s ^ swz(r).
+constexpr int PW_THREADS = 256;
+constexpr int PW_OPB = 256 * PF_ROWB;     // 32 KiB: one operand of one k-step
+constexpr int PW_NA = 2, PW_NB = 3;       // k-steps held per operand
+constexpr int PW_LDS = (PW_NA + PW_NB) * PW_OPB;
+constexpr int PW_LD = PW_OPB / 1024 / 4;  // 1 KiB loads per operand, wave and k-step
+static_assert(PW_LDS <= 160 * 1024, "LDS of one CU");
+
+constexpr bool PB_WIDE = true;
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt for at most N outstanding vector memory operations and no
+// outstanding LDS reads (exp untouched)
+template <int N>
+__device__ __forceinline__ void pw_wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt holds 6 bits");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4));
+}
+
+// workgroup barrier of the load ring.  The waits before it are explicit
+// (pw_wait_vm: this wave's buffer loads of the next step are in LDS and its
+// LDS reads are done), so it is a bare s_barrier: a fence here would make the
+// compiler wait for every buffer load in flight, the ones of later steps too.
+// The memory clobber keeps LDS reads and loads on their side of it.
+__device__ __forceinline__ void pw_barrier() { asm volatile("s_barrier" ::: "memory"); }
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pw_rsrc(const void* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, bytes, 0x00020000);
+}
+
+template <int MODE>
+__global__ void __launch_bounds__(PW_THREADS) k_pf_wide(PfArgs g) {
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[PW_LDS];
+    // workgroup -> (tile, column tile) as in k_pf_big: each XCD walks a
+    // contiguous run of the tiles, column tile fastest
+    const int b = blockIdx.x;
+    const int xcd = b % PF_XCD, i = b / PF_XCD;
+    const int nt = *g.n_tiles;
+    const int per_xcd = (nt + PF_XCD - 1) / PF_XCD;
+    const int local = i / g.ntiles_n;
+    const int e = xcd * per_xcd + local;
+    const int jn = i % g.ntiles_n;
+    if (local >= per_xcd || e >= nt) return;
+    const PfTile tl = g.tiles[e];
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: buffer resources and LDS bases in SGPRs
+    const int wr = wv >> 1, wc = wv & 1;
+    const int row_bytes = g.K * 2;
+
+    // load j of wave wv fills LDS rows 64 wv + 8 j + lane / 8 of an operand
+    uint32_t voff_a[PW_LD], voff_b[PW_LD];
+#pragma unroll
+    for (int j = 0; j < PW_LD; ++j) {
+        const int r = wv * 64 + j * 8 + (lane >> 3);
+        const int c = (lane & 7) ^ swz(r);
+        const int pos = tl.p0 + min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
+        int idx, w_row;
+        if constexpr (MODE == PF_GU) {
+            idx = g.pair_list[pos] / g.k;
+            // weight rows of wave column c: gate rows of 64 h columns, then their up rows;
+            // wave wv loads gate rows when wv is even, up rows when odd
+            w_row = jn * 128 + (wv >> 1) * 64 + j * 8 + (lane >> 3);
+        } else {
+            idx = pos;
+            w_row = jn * 256 + r;
+        }
+        voff_a[j] = (uint32_t)idx * (uint32_t)row_bytes + (uint32_t)(c * 16);
+        voff_b[j] = (uint32_t)w_row * (uint32_t)row_bytes + (uint32_t)(c * 16);
+    }
+    const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
+    int64_t plane;
+    if constexpr (MODE == PF_GU) plane = (wv & 1) ? g.w1 : g.w0;
+    else plane = g.w0;
+    const __amdgpu_buffer_rsrc_t ra = pw_rsrc(g.act, 0x7fffffff);
+    const __amdgpu_buffer_rsrc_t rb = pw_rsrc(slab + plane, g.N * row_bytes);
+
+    // the k walk starts at a step of the slot's own: the workgroups that share
+    // a token tile (all column tiles) or a weight tile (all token tiles of the
+    // slot) walk in step, so the second reader of a line finds it in L2
+    const int nk = g.K / PF_KT;
+    const int rot = (nk * PF_ROWB) % 4096 == 0 ? tl.slot % nk : 0;
+    unsigned char* const lds_a = lds;
+    unsigned char* const lds_b = lds + PW_NA * PW_OPB;
+    auto koff = [&](int kt) {
+        const int kr = kt + rot;
+        return (kr >= nk ? kr - nk : kr) * PF_ROWB;
+    };
+    // load j of step kt of the token (A) or weight (B) operand
+    auto load_a = [&](int kt, int j) {
+        unsigned char* base = lds_a + (kt % PW_NA) * PW_OPB + wv * (PW_LD * 1024);
+        const int so = koff(kt);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(base + j * 1024), 16, voff_a[j], so, 0, 0);
+    };
+    auto load_b = [&](int kt, int j) {
+        unsigned char* base = lds_b + (kt % PW_NB) * PW_OPB + wv * (PW_LD * 1024);
+        const int so = koff(kt);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(base + j * 1024), 16, voff_b[j], so, 0, 0);
+    };
+
+    // operand rows of a lane: (128 wr or 128 wc) + 32 blk + lane % 32, whose
+    // swizzle is swz(lane % 32) ^ 4 for odd blocks
+    const int l32 = lane & 31, kh = lane >> 5, f0 = swz(l32);
+    const int a_lane = (wr * 128 + l32) * PF_ROWB, b_lane = (wc * 128 + l32) * PF_ROWB;
+    f32x16 acc[4][4];
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb)
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+#pragma unroll
+            for (int x = 0; x < 16; ++x) acc[mb][nb][x] = 0.0f;
+    // operands of quarter ks (16 k) of step t
+    auto read = [&](int t, int ks, bf16x8* av, bf16x8* bv) {
+        const unsigned char* A = lds_a + (t % PW_NA) * PW_OPB;
+        const unsigned char* B = lds_b + (t % PW_NB) * PW_OPB;
+        const int c = ks * 2 + kh;
+        const int co0 = (c ^ f0) * 16, co1 = (c ^ f0 ^ 4) * 16;
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb)
+            av[mb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const v4u*>(A + a_lane + mb * 32 * PF_ROWB + ((mb & 1) ? co1 : co0)));
+#pragma unroll
+        for (int nb = 0; nb < 4; ++nb)
+            bv[nb] = __builtin_bit_cast(
+                bf16x8, *reinterpret_cast<const v4u*>(B + b_lane + nb * 32 * PF_ROWB + ((nb & 1) ? co1 : co0)));
+    };
+    // the sixteen MFMAs of a quarter, with buffer loads of step kt after each
+    // four of them (the loads go out spread over the MFMAs: issued in one burst
+    // they fill the address queue and hold up the MFMA issue behind them):
+    // LD_NONE, the weight loads 0..3 or 4..7 (one per four MFMAs), or the token
+    // loads (two per four MFMAs)
+    enum { LD_NONE, LD_B_LO, LD_B_HI, LD_A };
+    auto mfma = [&](const bf16x8* av, const bf16x8* bv, int what, int kt) {
+#pragma unroll
+        for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb)
+                acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (what == LD_B_LO) load_b(kt, mb);
+            else if (what == LD_B_HI) load_b(kt, 4 + mb);
+            else if (what == LD_A) {
+                load_a(kt, 2 * mb);
+                load_a(kt, 2 * mb + 1);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    // quarters 0..2 of step t, the weight loads of step kb (if kb >= 0) spread
+    // over quarters 0 and 1; the reads of the next quarter go out before the
+    // MFMAs of this one
+    auto body = [&](int t, int kb) {
+        read(t, 1, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(a0, b0, kb >= 0 ? LD_B_LO : LD_NONE, kb);
+        read(t, 2, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(a1, b1, kb >= 0 ? LD_B_HI : LD_NONE, kb);
+        read(t, 3, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(a0, b0, LD_NONE, 0);
+    };
+
+    // Step t: quarters 0..2 (with the weight loads of t + 2); wait for this
+    // wave's loads of t + 1 (only the weight loads of t + 2 may be
+    // outstanding) and barrier, after which every wave's loads of t + 1 are in
+    // LDS and every wave is done reading t, whose token buffer takes the loads
+    // of t + 2; read quarter 0 of t + 1 and multiply quarter 3 of t with those
+    // loads spread over it.  The weight buffer of t + 2 was last read at step
+    // t - 1.  Waves past the tile's rows multiply the repeated last row
+    // (dropped), so the loops have no branches and the accumulators stay in
+    // AGPRs.  nk >= 2.
+#pragma unroll
+    for (int j = 0; j < PW_LD; ++j) load_a(0, j);
+#pragma unroll
+    for (int j = 0; j < PW_LD; ++j) load_b(0, j);
+#pragma unroll
+    for (int j = 0; j < PW_LD; ++j) load_a(1, j);
+#pragma unroll
+    for (int j = 0; j < PW_LD; ++j) load_b(1, j);
+    pw_wait_vm<2 * PW_LD>();
+    pw_barrier();
+    read(0, 0, a0, b0);
+    int t = 0;
+    for (; t + 2 < nk; ++t) {
+        body(t, t + 2);
+        pw_wait_vm<PW_LD>();
+        pw_barrier();
+        read(t + 1, 0, a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma(a1, b1, LD_A, t + 2);
+    }
+    // t = nk - 2
+    body(t, -1);
+    pw_wait_vm<0>();
+    pw_barrier();
+    read(t + 1, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma(a1, b1, LD_NONE, 0);
+    ++t;
+    // t = nk - 1
+    body(t, -1);
+    mfma(a1, b1, LD_NONE, 0);
+
+    // the pick and routing weight of each tile row, staged in LDS once the
+    // loop is done with it (the down projection scales its rows by them)
+    int32_t* row_pick = reinterpret_cast<int32_t*>(lds);
+    float* row_wt = reinterpret_cast<float*>(lds + 1024);
+    if constexpr (MODE == PF_DOWN) {
+        const int pk = g.pair_list[tl.p0 + min(tid, tl.rows - 1)];
+        const float wt = g.wts[pk];
+        __syncthreads();
+        row_pick[tid] = pk;
+        row_wt[tid] = wt;
+        __syncthreads();
+    }
+
+    if (wr * 128 >= tl.rows) return;
+    const int col = lane & 31;
+#pragma unroll
+    for (int mb = 0; mb < 4; ++mb) {
+#pragma unroll
+        for (int x = 0; x < 16; ++x) {
+            const int r = wr * 128 + mb * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
             if (r >= tl.rows) continue;
             if constexpr (MODE == PF_GU) {
                 uint16_t* h = reinterpret_cast<uint16_t*>(g.out);
@@ -560,13 +824,15 @@ __global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
 #pragma unroll
                 for (int half = 0; half < 2; ++half) {
                     const float gv = acc[mb][half][x], uv = acc[mb][2 + half][x];
-                    h[hrow + half * 32 + col] = moe::f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
+                    // silu with the hardware exp and reciprocal: the result is rounded to bf16
+                    const float sg = gv * __builtin_amdgcn_rcpf(1.0f + __expf(-gv));
+                    h[hrow + half * 32 + col] = moe::f32_to_bf16(sg * uv);
                 }
             } else {
                 float* part = reinterpret_cast<float*>(g.out);
-                const int pk = g.pair_list[tl.p0 + r];
-                const float wt = g.wts[pk];
-                float* prow = part + (size_t)pk * g.N + jn * PB_NT + wc * 128;
+                const int pk = row_pick[r];
+                const float wt = row_wt[r];
+                float* prow = part + (size_t)pk * g.N + jn * 256 + wc * 128;
 #pragma unroll
                 for (int nb = 0; nb < 4; ++nb) prow[nb * 32 + col] = wt * acc[mb][nb][x];
             }
@@ -591,15 +857,24 @@ int pb_launch(const void* x, const float* w, int k, const void* slot_store, size
     }
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
     PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
-              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / 128};
-    hipLaunchKernelGGL((k_pf_big<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)), dim3(PB_THREADS),
-                       PB_LDS, st, gu);
+              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k,
+              I / (PB_NT / 2)};
+    if (PB_WIDE)
+        hipLaunchKernelGGL((k_pf_wide<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
+                           dim3(PW_THREADS), 0, st, gu);
+    else
+        hipLaunchKernelGGL((k_pf_big<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
+                           dim3(PB_THREADS), PB_LDS, st, gu);
     int rc;
     if ((rc = moe_check_launch("moe_ffn_slots/large_gate_up"))) return rc;
     PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
               reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k, H / PB_NT};
-    hipLaunchKernelGGL((k_pf_big<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)), dim3(PB_THREADS),
-                       PB_LDS, st, dn);
+    if (PB_WIDE)
+        hipLaunchKernelGGL((k_pf_wide<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+                           dim3(PW_THREADS), 0, st, dn);
+    else
+        hipLaunchKernelGGL((k_pf_big<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+                           dim3(PB_THREADS), PB_LDS, st, dn);
     return moe_check_launch("moe_ffn_slots/large_down");
 }
 
@@ -666,7 +941,10 @@ int moe_pf_tile_rows(int T, int k) { return T * k < PF_BIG_P ? DEC_MT : PF_MT; }
 bool moe_pf_big(int T, int k, int S, int H, int I) {
     // hundreds of picks per slot on average, and whole 256-row / 128-column tiles
     const int P = T * k;
-    return P >= PF_BIG_P && P / (S > 0 ? S : 1) >= PB_BIG_ROWS && H % PB_NT == 0 && I % 128 == 0;
+    // the buffer loads address each operand with 31-bit offsets
+    const bool fits = (int64_t)T * H * 2 < INT32_MAX && (int64_t)P * I * 2 < INT32_MAX;
+    return fits && P >= PF_BIG_P && P / (S > 0 ? S : 1) >= PB_BIG_ROWS && H % PB_NT == 0 && I % 128 == 0 &&
+           I >= 256;  // at least four 64-k steps in either contraction
 }
 
 int moe_pf_tile_rows(int T, int k, int S, int H, int I) {
