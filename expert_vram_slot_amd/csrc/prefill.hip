@@ -404,192 +404,21 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     }
 }
 
-// Large token groups (hundreds of picks per slot): 256 token rows x 256
-// weight rows per workgroup of PB_WR x PB_WC waves, wave (wr, wc) computing
-// PB_MB x PB_NB blocks of v_mfma_f32_32x32x16_bf16 (token blocks from row
-// 32 PB_MB wr, weight blocks from row 32 PB_NB wc), so each LDS operand read
-// feeds several MFMAs, and every weight row is read once per 256 tokens.
-// Gate/up: the weight rows of a wave are gate rows of 16 PB_NB h columns,
-// then the up rows of the same columns.  One register set of the next
-// k-step is in flight while the current one is multiplied; two LDS buffers
-// of 64 KiB.
-constexpr int PB_MT = 256;                           // token rows per tile
-constexpr int PB_NT = 256;                           // weight rows per tile
-constexpr int PB_A_BYTES = PB_MT * PF_ROWB;           // 32 KiB
-constexpr int PB_B_BYTES = PB_NT * PF_ROWB;           // 32 KiB
-constexpr int PB_LDS = 2 * (PB_A_BYTES + PB_B_BYTES);  // 128 KiB
-// waves of a workgroup: PB_WR along the tokens x PB_WC along the weight rows
-constexpr int PB_WR = 4, PB_WC = 2;
-constexpr int PB_THREADS = 64 * PB_WR * PB_WC;
-constexpr int PB_MB = PB_MT / 32 / PB_WR;  // 32-row token blocks per wave
-constexpr int PB_NB = PB_NT / 32 / PB_WC;  // 32-row weight blocks per wave
-constexpr int PB_LD = PB_MT * 8 / PB_THREADS;  // 16-byte chunks per thread and k-step, of A and of B each
+// Large token groups (hundreds of picks per slot): tiles of 256 token rows x
+// 256 weight rows, so every weight row is read once per 256 tokens.
+constexpr int PB_MT = 256;  // token rows per tile
+constexpr int PB_NT = 256;  // weight rows per tile
 
-template <int MODE>
-__global__ void __launch_bounds__(PB_THREADS) k_pf_big(PfArgs g) {
-    extern __shared__ __attribute__((aligned(16))) unsigned char pb_lds[];
-    // workgroup -> (tile, column tile): each XCD takes a contiguous run of the
-    // tiles (the tiles of one slot are adjacent in the list) and walks them
-    // with the column tile fastest, so the token tiles of a slot read each
-    // weight tile at about the same time from the XCD's L2, and the column
-    // tiles of a token tile share its activations there
-    const int b = blockIdx.x;
-    const int xcd = b % PF_XCD, i = b / PF_XCD;
-    const int nt = *g.n_tiles;
-    const int per_xcd = (nt + PF_XCD - 1) / PF_XCD;
-    const int local = i / g.ntiles_n;
-    const int e = xcd * per_xcd + local;
-    const int jn = i % g.ntiles_n;
-    if (local >= per_xcd || e >= nt) return;
-    const PfTile tl = g.tiles[e];
-    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-    const int wr = wv / PB_WC, wc = wv % PB_WC;
-    const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
-    const size_t row_bytes = (size_t)g.K * 2;
-    constexpr int HCW = PB_NB * 16;  // gate/up: h columns per wave (NB/2 gate blocks, NB/2 up blocks)
-
-    // this thread's A and B chunks of a k-step: row u / 8, chunk u % 8 for u = q * PB_THREADS + tid
-    const unsigned char* arow[PB_LD];
-    const unsigned char* brow[PB_LD];
-    int soff[PB_LD];
-#pragma unroll
-    for (int q = 0; q < PB_LD; ++q) {
-        const int u = q * PB_THREADS + tid, r = u >> 3, ch = u & 7;
-        const int pos = tl.p0 + min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
-        int idx;
-        if constexpr (MODE == PF_GU) idx = g.pair_list[pos] / g.k;
-        else idx = pos;
-        arow[q] = g.act + (size_t)idx * row_bytes + ch * 16;
-        soff[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
-        int64_t plane;
-        int w_row;
-        if constexpr (MODE == PF_GU) {  // wave column c: gate rows of HCW h columns, then their up rows
-            const int c = r / (32 * PB_NB), rr = r % (32 * PB_NB);
-            plane = rr < HCW ? g.w0 : g.w1;
-            w_row = jn * (HCW * PB_WC) + c * HCW + (rr % HCW);
-        } else {
-            plane = g.w0;
-            w_row = jn * PB_NT + r;
-        }
-        brow[q] = slab + plane + (size_t)w_row * row_bytes + ch * 16;
-    }
-    const int khalf = lane >> 5;
-    int a_off[4][PB_MB], b_off[4][PB_NB];
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-#pragma unroll
-        for (int mb = 0; mb < PB_MB; ++mb) {
-            const int r = wr * (32 * PB_MB) + mb * 32 + (lane & 31);
-            a_off[ks][mb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
-        }
-#pragma unroll
-        for (int nb = 0; nb < PB_NB; ++nb) {
-            const int r = wc * (32 * PB_NB) + nb * 32 + (lane & 31);
-            b_off[ks][nb] = r * PF_ROWB + (((ks * 2 + khalf) ^ swz(r)) * 16);
-        }
-    }
-    const bool active_wave = wr * (32 * PB_MB) < tl.rows;
-    f32x16 acc[PB_MB][PB_NB];
-#pragma unroll
-    for (int mb = 0; mb < PB_MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < PB_NB; ++nb)
-#pragma unroll
-            for (int x = 0; x < 16; ++x) acc[mb][nb][x] = 0.0f;
-
-    const int nk = g.K / PF_KT;
-    const int rot = k_rot(nk);
-    v4u ra[PB_LD], rb[PB_LD];
-    auto fetch = [&](int kt) {
-        const int kr = kt + rot;
-        const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
-#pragma unroll
-        for (int q = 0; q < PB_LD; ++q) {
-            ra[q] = ld16(arow[q] + ko);
-            rb[q] = ld16_nt(brow[q] + ko);
-        }
-    };
-    auto stash = [&](int buf) {
-        unsigned char* A = pb_lds + buf * (PB_A_BYTES + PB_B_BYTES);
-        unsigned char* B = A + PB_A_BYTES;
-#pragma unroll
-        for (int q = 0; q < PB_LD; ++q) {
-            *reinterpret_cast<v4u*>(A + soff[q]) = ra[q];
-            *reinterpret_cast<v4u*>(B + soff[q]) = rb[q];
-        }
-    };
-    auto compute = [&](int buf) {
-        if (!active_wave) return;
-        const unsigned char* A = pb_lds + buf * (PB_A_BYTES + PB_B_BYTES);
-        const unsigned char* B = A + PB_A_BYTES;
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks) {
-            bf16x8 av[PB_MB], bv[PB_NB];
-#pragma unroll
-            for (int mb = 0; mb < PB_MB; ++mb)
-                av[mb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(A + a_off[ks][mb]));
-#pragma unroll
-            for (int nb = 0; nb < PB_NB; ++nb)
-                bv[nb] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(B + b_off[ks][nb]));
-#pragma unroll
-            for (int mb = 0; mb < PB_MB; ++mb)
-#pragma unroll
-                for (int nb = 0; nb < PB_NB; ++nb)
-                    acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av[mb], bv[nb], acc[mb][nb], 0, 0, 0);
-        }
-    };
-    // step t: the loads of t + 1 are in flight while t is multiplied out of buffer t % 2
-    fetch(0);
-    stash(0);
-    __syncthreads();
-    for (int kt = 0; kt + 2 <= nk; kt += 2) {  // nk is even
-        fetch(kt + 1);
-        compute(0);
-        stash(1);
-        __syncthreads();
-        if (kt + 2 < nk) fetch(kt + 2);
-        compute(1);
-        if (kt + 2 < nk) stash(0);
-        __syncthreads();
-    }
-
-    if (!active_wave) return;
-    const int col = lane & 31;
-#pragma unroll
-    for (int mb = 0; mb < PB_MB; ++mb) {
-#pragma unroll
-        for (int x = 0; x < 16; ++x) {
-            const int r = wr * (32 * PB_MB) + mb * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
-            if (r >= tl.rows) continue;
-            if constexpr (MODE == PF_GU) {
-                uint16_t* h = reinterpret_cast<uint16_t*>(g.out);
-                const size_t hrow = (size_t)(tl.p0 + r) * g.N + jn * (HCW * PB_WC) + wc * HCW;
-#pragma unroll
-                for (int half = 0; half < PB_NB / 2; ++half) {
-                    const float gv = acc[mb][half][x], uv = acc[mb][PB_NB / 2 + half][x];
-                    h[hrow + half * 32 + col] = moe::f32_to_bf16(gv / (1.0f + expf(-gv)) * uv);
-                }
-            } else {
-                float* part = reinterpret_cast<float*>(g.out);
-                const int pk = g.pair_list[tl.p0 + r];
-                const float wt = g.wts[pk];
-                float* prow = part + (size_t)pk * g.N + jn * PB_NT + wc * (32 * PB_NB);
-#pragma unroll
-                for (int nb = 0; nb < PB_NB; ++nb) prow[nb * 32 + col] = wt * acc[mb][nb][x];
-            }
-        }
-    }
-}
-
-// The same 256 x 256 tiles with the operands carried straight from memory
+// The tiles are multiplied with the operands carried straight from memory
 // into LDS: four waves, wave (wr, wc) computing token rows [128 wr, 128 wr +
 // 128) against weight rows [128 wc, 128 wc + 128) as 4 x 4 blocks of
 // v_mfma_f32_32x32x16_bf16 (accumulators in AGPRs), so one LDS operand read
 // feeds four MFMAs.  A k-step covers 64 k: whole 128-byte lines of every row
 // (row pieces of half a line halve the rate of the loads).  The 160 KiB of
 // LDS hold two k-steps of the token operand and three of the weight operand
-// (the one that misses in L2), so the loads of step t + 2 (tokens) and t + 3
-// (weights) go out while step t is multiplied.  The loads write LDS in lane
+// (the one that misses in L2): the weight loads of step t + 2 go out while
+// the first half of step t is multiplied, the token loads of t + 2 while its
+// last quarter is, each spread over the MFMAs.  The loads write LDS in lane
 // order (lane l of a load fills bytes 16 l of its 1 KiB), so the swizzle that
 // keeps the MFMA operand reads free of bank conflicts is applied on the memory
 // side: LDS chunk s of row r holds the row's 16-byte chunk s ^ swz(r).
@@ -599,8 +428,6 @@ constexpr int PW_NA = 2, PW_NB = 3;       // k-steps held per operand
 constexpr int PW_LDS = (PW_NA + PW_NB) * PW_OPB;
 constexpr int PW_LD = PW_OPB / 1024 / 4;  // 1 KiB loads per operand, wave and k-step
 static_assert(PW_LDS <= 160 * 1024, "LDS of one CU");
-
-constexpr bool PB_WIDE = true;
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -626,8 +453,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t pw_rsrc(const void* base, int 
 template <int MODE>
 __global__ void __launch_bounds__(PW_THREADS) k_pf_wide(PfArgs g) {
     __shared__ __attribute__((aligned(1024))) unsigned char lds[PW_LDS];
-    // workgroup -> (tile, column tile) as in k_pf_big: each XCD walks a
-    // contiguous run of the tiles, column tile fastest
+    // workgroup -> (tile, column tile): each XCD takes a contiguous run of the
+    // tiles (the tiles of one slot are adjacent in the list) and walks them
+    // with the column tile fastest, so the token tiles of a slot read each
+    // weight tile at about the same time from the XCD's L2, and the column
+    // tiles of a token tile share its activations there
     const int b = blockIdx.x;
     const int xcd = b % PF_XCD, i = b / PF_XCD;
     const int nt = *g.n_tiles;
@@ -843,38 +673,18 @@ __global__ void __launch_bounds__(PW_THREADS) k_pf_wide(PfArgs g) {
 int pb_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
               const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
               int max_tiles, void* hbuf, float* part, hipStream_t st) {
-    static bool lds_set = false;
-    if (!lds_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_big<PF_GU>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, PB_LDS) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_big<PF_DOWN>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, PB_LDS) != hipSuccess) {
-            (void)hipGetLastError();
-            return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the large-group kernels",
-                            PB_LDS);
-        }
-        lds_set = true;
-    }
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
     PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
               reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k,
               I / (PB_NT / 2)};
-    if (PB_WIDE)
-        hipLaunchKernelGGL((k_pf_wide<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
-                           dim3(PW_THREADS), 0, st, gu);
-    else
-        hipLaunchKernelGGL((k_pf_big<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
-                           dim3(PB_THREADS), PB_LDS, st, gu);
+    hipLaunchKernelGGL((k_pf_wide<PF_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)), dim3(PW_THREADS), 0,
+                       st, gu);
     int rc;
     if ((rc = moe_check_launch("moe_ffn_slots/large_gate_up"))) return rc;
     PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
               reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k, H / PB_NT};
-    if (PB_WIDE)
-        hipLaunchKernelGGL((k_pf_wide<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
-                           dim3(PW_THREADS), 0, st, dn);
-    else
-        hipLaunchKernelGGL((k_pf_big<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
-                           dim3(PB_THREADS), PB_LDS, st, dn);
+    hipLaunchKernelGGL((k_pf_wide<PF_DOWN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)), dim3(PW_THREADS),
+                       0, st, dn);
     return moe_check_launch("moe_ffn_slots/large_down");
 }
 
