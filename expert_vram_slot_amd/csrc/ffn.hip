@@ -865,7 +865,11 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
                                                                                      sizeof(moe_pf_tile))
                                  : nullptr;
 
-    if (P > GROUP_MULTI_P) {
+    // decode-sized bf16 batches: the gate/up GEMM sorts the picks itself
+    const bool fused_sort = use_pf && moe_pf_fused_sort(T, k);
+    if (fused_sort) {
+        // no sort launch: the gate/up workgroups write the pick and tile lists
+    } else if (P > GROUP_MULTI_P) {
         const int nch = (P + GROUP_THREADS - 1) / GROUP_THREADS;
         int32_t* gcnt = reinterpret_cast<int32_t*>(ws + L.gcnt);
         hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt);
@@ -881,7 +885,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
 
     if (use_pf) {
         rc = moe_pf_run(x, w, T, k, slot_store, slab_bytes, S, H, I, lay, pair_list, ws + L.pf_tiles, hbuf, part,
-                        st);
+                        st, fused_sort ? slot_ids : nullptr);
         if (rc) return rc;
         const int64_t n4 = (int64_t)T * (H / 4);
         hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, slot_ids, T, k, S,

@@ -89,6 +89,15 @@ struct PfArgs {
     int N;                       // output columns (GU: I, DOWN: H)
     int k;                       // top-k (GU: token = pick / k)
     int ntiles_n;                // column tiles per token tile
+    // decode gate/up only: when sort_slots is set, each workgroup sorts the
+    // picks by slot itself (no separate sort launch) and the workgroups of
+    // column tile 0 write the tile list and the slot-sorted pick list for the
+    // down projection (into tiles_out / n_tiles_out / pair_out)
+    const int32_t* sort_slots;   // [sort_P] slot id per pick (< 0: not resident)
+    int sort_P, sort_S;
+    int32_t* pair_out;
+    PfTile* tiles_out;
+    int32_t* n_tiles_out;
 };
 
 __device__ __forceinline__ v4u ld16(const unsigned char* p) { return *reinterpret_cast<const v4u*>(p); }
@@ -254,6 +263,90 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     }
 }
 
+// Stable grouping of the picks by slot, done by every workgroup of the
+// decode gate/up kernel for itself (batches of at most DEC_SORT_MAX picks):
+// slot counts in LDS, their prefix sums give each slot's first tile and first
+// sorted position (slots ascending, DEC_MT picks per tile, the same list the
+// separate sort writes); the workgroup's tile e then takes the picks of its
+// slot whose rank (pick order) falls in its chunk.  Fills *tl and the tile's
+// picks at dec_lds + DEC_SORT_ROWS; the workgroups of column tile 0 also write
+// the tile and its picks for the down projection, workgroup 0 the tile count.
+// Returns false when e is past the last tile (the whole workgroup).
+constexpr int DEC_SORT_MAX = 1024;      // picks
+constexpr int DEC_SORT_ROWS = 4096;     // byte offset of the tile's picks in LDS (after S <= 1024 counts)
+constexpr int DEC_SORT_INFO = DEC_SORT_ROWS + DEC_MT * 4;
+constexpr int DEC_SORT_SCR = DEC_SORT_INFO + 64;
+
+template <int NTH>
+__device__ bool dec_sort_tile(const PfArgs& g, int e, int jn, unsigned char* lds, PfTile* tl) {
+    int* cnt = reinterpret_cast<int*>(lds);
+    int* rows_pick = reinterpret_cast<int*>(lds + DEC_SORT_ROWS);
+    int* info = reinterpret_cast<int*>(lds + DEC_SORT_INFO);
+    int* scr = reinterpret_cast<int*>(lds + DEC_SORT_SCR);
+    const int tid = threadIdx.x, P = g.sort_P, S = g.sort_S;
+    constexpr int PPT = DEC_SORT_MAX / NTH;  // picks per thread, in pick order
+    for (int s = tid; s < S; s += NTH) cnt[s] = 0;
+    __syncthreads();
+    int sv[PPT];
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        const int p = tid * PPT + j;
+        const int s = p < P ? g.sort_slots[p] : -1;
+        sv[j] = (s >= 0 && s < S) ? s : -1;
+        if (sv[j] >= 0) atomicAdd(&cnt[sv[j]], 1);  // LDS integer counts: order-free
+    }
+    __syncthreads();
+    const int spt = (S + NTH - 1) / NTH;  // slots per thread, ascending
+    int my_nt = 0, my_np = 0;
+    for (int j = 0; j < spt; ++j) {
+        const int s = tid * spt + j;
+        if (s < S) {
+            my_np += cnt[s];
+            my_nt += (cnt[s] + DEC_MT - 1) / DEC_MT;
+        }
+    }
+    int n_tiles, n_picks;
+    int toff = moe::block_exclusive_scan(my_nt, scr, &n_tiles);
+    int poff = moe::block_exclusive_scan(my_np, scr, &n_picks);
+    for (int j = 0; j < spt; ++j) {
+        const int s = tid * spt + j;
+        if (s >= S) break;
+        const int c = cnt[s], nt = (c + DEC_MT - 1) / DEC_MT;
+        if (e >= toff && e < toff + nt) {
+            const int r0 = (e - toff) * DEC_MT;
+            info[0] = s;
+            info[1] = poff + r0;
+            info[2] = min(DEC_MT, c - r0);
+            info[3] = r0;
+        }
+        toff += nt;
+        poff += c;
+    }
+    if (blockIdx.x == 0 && tid == 0) *g.n_tiles_out = n_tiles;
+    __syncthreads();
+    if (e >= n_tiles) return false;
+    const int slot = info[0], p0 = info[1], rows = info[2], r0 = info[3];
+    int f = 0;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) f += sv[j] == slot;
+    int tot;
+    int rk = moe::block_exclusive_scan(f, scr, &tot) - r0;
+#pragma unroll
+    for (int j = 0; j < PPT; ++j) {
+        if (sv[j] == slot) {
+            if (rk >= 0 && rk < rows) rows_pick[rk] = tid * PPT + j;
+            ++rk;
+        }
+    }
+    __syncthreads();
+    if (jn == 0) {
+        if (tid < rows) g.pair_out[p0 + tid] = rows_pick[tid];
+        if (tid == 0) g.tiles_out[e] = PfTile{p0, rows, slot, 0};
+    }
+    *tl = PfTile{p0, rows, slot, 0};
+    return true;
+}
+
 // Decode-shaped tile: DEC_MT = 32 token rows (a slot holds a few picks at
 // decode batch sizes) x 32 * NW weight rows; wave w owns weight rows
 // [32 w, 32 w + 32) and all 32 token rows, so every wave has MFMA work and
@@ -276,9 +369,15 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     const int xcd = b % PF_XCD, i = b / PF_XCD;
     const int e = xcd + PF_XCD * (i / g.ntiles_n);
     const int jn = i % g.ntiles_n;
-    if (e >= *g.n_tiles) return;
-    const PfTile tl = g.tiles[e];
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    PfTile tl;
+    const bool fused = MODE == PF_GU && g.sort_slots != nullptr;
+    if (fused) {
+        if (!dec_sort_tile<NTH>(g, e, jn, dec_lds, &tl)) return;
+    } else {
+        if (e >= *g.n_tiles) return;
+        tl = g.tiles[e];
+    }
     const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
     const size_t row_bytes = (size_t)g.K * 2;
 
@@ -287,13 +386,16 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
 #pragma unroll
     for (int q = 0; q < NA; ++q) {
         const int u = q * NTH + tid, r = u >> 3, ch = u & 7;
-        const int pos = tl.p0 + min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
+        const int rr = min(r, tl.rows - 1);  // rows past the picks repeat the last one (dropped)
         int idx;
-        if constexpr (MODE == PF_GU) idx = g.pair_list[pos] / g.k;
-        else idx = pos;
+        if constexpr (MODE == PF_GU)
+            idx = (fused ? reinterpret_cast<const int32_t*>(dec_lds + DEC_SORT_ROWS)[rr] : g.pair_list[tl.p0 + rr]) /
+                  g.k;
+        else idx = tl.p0 + rr;
         arow[q] = g.act + (size_t)idx * row_bytes + ch * 16;
         aso[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
     }
+    if (fused) __syncthreads();  // the sort's LDS is the first k-step's buffer
     const unsigned char* brow[NBU];
     int bso[NBU];
 #pragma unroll
@@ -691,11 +793,20 @@ int pb_launch(const void* x, const float* w, int k, const void* slot_store, size
 template <int NW>
 int dec_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
                const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
-               int max_tiles, void* hbuf, float* part, hipStream_t st) {
+               int max_tiles, void* hbuf, float* part, hipStream_t st, const int32_t* sort_slots, int P, int S) {
     const int lds = 2 * (DEC_MT + 32 * NW) * PF_ROWB;
+    static_assert(DEC_SORT_SCR + 64 <= 2 * (DEC_MT + 32 * DEC_NW) * PF_ROWB, "the sort fits the kernel's LDS");
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
     PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
               reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / (16 * NW)};
+    if (sort_slots) {  // the gate/up workgroups sort the picks (and write the lists the down kernel reads)
+        gu.sort_slots = sort_slots;
+        gu.sort_P = P;
+        gu.sort_S = S;
+        gu.pair_out = const_cast<int32_t*>(pair_list);
+        gu.tiles_out = const_cast<PfTile*>(tiles);
+        gu.n_tiles_out = const_cast<int32_t*>(n_tiles);
+    }
     hipLaunchKernelGGL((k_dec_gemm<PF_GU, NW, DEC_NR_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
                        dim3(64 * NW), lds, st, gu);
     int rc;
@@ -768,9 +879,14 @@ int moe_pf_max_tiles(int T, int k, int S) {
 
 size_t moe_pf_tiles_bytes(int T, int k, int S) { return (size_t)moe_pf_max_tiles(T, k, S) * sizeof(PfTile) + 16; }
 
+bool moe_pf_fused_sort(int T, int k) {
+    const int P = T * k;
+    return P < PF_BIG_P && P <= DEC_SORT_MAX;
+}
+
 int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_store, size_t slab_bytes, int S, int H,
                int I, const moe_slab_layout_t& lay, const int32_t* pair_list, void* tiles_ws, void* hbuf, float* part,
-               hipStream_t st) {
+               hipStream_t st, const int32_t* sort_slots) {
     const int P = T * k;
     const int max_tiles = moe_pf_max_tiles(T, k, S);
     const PfTile* tiles = reinterpret_cast<const PfTile*>(tiles_ws);
@@ -778,9 +894,10 @@ int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_sto
                                                               (size_t)max_tiles * sizeof(PfTile));
 
     // decode-sized batches (a few picks per slot): 32-row token tiles; large groups: 256-row tiles
+    if (sort_slots && !moe_pf_fused_sort(T, k)) return moe_fail(MOE_E_ARG, "moe_pf_run: no fused sort for %d picks", P);
     if (P < PF_BIG_P)
         return dec_launch<DEC_NW>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles,
-                                  hbuf, part, st);
+                                  hbuf, part, st, sort_slots, P, S);
     if (moe_pf_big(T, k, S, H, I))
         return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
                          part, st);

@@ -25,9 +25,15 @@ int moe_pf_tile_rows(int T, int k, int S, int H, int I);
 bool moe_pf_big(int T, int k, int S, int H, int I);
 // Largest number of tiles T*k picks over S slots can need.
 int moe_pf_max_tiles(int T, int k, int S);
-// Gate/up and down grouped GEMMs over the slot-sorted picks (pair_list and
-// the tile list written by the sorting kernels); h goes to hbuf in sorted
-// order, w * (W_d h) to part[pick][H].  Enqueued on `st`.
+// True when a batch of T*k picks can be sorted by the gate/up workgroups
+// themselves (decode-shaped tiles, at most 1024 picks).
+bool moe_pf_fused_sort(int T, int k);
+// Gate/up and down grouped GEMMs over the slot-sorted picks; h goes to hbuf
+// in sorted order, w * (W_d h) to part[pick][H].  Enqueued on `st`.  With
+// sort_slots == NULL, pair_list and the tile list in tiles_ws were written by
+// the sorting kernels; otherwise (moe_pf_fused_sort(T, k) must hold) the
+// gate/up kernel sorts the picks by sort_slots (slot per pick) and writes
+// both for the down kernel.
 int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_store, size_t slab_bytes, int S, int H,
                int I, const moe_slab_layout_t& lay, const int32_t* pair_list, void* tiles_ws, void* hbuf,
-               float* part, hipStream_t st);
+               float* part, hipStream_t st, const int32_t* sort_slots = nullptr);
