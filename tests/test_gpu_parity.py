@@ -509,6 +509,30 @@ def test_ffn_large_batch_sorted_picks(m, w_type, T):
     assert_close(y, yg, w_type, f"w{w_type} T={T} k={k}")
 
 
+@pytest.mark.parametrize("T,S", [(64, 24), (128, 40), (129, 40), (70, 1)])
+def test_ffn_decode_sort_in_gemm(m, T, S):
+    """bf16 decode batches of 512..1024 picks are grouped by slot inside the
+    gate/up GEMM (no sort launch); 1032 picks go through the sort kernel.
+    Slots with several 32-row tiles, non-resident picks, a single slot."""
+    E, k, H, I = 40, 8, 256, 128
+    rng = np.random.default_rng(T * 7 + S)
+    x = synth.normal(synth.key(T, 1, S), (T, H), 1.0, 1)
+    store = synth.slabs(1, 777, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(1, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 1, f"T={T} S={S}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+    np.testing.assert_array_equal(run_ffn(m, li, sl, w, dev(store[resident]), S), y)
+
+
 def test_ffn_workspace_reused_across_calls(m):
     """One workspace for consecutive calls of different sizes (its counters clear themselves)."""
     big = ffn_case(m, "c2", 64)
