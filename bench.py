@@ -54,7 +54,7 @@ MFMA_BF16_PEAK_TFS = 2500.0
 
 # kernels launched, in order, by one moe_ffn_slots call on the bf16 decode batch of 64 tokens (512 picks):
 # the pick sort, the MFMA gate/up and down grouped GEMMs on decode-shaped tiles, the reduction
-FFN_SEQ = ("k_group", "k_dec_gemm<0, 4, 2>", "k_dec_gemm<1, 4, 2>", "k_reduce")
+FFN_SEQ = ("k_dec_gemm<0, 4, 2>", "k_dec_gemm<1, 4, 2>", "k_reduce")  # the gate/up kernel sorts the picks itself
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
                "expert_vram_slot_amd/csrc/prefill.hpp", "expert_vram_slot_amd/csrc/common.hpp")
@@ -836,21 +836,16 @@ def _counter_per_dispatch(rows, counter):
 
 def _ffn_launches(rows, key):
     """Group per-dispatch rows into decode moe_ffn_slots launches: each
-    dispatch of the gate/up kernel FFN_SEQ[1] with the closest earlier
-    FFN_SEQ[0] and the closest later FFN_SEQ[2:] by dispatch id.  Returns a
-    list of {kernel short name: row}."""
+    dispatch of the gate/up kernel FFN_SEQ[0] with the closest later
+    FFN_SEQ[1:] by dispatch id.  Returns a list of {kernel short name: row}."""
     by_id = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     names = [_short(r["Kernel_Name"]) for r in by_id]
     launches = []
     for i, nm in enumerate(names):
-        if nm != FFN_SEQ[1]:
+        if nm != FFN_SEQ[0]:
             continue
         got = {nm: by_id[i]}
-        for j in range(i - 1, max(-1, i - 50), -1):
-            if names[j] == FFN_SEQ[0]:
-                got[FFN_SEQ[0]] = by_id[j]
-                break
-        for want in FFN_SEQ[2:]:
+        for want in FFN_SEQ[1:]:
             for j in range(i + 1, min(len(names), i + 50)):
                 if names[j] == want:
                     got[want] = by_id[j]

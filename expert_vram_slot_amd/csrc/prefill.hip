@@ -8,12 +8,16 @@
 // GEMMs once a slot holds tens of tokens:
 //
 //   k_group      picks sorted by slot (shared with the decode path), and the
-//                list of (slot, up to PF_MT consecutive picks) tiles
+//                list of (slot, up to PF_MT consecutive picks) tiles; batches
+//                of at most 1024 picks on decode-shaped tiles skip it (the
+//                gate/up kernel groups the picks itself, dec_sort_tile)
 //   k_pf_gemm<GU>   [g | u] = X_s [W_g; W_u]^T per tile of 64 h columns,
 //                   SwiGLU epilogue, h (bf16, RNE) stored in sorted-pick order
 //   k_pf_gemm<DOWN> O = H_s W_d^T per tile of 128 output columns,
 //                   part[pick] = w * O (fp32)
 //   k_dec_gemm<GU|DOWN>  the same two GEMMs on decode-shaped tiles
+//   k_pf_wide<GU|DOWN>   the same two GEMMs on 256 x 256 tiles when slots
+//                        hold hundreds of picks
 //   k_reduce     y[t] = sum over resident picks in top-k order (decode path's)
 //
 // Prefill-sized batches (4096 picks and more): a workgroup owns PF_MT = 128
