@@ -254,15 +254,23 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
         }
     } else {
         float* part = reinterpret_cast<float*>(g.out);
+        // the pick and routing weight of each of this lane's 16 rows: all
+        // loads of a kind issued together (looked up row by row behind the
+        // row test, the dependent pairs serialise)
+        int epk[16];
+        float ewt[16];
+#pragma unroll
+        for (int x = 0; x < 16; ++x)
+            epk[x] = g.pair_list[tl.p0 + min(wv * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3), tl.rows - 1)];
+#pragma unroll
+        for (int x = 0; x < 16; ++x) ewt[x] = g.wts[epk[x]];
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int r = wv * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
             if (r >= tl.rows) continue;
-            const int pk = g.pair_list[tl.p0 + r];
-            const float wt = g.wts[pk];
-            float* prow = part + (size_t)pk * g.N + jn * (NB * 32);
+            float* prow = part + (size_t)epk[x] * g.N + jn * (NB * 32);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) prow[nb * 32 + col] = wt * acc[nb][x];
+            for (int nb = 0; nb < NB; ++nb) prow[nb * 32 + col] = ewt[x] * acc[nb][x];
         }
     }
 }
@@ -309,9 +317,11 @@ __device__ bool dec_sort_tile(const PfArgs& g, int e, int jn, unsigned char* lds
             my_nt += (cnt[s] + DEC_MT - 1) / DEC_MT;
         }
     }
-    int n_tiles, n_picks;
-    int toff = moe::block_exclusive_scan(my_nt, scr, &n_tiles);
-    int poff = moe::block_exclusive_scan(my_np, scr, &n_picks);
+    // tiles and picks scanned together: both are at most 1024 (16 bits each)
+    int packed_tot;
+    const int packed = moe::block_exclusive_scan((my_nt << 16) | my_np, scr, &packed_tot);
+    const int n_tiles = packed_tot >> 16;
+    int toff = packed >> 16, poff = packed & 0xffff;
     for (int j = 0; j < spt; ++j) {
         const int s = tid * spt + j;
         if (s >= S) break;
@@ -602,6 +612,8 @@ __global__ void __launch_bounds__(PW_THREADS) k_pf_wide(PfArgs g) {
     int64_t plane;
     if constexpr (MODE == PF_GU) plane = (wv & 1) ? g.w1 : g.w0;
     else plane = g.w0;
+    // 32-bit buffer offsets: the host takes this kernel only for operands
+    // under 2 GiB (moe_pf_big)
     const __amdgpu_buffer_rsrc_t ra = pw_rsrc(g.act, 0x7fffffff);
     const __amdgpu_buffer_rsrc_t rb = pw_rsrc(slab + plane, g.N * row_bytes);
 
@@ -867,7 +879,8 @@ bool moe_pf_big(int T, int k, int S, int H, int I) {
     // hundreds of picks per slot on average, and whole 256-row / 128-column tiles
     const int P = T * k;
     // the buffer loads address each operand with 31-bit offsets
-    const bool fits = (int64_t)T * H * 2 < INT32_MAX && (int64_t)P * I * 2 < INT32_MAX;
+    const bool fits = (int64_t)T * H * 2 < INT32_MAX && (int64_t)P * I * 2 < INT32_MAX &&
+                      (int64_t)H * I * 2 < INT32_MAX;
     return fits && P >= PF_BIG_P && P / (S > 0 ? S : 1) >= PB_BIG_ROWS && H % PB_NT == 0 && I % 128 == 0 &&
            I >= 256;  // at least four 64-k steps in either contraction
 }
