@@ -632,6 +632,37 @@ def test_ffn_prefill_full_size_sampled(m, S):
     assert np.all(y[none] == 0)
 
 
+@pytest.mark.parametrize("S", [288, 144])
+def test_ffn_prefill_16384_tokens_sampled(m, S):
+    """The 288-expert layer at 16,384 tokens (about 455 picks per slot): the
+    256 x 256 tiles with the full contractions (64 and 24 k-steps, the k walk
+    rotated per slot for the 8 KiB gate/up rows); seeded random picks (eight
+    distinct experts per token, Dirichlet weights), sampled tokens against the
+    oracle, the tokens without a resident pick exactly zero."""
+    li, _, _ = prefill_inputs()
+    T, k, E, H, I = 16384, li.k, li.E, li.H, li.I
+    rng = np.random.default_rng(16384 + S)
+    x = synth.normal(synth.key(16384, 1, S), (T, H), 1.0, 1)
+    ids = np.argsort(rng.random((T, E)), axis=1)[:, :k].astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = np.arange(E) if S == E else rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    big = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=li.slab))
+    y = run_ffn(m, big, sl, w, dev(li.store[resident]), S)
+    assert np.all(np.isfinite(y))
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+    sample = np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), 10, replace=False)])
+    for t in sample:
+        ref = np.zeros(H)
+        for j in range(k):
+            if sl[t, j] >= 0:
+                ref += w[t, j] * oracle.expert(1, li.store[ids[t, j]], H, I, x[t], 1)
+        assert_close(y[t:t + 1], ref[None, :].astype(np.float32), 1, f"16384 tokens S={S} token {t}")
+
+
 def test_ffn_many_tokens_on_one_slot(m):
     """More tokens on a slot than one pass holds (token chunks of 8)."""
     li = synth.LayerInputs("c2", T=37)
