@@ -229,6 +229,51 @@ __device__ __forceinline__ void write_pf_tiles(int cnt, int off, int S, int mt, 
     if (threadIdx.x == 0) *n_tiles = tot;
 }
 
+// Activation preparation of a batch, by the workgroups 1.. of the sorting
+// launch (workgroup 0 sorts): W8A8 codes and per-row scales of x, one
+// workgroup per row (the arithmetic of k_quant_rows<true>), or the 32-input
+// block sums of x for 4-bit weights, 1024 blocks per workgroup (that of
+// k_block_sums).  Same bits as those kernels; one launch fewer.
+enum { XPREP_NONE = 0, XPREP_I8 = 1, XPREP_BSUM = 2 };
+
+__device__ void x_prep_wg(int kind, int wg, const uint16_t* __restrict__ x, int T, int H, int8_t* __restrict__ xq,
+                          float* __restrict__ xs, float* __restrict__ xbs) {
+    const int tid = threadIdx.x;
+    if (kind == XPREP_I8) {
+        __shared__ float red[GROUP_THREADS / 64];
+        const uint16_t* row = x + (int64_t)wg * H;
+        float m = 0.0f;
+        for (int i = tid; i < H; i += GROUP_THREADS) m = fmaxf(m, fabsf(moe::bf16_to_f32(row[i])));
+#pragma unroll
+        for (int o = 32; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+        if ((tid & 63) == 0) red[tid >> 6] = m;
+        __syncthreads();
+        float amax = 0.0f;
+#pragma unroll
+        for (int w = 0; w < GROUP_THREADS / 64; ++w) amax = fmaxf(amax, red[w]);
+        const float sc = amax > 0.0f ? amax / 127.0f : 1.0f;
+        for (int i = tid; i < H; i += GROUP_THREADS) {
+            float c = rintf(moe::bf16_to_f32(row[i]) / sc);
+            c = fminf(fmaxf(c, -127.0f), 127.0f);
+            xq[(int64_t)wg * H + i] = (int8_t)c;
+        }
+        if (tid == 0) xs[wg] = sc;
+    } else {
+        const int nb = H / 32;
+        const int64_t i = (int64_t)wg * GROUP_THREADS + tid;
+        if (i >= (int64_t)T * nb) return;
+        const uint16_t* p = x + (i / nb) * H + 32 * (i % nb);
+        float sum = 0.0f;
+        for (int e = 0; e < 32; ++e) sum += moe::bf16_to_f32(p[e]);
+        xbs[i] = sum;
+    }
+}
+
+// Workgroups the preparation of x takes in the sorting launch.
+__host__ __device__ inline int x_prep_wgs(int kind, int T, int H) {
+    return kind == XPREP_I8 ? T : kind == XPREP_BSUM ? (T * (H / 32) + GROUP_THREADS - 1) / GROUP_THREADS : 0;
+}
+
 // Stable counting sort of the P picks by slot.  Picks are taken 1024 at a
 // time; inside a wave the picks with the same slot are found with one ballot
 // per slot-id bit, their order is the lane order; per-wave counts are
@@ -237,7 +282,14 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
                                                          int32_t* __restrict__ slot_off, int32_t* __restrict__ pair_list,
                                                          int32_t* __restrict__ active, int32_t* __restrict__ n_active,
                                                          moe_pf_tile* __restrict__ pf_tiles,
-                                                         int32_t* __restrict__ pf_n_tiles, int pf_mt) {
+                                                         int32_t* __restrict__ pf_n_tiles, int pf_mt, int xprep,
+                                                         const uint16_t* __restrict__ x, int T, int H,
+                                                         int8_t* __restrict__ xq, float* __restrict__ xs,
+                                                         float* __restrict__ xbs) {
+    if (blockIdx.x > 0) {  // workgroups 1..: x for the gate/up kernel
+        x_prep_wg(xprep, blockIdx.x - 1, x, T, H, xq, xs, xbs);
+        return;
+    }
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
     __shared__ int ctot[MOE_MAX_S];
@@ -867,6 +919,12 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
 
     // decode-sized bf16 batches: the gate/up GEMM sorts the picks itself
     const bool fused_sort = use_pf && moe_pf_fused_sort(T, k);
+    // quantised batches sorted by one workgroup: x prepared in the same launch
+    int xprep = XPREP_NONE;
+    if (!use_pf && P <= GROUP_MULTI_P) {
+        if constexpr (F == MOE_W_W8A8) xprep = XPREP_I8;
+        if constexpr (F == MOE_W_Q4B32) xprep = XPREP_BSUM;
+    }
     if (fused_sort) {
         // no sort launch: the gate/up workgroups write the pick and tile lists
     } else if (P > GROUP_MULTI_P) {
@@ -878,8 +936,11 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
                            pair_list, active, n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k, S, H, I));
         if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
     } else {
-        hipLaunchKernelGGL(k_group, dim3(1), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, slot_off, pair_list, active,
-                           n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k, S, H, I));
+        hipLaunchKernelGGL(k_group, dim3(1 + x_prep_wgs(xprep, T, H)), dim3(GROUP_THREADS), 0, st, slot_ids, P, S,
+                           slot_off, pair_list, active, n_active, pf_tiles, pf_n_tiles,
+                           moe_pf_tile_rows(T, k, S, H, I), xprep, reinterpret_cast<const uint16_t*>(x), T, H,
+                           reinterpret_cast<int8_t*>(ws + L.xq), reinterpret_cast<float*>(ws + L.xs),
+                           reinterpret_cast<float*>(ws + L.xbs));
         if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
     }
 
@@ -899,17 +960,22 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     if constexpr (F == MOE_W_W8A8) {
         int8_t* xq = reinterpret_cast<int8_t*>(ws + L.xq);
         float* xs = reinterpret_cast<float*>(ws + L.xs);
-        hipLaunchKernelGGL((k_quant_rows<true>), dim3(T), dim3(256), 0, st, x, H, (const int32_t*)nullptr, xq, xs);
-        if ((rc = moe_check_launch("moe_ffn_slots/quant_x"))) return rc;
+        if (!xprep) {
+            hipLaunchKernelGGL((k_quant_rows<true>), dim3(T), dim3(256), 0, st, x, H, (const int32_t*)nullptr, xq,
+                               xs);
+            if ((rc = moe_check_launch("moe_ffn_slots/quant_x"))) return rc;
+        }
         gu_act = xq;
         xscale = xs;
     }
     if constexpr (F == MOE_W_Q4B32) {
         float* xbs = reinterpret_cast<float*>(ws + L.xbs);
-        const int64_t n = (int64_t)T * (H / 32);
-        hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                           reinterpret_cast<const uint16_t*>(x), T, H, (const int32_t*)nullptr, xbs);
-        if ((rc = moe_check_launch("moe_ffn_slots/block_sums_x"))) return rc;
+        if (!xprep) {
+            const int64_t n = (int64_t)T * (H / 32);
+            hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               reinterpret_cast<const uint16_t*>(x), T, H, (const int32_t*)nullptr, xbs);
+            if ((rc = moe_check_launch("moe_ffn_slots/block_sums_x"))) return rc;
+        }
         xbsum = xbs;
     }
 
