@@ -64,6 +64,9 @@ PROFILE_DIR = os.path.join(ROOT, "profiles")
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--replicate", type=int, default=0,
+                    help="run the benchmark this many times in fresh processes and print one line with the median "
+                         "value and the min-max of the headline figures")
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--batch", type=int, default=64, help="decode tokens per step (1, 8 or 64)")
@@ -96,6 +99,9 @@ def main():
         print(f"bench.py measures one GPU only: the expert-slot layer is a single-GPU path here "
               f"(--gpus {args.gpus} requested).", file=sys.stderr)
         sys.exit(2)
+    if args.replicate > 0:
+        replicate(args.replicate)
+        return
 
     import torch
 
@@ -750,21 +756,73 @@ def measure_gather(m, torch, synth):
             "slab_bytes": slab, "slabs_per_call": n, "link": "pinned hipMemcpyAsync H2D"}
 
 
-def cpu_baseline(synth, T, n_tok=128):
+def replicate(n):
+    """n fresh processes of this benchmark with the same arguments (each with
+    its own warm-up); one line: the first run's line with the median value and
+    step time, and min / median / max of the headline figures over the runs."""
+    import subprocess
+    argv = []
+    skip = False
+    for a in sys.argv[1:]:
+        if skip:
+            skip = False
+            continue
+        if a == "--replicate":
+            skip = True
+            continue
+        if a.startswith("--replicate="):
+            continue
+        argv.append(a)
+    lines = []
+    for i in range(n):
+        r = subprocess.run([sys.executable, os.path.abspath(__file__)] + argv, stdout=subprocess.PIPE, text=True)
+        if r.returncode != 0:
+            sys.exit(r.returncode)
+        lines.append(json.loads([l for l in r.stdout.splitlines() if l.startswith("{")][-1]))
+        print(f"run {i + 1}/{n}: {lines[-1].get('value')}", file=sys.stderr, flush=True)
+
+    def stats(get):
+        v = [get(d) for d in lines]
+        v = [x for x in v if x is not None]
+        return {"min": min(v), "median": float(np.median(v)), "max": max(v)} if v else None
+
+    out = dict(lines[0])
+    rep = {"runs": n, "value": stats(lambda d: d.get("value")), "ms_per_step": stats(lambda d: d.get("ms_per_step"))}
+    if "roofline" in out:
+        rep["roofline_frac"] = stats(lambda d: d["roofline"]["frac"])
+    for leg, key in (("prefill", "ffn_ms"), ("gather", "frac"), ("dynamic", "tokens_per_s")):
+        if isinstance(out.get(leg), dict) and key in out[leg]:
+            rep[f"{leg}_{key}"] = stats(lambda d, leg=leg, key=key: d[leg][key])
+    out["value"] = rep["value"]["median"]
+    out["ms_per_step"] = rep["ms_per_step"]["median"]
+    out["replicates"] = rep
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(synth, T, n_tok=48, reps=3):
     """The oracle (single-threaded C) on a bounded sample of the same workload:
     logits, top-k, weights and the full SwiGLU layer (every pick, resident or
-    not) for n_tok tokens of the same layer, on one thread."""
+    not) for n_tok tokens of the same layer, on one thread pinned to one core;
+    the median of reps samples."""
     import oracle
     li = synth.LayerInputs("c2", T=n_tok)
-    t0 = time.perf_counter()
-    z = oracle.logits(li.x, li.x_dtype, li.G)
-    ids = oracle.topk(z, li.k)
-    w = oracle.route_weights(z, ids)
-    oracle.layer(li.w_type, li.store, li.E, li.H, li.I, li.x, li.x_dtype, ids, w)
-    dt = time.perf_counter() - t0
+    cpus = sorted(os.sched_getaffinity(0))
+    os.sched_setaffinity(0, {cpus[-1]})
+    try:
+        dts = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            z = oracle.logits(li.x, li.x_dtype, li.G)
+            ids = oracle.topk(z, li.k)
+            w = oracle.route_weights(z, ids)
+            oracle.layer(li.w_type, li.store, li.E, li.H, li.I, li.x, li.x_dtype, ids, w)
+            dts.append(time.perf_counter() - t0)
+    finally:
+        os.sched_setaffinity(0, set(cpus))
+    dt = float(np.median(dts))
     return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
-            "sample": f"{n_tok} tokens of the same layer: route + full SwiGLU layer in double, single thread, "
-                      f"{dt:.1f} s"}
+            "sample": f"{n_tok} tokens of the same layer: route + full SwiGLU layer in double, one thread pinned "
+                      f"to one core, median of {reps} ({', '.join(f'{d:.1f}' for d in dts)} s)"}
 
 
 # ------------------------------------------------------------ HBM counters
