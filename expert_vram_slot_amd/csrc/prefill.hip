@@ -113,6 +113,7 @@ template <int MODE, int NB>
 __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     constexpr int HC = NB * 16;                          // gate/up: h columns per tile
     constexpr int B_BYTES = NB * 32 * PF_ROWB;           // B tile of one k-step
+    static_assert(NB >= 1 && NB <= 4, "the B rows are set up in the loop over the four A rows");
     extern __shared__ __attribute__((aligned(16))) unsigned char pf_lds[];
     // workgroup -> (tile, column tile): the column tiles of one token tile share an XCD
     const int b = blockIdx.x;
