@@ -113,7 +113,7 @@ template <int MODE, int NB>
 __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     constexpr int HC = NB * 16;                          // gate/up: h columns per tile
     constexpr int B_BYTES = NB * 32 * PF_ROWB;           // B tile of one k-step
-    static_assert(NB >= 1 && NB <= 4, "the B rows are set up in the loop over the four A rows");
+    static_assert(NB >= 1 && NB <= 8, "weight blocks per wave");
     extern __shared__ __attribute__((aligned(16))) unsigned char pf_lds[];
     // workgroup -> (tile, column tile): the column tiles of one token tile share an XCD
     const int b = blockIdx.x;
@@ -130,7 +130,7 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     const int lrow = tid >> 3, chunk = tid & 7;
     const unsigned char* arow[4];
     const unsigned char* brow[NB];
-    int soff[4];
+    int soff[4], bsoff[NB];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
         const int r = q * 32 + lrow;
@@ -141,18 +141,21 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
         else arow_idx = pos;                                             // h row in sorted order
         arow[q] = g.act + (size_t)arow_idx * row_bytes + chunk * 16;
         soff[q] = r * PF_ROWB + ((chunk ^ swz(r)) * 16);
-        if (q < NB) {
-            int wr;
-            int64_t plane;
-            if constexpr (MODE == PF_GU) {  // rows 0..HC-1 gate, HC..2HC-1 up, of h columns jn*HC ..
-                plane = r < HC ? g.w0 : g.w1;
-                wr = jn * HC + (r < HC ? r : r - HC);
-            } else {
-                plane = g.w0;
-                wr = jn * (NB * 32) + r;
-            }
-            brow[q < NB ? q : 0] = slab + plane + (size_t)wr * row_bytes + chunk * 16;
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q) {
+        const int r = q * 32 + lrow;
+        int wr;
+        int64_t plane;
+        if constexpr (MODE == PF_GU) {  // rows 0..HC-1 gate, HC..2HC-1 up, of h columns jn*HC ..
+            plane = r < HC ? g.w0 : g.w1;
+            wr = jn * HC + (r < HC ? r : r - HC);
+        } else {
+            plane = g.w0;
+            wr = jn * (NB * 32) + r;
         }
+        brow[q] = slab + plane + (size_t)wr * row_bytes + chunk * 16;
+        bsoff[q] = r * PF_ROWB + ((chunk ^ swz(r)) * 16);
     }
 
     // operand read offsets: A row wv*32 + lane%32, B rows nb*32 + lane%32; k half = lane/32
@@ -184,19 +187,17 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
         const int kr = kt + rot;
         const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            a[q] = ld16(arow[q] + ko);
-            if (q < NB) w[q < NB ? q : 0] = ld16_nt(brow[q < NB ? q : 0] + ko);
-        }
+        for (int q = 0; q < 4; ++q) a[q] = ld16(arow[q] + ko);
+#pragma unroll
+        for (int q = 0; q < NB; ++q) w[q] = ld16_nt(brow[q] + ko);
     };
     auto stash = [&](const v4u (&a)[4], const v4u (&w)[NB], int buf) {
         unsigned char* A = pf_lds + buf * (PF_TILE_BYTES + B_BYTES);
         unsigned char* B = A + PF_TILE_BYTES;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            *reinterpret_cast<v4u*>(A + soff[q]) = a[q];
-            if (q < NB) *reinterpret_cast<v4u*>(B + soff[q]) = w[q < NB ? q : 0];
-        }
+        for (int q = 0; q < 4; ++q) *reinterpret_cast<v4u*>(A + soff[q]) = a[q];
+#pragma unroll
+        for (int q = 0; q < NB; ++q) *reinterpret_cast<v4u*>(B + bsoff[q]) = w[q];
     };
     auto compute = [&](int buf) {
         if (!active_wave) return;
