@@ -859,9 +859,10 @@ __global__ void __launch_bounds__(256) k_block_sums(const uint16_t* __restrict__
 }
 
 // y[t][m] = sum_j part[t*k+j][m] over resident picks, j ascending; +0.0 if none.
-// The picks' rows are loaded eight at a time before any is added (a row of a
-// non-resident pick is read from an in-bounds row and not added), so a
-// thread waits on one round of loads per eight picks, not on every pick.
+// The picks' rows are loaded eight at a time before any is added, and their
+// addresses do not wait for the slot ids (the row of a non-resident pick is
+// read, in bounds, and not added), so a thread waits on one round of loads
+// per eight picks, not on the ids and then the rows.
 __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ part, const int32_t* __restrict__ slot_ids,
                                                 int T, int k, int S, int H, float* __restrict__ y) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // float4 index
@@ -877,7 +878,7 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ part, 
             const int j = j0 + u;
             const int sl = j < k ? slot_ids[t * k + j] : -1;
             ok[u] = sl >= 0 && sl < S;
-            const int64_t row = ok[u] ? (int64_t)(t * k + j) : (int64_t)t * k;
+            const int64_t row = (int64_t)t * k + (j < k ? j : 0);
             v[u] = reinterpret_cast<const float4*>(part + row * H)[m4];
         }
 #pragma unroll
