@@ -465,30 +465,51 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
 
 // Per row: scale = absmax / 127 (1 if the row is all zero), code =
 // clamp(rint(v / scale), -127, 127), in fp32.  Rows whose `valid` entry is
-// negative (picks not resident) are skipped.
+// negative (picks not resident) are skipped.  Rows of up to QR_VPT * 256
+// values are read once, into registers, and the row's loads do not wait for
+// its `valid` entry (the row is in bounds either way; a skipped row's values
+// are dropped), so the kernel waits on one round of loads.
+constexpr int QR_VPT = 8;
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256) k_quant_rows(const void* __restrict__ src, int len,
                                                     const int32_t* __restrict__ valid, int8_t* __restrict__ q,
                                                     float* __restrict__ scale) {
     __shared__ float red[4];
     const int row = blockIdx.x;
-    if (valid && valid[row] < 0) return;
+    const bool ok = !valid || valid[row] >= 0;
     auto val = [&](int i) -> float {
         if constexpr (SRC_BF16) return moe::bf16_to_f32(reinterpret_cast<const uint16_t*>(src)[(int64_t)row * len + i]);
         else return reinterpret_cast<const float*>(src)[(int64_t)row * len + i];
     };
+    const bool held = len <= QR_VPT * 256;
+    float v[QR_VPT];
     float m = 0.0f;
-    for (int i = threadIdx.x; i < len; i += 256) m = fmaxf(m, fabsf(val(i)));
+    if (held) {
+#pragma unroll
+        for (int u = 0; u < QR_VPT; ++u) {
+            const int i = threadIdx.x + 256 * u;
+            v[u] = i < len ? val(i) : 0.0f;
+            m = fmaxf(m, fabsf(v[u]));
+        }
+    } else {
+        for (int i = threadIdx.x; i < len; i += 256) m = fmaxf(m, fabsf(val(i)));
+    }
 #pragma unroll
     for (int s = 32; s >= 1; s >>= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
     __syncthreads();
+    if (!ok) return;  // the whole workgroup
     const float amax = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     const float sc = amax > 0.0f ? amax / 127.0f : 1.0f;
-    for (int i = threadIdx.x; i < len; i += 256) {
-        float c = rintf(val(i) / sc);
-        c = fminf(fmaxf(c, -127.0f), 127.0f);
-        q[(int64_t)row * len + i] = (int8_t)c;
+    auto code = [&](float x) { return (int8_t)fminf(fmaxf(rintf(x / sc), -127.0f), 127.0f); };
+    if (held) {
+#pragma unroll
+        for (int u = 0; u < QR_VPT; ++u) {
+            const int i = threadIdx.x + 256 * u;
+            if (i < len) q[(int64_t)row * len + i] = code(v[u]);
+        }
+    } else {
+        for (int i = threadIdx.x; i < len; i += 256) q[(int64_t)row * len + i] = code(val(i));
     }
     if (threadIdx.x == 0) scale[row] = sc;
 }
@@ -844,18 +865,27 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
 }
 
 // Per-block sums of rows of bf16 activations, for 4-bit weights: out[r][b] =
-// sum of row r's inputs 32b .. 32b+31 (fp32, in input order).
+// sum of row r's inputs 32b .. 32b+31 (fp32, in input order).  The block is
+// read as four 16-byte loads that do not wait for the row's `valid` entry
+// (in bounds either way; a skipped row's sum is not stored).
 __global__ void __launch_bounds__(256) k_block_sums(const uint16_t* __restrict__ src, int rows, int len,
                                                     const int32_t* __restrict__ valid, float* __restrict__ out) {
     const int nb = len / 32;
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i >= (int64_t)rows * nb) return;
     const int r = (int)(i / nb), b = (int)(i % nb);
-    if (valid && valid[r] < 0) return;
-    const uint16_t* p = src + (int64_t)r * len + 32 * b;
+    const bool ok = !valid || valid[r] >= 0;
+    const v4u* p = reinterpret_cast<const v4u*>(src + (int64_t)r * len + 32 * b);
+    v4u g[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) g[c] = p[c];
     float sum = 0.0f;
-    for (int e = 0; e < 32; ++e) sum += moe::bf16_to_f32(p[e]);
-    out[i] = sum;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) sum += moe::bf16_to_f32((uint16_t)(g[c][e >> 1] >> (16 * (e & 1))));
+    }
+    if (ok) out[i] = sum;
 }
 
 // y[t][m] = sum_j part[t*k+j][m] over resident picks, j ascending; +0.0 if none.
