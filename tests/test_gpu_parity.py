@@ -548,11 +548,13 @@ def test_ffn_workspace_reused_across_calls(m):
         assert_close(host(y), yg, 1, f"reused workspace T={li.T}")
 
 
-@pytest.mark.parametrize("T,S", [(300, 20), (257, 24), (1000, 17)])
-def test_ffn_prefill_grouped_gemm(m, T, S):
-    """bf16 batches of >= 2048 picks run on the MFMA grouped GEMM: slots with
-    more picks than one 128-row tile, ragged tiles, non-resident experts."""
-    E, k, H, I = 24, 8, 256, 384
+@pytest.mark.parametrize("T,S,H", [(300, 20, 256), (257, 24, 256), (1000, 17, 256), (600, 20, 384)])
+def test_ffn_prefill_grouped_gemm(m, T, S, H):
+    """bf16 batches of >= 512 picks run on the MFMA grouped GEMMs: slots with
+    more picks than one tile, ragged tiles, non-resident experts; from 4096
+    picks the 128-row tiles, with eight 32-row weight blocks per wave when H is
+    a multiple of 256 and four otherwise."""
+    E, k, I = 24, 8, 384
     rng = np.random.default_rng(T + S)
     x = synth.normal(synth.key(7, 1, T), (T, H), 1.0, 1)
     store = synth.slabs(1, 555, 0, 0, E, H, I, 0.05)
