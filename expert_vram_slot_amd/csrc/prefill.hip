@@ -21,7 +21,8 @@
 //   k_reduce     y[t] = sum over resident picks in top-k order (decode path's)
 //
 // Prefill-sized batches (4096 picks and more): a workgroup owns PF_MT = 128
-// token rows x NB * 32 weight rows (NB = 4) and walks K in steps of 64.
+// token rows x NB * 32 weight rows (NB = 8 when H is a multiple of 256, else 4)
+// and walks K in steps of 64.
 // Decode-sized batches (a few picks per slot) use k_dec_gemm below: 32 token
 // rows, each wave a 32-row weight block.  Each k-step is fetched into
 // registers two steps ahead and stored to one of two LDS buffers; 16-byte
@@ -105,6 +106,16 @@ struct PfArgs {
 };
 
 __device__ __forceinline__ v4u ld16(const unsigned char* p) { return *reinterpret_cast<const v4u*>(p); }
+
+// Barrier of the two LDS buffers of a k-loop: waits for this wave's LDS
+// stores and reads (lgkmcnt 0), then a bare s_barrier.  Loads from memory
+// into registers stay in flight across it (a fence here would wait for every
+// one of them, the ones of later k-steps too); the compiler waits for each
+// where its registers are stored to LDS.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(0xc07f);  // vmcnt 63, expcnt 7: no wait; lgkmcnt 0
+    asm volatile("s_barrier" ::: "memory");
+}
 __device__ __forceinline__ v4u ld16_nt(const unsigned char* p) {
     return __builtin_nontemporal_load(reinterpret_cast<const v4u*>(p));
 }
@@ -220,21 +231,21 @@ __global__ void __launch_bounds__(PF_THREADS) k_pf_gemm(PfArgs g) {
     fetch(ra[0], rb[0], 0);
     fetch(ra[1], rb[1], 1);
     stash(ra[0], rb[0], 0);
-    __syncthreads();
+    lds_barrier();
     for (int kt = 0; kt + 2 < nk; kt += 2) {
         fetch(ra[0], rb[0], kt + 2);  // buffer 0 holds step kt, registers 1 hold kt + 1
         compute(0);
         stash(ra[1], rb[1], 1);
-        __syncthreads();
+        lds_barrier();
         fetch(ra[1], rb[1], kt + 3);  // buffer 1 holds kt + 1, registers 0 hold kt + 2
         compute(1);
         stash(ra[0], rb[0], 0);
-        __syncthreads();
+        lds_barrier();
     }
     // last two steps: buffer 0 holds nk - 2, registers 1 hold nk - 1
     compute(0);
     stash(ra[1], rb[1], 1);
-    __syncthreads();
+    lds_barrier();
     compute(1);
 
     if (!active_wave) return;
@@ -480,12 +491,12 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     for (int r = 0; r < NR; ++r)
         if (r < nk) fetch(ra[r], rb[r], r);
     stash(ra[0], rb[0], 0);
-    __syncthreads();
+    lds_barrier();
     auto step = [&](int j, int t, bool tail) {  // j = t % U, static in every caller
         if (!tail || t + NR < nk) fetch(ra[j % NR], rb[j % NR], t + NR);  // set j % NR went to LDS last step
         compute(j % 2);
         if (!tail || t + 1 < nk) stash(ra[(j + 1) % NR], rb[(j + 1) % NR], (j + 1) % 2);
-        __syncthreads();
+        lds_barrier();
     };
     int kt = 0;
     for (; kt + U + NR <= nk; kt += U) {  // every fetch of these steps is in range
@@ -921,7 +932,7 @@ int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_sto
         return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
                          part, st);
     // eight 32-row weight blocks per wave where the output columns come in
-    // 256s (fewer, longer workgroups: the 2048-token layer 2.07 -> 2.02 ms)
+    // 256s (fewer, longer workgroups: the 2048-token layer 2.06 -> 2.02 ms)
     if (H % 256 == 0)
         return pf_launch<8>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
                             part, st);
