@@ -467,9 +467,11 @@ def test_ffn_slots_matches_oracle(m, cfg, T):
 
 
 @pytest.mark.parametrize("w_type,H,I", [(1, 112, 144), (1, 1040, 784), (0, 80, 48), (2, 1040, 784),
-                                        (3, 1056, 544)])
+                                        (2, 2320, 2080), (3, 1056, 544)])
 def test_ffn_ragged_shapes(m, w_type, H, I):
-    """Row tiles with a ragged tail and rows whose granules do not fill the waves."""
+    """Row tiles with a ragged tail and rows whose granules do not fill the waves;
+    W8A8 with h rows longer than 2048 (quantised without holding the row in
+    registers)."""
     E, k, T, S = 12, 3, 11, 7
     rng = np.random.default_rng(H + I)
     x_dtype = 0 if w_type == 0 else 1
@@ -488,11 +490,13 @@ def test_ffn_ragged_shapes(m, w_type, H, I):
     assert_close(y, yg, w_type, f"w{w_type} H={H} I={I}")
 
 
-@pytest.mark.parametrize("w_type,T", [(1, 401), (2, 401), (2, 1500), (0, 1700)])
-def test_ffn_large_batch_sorted_picks(m, w_type, T):
+@pytest.mark.parametrize("w_type,T,H", [(1, 401, 112), (2, 401, 112), (2, 1500, 112), (0, 1700, 112),
+                                        (2, 1400, 2112)])
+def test_ffn_large_batch_sorted_picks(m, w_type, T, H):
     """Large batches on the row-streaming path: one sorting workgroup up to
-    4096 picks, one per 1024 picks above."""
-    E, k, S, H, I = 12, 3, 7, 112, 144
+    4096 picks, one per 1024 picks above (then x is quantised by a launch of
+    its own, for H = 2112 without holding the row in registers)."""
+    E, k, S, I = 12, 3, 7, 144
     rng = np.random.default_rng(17 + w_type)
     x_dtype = 0 if w_type == 0 else 1
     x = synth.normal(synth.key(99, 1, w_type), (T, H), 1.0, x_dtype)
