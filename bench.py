@@ -85,6 +85,9 @@ def parse():
                                                      "COPY_WRITE_DIR"),
                     help="write a text summary of rocprofv3 CSV output (kernel trace + FETCH_SIZE/WRITE_SIZE runs of "
                          "this benchmark and of --copy-calibration) to --out; no GPU needed")
+    ap.add_argument("--summarize-prefill", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                              "COPY_WRITE_DIR"), default=None,
+                    help="write the prefill kernels' summary (2048- and 16384-token legs) from the same runs")
     ap.add_argument("--out", default=None, help="summary file for --summarize")
     ap.add_argument("--commands", default=None, help="text file with the profiling commands, quoted in the summary")
     return ap.parse_args()
@@ -94,6 +97,9 @@ def main():
     args = parse()
     if args.summarize:
         summarize(args)
+        return
+    if args.summarize_prefill:
+        summarize_prefill(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: the expert-slot layer is a single-GPU path here "
@@ -980,6 +986,81 @@ def summarize(args):
     lines.append("")
     lines.append("record: " + json.dumps(rec))
     out = args.out or profile_path(T)
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {out}")
+
+
+def summarize_prefill(args):
+    """Per-kernel time, HBM counters and algorithmic bytes of the prefill legs
+    (the 288-expert layer at 2048 and 16384 tokens) from the runs that
+    --summarize reads.  A k_reduce dispatch belongs to a leg by its grid."""
+    tr, fe, wr, cfe, cwr = args.summarize_prefill
+    import synth
+    c = synth.CONFIGS["c5"]
+    E, k, H, I = c["E"], c["k"], c["H"], c["I"]
+    trace = _csv_rows(tr, "kernel_trace.csv")
+    frows = [r for r in _csv_rows(fe, "counter_collection.csv") if r["Counter_Name"] == "FETCH_SIZE"]
+    wrows = [r for r in _csv_rows(wr, "counter_collection.csv") if r["Counter_Name"] == "WRITE_SIZE"]
+    cfetch = _counter_per_dispatch(_csv_rows(cfe, "counter_collection.csv"), "FETCH_SIZE")
+    cwrite = _counter_per_dispatch(_csv_rows(cwr, "counter_collection.csv"), "WRITE_SIZE")
+
+    def copy_kib(per):
+        return float(np.median([v for vs in per.values() for v in vs if v > 100_000]))
+
+    gib_kib = (1 << 30) / 1024.0
+    f_fetch, f_write = gib_kib / copy_kib(cfetch), gib_kib / copy_kib(cwrite)
+    w_gu, w_dn = E * 2 * I * H * 2, E * H * I * 2  # every expert is resident and picked at both sizes
+    legs = []
+    for T in (2048, 16384):
+        P = T * k
+        big = T == 16384
+        gu, dn = ("k_pf_wide<0>", "k_pf_wide<1>") if big else ("k_pf_gemm<0, 8>", "k_pf_gemm<1, 8>")
+        legs.append((T, [
+            (gu, w_gu + T * H * 2 + P * I * 2, 2.0 * P * 2 * I * H, None),
+            (dn, w_dn + P * I * 2 + P * H * 4, 2.0 * P * H * I, None),
+            ("k_reduce", P * H * 4 + T * H * 4, 0.0, T * H // 4),
+        ]))
+
+    def pick(rows, name, grid, grid_key):
+        out = []
+        for r in rows:
+            if _short(r["Kernel_Name"]) != name:
+                continue
+            if grid is not None and int(r[grid_key]) != grid:
+                continue
+            out.append(r)
+        return out
+
+    lines = ["rocprofv3 summary: moe_ffn_slots prefill legs, 288-expert bf16 layer (H=4096, I=1536, top-8, "
+             "all experts resident) at 2048 and 16384 tokens", ""]
+    if args.commands:
+        lines.append("commands (run from the repository root on one MI355X; TMPDIR=/tmp):")
+        with open(args.commands) as fh:
+            lines.extend("  " + l.rstrip() for l in fh if l.strip())
+        lines.append("")
+    lines.append(f"HBM counters scaled by a 1 GiB copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}. "
+                 "Algorithmic bytes: weights once, activations in and out once (x, h, fp32 partials, y).")
+    for T, ks in legs:
+        lines.append("")
+        lines.append(f"{T} tokens ({T * k} picks):")
+        lines.append(f"  {'kernel':<18}{'calls':>6}{'avg us':>10}{'HBM GB':>9}{'alg GB':>9}{'HBM/alg':>9}"
+                     f"{'alg GB/s':>10}{'TFLOP/s':>9}")
+        for name, alg, flops, grid in ks:
+            tr_rows = pick(trace, name, None if grid is None else grid, "Grid_Size_X")
+            f_rows = pick(frows, name, grid, "Grid_Size")
+            w_rows = pick(wrows, name, grid, "Grid_Size")
+            if not tr_rows:
+                continue
+            us = float(np.mean([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr_rows]))
+            fv = float(np.mean([float(r["Counter_Value"]) for r in f_rows])) if f_rows else 0.0
+            wv = float(np.mean([float(r["Counter_Value"]) for r in w_rows])) if w_rows else 0.0
+            hbm = (fv * f_fetch + wv * f_write) * 1024
+            tfs = f"{flops / us / 1e6:>9.1f}" if flops else f"{'':>9}"
+            lines.append(f"  {name:<18}{len(tr_rows):>6}{us:>10.1f}{hbm / 1e9:>9.2f}{alg / 1e9:>9.2f}"
+                         f"{hbm / alg:>9.2f}{alg / us / 1e3:>10.0f}{tfs}")
+    out = args.out or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                                   "moe_ffn_slots_bf16_prefill_c5.txt")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
