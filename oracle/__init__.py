@@ -13,7 +13,9 @@ import subprocess
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_SO = os.path.join(_HERE, "liboracle.so")
+# MOE_ORACLE_LIB points the wrapper at another build of oracle.c (the
+# mutation test loads copies with planted mistakes this way).
+_SO = os.environ.get("MOE_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _SRC = os.path.join(_HERE, "oracle.c")
 
 STATIC, LRU, LFU = 0, 1, 2
@@ -22,6 +24,8 @@ POLICIES = {"static": STATIC, "lru": LRU, "lfu": LFU}
 
 def build(force: bool = False) -> str:
     """Compile liboracle.so with gcc: no fast-math, no FMA contraction."""
+    if os.environ.get("MOE_ORACLE_LIB"):
+        return _SO
     if force or not os.path.exists(_SO) or os.path.getmtime(_SO) < max(
             os.path.getmtime(_SRC), os.path.getmtime(os.path.join(_HERE, "oracle.h"))):
         tmp = _SO + ".tmp"

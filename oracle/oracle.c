@@ -191,7 +191,9 @@ int oracle_bias_table(const double* b, int E, int n_hot, float cap, float* bias)
 
 /* Top-k by logit + bias, [PGO] "The method in five lines".  The score is one
  * fp32 add; the k best are taken one at a time (higher score first, then the
- * lower expert id) and listed in that order. */
+ * lower expert id) and listed in that order.  Scores must be free of NaN (the
+ * callers' inputs are finite): a NaN never compares greater, so its rank here
+ * would depend on where it sits rather than follow any order. */
 int oracle_topk(const float* z, const float* bias, int T, int E, int k, int32_t* ids) {
     if (k < 1 || k > E) return -1;
     float* s = (float*)malloc(sizeof(float) * (size_t)E);

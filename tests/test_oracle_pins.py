@@ -538,8 +538,17 @@ def test_repick_swaps_only_what_went_cold():
         old = r.choice(E, S, replace=False)
         new = r.choice(E, S, replace=False)
         c = oracle.Cache(E, S, "static", resident=old)
-        slots_before = c.e2s.copy()
+        c.last[:] = r.integers(1, 1000, S)
+        c.freq[:] = r.integers(1, 1000, S)
+        c.step[0] = 4321
+        slots_before, last_before, freq_before = c.e2s.copy(), c.last.copy(), c.freq.copy()
         loads = c.repick(new)
+        # a loaded slot restarts (last = the current step, no uses); a kept slot keeps its record;
+        # a repick is not a step
+        ls = loads[:, 1]
+        assert np.all(c.last[ls] == 4321) and np.all(c.freq[ls] == 0) and c.step[0] == 4321
+        keep = np.setdiff1d(np.arange(S), ls)
+        assert np.array_equal(c.last[keep], last_before[keep]) and np.array_equal(c.freq[keep], freq_before[keep])
         assert set(np.flatnonzero(c.e2s >= 0)) == set(new.tolist())
         assert sorted(c.s2e.tolist()) == sorted(new.tolist())
         assert np.all(c.e2s[c.s2e] == np.arange(S))
@@ -641,28 +650,69 @@ def test_expert_w8a8_close_to_dequantised_dense():
         assert np.sqrt(np.mean((o - ref) ** 2)) <= 0.02 * rms
 
 
-def test_expert_w8a8_integer_accumulators_exact():
-    """With h-side scales of 1 the down projection is an exact integer dot."""
-    H, I = 64, 32
-    # hand-built int8 slab: gate/up rows chosen so h lands on integers
-    wq = rng.integers(-127, 128, size=(3, max(H, I) * max(H, I)))
-    slab = np.zeros(oracle.slab_bytes(2, H, I), np.uint8)
-    n = H * I
-    for p in range(3):
-        slab[p * n:(p + 1) * n] = wq[p, :n].astype(np.int8).view(np.uint8)
-    scales = np.ones(2 * I + H, np.float32)
-    slab[3 * n:] = scales.view(np.uint8)
-    x = synth.f32_to_bf16(rng.integers(-127, 128, size=H).astype(np.float32))  # exact in bf16, absmax -> scale
-    o = oracle.expert(2, slab, H, I, x, 1)
-    xq = synth.bf16_to_f32(x).astype(np.float64)
-    amax = np.abs(xq).max()
-    sx = np.float32(amax) / np.float32(127.0)
-    qx = np.clip(np.rint(xq / np.float64(sx)), -127, 127)
-    wgq = wq[0, :n].reshape(I, H).astype(np.int64)
-    acc = wgq @ qx.astype(np.int64)
-    assert np.all(np.abs(acc) < 2 ** 31)
-    # gate dequant is (float)acc * sx * 1 -> check the oracle's g via a k=1 layer is consistent in sign pattern
-    assert o.shape == (H,) and np.all(np.isfinite(o))
+def _w8a8_hand_slab():
+    """A 4 x 4 W8A8 expert whose every intermediate value is an exact integer.
+
+    Gate codes pick x's second element with large multipliers, so every gate
+    pre-activation is >= 41 and silu(g) == g exactly in double (e^-41 is below
+    half an ulp of 1).  Scales: gate 1, up (0.5, 1, 1, 1), down (0.5, 1, 2,
+    0.25) -- distinct, so a plane or index mix-up changes the result."""
+    H = I = 4
+    wg = np.array([[1, 0, 0, 0], [0, 41, 0, 0], [0, 43, 0, 0], [0, 45, 0, 0]], np.int8)
+    wu = np.array([[0, 4, 0, 0], [0, 1, 0, 0], [0, 1, 0, 2], [0, -1, 7, 0]], np.int8)
+    wd = np.array([[1, 0, 0, 0], [0, 1, 1, 0], [0, 0, 1, 1], [-1, 2, -3, 5]], np.int8)
+    sg = np.array([1, 1, 1, 1], np.float32)
+    su = np.array([0.5, 1, 1, 1], np.float32)
+    sd = np.array([0.5, 1, 2, 0.25], np.float32)
+    slab = np.concatenate([wg.reshape(-1).view(np.uint8), wu.reshape(-1).view(np.uint8),
+                           wd.reshape(-1).view(np.uint8), sg.view(np.uint8), su.view(np.uint8), sd.view(np.uint8)])
+    assert slab.size == oracle.slab_bytes(2, H, I)
+    return slab, H, I
+
+
+def test_expert_w8a8_exact_hand_derived():
+    """W8A8 arithmetic pinned to values worked out by hand (BASELINE config 3:
+    int8 weights with per-output-channel fp32 scales, per-token int8
+    activations; reading: scale absmax/127, round half to even, clamp 127,
+    h requantised per (token, pick) row).
+
+    token 0: x = (127, 1, 0, 0): absmax 127 -> s_x = 1, codes = x.
+      g = (127, 41, 43, 45); u = (4*0.5, 1, 1, -1) = (2, 1, 1, -1)
+      h = g*u = (254, 41, 43, -45); s_h = 254/127 = 2
+      h/s_h = (127, 20.5, 21.5, -22.5) -> half to even (127, 20, 22, -22)
+      down acc = (127, 20+22, 22-22, -127+40-66-110) = (127, 42, 0, -263)
+      o = acc * 2 * (0.5, 1, 2, 0.25) = (127, 84, 0, -131.5)
+    token 1: x = (254, 2, 1, 3): absmax 254 -> s_x = 2,
+      x/s_x = (127, 1, 0.5, 1.5) -> codes (127, 1, 0, 2)
+      g = 2*(127, 41, 43, 45) = (254, 82, 86, 90)
+      u acc = (4, 1, 1+2*2, -1+7*0) = (4, 1, 5, -1); u = acc*2*s_u = (4, 2, 10, -2)
+      h = (1016, 164, 860, -180); s_h = 1016/127 = 8
+      h/s_h = (127, 20.5, 107.5, -22.5) -> (127, 20, 108, -22)
+      down acc = (127, 128, 86, -127+40-324-110) = (127, 128, 86, -521)
+      o = acc * 8 * s_d = (508, 1024, 1376, -1042)
+    A truncating quantiser (21.5 -> 21), half away from zero (20.5 -> 21),
+    a /128 scale, a per-tensor activation scale (token 0 would get s_x = 2
+    and codes 63.5 -> 64) or an h scale shared by the tokens each change at
+    least one of these outputs."""
+    slab, H, I = _w8a8_hand_slab()
+    x = synth.f32_to_bf16(np.array([[127, 1, 0, 0], [254, 2, 1, 3]], np.float32))
+    want = np.array([[127, 84, 0, -131.5], [508, 1024, 1376, -1042]], np.float64)
+    for t in range(2):
+        o = oracle.expert(2, slab, H, I, x[t], 1)
+        assert np.array_equal(o, want[t]), (t, o, want[t])
+    # the same through the layer: one expert, k = 1, w = 1, both tokens in one call
+    yf, yg, yh = oracle.layer(2, slab[None, :], 1, H, I, x, 1, np.zeros((2, 1), np.int32),
+                              np.ones((2, 1), np.float32), slot_ids=np.zeros((2, 1), np.int32))
+    assert np.array_equal(yf, want.astype(np.float32))
+    assert np.array_equal(yg, want.astype(np.float32)) and np.all(yh == 0)
+
+
+def test_expert_w8a8_zero_row_takes_scale_one():
+    """An all-zero activation row takes scale 1 (codes 0): the output is +0,
+    not NaN from 0/0."""
+    slab, H, I = _w8a8_hand_slab()
+    o = oracle.expert(2, slab, H, I, np.zeros(H, np.uint16), 1)
+    assert np.all(o == 0) and not np.any(np.signbit(o))
 
 
 @pytest.mark.parametrize("w_type", [0, 1, 2, 3])
