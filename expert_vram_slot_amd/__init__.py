@@ -13,7 +13,10 @@ import ctypes
 import os
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "lib", "libmoeslot.so")
+# MOE_SLOT_LIB points the binding at another build of the same sources (the
+# host-sanitized build that the CPU tests load); by default, the in-tree one.
+_LIB_DEFAULT = os.path.join(_HERE, "lib", "libmoeslot.so")
+LIB_PATH = os.environ.get("MOE_SLOT_LIB") or _LIB_DEFAULT
 
 MOE_OK = 0
 MOE_E_ARG, MOE_E_ALIGN, MOE_E_DTYPE, MOE_E_SHAPE, MOE_E_HIP, MOE_E_NOMEM = -1, -2, -3, -4, -5, -6
@@ -82,8 +85,9 @@ def lib():
             "moe_step_destroy": (None, [vp]),
             "moe_step_output": (vp, [vp]),
             "moe_step_stats": (i32, [vp, ctypes.POINTER(ctypes.c_int64), i32]),
-            "moe_layer_step": (i32, [vp, ctypes.POINTER(LayerDesc), vp, i32, vp, i32, i32, vp, vp, vp, vp]),
-            "moe_stack_step": (i32, [vp, ctypes.POINTER(LayerDesc), i32, vp, i32, i32, i32, vp, vp, vp, vp]),
+            "moe_layer_step": (i32, [vp, ctypes.POINTER(LayerDesc), vp, i32, vp, i32, i32, vp, vp, vp]),
+            "moe_stack_step": (i32, [vp, ctypes.POINTER(LayerDesc), i32, vp, i32, i32, i32, vp, vp, vp]),
+            "moe_fused_spin_limit": (ctypes.c_int64, [ctypes.c_int64]),
             "moe_host_alloc": (vp, [sz]),
             "moe_host_free": (i32, [vp]),
         }
@@ -248,15 +252,21 @@ def moe_step_stats(h, reset=False):
     return [int(v) for v in out]
 
 
-def moe_layer_step(h, desc, x, T, ids_in, host_pass, n_threads, y_out, s0, s_side, s_copy):
+def moe_layer_step(h, desc, x, T, ids_in, host_pass, n_threads, y_out, s0, s_copy):
     return _check("moe_layer_step", lib().moe_layer_step(h, ctypes.byref(desc), _p(x), T, _p(ids_in),
                                                          int(host_pass), n_threads, _p(y_out), _stream(s0),
-                                                         _stream(s_side), _stream(s_copy)))
+                                                         _stream(s_copy)))
 
 
-def moe_stack_step(h, descs, x, T, host_pass, n_threads, x_out, s0, s_side, s_copy):
+def moe_stack_step(h, descs, x, T, host_pass, n_threads, x_out, s0, s_copy):
     return _check("moe_stack_step", lib().moe_stack_step(h, descs, len(descs), _p(x), T, int(host_pass), n_threads,
-                                                         _p(x_out), _stream(s0), _stream(s_side), _stream(s_copy)))
+                                                         _p(x_out), _stream(s0), _stream(s_copy)))
+
+
+def moe_fused_spin_limit(polls: int = -1) -> int:
+    """Polls of cache_manage_gather's copying workgroups before they give up;
+    polls >= 0 sets it, < 0 queries.  Returns the previous limit."""
+    return int(lib().moe_fused_spin_limit(int(polls)))
 
 
 def moe_host_alloc(nbytes: int) -> int:

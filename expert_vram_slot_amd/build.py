@@ -29,6 +29,14 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-I" + os.path.join(ROOT, "include"), "-
 DEVICE = ["-x", "hip", f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
           "-ffp-contract=fast"]
 HOST = ["-x", "c++", "-I/opt/rocm/include", "-D__HIP_PLATFORM_AMD__", "-mf16c", "-mavx2", "-mfma", "-pthread"]
+# AddressSanitizer + UndefinedBehaviorSanitizer on the host code only (the CPU
+# host pass, the driver, argument checks); device code is built as usual.
+# Each -fsanitize= goes right after -Xarch_host so that no GPU code is built
+# with it.  The sanitized library is for CPU test runs, never for a GPU run.
+SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+            "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer"]
+SAN_DIR = os.path.join(ROOT, "_build", "sanitized")
+SAN_LIB = os.path.join(SAN_DIR, "libmoeslot.so")
 
 
 def exported_api() -> list[str]:
@@ -39,9 +47,9 @@ def exported_api() -> list[str]:
     return sorted(set(n for n in names if n not in ("if", "while", "return")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(OBJ_DIR, os.path.basename(src) + ".o")
-    flags = COMMON + (DEVICE if src.endswith(".hip") else HOST)
+def _compile(src: str, obj_dir: str = OBJ_DIR, extra=()) -> str:
+    obj = os.path.join(obj_dir, os.path.basename(src) + ".o")
+    flags = COMMON + (DEVICE if src.endswith(".hip") else HOST) + list(extra)
     cmd = [HIPCC] + flags + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
@@ -49,22 +57,30 @@ def _compile(src: str) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(OUT_DIR, exist_ok=True)
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build the library; sanitize=True builds the host code under ASan/UBSan
+    into _build/sanitized/ instead (load it with the sanitizer runtime
+    preloaded; MOE_SLOT_LIB points the binding at it)."""
+    out = SAN_LIB if sanitize else LIB
+    obj_dir = os.path.join(SAN_DIR, "obj") if sanitize else OBJ_DIR
+    extra = SANITIZE if sanitize else []
+    os.makedirs(os.path.dirname(out), exist_ok=True)
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith((".hip", ".cpp")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
+        objs = list(ex.map(lambda src: _compile(src, obj_dir, extra), srcs))
+    tmp = out + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs + ["-pthread"]
+    if sanitize:
+        cmd += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-shared-libasan"]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     check_exports(tmp)
-    os.replace(tmp, LIB)
+    os.replace(tmp, out)
     if verbose:
-        print("built", LIB)
-    return LIB
+        print("built", out)
+    return out
 
 
 def check_exports(path: str) -> None:

@@ -8,6 +8,8 @@
 // remapped to slot space.  Section "Prove it is correct before measuring":
 // the manager is deterministic (no atomics, no order-dependent reduction) and
 // the gather reads pinned host memory from the device in 16-byte units.
+#include <atomic>
+
 #include "common.hpp"
 
 namespace {
@@ -331,13 +333,19 @@ __device__ __forceinline__ void gather_core(const int32_t* __restrict__ miss, in
     }
 }
 
-constexpr uint32_t FUSED_SPIN_MAX = 1u << 22;  // polls of the hand-off word before a copying workgroup gives up
+// Polls of the hand-off word before a copying workgroup of the fused cache
+// step gives up (moe_fused_spin_limit changes it; 0 makes every copying
+// workgroup give up at once, which tests the reporting of that case).
+std::atomic<uint32_t> g_fused_spin_limit{1u << 22};
 
 // Fused cache step.  Workgroup 0 runs the cache step; its first wave then
 // mirrors the picks to pinned host memory and rings the doorbell (system-scope
 // release), and thread 0 releases the hand-off word (device scope).  The
-// other workgroups wait for the hand-off (a bounded number of polls) and all
-// of them copy the missing slabs.
+// other workgroups wait for the hand-off (at most spin_max polls) and all of
+// them copy the missing slabs.  A workgroup that stops waiting copies nothing
+// and says so in sync[1] (device) and in the doorbell's err word (pinned host
+// memory, system scope); both words are only ever set here, never cleared, so
+// a late managing workgroup cannot hide the report.
 __global__ void __launch_bounds__(MANAGE_THREADS) k_manage_gather(
     int32_t* __restrict__ e2s, int32_t* __restrict__ s2e, uint32_t* __restrict__ last, uint32_t* __restrict__ freq,
     uint32_t* __restrict__ stepp, int E, int S, int policy, const int32_t* __restrict__ ids, int n_ids,
@@ -345,7 +353,7 @@ __global__ void __launch_bounds__(MANAGE_THREADS) k_manage_gather(
     int32_t* __restrict__ n_miss, int32_t* __restrict__ host_miss, int32_t* __restrict__ n_host,
     int32_t* __restrict__ stats, const unsigned char* __restrict__ host, unsigned char* __restrict__ slots,
     uint64_t slab_bytes, int32_t* __restrict__ sync, int32_t seq, moe_doorbell* __restrict__ bell,
-    int32_t* __restrict__ bell_ids, int32_t* __restrict__ bell_slots, float* __restrict__ bell_w) {
+    int32_t* __restrict__ bell_ids, int32_t* __restrict__ bell_slots, float* __restrict__ bell_w, uint32_t spin_max) {
     __shared__ int ok;
     const int tid = threadIdx.x;
     if (blockIdx.x == 0) {
@@ -365,7 +373,6 @@ __global__ void __launch_bounds__(MANAGE_THREADS) k_manage_gather(
                     bell->n_miss = *n_miss;
                     bell->n_host = *n_host;
                     for (int q = 0; q < 4; ++q) bell->stats[q] = stats ? stats[q] : 0;
-                    bell->err = 0;
                 }
                 __threadfence_system();  // every lane's mirror stores before the doorbell
                 if (tid == 0) __hip_atomic_store(&bell->seq, seq, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
@@ -376,13 +383,16 @@ __global__ void __launch_bounds__(MANAGE_THREADS) k_manage_gather(
     } else if (tid == 0) {
         int v = 0;
         uint32_t n = 0;
-        for (; n < FUSED_SPIN_MAX; ++n) {
+        for (; n < spin_max; ++n) {
             v = __hip_atomic_load(&sync[0], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
             if (v == seq) break;
             __builtin_amdgcn_s_sleep(2);
         }
         ok = v == seq;
-        if (!ok) atomicOr(&sync[1], 1);
+        if (!ok) {
+            atomicOr(&sync[1], 1);
+            if (bell) __hip_atomic_store(&bell->err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        }
     }
     __syncthreads();
     if (!ok || policy == MOE_STATIC) return;
@@ -486,8 +496,15 @@ int cache_manage_gather(const moe_cache_state* st, int policy, const int32_t* id
                        st->freq, st->step, st->E, st->S, policy, ids, n_ids, w, slot_ids, miss, n_miss, host_miss,
                        n_host, stats, dev_host, reinterpret_cast<unsigned char*>(slot_store), (uint64_t)slab_bytes,
                        sync, seq, reinterpret_cast<moe_doorbell*>(dptr[0]), reinterpret_cast<int32_t*>(dptr[1]),
-                       reinterpret_cast<int32_t*>(dptr[2]), reinterpret_cast<float*>(dptr[3]));
+                       reinterpret_cast<int32_t*>(dptr[2]), reinterpret_cast<float*>(dptr[3]),
+                       g_fused_spin_limit.load(std::memory_order_relaxed));
     return moe_check_launch("cache_manage_gather");
+}
+
+int64_t moe_fused_spin_limit(int64_t polls) {
+    if (polls > (int64_t)UINT32_MAX) polls = UINT32_MAX;
+    if (polls < 0) return g_fused_spin_limit.load();
+    return g_fused_spin_limit.exchange((uint32_t)polls);
 }
 
 int cache_repick(const moe_cache_state* st, const int32_t* want, int32_t* miss, int32_t* n_miss, hipStream_t stream) {

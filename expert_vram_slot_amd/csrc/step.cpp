@@ -9,12 +9,13 @@
 // and remap come before the expert FFN, which runs in slot space.
 //
 //   compute  [x -> host]  moe_route -> cache_manage_gather -> moe_ffn_slots
-//                                       (the cache step, the gather and the doorbell in one launch; a static
-//                                        cache without a host pass runs plain cache_manage)
+//                                       (the cache step, the gather and the doorbell in one launch; without
+//                                        a host pass: cache_manage [-> cache_gather])
 //                                                       -> y_host -> moe_combine [-> moe_residual]
 //   copy     x -> host (pinned)
 //   caller's CPU thread               waits for the doorbell (the picks mirrored to pinned memory behind it),
-//                                     then moe_ffn_host_misses, only when the step has host misses
+//                                     then moe_ffn_host_misses, only when the step has host misses; when the
+//                                     step gathered, checks that no copying workgroup gave up
 #include <hip/hip_runtime.h>
 #include <immintrin.h>
 #include <string.h>
@@ -45,7 +46,7 @@ struct moe_step {
     float* h_y;
     moe_doorbell* bell;
     int32_t seq;  // sequence number of the last fused cache step
-    hipEvent_t ev_x, ev_copy;
+    hipEvent_t ev_x, ev_copy, ev_cache;
     int64_t stats_sum[4];  // cache counters summed over host-pass steps
 };
 
@@ -67,7 +68,7 @@ void release(moe_step* h) {
     void* host[] = {h->h_x, h->h_meta, h->h_y, h->bell};
     for (void* p : host)
         if (p) (void)hipHostFree(p);
-    hipEvent_t evs[] = {h->ev_x, h->ev_copy};
+    hipEvent_t evs[] = {h->ev_x, h->ev_copy, h->ev_cache};
     for (hipEvent_t e : evs)
         if (e) (void)hipEventDestroy(e);
     delete h;
@@ -148,7 +149,7 @@ moe_step* moe_step_create(int T_max, int E, int k, int H, int I, int S, int w_ty
     }
     memset(h->bell, 0, sizeof(moe_doorbell));
     h->seq = 0;
-    hipEvent_t* evs[] = {&h->ev_x, &h->ev_copy};
+    hipEvent_t* evs[] = {&h->ev_x, &h->ev_copy, &h->ev_cache};
     for (hipEvent_t* e : evs) {
         hipError_t r = hipEventCreateWithFlags(e, hipEventDisableTiming);
         if (r != hipSuccess) {
@@ -172,9 +173,26 @@ int moe_step_stats(moe_step* h, int64_t* out, int reset) {
     return moe_ok();
 }
 
+namespace {
+
+// After the fused cache step of a step that gathered: wait for its kernel
+// (normally finished long before) and read the doorbell's err word, set by a
+// copying workgroup that gave up waiting for the managing one.
+int check_gather(moe_step* h) {
+    hipError_t e = hipEventSynchronize(h->ev_cache);
+    if (e != hipSuccess) return hip_fail("moe_layer_step: wait for the cache step", e);
+    if (__atomic_load_n(&h->bell->err, __ATOMIC_ACQUIRE) != 0)
+        return moe_fail(MOE_E_HIP,
+                        "moe_layer_step: a copying workgroup of the cache step gave up waiting for the managing one; "
+                        "the gather of this step is incomplete (slot store and cache state disagree: cache_init "
+                        "the layer again)");
+    return MOE_OK;
+}
+
+}  // namespace
+
 int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, const int32_t* ids_in, int host_pass,
-                   int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy) {
-    (void)s_side;  // the gather runs inside the fused cache step on s0
+                   int n_threads, float* y_out, hipStream_t s0, hipStream_t s_copy) {
     if (!h || !L || !x) return moe_fail(MOE_E_ARG, "moe_layer_step: NULL argument");
     if (T < 0 || T > h->T_max) return moe_fail(MOE_E_SHAPE, "moe_layer_step: T=%d outside [0, %d]", T, h->T_max);
     if (L->state.E != h->E || L->state.S != h->S || L->slab_bytes < h->slab_bytes)
@@ -205,20 +223,25 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
         return rc;
     const bool dynamic = L->policy != MOE_STATIC && h->S > 0;
     int32_t seq = 0;
-    if (host_pass || dynamic) {
-        // one launch: the cache step, the gather of the misses, and (host pass) the picks
-        // mirrored to pinned memory behind a doorbell
+    if (host_pass) {
+        // one launch: the cache step, the gather of the misses, and the picks mirrored to
+        // pinned memory behind a doorbell; err is cleared here, before the launch, because
+        // only the kernel's copying workgroups ever set it
         seq = ++h->seq;
-        int32_t* m_ids = host_pass ? h->h_meta : nullptr;
-        int32_t* m_slots = host_pass ? h->h_meta + Pm : nullptr;
-        float* m_w = host_pass ? reinterpret_cast<float*>(h->h_meta + 2 * Pm) : nullptr;
+        h->bell->err = 0;
         if ((rc = cache_manage_gather(&L->state, L->policy, ids, P, w, slot_ids, h->miss, h->n_miss, h->host_miss,
                                       h->n_host, h->meta + 3 * Pm, L->host_store, L->slot_store, L->slab_bytes,
-                                      h->sync, seq, host_pass ? h->bell : nullptr, m_ids, m_slots, m_w, s0)))
+                                      h->sync, seq, h->bell, h->h_meta, h->h_meta + Pm,
+                                      reinterpret_cast<float*>(h->h_meta + 2 * Pm), s0)))
             return rc;
-    } else if ((rc = cache_manage(&L->state, L->policy, ids, P, slot_ids, h->miss, h->n_miss, h->host_miss,
-                                  h->n_host, h->meta + 3 * Pm, s0))) {
-        return rc;
+        if ((e = hipEventRecord(h->ev_cache, s0)) != hipSuccess) return hip_fail("moe_layer_step: event", e);
+    } else {
+        // no host waits at all: the cache step, then (dynamic cache) the gather, in stream order
+        if ((rc = cache_manage(&L->state, L->policy, ids, P, slot_ids, h->miss, h->n_miss, h->host_miss, h->n_host,
+                               h->meta + 3 * Pm, s0)))
+            return rc;
+        if (dynamic && (rc = cache_gather(h->miss, h->n_miss, h->S, L->host_store, L->slot_store, L->slab_bytes, s0)))
+            return rc;
     }
     if ((rc = moe_ffn_slots(x, h->x_dtype, slot_ids, w, T, h->k, L->slot_store, L->slab_bytes, h->S > 0 ? h->S : 1,
                             h->w_type, h->H, h->I, y, h->ffn_ws, h->ffn_ws_bytes, s0)))
@@ -236,7 +259,8 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
         }
     }
     for (int i = 0; i < 4; ++i) h->stats_sum[i] += h->bell->stats[i];
-    if (h->bell->n_host == 0) return moe_ok();  // every pick resident: nothing to add
+    const bool gathered = h->bell->n_miss > 0;
+    if (h->bell->n_host == 0) return gathered ? check_gather(h) : moe_ok();  // every pick resident: nothing to add
     // the host pass on this thread, while the GPU runs the FFN
     if ((e = hipEventSynchronize(h->ev_copy)) != hipSuccess) return hip_fail("moe_layer_step: wait for x", e);
     const int32_t* h_ids = h->h_meta;
@@ -247,15 +271,16 @@ int moe_layer_step(moe_step* h, const moe_layer_desc* L, const void* x, int T, c
         return rc;
     if ((e = hipMemcpyAsync(h->y_host_dev, h->h_y, (size_t)T * h->H * 4, hipMemcpyHostToDevice, s0)) != hipSuccess)
         return hip_fail("moe_layer_step: host result to device", e);
-    return moe_combine(y, h->y_host_dev, T, h->H, s0);
+    if ((rc = moe_combine(y, h->y_host_dev, T, h->H, s0))) return rc;
+    return gathered ? check_gather(h) : moe_ok();
 }
 
 int moe_stack_step(moe_step* h, const moe_layer_desc* layers, int n_layers, const void* x, int T, int host_pass,
-                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy) {
+                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_copy) {
     if (!h || !layers || n_layers < 1 || !x || !x_out) return moe_fail(MOE_E_ARG, "moe_stack_step: bad arguments");
     const void* cur = x;
     for (int l = 0; l < n_layers; ++l) {
-        int rc = moe_layer_step(h, &layers[l], cur, T, nullptr, host_pass, n_threads, nullptr, s0, s_side, s_copy);
+        int rc = moe_layer_step(h, &layers[l], cur, T, nullptr, host_pass, n_threads, nullptr, s0, s_copy);
         if (rc) return rc;
         void* nxt = l + 1 == n_layers ? x_out : h->xbuf[l & 1];
         if ((rc = moe_residual(cur, h->x_dtype, h->y, nxt, T, h->H, s0))) return rc;

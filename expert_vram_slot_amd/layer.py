@@ -239,7 +239,6 @@ class NativeStack:
         self.x_dtype = MOE_X_F32 if w_type == MOE_W_F32 else MOE_X_BF16
         self.n_threads = n_threads or host_threads()
         self.h = moe_step_create(T_max, E, k, H, I, S, w_type)
-        self.side = torch.cuda.Stream(device=dev)
         self.copy = torch.cuda.Stream(device=dev)
         self.keep = []  # tensors the descriptors point at
         descs = (LayerDesc * len(layers))()
@@ -266,16 +265,20 @@ class NativeStack:
     def e2s(self, l):
         return self.keep[l][0][0]
 
+    def init_cache(self, l, resident=None):
+        """Set layer l's cache state again (resident: device int32 [S], or None: empty)."""
+        cache_init(self.descs[l].state, resident)
+
     def layer_step(self, l, x, T, ids_in=None, host_pass=True):
         """One layer; returns y [T][H] fp32 (a view of this object's output buffer)."""
         moe_layer_step(self.h, self.descs[l], x, T, ids_in, host_pass, self.n_threads, self.y,
-                       torch.cuda.current_stream(), self.side, self.copy)
+                       torch.cuda.current_stream(), self.copy)
         return self.y[:T * self.H].view(T, self.H)
 
     def step(self, x, T, host_pass=True):
         """All layers with the residual join; returns the last residual output [T][H]."""
         moe_stack_step(self.h, self.descs, x, T, host_pass, self.n_threads, self.out, torch.cuda.current_stream(),
-                       self.side, self.copy)
+                       self.copy)
         nb = T * self.H * (4 if self.x_dtype == MOE_X_F32 else 2)
         return self.out[:nb].view(x.dtype).view(T, self.H)
 

@@ -243,7 +243,11 @@ int cache_manage(const moe_cache_state* st, int policy, const int32_t* ids, int 
  * a stream synchronisation).  seq is written last, with system-scope release
  * ordering: a host thread that reads seq == the call's seq (acquire) may read
  * the other fields and the picks mirrored beside it.  n_host == 0 means no
- * pick of the step needs the host pass. */
+ * pick of the step needs the host pass.  err is never written by the
+ * managing workgroup: a copying workgroup that stopped waiting for the cache
+ * step sets it to 1 (system scope) and copies nothing, so the caller clears
+ * it before the call and reads it once the call's kernel has finished; a
+ * nonzero err with n_miss > 0 means the gather is incomplete. */
 typedef struct {
     int32_t seq;
     int32_t n_miss;
@@ -260,9 +264,11 @@ typedef struct {
  *   sync        device int32[2], zeroed once by the caller, owned by this
  *               call sequence (not shared by calls that may overlap): the
  *               in-kernel hand-off from the managing workgroup to the copying
- *               ones; sync[1] != 0 afterwards means a copying workgroup gave
- *               up waiting (the gather is then incomplete; with co-resident
- *               workgroups this does not happen)
+ *               ones; sync[1] is set (never cleared) by a copying workgroup
+ *               that gave up waiting: the gather of that call is then
+ *               incomplete (with co-resident workgroups this does not happen
+ *               within the default wait); the caller clears sync[1] to
+ *               re-arm the report
  *   seq         a number new for every call on this sync word and doorbell
  *   bell        pinned host moe_doorbell or NULL
  *   bell_ids, bell_slots, bell_w
@@ -272,12 +278,23 @@ typedef struct {
  * and releases the others, which wait for it (bounded) and then copy the
  * missing slabs together with it.  Results equal cache_manage followed by
  * cache_gather.
- * Errors: those of cache_manage and cache_gather; ARG (sync NULL). */
+ * Errors: those of cache_manage and cache_gather; ARG (sync NULL).  A
+ * copying workgroup that gives up is reported in sync[1] and bell->err (the
+ * call itself has already returned by then). */
 int cache_manage_gather(const moe_cache_state* st, int policy, const int32_t* ids, int n_ids, const float* w,
                         int32_t* slot_ids, int32_t* miss, int32_t* n_miss, int32_t* host_miss, int32_t* n_host,
                         int32_t* stats, const void* host_store, void* slot_store, size_t slab_bytes, int32_t* sync,
                         int32_t seq, moe_doorbell* bell, int32_t* bell_ids, int32_t* bell_slots, float* bell_w,
                         hipStream_t stream);
+
+/* How many times a copying workgroup of cache_manage_gather polls the
+ * hand-off word (with a short sleep between polls) before it gives up; the
+ * default is 2^22 (a fraction of a second).  polls >= 0 sets the limit for
+ * later calls in this process (0: every copying workgroup gives up at once,
+ * which exercises the report of an incomplete gather without a fault or a
+ * hang); polls < 0 only queries.  Returns the limit in force before the
+ * call.  Not for concurrent use with calls being enqueued. */
+int64_t moe_fused_spin_limit(int64_t polls);
 
 /* Periodic repick of the resident set, [RTX] "Full Transcript" (every ~500
  * tokens have another look, swap out whatever has gone cold, then leave the
@@ -404,29 +421,36 @@ int moe_step_stats(moe_step* h, int64_t* out, int reset);
 
 /* One layer step for T tokens of x (device [T][H], activation format):
  * moe_route (ids_in: given device picks [T][k] or NULL) -> the cache step ->
- * moe_ffn_slots on s0.  The cache step is cache_manage_gather (one launch:
- * cache step, gather of the misses, and with host_pass != 0 the picks
- * mirrored to pinned memory behind a doorbell); a static cache without a
- * host pass runs plain cache_manage.  With host_pass != 0, x goes to pinned
+ * moe_ffn_slots on s0.  With host_pass != 0 the cache step is
+ * cache_manage_gather (one launch: cache step, gather of the misses, and the
+ * picks mirrored to pinned memory behind a doorbell); x goes to pinned
  * memory on s_copy while the router runs; this thread waits for the
  * doorbell and, only when the step has host misses, runs
  * moe_ffn_host_misses on n_threads threads while the GPU runs the FFN; the
- * result is added on s0 (moe_combine).  y_out: device float[T][H] out, or
- * NULL for the driver's own buffer (moe_step_output); final in s0's order
- * when the call returns.  s_side is not used (kept for callers that pass
- * three streams); s0 and s_copy must be distinct streams of one device.
+ * result is added on s0 (moe_combine).  When the step gathered slabs, the
+ * call waits for the cache step's kernel to finish (normally long done by
+ * then) and checks its doorbell for a copying workgroup that gave up.
+ * Without the host pass the cache step is cache_manage, followed by
+ * cache_gather for a dynamic cache (no wait on the host at all).  The gather
+ * stays in s0's order: the FFN needs the gathered slabs, and the steps'
+ * gather time is bound by the host link, not by the GPU.  y_out: device
+ * float[T][H] out, or NULL for the driver's own buffer (moe_step_output);
+ * final in s0's order when the call returns.  s0 and s_copy must be distinct
+ * streams of one device.
  * Errors: those of the entry points it calls; SHAPE when the layer does not
- * match the step; HIP when the doorbell stays silent for 10 s. */
+ * match the step; HIP when the doorbell stays silent for 10 s, or when a
+ * copying workgroup of the cache step gave up (the gather of this step is
+ * incomplete: the layer's slot store no longer matches its cache state,
+ * which must be initialised again with cache_init). */
 int moe_layer_step(moe_step* h, const moe_layer_desc* layer, const void* x, int T, const int32_t* ids_in,
-                   int host_pass, int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side,
-                   hipStream_t s_copy);
+                   int host_pass, int n_threads, float* y_out, hipStream_t s0, hipStream_t s_copy);
 
 /* n_layers layer steps joined by moe_residual: x_{l+1} = x_l + y_l in the
  * activation format ([PGO] "Experts that don't fit": a deep model of routed
  * layers).  x_out: device [T][H] out, the last layer's residual output (may
  * not alias x). */
 int moe_stack_step(moe_step* h, const moe_layer_desc* layers, int n_layers, const void* x, int T, int host_pass,
-                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy);
+                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_copy);
 
 #ifdef __cplusplus
 }

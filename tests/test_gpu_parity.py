@@ -890,6 +890,76 @@ def test_native_dynamic_cache_steps(m):
     nat.close()
 
 
+def test_native_dynamic_cache_steps_without_host_pass(m):
+    """The native driver without the host pass runs the cache step and the
+    gather as two launches: bit for bit the Python orchestration's GPU pass,
+    which is the oracle's y_gpu (resident picks only)."""
+    from expert_vram_slot_amd.layer import NativeStack, SlotLayer
+    li = synth.LayerInputs("c3", T=16)
+    E, k, S, T = li.E, li.k, 32, 16
+    steps = 4
+    seq = synth.zipf_ids(synth.key(li.base, synth.TAG_ZIPF_PERM), synth.key(li.base, synth.TAG_ZIPF_DRAW, 1),
+                         steps * T, E, k, 0.8).reshape(steps, T, k)
+    spec = _layer_spec(li, [], policy="lru", S=S)
+    spec_py = dict(spec, slot_store=torch.zeros_like(spec["slot_store"]))
+    nat = NativeStack(E=E, k=k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, layers=[spec])
+    L = SlotLayer(E=E, k=k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, policy="lru",
+                  host_store=spec_py["host_store"], slot_store=spec_py["slot_store"], G=spec_py["G"])
+    L.init_cache(None)
+    cache = oracle.Cache(E, S, "lru")
+    for st in range(steps):
+        x_np = synth.normal(synth.key(li.base, synth.TAG_X, 0, 200 + st), (T, li.H), 1.0, 1)
+        x = dev(x_np.view(np.int16))
+        ids_in = dev(seq[st])
+        y_nat = host(nat.layer_step(0, x, T, ids_in=ids_in, host_pass=False))
+        y_py = host(L.step(x, T, ids_in=ids_in, host_pass=False))
+        np.testing.assert_array_equal(y_nat, y_py, err_msg=f"step {st}")
+        z = oracle.logits(x_np, 1, li.G)
+        w = oracle.route_weights(z, seq[st])
+        sl = cache.manage(seq[st])["slot_ids"].reshape(T, k)
+        _, yg, _ = oracle.layer(li.w_type, li.store, E, li.H, li.I, x_np, 1, seq[st], w, sl)
+        assert_close(y_nat, yg, li.w_type, f"gpu pass, step {st}")
+    np.testing.assert_array_equal(host(spec["slot_store"]), host(spec_py["slot_store"]))
+    nat.close()
+
+
+def test_native_gather_give_up_is_reported(m):
+    """A copying workgroup of the fused cache step that stops waiting for the
+    managing one copies nothing; the step must then fail loudly rather than
+    compute on stale slots.  Forced from the host with a wait of zero polls
+    (every workgroup still runs to its end, nothing hangs): the step returns
+    an error naming the incomplete gather.  With the default wait back and
+    the cache set again, the same step matches the oracle."""
+    from expert_vram_slot_amd.layer import NativeStack
+    li = synth.LayerInputs("c3", T=16)
+    E, k, S, T = li.E, li.k, 32, 16
+    ids_np = synth.zipf_ids(synth.key(li.base, synth.TAG_ZIPF_PERM), synth.key(li.base, synth.TAG_ZIPF_DRAW, 2),
+                            T, E, k, 0.8)
+    spec = _layer_spec(li, [], policy="lru", S=S)
+    nat = NativeStack(E=E, k=k, H=li.H, I=li.I, S=S, w_type=li.w_type, T_max=T, layers=[spec])
+    x_np = synth.normal(synth.key(li.base, synth.TAG_X, 0, 300), (T, li.H), 1.0, 1)
+    x, ids_in = dev(x_np.view(np.int16)), dev(ids_np)
+    default = m.moe_fused_spin_limit(-1)
+    assert default > 0
+    prev = m.moe_fused_spin_limit(0)
+    try:
+        with pytest.raises(m.MoeError) as ei:
+            nat.layer_step(0, x, T, ids_in=ids_in)
+        assert ei.value.code == m.MOE_E_HIP and "gather of this step is incomplete" in str(ei.value)
+    finally:
+        m.moe_fused_spin_limit(prev)
+    torch.cuda.synchronize()
+    assert m.moe_fused_spin_limit(-1) == default
+    nat.init_cache(0, None)
+    spec["slot_store"].zero_()
+    y = host(nat.layer_step(0, x, T, ids_in=ids_in))
+    z = oracle.logits(x_np, 1, li.G)
+    w = oracle.route_weights(z, ids_np)
+    yf, _, _ = oracle.layer(li.w_type, li.store, E, li.H, li.I, x_np, 1, ids_np, w)
+    assert_close(y, yf, li.w_type, "step after the reported give-up")
+    nat.close()
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_native_stack_equals_python_stack(m, T):
     from expert_vram_slot_amd.layer import NativeStack, SlotStack
