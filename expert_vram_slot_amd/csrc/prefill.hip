@@ -35,6 +35,8 @@
 // XCD's L2.  Every weight row is read by exactly one workgroup per tile.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "prefill.hpp"
 
@@ -852,17 +854,29 @@ template <int NB>
 int pf_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
               const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
               int max_tiles, void* hbuf, float* part, hipStream_t st) {
-    static bool lds_set = false;  // once per process and NB: 64 KiB of LDS at NB = 4, 96 KiB at NB = 8
+    // 64 KiB of LDS at NB = 4, 96 KiB at NB = 8: allowed once per device (under a lock, so
+    // threads that launch on several devices at once each see it done for theirs)
+    static std::mutex mu;
+    static uint64_t done = 0;  // bit d: set for device d
     const int lds = pf_lds_bytes(NB);
-    if (!lds_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_GU, NB>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
-            hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_DOWN, NB>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
-            (void)hipGetLastError();
-            return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the prefill kernels", lds);
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return moe_fail(MOE_E_HIP, "moe_ffn_slots: no current device (or device %d beyond 63)", dev);
+    }
+    {
+        std::lock_guard<std::mutex> lk(mu);
+        if (!(done >> dev & 1)) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_GU, NB>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_DOWN, NB>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+                (void)hipGetLastError();
+                return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the prefill kernels",
+                                lds);
+            }
+            done |= 1ull << dev;
         }
-        lds_set = true;
     }
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
     PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
