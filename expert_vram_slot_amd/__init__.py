@@ -78,6 +78,8 @@ def lib():
                                           sz, vp, i32, vp, vp, vp, vp, vp]),
             "moe_ffn_workspace_bytes": (sz, [i32, i32, i32, i32, i32, i32]),
             "moe_ffn_slots": (i32, [vp, i32, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, vp, sz, vp]),
+            "moe_ffn_slots_noalloc": (i32, [vp, i32, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, vp]),
+            "moe_ffn_noalloc_scratch_bytes": (sz, []),
             "moe_ffn_host_misses": (i32, [vp, i32, vp, vp, vp, i32, i32, vp, sz, i32, i32, i32, i32, vp, i32]),
             "moe_combine": (i32, [vp, vp, i32, i32, vp]),
             "moe_residual": (i32, [vp, i32, vp, vp, i32, i32, vp]),
@@ -213,6 +215,16 @@ def moe_ffn_slots(x, x_dtype, slot_ids, w, T, k, slot_store, slab_bytes, S, w_ty
     return _check("moe_ffn_slots", lib().moe_ffn_slots(_p(x), x_dtype, _p(slot_ids), _p(w), T, k, _p(slot_store),
                                                        slab_bytes, S, w_type, H, I, _p(y), _p(ws), ws_bytes,
                                                        _stream(stream)))
+
+
+def moe_ffn_slots_noalloc(x, x_dtype, slot_ids, w, T, k, slot_store, slab_bytes, S, w_type, H, I, y, stream=None):
+    return _check("moe_ffn_slots_noalloc",
+                  lib().moe_ffn_slots_noalloc(_p(x), x_dtype, _p(slot_ids), _p(w), T, k, _p(slot_store), slab_bytes, S,
+                                              w_type, H, I, _p(y), _stream(stream)))
+
+
+def moe_ffn_noalloc_scratch_bytes() -> int:
+    return int(lib().moe_ffn_noalloc_scratch_bytes())
 
 
 def moe_ffn_host_misses(x_h, x_dtype, ids_h, slot_ids_h, w_h, T, k, host_store, slab_bytes, E, w_type, H, I, y_h,

@@ -28,8 +28,17 @@
 // the wave in one multi-value butterfly.
 #include <math.h>
 
+#include <mutex>
+
 #include "common.hpp"
 #include "prefill.hpp"
+
+// The workspace of moe_ffn_slots_noalloc: one array per device, in the code
+// object, held until the process ends.  In host code `scratch` only names the
+// array (a host-side stand-in, not a device address): its device address is
+// looked up per device with hipGetSymbolAddress and kept in scratch_dev below.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;
+static __device__ __align__(256) unsigned char scratch[NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -218,13 +227,13 @@ __device__ __forceinline__ int wave_slot_rank(int s, bool valid, int nbits, int*
 // Tiles of the grouped GEMM: ceil(cnt / mt) per slot, slots in ascending
 // order.  Called by the whole workgroup (thread s holds slot s's pick count
 // and offset; S <= blockDim.x); tiles == NULL writes nothing.
-__device__ __forceinline__ void write_pf_tiles(int cnt, int off, int S, int mt, int* scratch, moe_pf_tile* tiles,
+__device__ __forceinline__ void write_pf_tiles(int cnt, int off, int S, int mt, int* scan_lds, moe_pf_tile* tiles,
                                                int32_t* n_tiles) {
     if (!tiles) return;
     const int s = threadIdx.x;
     const int nc = (s < S) ? (cnt + mt - 1) / mt : 0;
     int tot;
-    const int toff = moe::block_exclusive_scan(nc, scratch, &tot);
+    const int toff = moe::block_exclusive_scan(nc, scan_lds, &tot);
     for (int c = 0; c < nc; ++c) tiles[toff + c] = moe_pf_tile{off + c * mt, min(mt, cnt - c * mt), s, 0};
     if (threadIdx.x == 0) *n_tiles = tot;
 }
@@ -293,7 +302,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
     __shared__ int ctot[MOE_MAX_S];
-    __shared__ int scratch[GROUP_THREADS / 64 + 1];
+    __shared__ int scan_lds[GROUP_THREADS / 64 + 1];
     const int tid = threadIdx.x, wid = tid >> 6;
     int nbits = 0;
     while ((1 << nbits) < S) ++nbits;
@@ -320,7 +329,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             }
         }
         int tot;
-        const int off = moe::block_exclusive_scan(tot_s, scratch, &tot);
+        const int off = moe::block_exclusive_scan(tot_s, scan_lds, &tot);
         if (tid < S) {
             slot_off[tid] = off;
             base[tid] = off;
@@ -328,10 +337,10 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
         if (tid == 0) slot_off[S] = tot;
         const int flag = (tid < S && tot_s > 0) ? 1 : 0;
         int na;
-        const int apos = moe::block_exclusive_scan(flag, scratch, &na);
+        const int apos = moe::block_exclusive_scan(flag, scan_lds, &na);
         if (flag) active[apos] = tid;
         if (tid == 0) *n_active = na;
-        write_pf_tiles(tot_s, off, S, pf_mt, scratch, pf_tiles, pf_n_tiles);
+        write_pf_tiles(tot_s, off, S, pf_mt, scan_lds, pf_tiles, pf_n_tiles);
         __syncthreads();
         if (valid) pair_list[base[s] + wtab[wid][s] + rank] = p;
         return;
@@ -369,7 +378,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             // counts -> offsets; slots with work, ascending
             const int cnt = tid < S ? base[tid] : 0;
             int tot;
-            const int off = moe::block_exclusive_scan(cnt, scratch, &tot);
+            const int off = moe::block_exclusive_scan(cnt, scan_lds, &tot);
             if (tid < S) {
                 slot_off[tid] = off;
                 base[tid] = off;
@@ -377,10 +386,10 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
             if (tid == 0) slot_off[S] = tot;
             const int flag = (tid < S && cnt > 0) ? 1 : 0;
             int na;
-            const int apos = moe::block_exclusive_scan(flag, scratch, &na);
+            const int apos = moe::block_exclusive_scan(flag, scan_lds, &na);
             if (flag) active[apos] = tid;
             if (tid == 0) *n_active = na;
-            write_pf_tiles(cnt, off, S, pf_mt, scratch, pf_tiles, pf_n_tiles);
+            write_pf_tiles(cnt, off, S, pf_mt, scan_lds, pf_tiles, pf_n_tiles);
             __syncthreads();
         }
     }
@@ -414,7 +423,7 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
                                                                int32_t* __restrict__ pf_n_tiles, int pf_mt) {
     __shared__ uint16_t wtab[GROUP_THREADS / 64][MOE_MAX_S];
     __shared__ int base[MOE_MAX_S];
-    __shared__ int scratch[GROUP_THREADS / 64 + 1];
+    __shared__ int scan_lds[GROUP_THREADS / 64 + 1];
     const int tid = threadIdx.x, wid = tid >> 6, c = blockIdx.x;
     int tot = 0, pre = 0;
     if (tid < S) {
@@ -425,17 +434,17 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group_place(const int32_t* __
         }
     }
     int all;
-    const int off = moe::block_exclusive_scan(tot, scratch, &all);
+    const int off = moe::block_exclusive_scan(tot, scan_lds, &all);
     if (tid < S) base[tid] = off + pre;
     if (c == 0) {
         if (tid < S) slot_off[tid] = off;
         if (tid == 0) slot_off[S] = all;
         const int flag = (tid < S && tot > 0) ? 1 : 0;
         int na;
-        const int apos = moe::block_exclusive_scan(flag, scratch, &na);
+        const int apos = moe::block_exclusive_scan(flag, scan_lds, &na);
         if (flag) active[apos] = tid;
         if (tid == 0) *n_active = na;
-        write_pf_tiles(tot, off, S, pf_mt, scratch, pf_tiles, pf_n_tiles);
+        write_pf_tiles(tot, off, S, pf_mt, scan_lds, pf_tiles, pf_n_tiles);
     }
     for (int i = tid; i < (GROUP_THREADS / 64) * S; i += GROUP_THREADS) wtab[i / S][i % S] = 0;
     __syncthreads();
@@ -1054,37 +1063,65 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     return moe_check_launch("moe_ffn_slots/reduce");
 }
 
-}  // namespace
+// ------------------------------------------------ allocation-free entry
 
-extern "C" {
+// `scratch` (the workspace of moe_ffn_slots_noalloc) is declared at the top
+// of this file.
 
-size_t moe_ffn_workspace_bytes(int T, int k, int S, int w_type, int H, int I) {
-    if (T < 0 || k < 1 || S < 1 || H < 1 || I < 1) return 0;
-    return ws_layout(T, k, S, w_type, H, I).total;
+constexpr int NOALLOC_MAX_DEVICES = 64;
+std::mutex scratch_mu;
+unsigned char* scratch_dev[NOALLOC_MAX_DEVICES];  // device address of `scratch` per device, once looked up
+
+// The current device's copy of the scratch array (looked up on the first
+// call on that device, with the device current).
+int scratch_for_current_device(unsigned char** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess || dev < 0 || dev >= NOALLOC_MAX_DEVICES) {
+        (void)hipGetLastError();
+        return moe_fail(MOE_E_HIP, "moe_ffn_slots_noalloc: no current device (%s) or device %d beyond %d",
+                        hipGetErrorString(e), dev, NOALLOC_MAX_DEVICES - 1);
+    }
+    std::lock_guard<std::mutex> lk(scratch_mu);
+    if (!scratch_dev[dev]) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return moe_fail(MOE_E_HIP, "moe_ffn_slots_noalloc: cannot find the scratch array on device %d (%s)", dev,
+                            hipGetErrorString(e));
+        }
+        scratch_dev[dev] = reinterpret_cast<unsigned char*>(p);
+    }
+    *out = scratch_dev[dev];
+    return MOE_OK;
 }
 
-int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
-                  const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y, void* ws,
-                  size_t ws_bytes, hipStream_t stream) {
+// Argument checks shared by both entry points; the workspace layout on success.
+int ffn_check(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
+              const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y,
+              moe_slab_layout_t* lay, const char* who) {
     MOE_REQUIRE(T >= 0 && k >= 1 && k <= MOE_MAX_K && S >= 1 && H >= 1 && I >= 1, MOE_E_ARG,
-                "moe_ffn_slots: T=%d k=%d S=%d H=%d I=%d out of range", T, k, S, H, I);
-    MOE_REQUIRE(S <= MOE_MAX_S, MOE_E_SHAPE, "moe_ffn_slots: S=%d exceeds %d", S, MOE_MAX_S);
-    if (T == 0) return moe_ok();
-    MOE_REQUIRE(x && slot_ids && w && slot_store && y && ws, MOE_E_ARG,
-                "moe_ffn_slots: x, slot_ids, w, slot_store, y and ws must be non-NULL");
-    moe_slab_layout_t lay;
-    int rc = moe_layout(w_type, H, I, &lay);
+                "%s: T=%d k=%d S=%d H=%d I=%d out of range", who, T, k, S, H, I);
+    MOE_REQUIRE(S <= MOE_MAX_S, MOE_E_SHAPE, "%s: S=%d exceeds %d", who, S, MOE_MAX_S);
+    if (T == 0) return MOE_OK;
+    MOE_REQUIRE(x && slot_ids && w && slot_store && y, MOE_E_ARG,
+                "%s: x, slot_ids, w, slot_store and y must be non-NULL", who);
+    int rc = moe_layout(w_type, H, I, lay);
     if (rc) return rc;
-    MOE_REQUIRE(slab_bytes >= (size_t)lay.total && slab_bytes % 16 == 0, MOE_E_ALIGN,
-                "moe_ffn_slots: slab_bytes=%zu must be a 16-byte multiple >= %lld", slab_bytes, (long long)lay.total);
-    MOE_REQUIRE(moe_aligned16(slot_store) && moe_aligned16(x) && moe_aligned16(ws) && moe_aligned16(y), MOE_E_ALIGN,
-                "moe_ffn_slots: x, slot_store, y and ws must be 16-byte aligned");
+    MOE_REQUIRE(slab_bytes >= (size_t)lay->total && slab_bytes % 16 == 0, MOE_E_ALIGN,
+                "%s: slab_bytes=%zu must be a 16-byte multiple >= %lld", who, slab_bytes, (long long)lay->total);
+    MOE_REQUIRE(moe_aligned16(slot_store) && moe_aligned16(x) && moe_aligned16(y), MOE_E_ALIGN,
+                "%s: x, slot_store and y must be 16-byte aligned", who);
     const int want_x = w_type == MOE_W_F32 ? MOE_X_F32 : MOE_X_BF16;
-    MOE_REQUIRE(x_dtype == want_x, MOE_E_DTYPE, "moe_ffn_slots: weight format %d needs activation format %d, got %d",
+    MOE_REQUIRE(x_dtype == want_x, MOE_E_DTYPE, "%s: weight format %d needs activation format %d, got %d", who,
                 w_type, want_x, x_dtype);
-    const WsLayout L = ws_layout(T, k, S, w_type, H, I);
-    MOE_REQUIRE(ws_bytes >= L.total, MOE_E_ARG, "moe_ffn_slots: workspace of %zu bytes, need %zu", ws_bytes, L.total);
-    unsigned char* wsb = reinterpret_cast<unsigned char*>(ws);
+    return MOE_OK;
+}
+
+int ffn_dispatch(const void* x, const int32_t* slot_ids, const float* w, int T, int k, const void* slot_store,
+                 size_t slab_bytes, int S, int w_type, int H, int I, float* y, unsigned char* wsb,
+                 const WsLayout& L, const moe_slab_layout_t& lay, hipStream_t stream) {
     switch (w_type) {
         case MOE_W_F32:
             return run_ffn<MOE_W_F32>(x, slot_ids, w, T, k, slot_store, slab_bytes, S, H, I, y, wsb, L, lay, stream);
@@ -1098,6 +1135,48 @@ int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const flo
             return moe_fail(MOE_E_DTYPE, "moe_ffn_slots: unknown weight format %d", w_type);
     }
 }
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_ffn_workspace_bytes(int T, int k, int S, int w_type, int H, int I) {
+    if (T < 0 || k < 1 || S < 1 || H < 1 || I < 1) return 0;
+    return ws_layout(T, k, S, w_type, H, I).total;
+}
+
+int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
+                  const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y, void* ws,
+                  size_t ws_bytes, hipStream_t stream) {
+    moe_slab_layout_t lay;
+    int rc = ffn_check(x, x_dtype, slot_ids, w, T, k, slot_store, slab_bytes, S, w_type, H, I, y, &lay,
+                       "moe_ffn_slots");
+    if (rc || T == 0) return rc ? rc : moe_ok();
+    MOE_REQUIRE(ws && moe_aligned16(ws), MOE_E_ARG, "moe_ffn_slots: ws must be non-NULL and 16-byte aligned");
+    const WsLayout L = ws_layout(T, k, S, w_type, H, I);
+    MOE_REQUIRE(ws_bytes >= L.total, MOE_E_ARG, "moe_ffn_slots: workspace of %zu bytes, need %zu", ws_bytes, L.total);
+    return ffn_dispatch(x, slot_ids, w, T, k, slot_store, slab_bytes, S, w_type, H, I, y,
+                        reinterpret_cast<unsigned char*>(ws), L, lay, stream);
+}
+
+int moe_ffn_slots_noalloc(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
+                          const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y,
+                          hipStream_t stream) {
+    moe_slab_layout_t lay;
+    int rc = ffn_check(x, x_dtype, slot_ids, w, T, k, slot_store, slab_bytes, S, w_type, H, I, y, &lay,
+                       "moe_ffn_slots_noalloc");
+    if (rc || T == 0) return rc ? rc : moe_ok();
+    const WsLayout L = ws_layout(T, k, S, w_type, H, I);
+    MOE_REQUIRE(L.total <= NOALLOC_SCRATCH_BYTES, MOE_E_SHAPE,
+                "moe_ffn_slots_noalloc: T=%d k=%d S=%d H=%d I=%d needs %zu bytes of workspace; the static scratch "
+                "holds %zu (use moe_ffn_slots with a workspace of your own)",
+                T, k, S, H, I, L.total, NOALLOC_SCRATCH_BYTES);
+    unsigned char* ws = nullptr;
+    if ((rc = scratch_for_current_device(&ws))) return rc;
+    return ffn_dispatch(x, slot_ids, w, T, k, slot_store, slab_bytes, S, w_type, H, I, y, ws, L, lay, stream);
+}
+
+size_t moe_ffn_noalloc_scratch_bytes(void) { return NOALLOC_SCRATCH_BYTES; }
 
 int moe_combine(float* y, const float* y_add, int T, int H, hipStream_t stream) {
     MOE_REQUIRE(y && y_add && T >= 0 && H >= 1, MOE_E_ARG, "moe_combine: bad arguments");

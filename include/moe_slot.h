@@ -345,6 +345,28 @@ int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const flo
                   const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y, void* ws,
                   size_t ws_bytes, hipStream_t stream);
 
+/* moe_ffn_slots without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  Arguments, results (bit for bit) and
+ * errors as moe_ffn_slots.  The workspace is a static device array of
+ * moe_ffn_noalloc_scratch_bytes() = 32 MiB in the library's code object: each
+ * GPU the library runs on holds its own copy until the process ends, and the
+ * call allocates nothing (no hipMalloc, no hipFree, no allocating library
+ * routine).  Sizes whose workspace (moe_ffn_workspace_bytes) exceeds it are
+ * refused with SHAPE before anything is enqueued: decode batches fit (the
+ * 128-expert, top-8, 2048 x 768 bf16 layer up to about 400 tokens), prefill
+ * batches of thousands of tokens do not.  The scratch keeps the last call's
+ * contents; no part of it needs to start at zero.  Calls that may overlap on
+ * one GPU (different streams, or different host threads) share the array
+ * and race: serialise them.  HIP when the array's device address cannot be
+ * found on the current device. */
+int moe_ffn_slots_noalloc(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
+                          const void* slot_store, size_t slab_bytes, int S, int w_type, int H, int I, float* y,
+                          hipStream_t stream);
+/* Bytes of the static workspace of moe_ffn_slots_noalloc (for callers that
+ * cannot allocate device memory). */
+size_t moe_ffn_noalloc_scratch_bytes(void);
+
 /* Host pass over the picks that are not resident, [RTX] "What the video
  * covers" / transcript (a CPU pass over the experts still in RAM).  Runs
  * synchronously on the calling thread plus n_threads - 1 workers; safe to
