@@ -87,8 +87,10 @@ def lib():
             "moe_step_destroy": (None, [vp]),
             "moe_step_output": (vp, [vp]),
             "moe_step_stats": (i32, [vp, ctypes.POINTER(ctypes.c_int64), i32]),
-            "moe_layer_step": (i32, [vp, ctypes.POINTER(LayerDesc), vp, i32, vp, i32, i32, vp, vp, vp]),
-            "moe_stack_step": (i32, [vp, ctypes.POINTER(LayerDesc), i32, vp, i32, i32, i32, vp, vp, vp]),
+            "moe_layer_step": (i32, [vp, ctypes.POINTER(LayerDesc), vp, i32, vp, i32, i32, vp, vp, vp, vp]),
+            "moe_stack_step": (i32, [vp, ctypes.POINTER(LayerDesc), i32, vp, i32, i32, i32, vp, vp, vp, vp]),
+            "moe_step_set_stream_threshold": (i32, [vp, i32]),
+            "moe_step_last_host_mode": (i32, [vp]),
             "moe_fused_spin_limit": (ctypes.c_int64, [ctypes.c_int64]),
             "moe_host_alloc": (vp, [sz]),
             "moe_host_free": (i32, [vp]),
@@ -264,15 +266,23 @@ def moe_step_stats(h, reset=False):
     return [int(v) for v in out]
 
 
-def moe_layer_step(h, desc, x, T, ids_in, host_pass, n_threads, y_out, s0, s_copy):
+def moe_layer_step(h, desc, x, T, ids_in, host_pass, n_threads, y_out, s0, s_side, s_copy):
     return _check("moe_layer_step", lib().moe_layer_step(h, ctypes.byref(desc), _p(x), T, _p(ids_in),
                                                          int(host_pass), n_threads, _p(y_out), _stream(s0),
-                                                         _stream(s_copy)))
+                                                         _stream(s_side), _stream(s_copy)))
 
 
-def moe_stack_step(h, descs, x, T, host_pass, n_threads, x_out, s0, s_copy):
+def moe_stack_step(h, descs, x, T, host_pass, n_threads, x_out, s0, s_side, s_copy):
     return _check("moe_stack_step", lib().moe_stack_step(h, descs, len(descs), _p(x), T, int(host_pass), n_threads,
-                                                         _p(x_out), _stream(s0), _stream(s_copy)))
+                                                         _p(x_out), _stream(s0), _stream(s_side), _stream(s_copy)))
+
+
+def moe_step_set_stream_threshold(h, picks_per_expert: int):
+    return _check("moe_step_set_stream_threshold", lib().moe_step_set_stream_threshold(h, int(picks_per_expert)))
+
+
+def moe_step_last_host_mode(h) -> int:
+    return int(lib().moe_step_last_host_mode(h))
 
 
 def moe_fused_spin_limit(polls: int = -1) -> int:

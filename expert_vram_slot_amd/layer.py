@@ -28,7 +28,7 @@ import torch
 from . import (MOE_W_F32, MOE_X_BF16, MOE_X_F32, POLICIES, LayerDesc, cache_gather, cache_init, cache_manage,
                cache_state, moe_combine, moe_ffn_host_misses, moe_ffn_slots, moe_ffn_workspace_bytes, moe_layer_step,
                moe_residual, moe_route_ex, moe_slab_layout, moe_stack_step, moe_step_create,
-               moe_step_destroy, moe_step_stats)
+               moe_step_destroy, moe_step_last_host_mode, moe_step_set_stream_threshold, moe_step_stats)
 
 
 def host_threads() -> int:
@@ -239,6 +239,7 @@ class NativeStack:
         self.x_dtype = MOE_X_F32 if w_type == MOE_W_F32 else MOE_X_BF16
         self.n_threads = n_threads or host_threads()
         self.h = moe_step_create(T_max, E, k, H, I, S, w_type)
+        self.side = torch.cuda.Stream(device=dev)
         self.copy = torch.cuda.Stream(device=dev)
         self.keep = []  # tensors the descriptors point at
         descs = (LayerDesc * len(layers))()
@@ -272,18 +273,26 @@ class NativeStack:
     def layer_step(self, l, x, T, ids_in=None, host_pass=True):
         """One layer; returns y [T][H] fp32 (a view of this object's output buffer)."""
         moe_layer_step(self.h, self.descs[l], x, T, ids_in, host_pass, self.n_threads, self.y,
-                       torch.cuda.current_stream(), self.copy)
+                       torch.cuda.current_stream(), self.side, self.copy)
         return self.y[:T * self.H].view(T, self.H)
 
     def step(self, x, T, host_pass=True):
         """All layers with the residual join; returns the last residual output [T][H]."""
         moe_stack_step(self.h, self.descs, x, T, host_pass, self.n_threads, self.out, torch.cuda.current_stream(),
-                       self.copy)
+                       self.side, self.copy)
         nb = T * self.H * (4 if self.x_dtype == MOE_X_F32 else 2)
         return self.out[:nb].view(x.dtype).view(T, self.H)
 
     def stats(self, reset=False):
         return moe_step_stats(self.h, reset)
+
+    def set_stream_threshold(self, picks_per_expert):
+        """Picks per non-resident expert from which a step streams its misses (0: always, < 0: never)."""
+        moe_step_set_stream_threshold(self.h, picks_per_expert)
+
+    def last_host_mode(self):
+        """0: no host misses, 1: the CPU lane, 2: streamed through the GPU (last layer step)."""
+        return moe_step_last_host_mode(self.h)
 
     def close(self):
         if self.h:

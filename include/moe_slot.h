@@ -447,32 +447,52 @@ int moe_step_stats(moe_step* h, int64_t* out, int reset);
  * cache_manage_gather (one launch: cache step, gather of the misses, and the
  * picks mirrored to pinned memory behind a doorbell); x goes to pinned
  * memory on s_copy while the router runs; this thread waits for the
- * doorbell and, only when the step has host misses, runs
- * moe_ffn_host_misses on n_threads threads while the GPU runs the FFN; the
- * result is added on s0 (moe_combine).  When the step gathered slabs, the
- * call waits for the cache step's kernel to finish (normally long done by
- * then) and checks its doorbell for a copying workgroup that gave up.
- * Without the host pass the cache step is cache_manage, followed by
- * cache_gather for a dynamic cache (no wait on the host at all).  The gather
- * stays in s0's order: the FFN needs the gathered slabs, and the steps'
- * gather time is bound by the host link, not by the GPU.  y_out: device
- * float[T][H] out, or NULL for the driver's own buffer (moe_step_output);
- * final in s0's order when the call returns.  s0 and s_copy must be distinct
- * streams of one device.
+ * doorbell and, only when the step has host misses, serves them in one of
+ * two ways ([RTX] "Full Transcript": the concurrent CPU lane pays off on
+ * small batches; on a big prompt batch it is switched off):
+ *  - the CPU lane: moe_ffn_host_misses on n_threads threads while the GPU
+ *    runs the FFN, the result added on s0 (moe_combine);
+ *  - streamed (large batches, when the host picks reach the step's
+ *    threshold per non-resident expert, see moe_step_set_stream_threshold):
+ *    the non-resident experts' slabs are gathered, 8 at a time, into a ring
+ *    of 16 staging slots on s_side, each chunk's gather overlapping the FFN
+ *    of the previous chunk on s0, and each chunk's FFN result is added to y.
+ *    Only steps created with T_max >= 128 have the ring.
+ * When the step gathered slabs into its slots, the call waits for the cache
+ * step's kernel to finish (normally long done by then) and checks its
+ * doorbell for a copying workgroup that gave up.  Without the host pass the
+ * cache step is cache_manage, followed by cache_gather for a dynamic cache,
+ * all on s0 (the FFN needs the gathered slabs; no host wait at all), and
+ * non-resident picks add zero.  y_out: device float[T][H] out, or NULL for
+ * the driver's own buffer (moe_step_output); final in s0's order when the
+ * call returns.  s0, s_side and s_copy are streams of one device (s0 and
+ * s_copy distinct).
  * Errors: those of the entry points it calls; SHAPE when the layer does not
  * match the step; HIP when the doorbell stays silent for 10 s, or when a
  * copying workgroup of the cache step gave up (the gather of this step is
  * incomplete: the layer's slot store no longer matches its cache state,
  * which must be initialised again with cache_init). */
 int moe_layer_step(moe_step* h, const moe_layer_desc* layer, const void* x, int T, const int32_t* ids_in,
-                   int host_pass, int n_threads, float* y_out, hipStream_t s0, hipStream_t s_copy);
+                   int host_pass, int n_threads, float* y_out, hipStream_t s0, hipStream_t s_side,
+                   hipStream_t s_copy);
+
+/* Threshold of the streamed miss pass: a step streams its non-resident
+ * experts when its non-resident picks number at least picks_per_expert per
+ * non-resident expert (default 32: on the 288-expert bf16 layer with 144
+ * resident the CPU lane took 95 ms at 28 picks per expert and 185 ms at 57,
+ * the streamed pass 100-104 ms).  0 streams every step that has host misses
+ * (given a ring); a negative value never streams. */
+int moe_step_set_stream_threshold(moe_step* h, int picks_per_expert);
+/* How the last moe_layer_step served its non-resident picks: 0 none (or no
+ * host pass), 1 the CPU lane, 2 streamed through the GPU; -1 for NULL. */
+int moe_step_last_host_mode(const moe_step* h);
 
 /* n_layers layer steps joined by moe_residual: x_{l+1} = x_l + y_l in the
  * activation format ([PGO] "Experts that don't fit": a deep model of routed
  * layers).  x_out: device [T][H] out, the last layer's residual output (may
  * not alias x). */
 int moe_stack_step(moe_step* h, const moe_layer_desc* layers, int n_layers, const void* x, int T, int host_pass,
-                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_copy);
+                   int n_threads, void* x_out, hipStream_t s0, hipStream_t s_side, hipStream_t s_copy);
 
 #ifdef __cplusplus
 }

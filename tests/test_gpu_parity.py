@@ -829,7 +829,7 @@ def _layer_spec(li, resident, policy="static", S=None):
                 resident=dev(np.asarray(resident, np.int32)) if policy == "static" else None, policy=policy)
 
 
-@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 8)])
+@pytest.mark.parametrize("cfg,T", [("c1", 16), ("c2", 8), ("c2", 64)])
 def test_native_layer_step_equals_python_orchestration(m, cfg, T):
     """moe_layer_step issues the same kernels as SlotLayer: identical bits, and the oracle's layer."""
     from expert_vram_slot_amd.layer import NativeStack, SlotLayer
@@ -958,6 +958,52 @@ def test_native_gather_give_up_is_reported(m):
     yf, _, _ = oracle.layer(li.w_type, li.store, E, li.H, li.I, x_np, 1, ids_np, w)
     assert_close(y, yf, li.w_type, "step after the reported give-up")
     nat.close()
+
+
+@functools.lru_cache(maxsize=1)
+def prefill_144_host():
+    """The 144-slot variant of the 288-expert layer: its resident set (the 144
+    most-picked experts of a 1024-token profile batch) and the pinned host
+    store of all 288 experts."""
+    li, _, _ = prefill_inputs()
+    warm = synth.LayerInputs("c5", T=1024, step=10_000, with_store=False)
+    resident = oracle.pick_static(oracle.topk(oracle.logits(warm.x, 1, warm.G), li.k), li.E, 144)
+    return resident.astype(np.int32), torch.from_numpy(li.store).pin_memory()
+
+
+@pytest.mark.parametrize("mode", ["cpu", "streamed"])
+def test_native_prefill_144_slots_with_host_misses(m, mode):
+    """The full 288-expert layer at 2048 tokens with 144 experts resident and
+    the other 144 served by the step itself, either by the CPU lane (forced)
+    or, as the switch picks at this batch size (about 57 picks per
+    non-resident expert), streamed through the GPU's staging slots: the whole
+    layer's output on sampled tokens against the oracle."""
+    from expert_vram_slot_amd.layer import NativeStack
+    li, ids, w = prefill_inputs()
+    resident, host_store = prefill_144_host()
+    S, T = 144, li.T
+    spec = dict(host_store=host_store, slot_store=dev(li.store[resident]), G=dev(li.G.view(np.int16)), bias=None,
+                resident=dev(resident))
+    nat = NativeStack(E=li.E, k=li.k, H=li.H, I=li.I, S=S, w_type=1, T_max=T, layers=[spec])
+    if mode == "cpu":
+        nat.set_stream_threshold(-1)
+    y = host(nat.layer_step(0, dev(li.x.view(np.int16)), T))
+    assert nat.last_host_mode() == (1 if mode == "cpu" else 2)
+    hits, distinct, gathered, nhost = nat.stats()
+    e2s = np.full(li.E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    assert hits == int(np.sum(e2s[ids] >= 0)) and gathered == 0 and nhost == len(set(ids[e2s[ids] < 0].tolist()))
+    assert np.all(np.isfinite(y))
+    rng = np.random.default_rng(144)
+    sample = np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), 6, replace=False)])
+    for t in sample:
+        ref = np.zeros(li.H)
+        for j in range(li.k):
+            ref += w[t, j] * oracle.expert(1, li.store[ids[t, j]], li.H, li.I, li.x[t], 1)
+        assert_close(y[t:t + 1], ref[None, :].astype(np.float32), 1, f"{mode} token {t}")
+    nat.close()
+    del spec
+    torch.cuda.empty_cache()
 
 
 @pytest.mark.parametrize("T", [1, 32])
