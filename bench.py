@@ -25,12 +25,22 @@ line carries two more workloads of the layer:
            manage -> moe_ffn_slots on the MFMA grouped GEMM; HBM and MFMA
            fractions; plus the same layer at 16384 tokens, the shape where
            the grouped GEMM is compute-bound (supplemental)
+  decode_batches  the same bf16 layer's FFN at 1, 8 and 64 tokens per step:
+           expert-weight GB/s against the HBM peak
+  prefill_144  the 288-expert layer at 2048 tokens with 144 experts resident
+           and 144 in pinned host memory, served by the step as the native
+           driver chooses (streamed through staging slots at this batch), and
+           with the CPU lane forced
   dynamic  the 128-expert W8A8 layer under Zipf(0.8) routing with a 32-slot
            LRU cache, 256 steps of 16 tokens from an empty cache: hit rate per
            routing id, experts gathered per step, gather GB/s against the
            measured host link, layer tokens/s with the host pass
+  stack    the 48-layer, 512-expert top-10 4-bit stack (43.5 GB pinned host
+           store, 192 resident experts per layer, graded bias cap -1) at 1
+           and 32 tokens: tokens/s, the FFN's expert-weight GB/s, hit rates
+           with and without the bias (--no-stack leaves it out)
 
-`--workload stack` runs the 48-layer, 512-expert 4-bit stack instead,
+`--workload stack` runs only the 48-layer, 512-expert 4-bit stack,
 `--workload bias` the routing-bias variants (flat bias, hard mask, graded
 table, damped weights; live-cache affinity on a dynamic cache), and
 `--workload replay` a routing trace replayed under the cache policies
@@ -77,6 +87,7 @@ def parse():
     ap.add_argument("--no-gather", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
+    ap.add_argument("--no-stack", action="store_true", help="leave out the 48-layer 4-bit stack leg")
     ap.add_argument("--workload", choices=["decode", "stack", "bias", "replay"], default="decode")
     ap.add_argument("--stack-steps", type=int, default=20, help="timed 48-layer steps at T=1 (half at T=32)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -197,49 +208,22 @@ def main():
     # ---- the same steps again on the GPU alone (route -> manage -> moe_ffn_slots, no host pass), issued
     # from Python with HIP events around every moe_ffn_slots launch on the compute stream: the FFN's
     # duration for the roofline, free of gaps from CPU threads competing with the launching thread
-    ffn_ms = []
-    ffn_bytes = []
-    ev_pairs = []
-
-    def one_step(i, record):
-        L, xs = layers[i % len(layers)]
-        x = xs[(i // len(layers)) % n_x]
-        if record:
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            L.ffn_events = (e0, e1)
-        else:
-            L.ffn_events = None
-        L.step(x, T, host_pass=False)
-        if record:
-            ev_pairs.append((e0, e1, L))
-
-    for i in range(args.warmup):
-        one_step(i, False)
-    torch.cuda.synchronize()
     t1 = time.perf_counter()
-    for i in range(args.steps):
-        one_step(args.warmup + i, True)
-    torch.cuda.synchronize()
+    ffn_ms_arr, per_launch, distinct = gpu_ffn_pass(m, torch, layers, n_x, T, args.steps, args.warmup, x_dtype,
+                                                    H, E, k, slab)
     elapsed_py = time.perf_counter() - t1
-    for e0, e1, L in ev_pairs:
-        ffn_ms.append(e0.elapsed_time(e1))
-
-    # algorithmic bytes of one moe_ffn_slots launch: every distinct resident slab the step touched, read
-    # once, plus x in and y out.  Distinct slabs per step: rerun each timed step's routing (untimed).
-    distinct = []
-    for i in range(args.steps):
-        L, xs = layers[(args.warmup + i) % len(layers)]
-        x = xs[((args.warmup + i) // len(layers)) % n_x]
-        m.moe_route(x, x_dtype, L.G, None, None, T, H, E, k, L.ids, L.w, None)
-        torch.cuda.synchronize()
-        ids = L.ids[:T * k].cpu().numpy()
-        e2s = L.e2s.cpu().numpy()
-        sl = e2s[ids]
-        distinct.append(len(set(sl[sl >= 0].tolist())))
-    act_bytes = T * H * 2 + T * H * 4  # x (bf16) in, y (fp32) out
-    per_launch = [d * slab + act_bytes for d in distinct]
-    ffn_ms_arr = np.array(ffn_ms)
     achieved = float(np.mean(per_launch) / (np.mean(ffn_ms_arr) * 1e-3) / 1e9)
+    # the smaller decode batches of the same layer (same layers, same steps, first T rows of x)
+    batches = {}
+    for Tb in (1, 8):
+        ms_b, pl_b, d_b = gpu_ffn_pass(m, torch, layers, n_x, Tb, args.steps, args.warmup, x_dtype, H, E, k, slab)
+        gbs = float(np.mean(pl_b) / (np.mean(ms_b) * 1e-3) / 1e9)
+        batches[f"T{Tb}"] = {"ffn_us": round(float(np.mean(ms_b)) * 1e3, 2), "bytes_per_launch": int(np.mean(pl_b)),
+                             "distinct_slabs_per_step": round(float(np.mean(d_b)), 2), "gbs": round(gbs, 1),
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+    batches["T64"] = {"ffn_us": round(float(np.mean(ffn_ms_arr)) * 1e3, 2), "bytes_per_launch": int(np.mean(per_launch)),
+                      "distinct_slabs_per_step": round(float(np.mean(distinct)), 2), "gbs": round(achieved, 1),
+                      "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
 
     out = {
         "metric": "MoE-layer tokens/s; expert-weight HBM GB/s as % of peak; gather GB/s",
@@ -264,21 +248,86 @@ def main():
                      "kernel": "moe_ffn_slots (pick sort, MFMA gate/up and down grouped GEMMs, reduction)",
                      "bytes_per_launch": int(np.mean(per_launch)), "ms_per_launch": round(float(np.mean(ffn_ms_arr)), 5),
                      "distinct_slabs_per_step": round(float(np.mean(distinct)), 2)},
+        "decode_batches": dict(batches, workload="the same 128-expert bf16 layer, 64 resident slots, moe_ffn_slots "
+                                                 "alone (HIP events), 4 layer copies rotated"),
     }
 
-    del layers
+    del layers, specs
     native.close()
+    del native
+    release(torch)
     link = None
     if not args.no_gather:
         out["gather"] = measure_gather(m, torch, synth)
         link = out["gather"]["link_gbs"]
+        release(torch)
     if not args.no_prefill:
-        out["prefill"] = bench_prefill(m, torch, synth, SlotLayer)
+        out["prefill"], store5 = bench_prefill(m, torch, synth, SlotLayer)
+        out["prefill_144"] = bench_prefill_144(m, torch, synth, NativeStack, store5, nthreads)
+        del store5
+        release(torch)
     if not args.no_dynamic:
         out["dynamic"] = bench_dynamic(m, torch, synth, SlotLayer, NativeStack, nthreads, link)
+        release(torch)
+    if not args.no_stack:
+        st = bench_stack(m, torch, synth, SlotStack, NativeStack, nthreads, args)
+        out["stack"] = {key: st[key] for key in ("workload", "T1", "T32")}
+        release(torch)
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(synth, T)
     print(json.dumps(out), flush=True)
+
+
+def release(torch):
+    """Hand the memory of finished legs back: device memory and pinned host
+    memory that torch keeps cached (the 48-layer stack pins 43.5 GB)."""
+    import gc
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    if hasattr(torch._C, "_host_emptyCache"):
+        torch._C._host_emptyCache()
+
+
+def gpu_ffn_pass(m, torch, layers, n_x, T, steps, warmup, x_dtype, H, E, k, slab):
+    """route -> manage -> moe_ffn_slots for T tokens over the rotated layers,
+    no host pass, HIP events around every moe_ffn_slots launch; returns the
+    per-launch times (ms), the algorithmic bytes of each launch (every
+    distinct resident slab the step touched, read once, plus x in and y out)
+    and the distinct slabs per step (from rerunning each step's routing,
+    untimed)."""
+    ev_pairs = []
+
+    def one_step(i, record):
+        L, xs = layers[i % len(layers)]
+        x = xs[(i // len(layers)) % n_x][:T]
+        if record:
+            L.ffn_events = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+        else:
+            L.ffn_events = None
+        L.step(x, T, host_pass=False)
+        if record:
+            ev_pairs.append(L.ffn_events)
+        L.ffn_events = None
+
+    for i in range(warmup):
+        one_step(i, False)
+    torch.cuda.synchronize()
+    for i in range(steps):
+        one_step(warmup + i, True)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev_pairs])
+    distinct = []
+    for i in range(steps):
+        L, xs = layers[(warmup + i) % len(layers)]
+        x = xs[((warmup + i) // len(layers)) % n_x][:T]
+        m.moe_route(x, x_dtype, L.G, None, None, T, H, E, k, L.ids, L.w, None)
+        torch.cuda.synchronize()
+        ids = L.ids[:T * k].cpu().numpy()
+        sl = L.e2s.cpu().numpy()[ids]
+        distinct.append(len(set(sl[sl >= 0].tolist())))
+    act_bytes = T * H * 2 + T * H * 4  # x (bf16) in, y (fp32) out
+    return ms, [d * slab + act_bytes for d in distinct], distinct
 
 
 def bench_prefill(m, torch, synth, SlotLayer, steps=10, warmup=2):
@@ -288,7 +337,7 @@ def bench_prefill(m, torch, synth, SlotLayer, steps=10, warmup=2):
     E, k, H, I, T = c["E"], c["k"], c["H"], c["I"], c["T"]
     base = synth.config_seed("c5")
     slab = synth.slab_bytes(synth.W_BF16, H, I)
-    store = torch.empty((E, slab), dtype=torch.uint8)
+    store = torch.empty((E, slab), dtype=torch.uint8, pin_memory=True)  # also the 144-slot variant's host store
     synth.slabs_into(store.data_ptr(), synth.W_BF16, base, 0, 0, E, H, I, c["sigma_w"], slab)
     slots = store.cuda()
     G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
@@ -342,7 +391,61 @@ def bench_prefill(m, torch, synth, SlotLayer, steps=10, warmup=2):
     flops2 = 2.0 * T2 * k * 3 * H * I
     out["supplemental_16384_tokens"] = {"ffn_ms": round(ms2, 3), "ffn_tflops": round(flops2 / ms2 / 1e9, 1),
                                         "mfma_frac": round(flops2 / ms2 / 1e9 / MFMA_BF16_PEAK_TFS, 4)}
-    return out
+    del L, slots, ws, x2, y
+    return out, store
+
+
+def bench_prefill_144(m, torch, synth, NativeStack, store, nthreads, steps=3):
+    """The 144-slot variant of the 288-expert layer at 2048 tokens: the 144
+    most-picked experts of a 1024-token profile batch resident, the other 144
+    in pinned host memory, served by the step itself.  Timed with the native
+    driver as it chooses (at this batch: streamed through the GPU's staging
+    slots), then with the CPU lane forced, and on the GPU alone (the
+    non-resident picks add zero) for the CPU lane's overlap."""
+    c = synth.CONFIGS["c5"]
+    E, k, H, I, T, S = c["E"], c["k"], c["H"], c["I"], c["T"], c["S_variant"]
+    base = synth.config_seed("c5")
+    slab = synth.slab_bytes(synth.W_BF16, H, I)
+    G = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_G, 0), (E, H), c["sigma_g"], 1).view(np.int16)).cuda()
+    warm = torch.from_numpy(synth.normal(synth.key(base, synth.TAG_WARM, 0), (1024, H), 1.0, 1).view(np.int16)).cuda()
+    wids = torch.empty((1024, k), dtype=torch.int32, device="cuda")
+    ww = torch.empty((1024, k), dtype=torch.float32, device="cuda")
+    m.moe_route(warm, 1, G, None, None, 1024, H, E, k, wids, ww, None)
+    resident = torch.empty(S, dtype=torch.int32, device="cuda")
+    m.cache_pick_static(wids, 1024 * k, E, S, resident)
+    torch.cuda.synchronize()
+    slots = store[torch.from_numpy(resident.cpu().numpy().astype(np.int64))].cuda()
+    spec = dict(host_store=store, slot_store=slots, G=G, bias=None, resident=resident)
+    nat = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=synth.W_BF16, T_max=T, layers=[spec], n_threads=nthreads)
+    xs = [torch.from_numpy(synth.normal(synth.key(base, synth.TAG_X, 0, st), (T, H), 1.0, 1).view(np.int16)).cuda()
+          for st in range(2)]
+
+    def timed(host_pass):
+        nat.layer_step(0, xs[0], T, host_pass=host_pass)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            nat.layer_step(0, xs[1 - i % 2], T, host_pass=host_pass)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / steps * 1e3
+
+    auto_ms = timed(True)
+    mode = nat.last_host_mode()
+    nat.stats(reset=True)
+    nat.layer_step(0, xs[0], T)
+    hits, distinct, _, n_host = nat.stats(reset=True)
+    nat.set_stream_threshold(-1)
+    cpu_ms = timed(True)
+    gpu_ms = timed(False)
+    nat.close()
+    return {"workload": "288-expert bf16 MoE layer, H=4096 I=1536 top-8, 2048 tokens, 144 experts resident, the "
+                        f"other 144 in pinned host memory, native moe_layer_step, {nthreads} host threads",
+            "tokens_per_s": round(T / auto_ms * 1e3, 1), "ms_per_step": round(auto_ms, 2),
+            "host_misses_served_by": {1: "CPU lane", 2: "streamed through the GPU"}.get(mode, str(mode)),
+            "hit_rate": round(hits / (T * k), 4), "host_experts_per_step": n_host,
+            "streamed_gb_per_step": round(n_host * slab / 1e9, 3) if mode == 2 else 0,
+            "cpu_lane": {"tokens_per_s": round(T / cpu_ms * 1e3, 1), "ms_per_step": round(cpu_ms, 2)},
+            "gpu_only_ms_per_step": round(gpu_ms, 3)}
 
 
 def bench_dynamic(m, torch, synth, SlotLayer, NativeStack, nthreads, link_gbs, steps=256, warmup=8):
@@ -749,19 +852,21 @@ def measure_gather(m, torch, synth):
     e1.record()
     torch.cuda.synchronize()
     g_gbs = reps * n * slab / (e0.elapsed_time(e1) * 1e-3) / 1e9
-    # host link: pinned H2D copy engine, same bytes
-    src = store[:n].reshape(-1)
-    dst = slots.reshape(-1)
+    # host link: pinned H2D copies of 1 GiB by the copy engine, ten of them
+    del slots
+    src = torch.empty(1 << 30, dtype=torch.uint8, pin_memory=True)
+    src[::4096].fill_(3)
+    dst = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
     dst.copy_(src, non_blocking=True)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(reps):
+    for _ in range(10):
         dst.copy_(src, non_blocking=True)
     e1.record()
     torch.cuda.synchronize()
-    link = reps * n * slab / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    link = 10 * (1 << 30) / (e0.elapsed_time(e1) * 1e-3) / 1e9
     return {"gbs": round(g_gbs, 2), "link_gbs": round(link, 2), "frac": round(g_gbs / link, 4),
-            "slab_bytes": slab, "slabs_per_call": n, "link": "pinned hipMemcpyAsync H2D"}
+            "slab_bytes": slab, "slabs_per_call": n, "link": "pinned hipMemcpyAsync H2D, 1 GiB x 10"}
 
 
 def replicate(n):
@@ -828,9 +933,16 @@ def cpu_baseline(synth, T, n_tok=48, reps=3):
     finally:
         os.sched_setaffinity(0, set(cpus))
     dt = float(np.median(dts))
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), None)
+    except OSError:
+        pass
     return {"value": round(n_tok / dt, 3), "unit": "tokens/s", "cores": 1, "kind": "oracle",
             "sample": f"{n_tok} tokens of the same layer: route + full SwiGLU layer in double, one thread pinned "
-                      f"to one core, median of {reps} ({', '.join(f'{d:.1f}' for d in dts)} s)"}
+                      f"to one core, median of {reps} ({', '.join(f'{d:.1f}' for d in dts)} s)",
+            "nproc": len(cpus), "cpu_model": model}
 
 
 # ------------------------------------------------------------ HBM counters
