@@ -54,6 +54,10 @@ constexpr bool X_PREFETCH = true;  // activation granules one chunk ahead (16-by
 constexpr int GROUP_MULTI_P = 4096;  // larger batches sort with one workgroup per 1024 picks
 // bf16 batches with at least this many picks take the MFMA grouped-GEMM path
 constexpr int PF_MIN_P = 512;
+// and W8A8 batches from this many (int8 MFMA tiles; measured on the 128-expert, 2048 x 768 layer with 32
+// slots: at 16 tokens a wash against the row-streaming kernels, 47 vs 49 us with every slot busy and 38 vs 33 us
+// with half of them; from 32 tokens on the tiles win: 49 vs 63 us, 55 vs 99 at 64, 88 vs 341 at 256)
+constexpr int PF_MIN_P_I8 = 256;
 
 // ------------------------------------------------------------ formats
 
@@ -171,7 +175,7 @@ __device__ __forceinline__ void granule_dot_reg(const v4u& w, const v4u& xv, typ
 // ---------------------------------------------------------- workspace
 
 struct WsLayout {
-    size_t slot_off, pair_list, active, n_active, gcnt, pf_tiles, h, hq, hs, xq, xs, xbs, hbs, part, total;
+    size_t slot_off, pair_list, active, n_active, gcnt, pf_tiles, h, hq, hs, hmax, xq, xs, xbs, hbs, part, total;
 };
 
 WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
@@ -194,6 +198,7 @@ WsLayout ws_layout(int T, int k, int S, int w_type, int H, int I) {
     if (w_type == MOE_W_W8A8) {
         L.hq = take(P * I);
         L.hs = take(4 * P);
+        L.hmax = take(4 * (P ? P : 1) * (size_t)((I + 63) / 64));
         L.xq = take((size_t)T * H);
         L.xs = take(4 * (size_t)T);
     }
@@ -950,18 +955,23 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     void* hbuf = ws + L.h;
     float* part = reinterpret_cast<float*>(ws + L.part);
     int rc;
-    // bf16 batches of PF_MIN_P picks or more run on the MFMA grouped GEMM; the sort writes its tile list
-    const bool use_pf = F == MOE_W_BF16 && P >= PF_MIN_P && moe_pf_supported(F, H, I);
+    // bf16 batches of PF_MIN_P picks or more, and int8 batches of PF_MIN_P_I8 or more, run on the MFMA grouped GEMMs;
+    // the sort writes their tile list
+    const bool use_pf = ((F == MOE_W_BF16 && P >= PF_MIN_P) || (F == MOE_W_W8A8 && P >= PF_MIN_P_I8)) &&
+                        moe_pf_supported(F, H, I);
+    const int pf_mt = moe_pf_tile_rows_for(F, T, k, S, H, I);
     moe_pf_tile* pf_tiles = use_pf ? reinterpret_cast<moe_pf_tile*>(ws + L.pf_tiles) : nullptr;
     int32_t* pf_n_tiles = use_pf ? reinterpret_cast<int32_t*>(ws + L.pf_tiles + (size_t)moe_pf_max_tiles(T, k, S) *
                                                                                      sizeof(moe_pf_tile))
                                  : nullptr;
 
     // decode-sized bf16 batches: the gate/up GEMM sorts the picks itself
-    const bool fused_sort = use_pf && moe_pf_fused_sort(T, k);
+    const bool fused_sort = F == MOE_W_BF16 && use_pf && moe_pf_fused_sort(T, k);
+    // int8 matrix-core path: per gate/up column tile and pick, the max |h|
+    float* hmax = (F == MOE_W_W8A8 && use_pf) ? reinterpret_cast<float*>(ws + L.hmax) : nullptr;
     // quantised batches sorted by one workgroup: x prepared in the same launch
     int xprep = XPREP_NONE;
-    if (!use_pf && P <= GROUP_MULTI_P) {
+    if (P <= GROUP_MULTI_P) {
         if constexpr (F == MOE_W_W8A8) xprep = XPREP_I8;
         if constexpr (F == MOE_W_Q4B32) xprep = XPREP_BSUM;
     }
@@ -973,20 +983,31 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hipLaunchKernelGGL(k_group_hist, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt);
         if ((rc = moe_check_launch("moe_ffn_slots/group_hist"))) return rc;
         hipLaunchKernelGGL(k_group_place, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt, nch, slot_off,
-                           pair_list, active, n_active, pf_tiles, pf_n_tiles, moe_pf_tile_rows(T, k, S, H, I));
+                           pair_list, active, n_active, pf_tiles, pf_n_tiles, pf_mt);
         if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
     } else {
         hipLaunchKernelGGL(k_group, dim3(1 + x_prep_wgs(xprep, T, H)), dim3(GROUP_THREADS), 0, st, slot_ids, P, S,
-                           slot_off, pair_list, active, n_active, pf_tiles, pf_n_tiles,
-                           moe_pf_tile_rows(T, k, S, H, I), xprep, reinterpret_cast<const uint16_t*>(x), T, H,
+                           slot_off, pair_list, active, n_active, pf_tiles, pf_n_tiles, pf_mt, xprep,
+                           reinterpret_cast<const uint16_t*>(x), T, H,
                            reinterpret_cast<int8_t*>(ws + L.xq), reinterpret_cast<float*>(ws + L.xs),
                            reinterpret_cast<float*>(ws + L.xbs));
         if ((rc = moe_check_launch("moe_ffn_slots/group"))) return rc;
     }
 
     if (use_pf) {
-        rc = moe_pf_run(x, w, T, k, slot_store, slab_bytes, S, H, I, lay, pair_list, ws + L.pf_tiles, hbuf, part,
-                        st, fused_sort ? slot_ids : nullptr);
+        const void* act = x;
+        const float* xs = nullptr;
+        if constexpr (F == MOE_W_W8A8) {
+            act = ws + L.xq;
+            xs = reinterpret_cast<const float*>(ws + L.xs);
+            if (!xprep) {  // the sort ran as hist + place: x's codes in a launch of their own
+                hipLaunchKernelGGL((k_quant_rows<true>), dim3(T), dim3(256), 0, st, x, H, (const int32_t*)nullptr,
+                                   reinterpret_cast<int8_t*>(ws + L.xq), reinterpret_cast<float*>(ws + L.xs));
+                if ((rc = moe_check_launch("moe_ffn_slots/quant_x"))) return rc;
+            }
+        }
+        rc = moe_pf_run(act, w, T, k, slot_store, slab_bytes, S, H, I, lay, pair_list, ws + L.pf_tiles, hbuf, part,
+                        st, fused_sort ? slot_ids : nullptr, F, xs, hmax);
         if (rc) return rc;
         const int64_t n4 = (int64_t)T * (H / 4);
         hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, slot_ids, T, k, S,

@@ -36,6 +36,7 @@
 #include <math.h>
 
 #include <mutex>
+#include <type_traits>
 
 #include "common.hpp"
 #include "prefill.hpp"
@@ -44,6 +45,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x16 __attribute__((ext_vector_type(16)));
 using v4u = uint32_t __attribute__((ext_vector_type(4)));
 
 constexpr int PF_THREADS = 256;
@@ -76,8 +79,11 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // The sum over k is then taken in a rotated order, fixed per workgroup.
 // Rows whose length is not a multiple of 4 KiB spread by themselves (and the
 // down GEMM of the decode layer ran slower rotated), so they start at 0.
+#ifndef ROT_BYTES
+#define ROT_BYTES 4096
+#endif
 __device__ __forceinline__ int k_rot(int nk) {
-    return (nk * PF_ROWB) % 4096 == 0 ? (int)(blockIdx.x % (unsigned)nk) : 0;
+    return (nk * PF_ROWB) % ROT_BYTES == 0 ? (int)(blockIdx.x % (unsigned)nk) : 0;
 }
 
 using PfTile = moe_pf_tile;
@@ -105,6 +111,12 @@ struct PfArgs {
     int32_t* pair_out;
     PfTile* tiles_out;
     int32_t* n_tiles_out;
+    // int8 weights (W8A8) only: the per-row scale planes (GU: gate, up; DOWN:
+    // down) and the per-token activation scales of x (GU)
+    int64_t s0, s1;
+    const float* xscale;
+    float* hmax;                 // [GU column tiles][P]: each tile's max |h| per pick (sorted order)
+    int hstride;                 // P, the stride of hmax between column tiles
 };
 
 __device__ __forceinline__ v4u ld16(const unsigned char* p) { return *reinterpret_cast<const v4u*>(p); }
@@ -384,16 +396,40 @@ __device__ bool dec_sort_tile(const PfArgs& g, int e, int jn, unsigned char* lds
 // 16 (gate) and c + 16 (up) of one wave pair up through one lane exchange.
 // The k-loop is the grouped GEMM's: two register sets ahead of two LDS
 // buffers, XOR-swizzled 16-byte chunks.
-template <int MODE, int NW, int NR>
+//
+// Q8 (W8A8 weights): the same tiles and pipeline on v_mfma_i32_32x32x32_i8,
+// whose operands take 16 bytes per lane in the same places as the bf16 one
+// (a k-step is then 128 int8 elements), with exact int32 accumulators.  The
+// gate/up A operand is x's int8 codes (made with the pick sort); its epilogue
+// dequantises (acc * s_x) * s_w in fp32, evaluates SwiGLU in double, stores h
+// in fp32 (sorted order) and stores, per pick, the max |h| over its own 64 h
+// columns (one plain store per pick and column tile: no atomics, nothing to
+// clear).  The down kernel quantises h itself: its prologue takes each pick's
+// max over those column tiles (scale max / 127, 1 for a zero row), and the A
+// operand is fetched as fp32 h and turned into int8 codes (round half to
+// even, clamp 127) when it is stored to LDS; its epilogue is w * ((acc *
+// s_h) * s_w).  The first k-steps' loads go out before the prologues, which
+// only wait for small reads.  (Quantising x in the gate/up kernel as well,
+// with the picks sorted there too, was slower: the sort's latency is exposed
+// in every workgroup, which cannot fetch a weight before it knows its slot.)  This is the arithmetic of the row-streaming
+// W8A8 kernels and of k_quant_rows, so the results match them.
+template <int MODE, int NW, int NR, bool Q8 = false>
 __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     constexpr int NTH = 64 * NW;
     constexpr int WR = 32 * NW;                  // weight rows per tile
+    constexpr int ESZ = Q8 ? 1 : 2;               // bytes per operand element
     constexpr int A_BYTES = DEC_MT * PF_ROWB;     // 4 KiB per k-step
     constexpr int B_BYTES = WR * PF_ROWB;
     constexpr int NA = DEC_MT * 8 / NTH;          // A chunks per thread and k-step
     constexpr int NBU = WR * 8 / NTH;             // B chunks per thread and k-step (4)
+    // the down kernel's int8 A operand is fetched as fp32 h and quantised on the way to LDS: four 16-byte
+    // pieces per 16-byte chunk of codes
+    constexpr bool AQ = Q8 && MODE == PF_DOWN;
+    constexpr int APC = AQ ? 4 : 1;
     static_assert(NA >= 1 && NBU >= 1, "tile shape");
     extern __shared__ __attribute__((aligned(16))) unsigned char dec_lds[];
+    __shared__ float q_row[DEC_MT];               // Q8: per token row, s_x (gate/up) or s_h (down)
+    __shared__ float q_max[NW][DEC_MT];           // Q8 gate/up: per wave and token row, the max |h|
     const int b = blockIdx.x;
     const int xcd = b % PF_XCD, i = b / PF_XCD;
     const int e = xcd + PF_XCD * (i / g.ntiles_n);
@@ -408,7 +444,7 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
         tl = g.tiles[e];
     }
     const unsigned char* slab = g.slots + (size_t)tl.slot * g.slab_bytes;
-    const size_t row_bytes = (size_t)g.K * 2;
+    const size_t row_bytes = (size_t)g.K * ESZ;
 
     const unsigned char* arow[NA];
     int aso[NA];
@@ -421,10 +457,9 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
             idx = (fused ? reinterpret_cast<const int32_t*>(dec_lds + DEC_SORT_ROWS)[rr] : g.pair_list[tl.p0 + rr]) /
                   g.k;
         else idx = tl.p0 + rr;
-        arow[q] = g.act + (size_t)idx * row_bytes + ch * 16;
+        arow[q] = g.act + (size_t)idx * row_bytes * APC + ch * 16 * APC;
         aso[q] = r * PF_ROWB + ((ch ^ swz(r)) * 16);
     }
-    if (fused) __syncthreads();  // the sort's LDS is the first k-step's buffer
     const unsigned char* brow[NBU];
     int bso[NBU];
 #pragma unroll
@@ -450,26 +485,49 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
         a_off[ks] = ar * PF_ROWB + (((ks * 2 + khalf) ^ swz(ar)) * 16);
         b_off[ks] = br * PF_ROWB + (((ks * 2 + khalf) ^ swz(br)) * 16);
     }
-    f32x16 acc;
+    using AccV = typename std::conditional<Q8, i32x16, f32x16>::type;
+    AccV acc;
 #pragma unroll
-    for (int x = 0; x < 16; ++x) acc[x] = 0.0f;
+    for (int x = 0; x < 16; ++x) acc[x] = 0;
 
-    const int nk = g.K / PF_KT;
-    v4u ra[NR][NA], rb[NR][NBU];
+    const int nk = (int)(row_bytes / PF_ROWB);
+    v4u ra[NR][NA * APC], rb[NR][NBU];
+    float ascale[NA];  // Q8: the scale of each A chunk's token row
     const int rot = k_rot(nk);  // each workgroup walks k from its own starting step
-    auto fetch = [&](v4u (&a)[NA], v4u (&w)[NBU], int kt) {
+    auto fetch = [&](v4u (&a)[NA * APC], v4u (&w)[NBU], int kt) {
         const int kr = kt + rot;
         const size_t ko = (size_t)(kr >= nk ? kr - nk : kr) * PF_ROWB;
 #pragma unroll
-        for (int q = 0; q < NA; ++q) a[q] = ld16(arow[q] + ko);
+        for (int q = 0; q < NA; ++q)
+#pragma unroll
+            for (int c = 0; c < APC; ++c) a[q * APC + c] = ld16(arow[q] + ko * APC + 16 * c);
 #pragma unroll
         for (int q = 0; q < NBU; ++q) w[q] = ld16_nt(brow[q] + ko);
     };
-    auto stash = [&](const v4u (&a)[NA], const v4u (&w)[NBU], int buf) {
+    auto stash = [&](const v4u (&a)[NA * APC], const v4u (&w)[NBU], int buf) {
         unsigned char* A = dec_lds + buf * (A_BYTES + B_BYTES);
         unsigned char* B = A + A_BYTES;
 #pragma unroll
-        for (int q = 0; q < NA; ++q) *reinterpret_cast<v4u*>(A + aso[q]) = a[q];
+        for (int q = 0; q < NA; ++q) {
+            if constexpr (AQ) {
+                // 16 fp32 h values -> 16 int8 codes: rint(v / s), clamped to +-127
+                uint32_t packed[4];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    uint32_t word = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float v = __uint_as_float(a[q * APC + c][e]);
+                        const float cd = fminf(fmaxf(rintf(v / ascale[q]), -127.0f), 127.0f);
+                        word |= ((uint32_t)(int)cd & 0xFFu) << (8 * e);
+                    }
+                    packed[c] = word;
+                }
+                *reinterpret_cast<v4u*>(A + aso[q]) = v4u{packed[0], packed[1], packed[2], packed[3]};
+            } else {
+                *reinterpret_cast<v4u*>(A + aso[q]) = a[q];
+            }
+        }
 #pragma unroll
         for (int q = 0; q < NBU; ++q) *reinterpret_cast<v4u*>(B + bso[q]) = w[q];
     };
@@ -478,9 +536,14 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
         const unsigned char* B = A + A_BYTES;
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
-            const bf16x8 av = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(A + a_off[ks]));
-            const bf16x8 bv = __builtin_bit_cast(bf16x8, *reinterpret_cast<const v4u*>(B + b_off[ks]));
-            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(av, bv, acc, 0, 0, 0);
+            const v4u a16 = *reinterpret_cast<const v4u*>(A + a_off[ks]);
+            const v4u b16 = *reinterpret_cast<const v4u*>(B + b_off[ks]);
+            if constexpr (Q8)
+                acc = __builtin_amdgcn_mfma_i32_32x32x32_i8(__builtin_bit_cast(i32x4, a16),
+                                                            __builtin_bit_cast(i32x4, b16), acc, 0, 0, 0);
+            else
+                acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a16),
+                                                              __builtin_bit_cast(bf16x8, b16), acc, 0, 0, 0);
         }
     };
     // NR register sets in a ring ahead of the two LDS buffers: step t is
@@ -492,6 +555,28 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
 #pragma unroll
     for (int r = 0; r < NR; ++r)
         if (r < nk) fetch(ra[r], rb[r], r);
+    if constexpr (Q8) {
+        // the token rows' scales, while the first k-steps are in flight
+        if constexpr (MODE == PF_GU) {
+            // each token row's activation scale (made with x's codes)
+            if (tid < DEC_MT && tid < tl.rows) {
+                const int pk = fused ? reinterpret_cast<const int32_t*>(dec_lds + DEC_SORT_ROWS)[tid]
+                                     : g.pair_list[tl.p0 + tid];
+                q_row[tid] = g.xscale[pk / g.k];
+            }
+        } else {
+            // h's per-row scale from the gate/up column tiles' maxima of |h|
+            if (tid < DEC_MT && tid < tl.rows) {
+                float mx = 0.0f;
+                for (int j = 0; j < g.K / 64; ++j) mx = fmaxf(mx, g.hmax[(size_t)j * g.hstride + tl.p0 + tid]);
+                q_row[tid] = mx > 0.0f ? mx / 127.0f : 1.0f;
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < NA; ++q) ascale[q] = q_row[min((q * NTH + tid) >> 3, tl.rows - 1)];
+    }
+    if (fused) __syncthreads();  // the sort's LDS is the first k-step's buffer
     stash(ra[0], rb[0], 0);
     lds_barrier();
     auto step = [&](int j, int t, bool tail) {  // j = t % U, static in every caller
@@ -512,25 +597,57 @@ __global__ void __launch_bounds__(64 * NW) k_dec_gemm(PfArgs g) {
     // accumulator element x of lane l: column l % 32 of this wave's block, row (x/4)*8 + (l/32)*4 + x%4
     const int col = lane & 31;
     if constexpr (MODE == PF_GU) {
-        uint16_t* h = reinterpret_cast<uint16_t*>(g.out);
+        const int n = jn * (16 * NW) + wv * 16 + (col & 15);  // the h column (gate row and up row) of this lane
+        float sg = 0.0f, su = 0.0f;
+        if constexpr (Q8) {
+            sg = reinterpret_cast<const float*>(slab + g.s0)[n];
+            su = reinterpret_cast<const float*>(slab + g.s1)[n];
+        }
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
-            const float up = __shfl_xor(acc[x], 16, 64);  // every lane takes part
+            const auto up = __shfl_xor(acc[x], 16, 64);  // every lane takes part
             const int r = (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
-            if (r < tl.rows && col < 16) {
+            if constexpr (Q8) {
+                float hv = 0.0f;
+                if (r < tl.rows && col < 16) {
+                    const float sx = q_row[r];
+                    const float gv = ((float)acc[x] * sx) * sg;
+                    const float uv = ((float)up * sx) * su;
+                    hv = (float)(((double)gv / (1.0 + exp(-(double)gv))) * (double)uv);
+                    reinterpret_cast<float*>(g.out)[(size_t)(tl.p0 + r) * g.N + n] = hv;
+                }
+                // max |h| of row r over this wave's 16 h columns (lanes col 0..15 of the half-wave; the up
+                // lanes hold 0)
+                float mx = fabsf(hv);
+#pragma unroll
+                for (int o = 1; o < 32; o <<= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+                if (col == 0) q_max[wv][r] = mx;
+            } else if (r < tl.rows && col < 16) {
                 const float gv = acc[x];
                 const float hv = gv / (1.0f + expf(-gv)) * up;
-                h[(size_t)(tl.p0 + r) * g.N + jn * (16 * NW) + wv * 16 + col] = moe::f32_to_bf16(hv);
+                reinterpret_cast<uint16_t*>(g.out)[(size_t)(tl.p0 + r) * g.N + n] = moe::f32_to_bf16(hv);
+            }
+        }
+        if constexpr (Q8) {  // this column tile's max |h| per pick, over its 16 * NW h columns
+            __syncthreads();
+            if (tid < tl.rows) {
+                float mx = q_max[0][tid];
+#pragma unroll
+                for (int w = 1; w < NW; ++w) mx = fmaxf(mx, q_max[w][tid]);
+                g.hmax[(size_t)jn * g.hstride + tl.p0 + tid] = mx;
             }
         }
     } else {
         float* part = reinterpret_cast<float*>(g.out);
+        const int m = jn * WR + wv * 32 + col;  // output column (down row) of this lane
+        const float sd = Q8 ? reinterpret_cast<const float*>(slab + g.s0)[m] : 1.0f;
 #pragma unroll
         for (int x = 0; x < 16; ++x) {
             const int r = (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
             if (r >= tl.rows) continue;
             const int pk = g.pair_list[tl.p0 + r];
-            part[(size_t)pk * g.N + jn * WR + wv * 32 + col] = g.wts[pk] * acc[x];
+            if constexpr (Q8) part[(size_t)pk * g.N + m] = g.wts[pk] * (((float)acc[x] * q_row[r]) * sd);
+            else part[(size_t)pk * g.N + m] = g.wts[pk] * acc[x];
         }
     }
 }
@@ -821,10 +938,11 @@ int pb_launch(const void* x, const float* w, int k, const void* slot_store, size
     return moe_check_launch("moe_ffn_slots/large_down");
 }
 
-template <int NW>
+template <int NW, bool Q8>
 int dec_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
                const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
-               int max_tiles, void* hbuf, float* part, hipStream_t st, const int32_t* sort_slots, int P, int S) {
+               int max_tiles, void* hbuf, float* part, hipStream_t st, const int32_t* sort_slots, int P, int S,
+               const float* xscale, float* hmax) {
     const int lds = 2 * (DEC_MT + 32 * NW) * PF_ROWB;
     static_assert(DEC_SORT_SCR + 64 <= 2 * (DEC_MT + 32 * DEC_NW) * PF_ROWB, "the sort fits the kernel's LDS");
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
@@ -838,14 +956,26 @@ int dec_launch(const void* x, const float* w, int k, const void* slot_store, siz
         gu.tiles_out = const_cast<PfTile*>(tiles);
         gu.n_tiles_out = const_cast<int32_t*>(n_tiles);
     }
-    hipLaunchKernelGGL((k_dec_gemm<PF_GU, NW, DEC_NR_GU>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
+    if (Q8) {
+        gu.s0 = lay.s[0];
+        gu.s1 = lay.s[1];
+        gu.xscale = xscale;
+        gu.hmax = hmax;
+        gu.hstride = P;
+    }
+    hipLaunchKernelGGL((k_dec_gemm<PF_GU, NW, DEC_NR_GU, Q8>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
                        dim3(64 * NW), lds, st, gu);
     int rc;
     if ((rc = moe_check_launch("moe_ffn_slots/decode_gate_up"))) return rc;
     PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
               reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k,
               H / (32 * NW)};
-    hipLaunchKernelGGL((k_dec_gemm<PF_DOWN, NW, DEC_NR_DN>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+    if (Q8) {
+        dn.s0 = lay.s[2];
+        dn.hmax = hmax;
+        dn.hstride = P;
+    }
+    hipLaunchKernelGGL((k_dec_gemm<PF_DOWN, NW, DEC_NR_DN, Q8>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
                        dim3(64 * NW), lds, st, dn);
     return moe_check_launch("moe_ffn_slots/decode_down");
 }
@@ -896,8 +1026,8 @@ int pf_launch(const void* x, const float* w, int k, const void* slot_store, size
 }  // namespace
 
 bool moe_pf_supported(int w_type, int H, int I) {
-    // column tiles of 64 h columns / 128 output rows; contraction in pairs of 64-wide steps
-    return w_type == MOE_W_BF16 && H % 128 == 0 && I % 128 == 0;
+    // column tiles of 64 h columns / 128 output rows; contraction in 128-byte steps (pairs of them for bf16)
+    return (w_type == MOE_W_BF16 || w_type == MOE_W_W8A8) && H % 128 == 0 && I % 128 == 0;
 }
 
 int moe_pf_tile_rows(int T, int k) { return T * k < PF_BIG_P ? DEC_MT : PF_MT; }
@@ -916,9 +1046,14 @@ int moe_pf_tile_rows(int T, int k, int S, int H, int I) {
     return moe_pf_big(T, k, S, H, I) ? PB_MT : moe_pf_tile_rows(T, k);
 }
 
+int moe_pf_tile_rows_for(int w_type, int T, int k, int S, int H, int I) {
+    return w_type == MOE_W_W8A8 ? DEC_MT : moe_pf_tile_rows(T, k, S, H, I);
+}
+
 int moe_pf_max_tiles(int T, int k, int S) {
     const int P = T * k;
-    return (S < P ? S : P) + P / moe_pf_tile_rows(T, k) + 1;  // bounds the sum over slots of ceil(n_s / rows)
+    // bounds the sum over slots of ceil(n_s / rows) for every tile height in use (32 rows and up)
+    return (S < P ? S : P) + P / DEC_MT + 1;
 }
 
 size_t moe_pf_tiles_bytes(int T, int k, int S) { return (size_t)moe_pf_max_tiles(T, k, S) * sizeof(PfTile) + 16; }
@@ -930,18 +1065,25 @@ bool moe_pf_fused_sort(int T, int k) {
 
 int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_store, size_t slab_bytes, int S, int H,
                int I, const moe_slab_layout_t& lay, const int32_t* pair_list, void* tiles_ws, void* hbuf, float* part,
-               hipStream_t st, const int32_t* sort_slots) {
+               hipStream_t st, const int32_t* sort_slots, int w_type, const float* xscale, float* hmax) {
     const int P = T * k;
     const int max_tiles = moe_pf_max_tiles(T, k, S);
     const PfTile* tiles = reinterpret_cast<const PfTile*>(tiles_ws);
     const int32_t* n_tiles = reinterpret_cast<const int32_t*>(reinterpret_cast<unsigned char*>(tiles_ws) +
                                                               (size_t)max_tiles * sizeof(PfTile));
+    if (w_type == MOE_W_W8A8) {
+        // int8 weights: decode-shaped tiles at every batch size (x given as int8 codes with per-token scales;
+        // the sort wrote 32-row tiles, moe_pf_tile_rows_for)
+        // (2 waves per workgroup, or 3 / 4 register sets in the ring: slower at 16 tokens of the 128-expert layer)
+        return dec_launch<DEC_NW, true>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
+                                        max_tiles, hbuf, part, st, sort_slots, P, S, xscale, hmax);
+    }
 
     // decode-sized batches (a few picks per slot): 32-row token tiles; large groups: 256-row tiles
     if (sort_slots && !moe_pf_fused_sort(T, k)) return moe_fail(MOE_E_ARG, "moe_pf_run: no fused sort for %d picks", P);
     if (P < PF_BIG_P)
-        return dec_launch<DEC_NW>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles,
-                                  hbuf, part, st, sort_slots, P, S);
+        return dec_launch<DEC_NW, false>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
+                                         max_tiles, hbuf, part, st, sort_slots, P, S, nullptr, nullptr);
     if (moe_pf_big(T, k, S, H, I))
         return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
                          part, st);

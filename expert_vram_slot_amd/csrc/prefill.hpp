@@ -23,6 +23,9 @@ size_t moe_pf_tiles_bytes(int T, int k, int S);
 int moe_pf_tile_rows(int T, int k);
 int moe_pf_tile_rows(int T, int k, int S, int H, int I);
 bool moe_pf_big(int T, int k, int S, int H, int I);
+// Token rows per tile for a weight format: int8 weights always take 32-row
+// (decode-shaped) tiles; bf16 as moe_pf_tile_rows(T, k, S, H, I).
+int moe_pf_tile_rows_for(int w_type, int T, int k, int S, int H, int I);
 // Largest number of tiles T*k picks over S slots can need.
 int moe_pf_max_tiles(int T, int k, int S);
 // True when a batch of T*k picks can be sorted by the gate/up workgroups
@@ -34,6 +37,12 @@ bool moe_pf_fused_sort(int T, int k);
 // the sorting kernels; otherwise (moe_pf_fused_sort(T, k) must hold) the
 // gate/up kernel sorts the picks by sort_slots (slot per pick) and writes
 // both for the down kernel.
+// int8 weights (w_type MOE_W_W8A8): x is the int8 codes [T][H] with per-token
+// scales xscale[T], h goes to hbuf in fp32 (sorted order) and each gate/up
+// column tile's max |h| per pick to hmax[I / 64][P] (sorted order; written in
+// full, nothing to clear), decode-shaped tiles at every batch size (the tile
+// rows the sort wrote must be 32; no fused sort).
 int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_store, size_t slab_bytes, int S, int H,
                int I, const moe_slab_layout_t& lay, const int32_t* pair_list, void* tiles_ws, void* hbuf,
-               float* part, hipStream_t st, const int32_t* sort_slots = nullptr);
+               float* part, hipStream_t st, const int32_t* sort_slots = nullptr, int w_type = MOE_W_BF16,
+               const float* xscale = nullptr, float* hmax = nullptr);

@@ -513,6 +513,34 @@ def test_ffn_large_batch_sorted_picks(m, w_type, T, H):
     assert_close(y, yg, w_type, f"w{w_type} T={T} k={k}")
 
 
+@pytest.mark.parametrize("T,S,H,I", [(32, 5, 256, 128), (64, 32, 2048, 768), (200, 9, 384, 256), (600, 12, 256, 384),
+                                     (40, 1, 128, 256)])
+def test_ffn_int8_matrix_core_tiles(m, T, S, H, I):
+    """W8A8 batches of 256 picks and more, on the int8 matrix-core tiles (32
+    token rows per tile): one k-step and several, ragged tiles, several tiles
+    per slot, non-resident picks, one slot, the 128-expert layer's shape at 64
+    tokens, 1600 picks (one sorting workgroup with x's codes made in the same
+    launch) and 4800 picks (the sort in two launches, x's codes in a launch of
+    their own); repeat calls give the same bits."""
+    E, k = max(16, 2 * S), 8
+    rng = np.random.default_rng(T * 13 + S)
+    x = synth.normal(synth.key(T, 8, S), (T, H), 1.0, 1)
+    store = synth.slabs(2, 555 + H, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=2, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(2, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 2, f"int8 tiles T={T} S={S} H={H} I={I}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+    np.testing.assert_array_equal(run_ffn(m, li, sl, w, dev(store[resident]), S), y)
+
+
 @pytest.mark.parametrize("T,S", [(64, 24), (128, 40), (129, 40), (70, 1)])
 def test_ffn_decode_sort_in_gemm(m, T, S):
     """bf16 decode batches of 512..1024 picks are grouped by slot inside the

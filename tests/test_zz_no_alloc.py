@@ -3,6 +3,8 @@ moe_ffn_slots (workspace passed in): identical bits, on two calls in a row
 where the second is smaller, for the bf16 MFMA decode path, the bf16 and
 W8A8 row-streaming paths and the 4-bit path; sizes beyond the static scratch
 are refused before anything is enqueued."""
+import gc
+
 import numpy as np
 import pytest
 
@@ -49,11 +51,12 @@ def both(m, li, x, sl, w, slots, S):
     y_ref = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
     m.moe_ffn_slots(x, li.x_dtype, sl, w, T, k, slots, li.slab, S, li.w_type, H, I, y_ref, ws, ws_b)
     y = torch.full((T, H), float("nan"), dtype=torch.float32, device="cuda")
+    gc.collect()  # tensors of earlier cases are freed now, not during the call
     torch.cuda.synchronize()
     before = torch.cuda.memory_allocated()
     m.moe_ffn_slots_noalloc(x, li.x_dtype, sl, w, T, k, slots, li.slab, S, li.w_type, H, I, y)
     torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated() == before
+    assert torch.cuda.memory_allocated() <= before  # nothing allocated through torch by the call
     return y.cpu().numpy(), y_ref.cpu().numpy()
 
 
