@@ -1042,8 +1042,10 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
 
     SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
     const int tiles_gu = (I + 4 * RPW_GU - 1) / (4 * RPW_GU);
+    // at most min(S, P) slots have work: workgroups beyond them would only read n_active and leave
+    const int max_active = S < P ? S : P;
 #define MOE_LAUNCH_GU(G)                                                                                       \
-    hipLaunchKernelGGL((k_gu<F, G>), dim3(S * ((tiles_gu + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, gv,    \
+    hipLaunchKernelGGL((k_gu<F, G>), dim3(max_active * ((tiles_gu + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, gv,    \
                        gu_act, xscale, xbsum, H,                                                                    \
                        I, k, slot_off, pair_list, active, n_active, hbuf, tiles_gu)
     MOE_NCHG_DISPATCH(H / Fmt<F>::EPG, MOE_LAUNCH_GU);
@@ -1072,7 +1074,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
     const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
 #define MOE_LAUNCH_DN(G, LP)                                                                                 \
-    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(S * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, \
+    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(max_active * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, \
                        dv, dn_act, hscale, hbsum,                                                                   \
                        w, H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
     MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
