@@ -62,9 +62,14 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 MFMA_BF16_PEAK_TFS = 2500.0
 
-# kernels launched, in order, by one moe_ffn_slots call on the bf16 decode batch of 64 tokens (512 picks):
-# the pick sort, the MFMA gate/up and down grouped GEMMs on decode-shaped tiles, the reduction
-FFN_SEQ = ("k_dec_gemm<0, 4, 2>", "k_dec_gemm<1, 4, 2>", "k_reduce")  # the gate/up kernel sorts the picks itself
+# kernels launched, in order, by one moe_ffn_slots call on the bf16 decode layer: at 64 tokens (512 picks) the
+# MFMA gate/up GEMM on decode-shaped tiles (which sorts the picks itself), the down GEMM and the reduction; at 1
+# and 8 tokens the pick sort and the row-streaming gate/up and down kernels, then the reduction.  The first
+# name anchors a launch; the names before it are the closest earlier dispatches, those after it the closest
+# later ones.
+FFN_SEQS = {64: ((), "k_dec_gemm<0, 4, 2, false>", ("k_dec_gemm<1, 4, 2, false>", "k_reduce")),
+            8: (("k_group",), "k_gu<1, 4>", ("k_down<1, 3, 32>", "k_reduce")),
+            1: (("k_group",), "k_gu<1, 4>", ("k_down<1, 3, 32>", "k_reduce"))}
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
                "expert_vram_slot_amd/csrc/prefill.hpp", "expert_vram_slot_amd/csrc/common.hpp")
@@ -88,6 +93,13 @@ def parse():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-dynamic", action="store_true")
     ap.add_argument("--no-stack", action="store_true", help="leave out the 48-layer 4-bit stack leg")
+    ap.add_argument("--no-extra-batches", action="store_true",
+                    help="time only --batch on the decode layer (not also 1 and 8 tokens)")
+    ap.add_argument("--summarize-kernels", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
+                                                             "COPY_WRITE_DIR"), default=None,
+                    help="write a per-kernel summary (time, scaled HBM counters) of any profiled run to --out, "
+                         "titled --title")
+    ap.add_argument("--title", default="")
     ap.add_argument("--workload", choices=["decode", "stack", "bias", "replay"], default="decode")
     ap.add_argument("--stack-steps", type=int, default=20, help="timed 48-layer steps at T=1 (half at T=32)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -111,6 +123,9 @@ def main():
         return
     if args.summarize_prefill:
         summarize_prefill(args)
+        return
+    if args.summarize_kernels:
+        summarize_kernels(args)
         return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print(f"bench.py measures one GPU only: the expert-slot layer is a single-GPU path here "
@@ -215,7 +230,7 @@ def main():
     achieved = float(np.mean(per_launch) / (np.mean(ffn_ms_arr) * 1e-3) / 1e9)
     # the smaller decode batches of the same layer (same layers, same steps, first T rows of x)
     batches = {}
-    for Tb in (1, 8):
+    for Tb in (() if args.no_extra_batches else (1, 8)):
         ms_b, pl_b, d_b = gpu_ffn_pass(m, torch, layers, n_x, Tb, args.steps, args.warmup, x_dtype, H, E, k, slab)
         gbs = float(np.mean(pl_b) / (np.mean(ms_b) * 1e-3) / 1e9)
         batches[f"T{Tb}"] = {"ffn_us": round(float(np.mean(ms_b)) * 1e3, 2), "bytes_per_launch": int(np.mean(pl_b)),
@@ -1012,23 +1027,30 @@ def _counter_per_dispatch(rows, counter):
     return per
 
 
-def _ffn_launches(rows, key):
-    """Group per-dispatch rows into decode moe_ffn_slots launches: each
-    dispatch of the gate/up kernel FFN_SEQ[0] with the closest later
-    FFN_SEQ[1:] by dispatch id.  Returns a list of {kernel short name: row}."""
+def _ffn_launches(rows, key, T=64):
+    """Group per-dispatch rows into decode moe_ffn_slots launches of the
+    batch T: each dispatch of its anchor kernel with the closest earlier and
+    later kernels of its sequence (FFN_SEQS) by dispatch id.  Returns a list
+    of {kernel short name: row}."""
+    before, anchor, after = FFN_SEQS[T]
     by_id = sorted(rows, key=lambda r: int(r["Dispatch_Id"]))
     names = [_short(r["Kernel_Name"]) for r in by_id]
     launches = []
     for i, nm in enumerate(names):
-        if nm != FFN_SEQ[0]:
+        if nm != anchor:
             continue
         got = {nm: by_id[i]}
-        for want in FFN_SEQ[1:]:
+        for want in before:
+            for j in range(i - 1, max(-1, i - 8), -1):
+                if names[j] == want:
+                    got[want] = by_id[j]
+                    break
+        for want in after:
             for j in range(i + 1, min(len(names), i + 50)):
                 if names[j] == want:
                     got[want] = by_id[j]
                     break
-        if len(got) == len(FFN_SEQ):
+        if len(got) == 1 + len(before) + len(after):
             launches.append(got)
     return launches
 
@@ -1066,13 +1088,14 @@ def summarize(args):
         lines.append(f"  {_short(r['Name']):<34}{int(r['Calls']):>7}{float(r['AverageNs']) / 1e3:>10.2f}"
                      f"{float(r['MinNs']) / 1e3:>10.2f}{float(r['MaxNs']) / 1e3:>10.2f}")
     lines.append("")
-    launches = _ffn_launches(trace, "trace")
+    launches = _ffn_launches(trace, "trace", T)
     per_k = {}
     for L in launches:
         for nm, r in L.items():
             per_k.setdefault(nm, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    seq = FFN_SEQS[T][0] + (FFN_SEQS[T][1],) + FFN_SEQS[T][2]
     lines.append(f"decode moe_ffn_slots launches found in the trace: {len(launches)} (each: "
-                 f"{', '.join(FFN_SEQ)}, matched by dispatch id)")
+                 f"{', '.join(seq)}, matched by dispatch id)")
     ffn_avg = 0.0
     for nm, v in per_k.items():
         lines.append(f"  {nm:<34}{np.mean(v):>10.2f} us")
@@ -1083,7 +1106,7 @@ def summarize(args):
                  f"calibration: a 1 GiB copy reads FETCH_SIZE {copy_kib(cfetch):.0f} KiB, WRITE_SIZE "
                  f"{copy_kib(cwrite):.0f} KiB, so factors {f_fetch:.3f} and {f_write:.3f}):")
     lines.append(f"  {'kernel':<34}{'FETCH KiB':>14}{'WRITE KiB':>14}{'scaled MB':>12}")
-    fl, wl = _ffn_launches(frows, "fetch"), _ffn_launches(wrows, "write")
+    fl, wl = _ffn_launches(frows, "fetch", T), _ffn_launches(wrows, "write", T)
     traffic = 0.0
     for nm in (fl[0].keys() if fl else []):
         fv = float(np.mean([float(L[nm]["Counter_Value"]) for L in fl]))
@@ -1103,10 +1126,51 @@ def summarize(args):
     print(f"wrote {out}")
 
 
+def summarize_kernels(args):
+    """Per kernel of a profiled run: calls, average duration, and HBM bytes
+    per dispatch from FETCH_SIZE / WRITE_SIZE runs of the same command,
+    scaled by what the counters read for a plain 1 GiB copy."""
+    tr, fe, wr, cfe, cwr = args.summarize_kernels
+    stats = _csv_rows(tr, "kernel_stats.csv")
+    fetch = _counter_per_dispatch(_csv_rows(fe, "counter_collection.csv"), "FETCH_SIZE")
+    write = _counter_per_dispatch(_csv_rows(wr, "counter_collection.csv"), "WRITE_SIZE")
+    cfetch = _counter_per_dispatch(_csv_rows(cfe, "counter_collection.csv"), "FETCH_SIZE")
+    cwrite = _counter_per_dispatch(_csv_rows(cwr, "counter_collection.csv"), "WRITE_SIZE")
+
+    def copy_kib(per):
+        return float(np.median([v for vs in per.values() for v in vs if v > 100_000]))
+
+    gib_kib = (1 << 30) / 1024.0
+    f_fetch, f_write = gib_kib / copy_kib(cfetch), gib_kib / copy_kib(cwrite)
+    lines = [f"rocprofv3 summary: {args.title}", ""]
+    if args.commands:
+        lines.append("commands (run from the repository root on one MI355X; TMPDIR=/tmp):")
+        with open(args.commands) as fh:
+            lines.extend("  " + l.rstrip() for l in fh if l.strip())
+        lines.append("")
+    lines.append(f"HBM counters scaled by a 1 GiB copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}; "
+                 "per dispatch, mean over the kernel's dispatches")
+    lines.append(f"  {'kernel':<34}{'calls':>7}{'avg us':>10}{'HBM MB':>10}{'GB/s':>9}")
+    for r in sorted(stats, key=lambda r: -float(r["TotalDurationNs"]))[:24]:
+        nm = _short(r["Name"])
+        us = float(r["AverageNs"]) / 1e3
+        mb = None
+        if nm in fetch:
+            mb = (float(np.mean(fetch[nm])) * f_fetch + float(np.mean(write.get(nm, [0.0]))) * f_write) * 1024 / 1e6
+        lines.append(f"  {nm:<34}{int(r['Calls']):>7}{us:>10.2f}" +
+                     (f"{mb:>10.2f}{mb / us * 1e3:>9.0f}" if mb is not None else ""))
+    with open(args.out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    print(f"wrote {args.out}")
+
+
 def summarize_prefill(args):
     """Per-kernel time, HBM counters and algorithmic bytes of the prefill legs
     (the 288-expert layer at 2048 and 16384 tokens) from the runs that
-    --summarize reads.  A k_reduce dispatch belongs to a leg by its grid."""
+    --summarize reads.  A dispatch belongs to a leg by its grid (the 144-slot
+    leg runs the same kernels on other grids): the GEMMs' grids are 8 XCDs x
+    ceil(max tiles / 8) x column tiles workgroups of 256 threads, max tiles
+    = min(S, P) + P / 32 + 1 as the library sizes its tile list."""
     tr, fe, wr, cfe, cwr = args.summarize_prefill
     import synth
     c = synth.CONFIGS["c5"]
@@ -1128,9 +1192,10 @@ def summarize_prefill(args):
         P = T * k
         big = T == 16384
         gu, dn = ("k_pf_wide<0>", "k_pf_wide<1>") if big else ("k_pf_gemm<0, 8>", "k_pf_gemm<1, 8>")
+        tile_groups = (min(E, P) + P // 32 + 1 + 7) // 8
         legs.append((T, [
-            (gu, w_gu + T * H * 2 + P * I * 2, 2.0 * P * 2 * I * H, None),
-            (dn, w_dn + P * I * 2 + P * H * 4, 2.0 * P * H * I, None),
+            (gu, w_gu + T * H * 2 + P * I * 2, 2.0 * P * 2 * I * H, 8 * tile_groups * (I // 128) * 256),
+            (dn, w_dn + P * I * 2 + P * H * 4, 2.0 * P * H * I, 8 * tile_groups * (H // 256) * 256),
             ("k_reduce", P * H * 4 + T * H * 4, 0.0, T * H // 4),
         ]))
 
@@ -1154,6 +1219,8 @@ def summarize_prefill(args):
     lines.append(f"HBM counters scaled by a 1 GiB copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}. "
                  "Algorithmic bytes: weights once, activations in and out once (x, h, fp32 partials, y).")
     for T, ks in legs:
+        # the leg's reductions: those dispatched right after its down GEMMs
+        dn_ids = [int(r["Dispatch_Id"]) for r in pick(trace, ks[1][0], ks[1][3], "Grid_Size_X")]
         lines.append("")
         lines.append(f"{T} tokens ({T * k} picks):")
         lines.append(f"  {'kernel':<18}{'calls':>6}{'avg us':>10}{'HBM GB':>9}{'alg GB':>9}{'HBM/alg':>9}"
@@ -1162,6 +1229,8 @@ def summarize_prefill(args):
             tr_rows = pick(trace, name, None if grid is None else grid, "Grid_Size_X")
             f_rows = pick(frows, name, grid, "Grid_Size")
             w_rows = pick(wrows, name, grid, "Grid_Size")
+            if name == "k_reduce" and dn_ids:
+                tr_rows = [r for r in tr_rows if int(r["Dispatch_Id"]) - 1 in dn_ids]
             if not tr_rows:
                 continue
             us = float(np.mean([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr_rows]))
