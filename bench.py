@@ -257,7 +257,9 @@ def main():
                                f"static 64-slot cache + host pass of the other 64 experts",
                    "global_batch": T, "layers_rotated": args.layers, "host_threads": nthreads,
                    "host_pass": not args.no_host_pass, "driver": "native moe_layer_step",
-                   "gpu_only_step_ms": round(elapsed_py / args.steps * 1e3, 4)},
+                   "gpu_only_step_ms": round(elapsed_py / args.steps * 1e3, 4),
+                   "step_bound_by": ("the CPU host pass: the 64 non-resident experts' slabs (604 MB) are read from "
+                                     "pinned host memory every step" if not args.no_host_pass else "the GPU")},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": stored_traffic(T),
                      "kernel": "moe_ffn_slots (pick sort, MFMA gate/up and down grouped GEMMs, reduction)",
