@@ -1055,3 +1055,106 @@ def test_native_stack_equals_python_stack(m, T):
     out_nat2 = host(nat.step(x0, T))
     np.testing.assert_array_equal(out_nat2, out_py)
     nat.close()
+
+
+# ------------------------------------------------------------- edge cases
+
+
+def _small_layer(name, T, E, H, k, x_dtype, seed):
+    """Router inputs of a synthetic layer (x ~ N(0, 1), G ~ N(0, 0.05))."""
+    x = synth.normal(synth.key(seed, 1, T), (T, H), 1.0, x_dtype)
+    G = synth.normal(synth.key(seed, 2, E), (E, H), 0.05, x_dtype)
+    return type(name, (), dict(T=T, H=H, E=E, k=k, x=x, G=G, x_dtype=x_dtype))
+
+
+@pytest.mark.parametrize("E,k", [(4096, 32), (4096, 1), (33, 32), (32, 32)])
+def test_route_limits_of_experts_and_top_k(m, E, k):
+    """The ABI's limits: 4,096 experts, top-32; top-1; k = E (every expert
+    picked, in rank order).  Ids bitwise against the oracle on the GPU's own
+    logits and at this seed, weights within fp32 tolerance, both router forms."""
+    li = _small_layer("L", 6, E, 64, k, 0, 4000 + E + k)
+    check_route(m, li)
+    ids_f, w_f, _ = gpu_route(m, li, with_logits=False)
+    z = oracle.logits(li.x, 0, li.G)
+    np.testing.assert_array_equal(ids_f, oracle.topk(z, k))
+    np.testing.assert_allclose(w_f, oracle.route_weights(z, ids_f), rtol=2e-6, atol=1e-9)
+    if k == E:
+        np.testing.assert_allclose(w_f.sum(axis=1), 1.0, rtol=1e-5)
+
+
+@pytest.mark.parametrize("policy", ["lru", "lfu"])
+def test_manage_limits_of_experts_and_slots(m, policy):
+    """4,096 experts over 1,024 slots (the ABI's limits), steps of 2,048 ids
+    drawn Zipf(0.8), overflow into the host list on every step: each step's
+    slot ids, miss list, host list, counters and state bitwise against the
+    oracle."""
+    E, S, k = 4096, 1024, 32
+    g = GpuCache(m, E, S)
+    o = oracle.Cache(E, S, policy)
+    for st in range(4):
+        ids = synth.zipf_ids(synth.key(0xE5510F00, 7, st), synth.key(0xE5510F00, 8, st), 64, E, k, 0.8)
+        rg, ro = g.manage(policy, ids), o.manage(ids)
+        for key in ("slot_ids", "miss", "host_miss", "stats"):
+            np.testing.assert_array_equal(rg[key], ro[key], err_msg=f"{policy} step {st} {key}")
+    np.testing.assert_array_equal(host(g.e2s), o.e2s)
+    np.testing.assert_array_equal(host(g.s2e), o.s2e)
+
+
+@pytest.mark.parametrize("w_type,k", [(0, 1), (1, 1), (2, 1), (3, 1), (0, 32), (1, 32), (2, 32), (3, 32)])
+def test_ffn_top1_and_top32(m, w_type, k):
+    """One pick per token and 32 picks per token (the ABI's limit; 288 picks
+    take the int8 tiles for W8A8), every weight format, a third of the
+    experts resident."""
+    E, S, T, H, I = 48, 16, 9, 256, 128
+    rng = np.random.default_rng(w_type * 100 + k)
+    x_dtype = 0 if w_type == 0 else 1
+    x = synth.normal(synth.key(k, 3, w_type), (T, H), 1.0, x_dtype)
+    store = synth.slabs(w_type, 8800 + w_type, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=x_dtype, w_type=w_type, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(w_type, store, E, H, I, x, x_dtype, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, w_type, f"w{w_type} k={k}")
+
+
+def test_empty_batch_is_a_no_op(m):
+    """T = 0 tokens through every entry point that takes a batch: each returns
+    success and leaves its outputs as they were; the native step too."""
+    from expert_vram_slot_amd.layer import NativeStack
+    li = synth.LayerInputs("c1")
+    E, k, H, I, S = li.E, li.k, li.H, li.I, 4
+    x = dev(li.x)
+    G = dev(li.G)
+    sentinel = -12345
+    ids = torch.full((4, k), sentinel, dtype=torch.int32, device="cuda")
+    w = torch.full((4, k), 7.0, dtype=torch.float32, device="cuda")
+    m.moe_route(x, 0, G, None, None, 0, H, E, k, ids, w, None)
+    g = GpuCache(m, E, S, [0, 1, 2, 3])
+    slot_ids = torch.full((4 * k,), sentinel, dtype=torch.int32, device="cuda")
+    m.cache_manage(g.st, oracle.POLICIES["lru"], ids, 0, slot_ids, g.miss, g.n_miss, g.host_miss, g.n_host, g.stats)
+    slots = dev(li.store[:S])
+    y = torch.full((4, H), 7.0, dtype=torch.float32, device="cuda")
+    wsb = m.moe_ffn_workspace_bytes(1, k, S, 0, H, I)
+    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    m.moe_ffn_slots(x, 0, slot_ids, w, 0, k, slots, li.slab, S, 0, H, I, y, ws, wsb)
+    m.moe_ffn_slots_noalloc(x, 0, slot_ids, w, 0, k, slots, li.slab, S, 0, H, I, y)
+    m.moe_combine(y, y, 0, H)
+    xo = torch.full((4, H), 7.0, dtype=torch.float32, device="cuda")
+    m.moe_residual(x, 0, y, xo, 0, H)
+    spec = _layer_spec(li, [0, 1, 2, 3])
+    nat = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=0, T_max=4, layers=[spec])
+    nat.y.fill_(7.0)
+    nat.layer_step(0, x, 0)
+    torch.cuda.synchronize()
+    assert torch.all(ids == sentinel) and torch.all(w == 7.0) and torch.all(slot_ids == sentinel)
+    assert torch.all(y == 7.0) and torch.all(xo == 7.0) and torch.all(nat.y == 7.0)
+    assert int(host(g.step)[0]) == 1  # an empty cache step still counts as a step (oracle: same)
+    o = oracle.Cache(E, S, "lru", [0, 1, 2, 3])
+    o.manage(np.zeros(0, np.int32))
+    assert int(o.step[0]) == 1
+    nat.close()
