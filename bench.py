@@ -1193,10 +1193,12 @@ def summarize_prefill(args):
     for T in (2048, 16384):
         P = T * k
         big = T == 16384
-        gu, dn = ("k_pf_wide<0>", "k_pf_wide<1>") if big else ("k_pf_gemm<0, 8>", "k_pf_gemm<1, 8>")
+        gu, dn = ("k_pf_wide<0>", "k_pf_wide<1>") if big else ("k_pf_gemm<0, 4>", "k_pf_gemm<1, 8>")
         tile_groups = (min(E, P) + P // 32 + 1 + 7) // 8
+        # gate/up column tiles: 128 gate + up rows (wide tiles), 64 (128-row tiles, four 32-row blocks per wave)
+        gu_cols = I // 128 if big else I // 64
         legs.append((T, [
-            (gu, w_gu + T * H * 2 + P * I * 2, 2.0 * P * 2 * I * H, 8 * tile_groups * (I // 128) * 256),
+            (gu, w_gu + T * H * 2 + P * I * 2, 2.0 * P * 2 * I * H, 8 * tile_groups * gu_cols * 256),
             (dn, w_dn + P * I * 2 + P * H * 4, 2.0 * P * H * I, 8 * tile_groups * (H // 256) * 256),
             ("k_reduce", P * H * 4 + T * H * 4, 0.0, T * H // 4),
         ]))

@@ -980,7 +980,8 @@ int dec_launch(const void* x, const float* w, int k, const void* slot_store, siz
     return moe_check_launch("moe_ffn_slots/decode_down");
 }
 
-template <int NB>
+// NBG / NBD: 32-row weight blocks per wave of the gate/up and down GEMMs.
+template <int NBG, int NBD>
 int pf_launch(const void* x, const float* w, int k, const void* slot_store, size_t slab_bytes, int H, int I,
               const moe_slab_layout_t& lay, const int32_t* pair_list, const PfTile* tiles, const int32_t* n_tiles,
               int max_tiles, void* hbuf, float* part, hipStream_t st) {
@@ -988,7 +989,7 @@ int pf_launch(const void* x, const float* w, int k, const void* slot_store, size
     // threads that launch on several devices at once each see it done for theirs)
     static std::mutex mu;
     static uint64_t done = 0;  // bit d: set for device d
-    const int lds = pf_lds_bytes(NB);
+    const int lds_g = pf_lds_bytes(NBG), lds_d = pf_lds_bytes(NBD);
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
         (void)hipGetLastError();
@@ -997,29 +998,29 @@ int pf_launch(const void* x, const float* w, int k, const void* slot_store, size
     {
         std::lock_guard<std::mutex> lk(mu);
         if (!(done >> dev & 1)) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_GU, NB>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess ||
-                hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_DOWN, NB>),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds) != hipSuccess) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_GU, NBG>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_g) != hipSuccess ||
+                hipFuncSetAttribute(reinterpret_cast<const void*>(&k_pf_gemm<PF_DOWN, NBD>),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, lds_d) != hipSuccess) {
                 (void)hipGetLastError();
-                return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d bytes of LDS for the prefill kernels",
-                                lds);
+                return moe_fail(MOE_E_HIP, "moe_ffn_slots: cannot allow %d / %d bytes of LDS for the prefill kernels",
+                                lds_g, lds_d);
             }
             done |= 1ull << dev;
         }
     }
     const int tile_groups = (max_tiles + PF_XCD - 1) / PF_XCD;
     PfArgs gu{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1],
-              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / (NB * 16)};
-    hipLaunchKernelGGL((k_pf_gemm<PF_GU, NB>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
-                       dim3(PF_THREADS), lds, st, gu);
+              reinterpret_cast<const unsigned char*>(x), pair_list, w, tiles, n_tiles, hbuf, H, I, k, I / (NBG * 16)};
+    hipLaunchKernelGGL((k_pf_gemm<PF_GU, NBG>), dim3((unsigned)(PF_XCD * tile_groups * gu.ntiles_n)),
+                       dim3(PF_THREADS), lds_g, st, gu);
     int rc;
     if ((rc = moe_check_launch("moe_ffn_slots/prefill_gate_up"))) return rc;
     PfArgs dn{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0,
               reinterpret_cast<const unsigned char*>(hbuf), pair_list, w, tiles, n_tiles, part, I, H, k,
-              H / (NB * 32)};
-    hipLaunchKernelGGL((k_pf_gemm<PF_DOWN, NB>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
-                       dim3(PF_THREADS), lds, st, dn);
+              H / (NBD * 32)};
+    hipLaunchKernelGGL((k_pf_gemm<PF_DOWN, NBD>), dim3((unsigned)(PF_XCD * tile_groups * dn.ntiles_n)),
+                       dim3(PF_THREADS), lds_d, st, dn);
     return moe_check_launch("moe_ffn_slots/prefill_down");
 }
 
@@ -1087,11 +1088,13 @@ int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_sto
     if (moe_pf_big(T, k, S, H, I))
         return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
                          part, st);
-    // eight 32-row weight blocks per wave where the output columns come in
-    // 256s (fewer, longer workgroups: the 2048-token layer 2.06 -> 2.02 ms)
+    // down: eight 32-row weight blocks per wave where the output columns come
+    // in 256s (fewer, longer workgroups: the 2048-token layer 2.06 -> 2.02 ms);
+    // gate/up: four (64 KiB of LDS, two workgroups per CU: 2.13 -> 2.08 ms
+    // against eight; two blocks: 2.35 ms)
     if (H % 256 == 0)
-        return pf_launch<8>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
-                            part, st);
-    return pf_launch<4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf, part,
-                        st);
+        return pf_launch<4, 8>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles,
+                               hbuf, part, st);
+    return pf_launch<4, 4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
+                           part, st);
 }

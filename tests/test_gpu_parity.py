@@ -541,6 +541,54 @@ def test_ffn_int8_matrix_core_tiles(m, T, S, H, I):
     np.testing.assert_array_equal(run_ffn(m, li, sl, w, dev(store[resident]), S), y)
 
 
+@pytest.mark.parametrize("T,k,S,H,I,mix", [(16, 8, 32, 2048, 768, "zipf"), (31, 8, 6, 256, 128, "hot"),
+                                            (255, 1, 3, 128, 256, "hot"), (1, 8, 64, 2048, 768, "rand"),
+                                            (5, 4, 16, 3072, 2048, "rand"), (7, 3, 8, 16, 16, "rand"),
+                                            (9, 8, 700, 64, 1040, "rand")])
+def test_ffn_int8_small_batches(m, T, k, S, H, I, mix):
+    """W8A8 batches of fewer than 256 picks (the row-streaming kernels): the
+    128-expert layer's 16-token Zipf batch; one slot picked by all 31 tokens
+    (eight passes of four tokens over its rows); 255 one-pick tokens over 3
+    slots; more slots than picks; rows of 3072 inputs and 2048 intermediate
+    values; 16 x 16 experts; 700 slots with 1040-wide down rows.  Against the
+    oracle, and every token's output is bit-identical to a batch of that token
+    alone (int8 dots are exact, so a pick's result cannot depend on the
+    batch)."""
+    E = max(2 * S, 16, k + 4)
+    rng = np.random.default_rng(T * 31 + S + H)
+    x = synth.normal(synth.key(T, 9, S), (T, H), 1.0, 1)
+    store = synth.slabs(2, 444 + H + I, 0, 0, E, H, I, 0.05)
+    if mix == "zipf":
+        ids = synth.zipf_ids(synth.key(T, 10), synth.key(T, 11), T, E, k, 0.8).astype(np.int32)
+        resident = np.argsort(-np.bincount(ids.reshape(-1), minlength=E), kind="stable")[:S]
+    elif mix == "hot":
+        # expert 0 in every token's picks (k == 1: picks drawn from the first four experts)
+        ids = (rng.integers(0, 4, size=(T, 1)) if k == 1 else
+               np.stack([np.concatenate([[0], rng.choice(np.arange(1, E), k - 1, replace=False)]) for _ in range(T)]))
+        ids = ids.astype(np.int32)
+        resident = np.arange(S)
+    else:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        resident = rng.choice(E, S, replace=False)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    assert T * k < 256 and (mix == "hot" or np.any(sl < 0))
+    slots = dev(store[resident])
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=2, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(2, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, slots, S)
+    assert_close(y, yg, 2, f"int8 small T={T} k={k} S={S} H={H} I={I}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+    np.testing.assert_array_equal(run_ffn(m, li, sl, w, slots, S), y)
+    for t in sorted({0, T // 2, T - 1}):
+        one = type("L", (), dict(T=1, k=k, H=H, I=I, E=E, x=x[t:t + 1], x_dtype=1, w_type=2, slab=store.shape[1]))
+        np.testing.assert_array_equal(run_ffn(m, one, sl[t:t + 1], w[t:t + 1], slots, S), y[t:t + 1],
+                                      err_msg=f"token {t} alone")
+
+
 @pytest.mark.parametrize("T,S", [(64, 24), (128, 40), (129, 40), (70, 1)])
 def test_ffn_decode_sort_in_gemm(m, T, S):
     """bf16 decode batches of 512..1024 picks are grouped by slot inside the
@@ -580,12 +628,14 @@ def test_ffn_workspace_reused_across_calls(m):
         assert_close(host(y), yg, 1, f"reused workspace T={li.T}")
 
 
-@pytest.mark.parametrize("T,S,H", [(300, 20, 256), (257, 24, 256), (1000, 17, 256), (600, 20, 384)])
+@pytest.mark.parametrize("T,S,H", [(300, 20, 256), (257, 24, 256), (1000, 17, 256), (600, 20, 384), (520, 18, 512),
+                                   (700, 20, 1024)])
 def test_ffn_prefill_grouped_gemm(m, T, S, H):
     """bf16 batches of >= 512 picks run on the MFMA grouped GEMMs: slots with
     more picks than one tile, ragged tiles, non-resident experts; from 4096
-    picks the 128-row tiles, with eight 32-row weight blocks per wave when H is
-    a multiple of 256 and four otherwise."""
+    picks the 128-row tiles, with four 32-row weight blocks per wave in the
+    gate/up GEMM and, in the down GEMM, eight when H is a multiple of 256 (two
+    and four 256-column tiles at H = 512 and 1024) and four otherwise."""
     E, k, I = 24, 8, 384
     rng = np.random.default_rng(T + S)
     x = synth.normal(synth.key(7, 1, T), (T, H), 1.0, 1)
