@@ -47,8 +47,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
 constexpr int FFN_THREADS = 256;
 constexpr int NTMAX = 4;       // tokens of one slot handled per pass
-constexpr int RPW_GU = 1;      // gate rows (and as many up rows) per wave
-constexpr int RPW_DN = 4;      // down rows per wave
 constexpr int GROUP_THREADS = 1024;
 constexpr bool X_PREFETCH = true;  // activation granules one chunk ahead (16-byte activation granules)
 constexpr int GROUP_MULTI_P = 4096;  // larger batches sort with one workgroup per 1024 picks
@@ -66,6 +64,8 @@ struct Fmt;
 template <>
 struct Fmt<MOE_W_F32> {
     static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
+    static constexpr int RGU = 1;  // gate rows (and as many up rows) per wave
+    static constexpr int RDN = 4;  // down rows per wave
     static constexpr int EPG = 4;       // weights per 16-byte granule
     static constexpr int ABYTES = 4;    // bytes per activation element in LDS
     using Acc = float;
@@ -73,6 +73,8 @@ struct Fmt<MOE_W_F32> {
 template <>
 struct Fmt<MOE_W_BF16> {
     static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
+    static constexpr int RGU = 1;  // gate rows (and as many up rows) per wave
+    static constexpr int RDN = 4;  // down rows per wave
     static constexpr int EPG = 8;
     static constexpr int ABYTES = 2;
     using Acc = float;
@@ -80,6 +82,11 @@ struct Fmt<MOE_W_BF16> {
 template <>
 struct Fmt<MOE_W_W8A8> {
     static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
+    // two gate rows (and two up rows) per wave: a 2 KiB row is two chunks of
+    // 64 granules, so one row pair left each lane four loads in flight
+    // (128-expert layer, 16 tokens, 32 busy slots: 51.8 -> 48.4 us)
+    static constexpr int RGU = 2;  // gate rows (and as many up rows) per wave
+    static constexpr int RDN = 4;  // down rows per wave
     static constexpr int EPG = 16;
     static constexpr int ABYTES = 1;
     using Acc = int;
@@ -87,6 +94,13 @@ struct Fmt<MOE_W_W8A8> {
 template <>
 struct Fmt<MOE_W_Q4B32> {
     static constexpr int REP = 2;  // row tiles per GEMV workgroup, taken one after the other
+    // 4-bit rows are short (a 2048-input row is one 64-granule chunk, a
+    // 512-input down row 16 granules): two gate/up row pairs and eight down
+    // rows per wave, the down rows on 16 lanes each, so every lane has loads
+    // in flight (512-expert layer, 32 tokens: 94.6 -> 64.5 us; 1 token
+    // unchanged)
+    static constexpr int RGU = 2;  // gate rows (and as many up rows) per wave
+    static constexpr int RDN = 8;  // down rows per wave
     static constexpr int EPG = 32;
     static constexpr int ABYTES = 2;
     using Acc = float;
@@ -661,10 +675,12 @@ __host__ __device__ constexpr int chunk_group(int KG, int LPR = 64) {
 // Lanes per row of the down projection.  Narrower lane groups keep every
 // lane busy on short rows but give each lane fewer rows to share one
 // activation read with; that pays for fp32/bf16 (one activation byte per
-// weight byte), not for int8 and 4-bit weights, whose activations are as
-// large as (int8) or four times (4-bit against bf16) the weight bytes.
+// weight byte), not for int8 weights, whose activations are as large as the
+// weight bytes.  4-bit rows of up to 16 (32) granules take 16 (32) lanes,
+// with eight rows per wave (Fmt<MOE_W_Q4B32>::RDN).
 __host__ __device__ constexpr int down_lpr(int KG, int w_type) {
-    return (w_type == MOE_W_W8A8 || w_type == MOE_W_Q4B32 || KG % 64 == 0 || KG >= 128) ? 64
+    return w_type == MOE_W_Q4B32 ? (KG <= 16 ? 16 : KG <= 32 ? 32 : 64)
+           : (w_type == MOE_W_W8A8 || KG % 64 == 0 || KG >= 128) ? 64
            : KG % 32 == 0                                                              ? 32
            : KG % 16 == 0                                                              ? 16
                                                                                        : 64;
@@ -705,12 +721,12 @@ __device__ __forceinline__ void pass_picks(const int32_t* __restrict__ pair_list
 }
 
 template <int F, int NT, int NCHG>
-__device__ __forceinline__ void gu_pass(const RowPtrs<2 * RPW_GU>& rp, const SlabView& sv, const unsigned char* slab,
+__device__ __forceinline__ void gu_pass(const RowPtrs<2 * Fmt<F>::RGU>& rp, const SlabView& sv, const unsigned char* slab,
                                         const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
                                         int H, int I, int k, int r_base, const float* __restrict__ xscale,
                                         void* __restrict__ hbuf) {
     using Acc = typename Fmt<F>::Acc;
-    constexpr int ROWS = 2 * RPW_GU;  // gate rows, then the same up rows
+    constexpr int ROWS = 2 * Fmt<F>::RGU;  // gate rows, then the same up rows
     constexpr int V = ROWS * NT;
     const int lane = threadIdx.x & 63;
     int pick[NT], tok[NT];
@@ -758,8 +774,8 @@ constexpr int NT_TOP = NTMAX > 4 ? NTMAX : 4;
         else { BODY(NT_TOP); }                 \
     } while (0)
 
-// One workgroup per (slot with work, tile of 4 * RPW_GU gate rows and the
-// same up rows); each wave owns RPW_GU gate and RPW_GU up rows.  Waves are
+// One workgroup per (slot with work, tile of 4 * RGU gate rows and the
+// same up rows); each wave owns RGU gate and RGU up rows.  Waves are
 // independent: no LDS, no barrier.
 template <int F, int NCHG>
 __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __restrict__ act,
@@ -769,6 +785,7 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, void* __restrict__ hbuf,
                                                     int tiles) {
+    constexpr int RPW_GU = Fmt<F>::RGU;
     constexpr int ROWS = 2 * RPW_GU;
     const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
@@ -804,12 +821,13 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
 }
 
 template <int F, int NT, int NCHG, int LPR>
-__device__ __forceinline__ void down_pass(const RowPtrs<RPW_DN>& rp, const SlabView& sv, const unsigned char* slab,
+__device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const SlabView& sv, const unsigned char* slab,
                                           const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
                                           int H, int I, int r_base, const float* __restrict__ hscale,
                                           const float* __restrict__ wts, float* __restrict__ part) {
     using Acc = typename Fmt<F>::Acc;
     constexpr int RPI = 64 / LPR;
+    constexpr int RPW_DN = Fmt<F>::RDN;
     constexpr int V = (RPW_DN / RPI) * NT;  // values per lane
     static_assert(V <= LPR, "a lane group reduces at most LPR values at once");
     const int lane = threadIdx.x & 63;
@@ -847,6 +865,7 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, float* __restrict__ part,
                                                       int tiles) {
+    constexpr int RPW_DN = Fmt<F>::RDN;
     const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
     if (a >= *n_active) return;
@@ -1041,7 +1060,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     }
 
     SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
-    const int tiles_gu = (I + 4 * RPW_GU - 1) / (4 * RPW_GU);
+    const int tiles_gu = (I + 4 * Fmt<F>::RGU - 1) / (4 * Fmt<F>::RGU);
     // at most min(S, P) slots have work: workgroups beyond them would only read n_active and leave
     const int max_active = S < P ? S : P;
 #define MOE_LAUNCH_GU(G)                                                                                       \
@@ -1072,7 +1091,7 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hbsum = hbs;
     }
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
-    const int tiles_dn = (H + 4 * RPW_DN - 1) / (4 * RPW_DN);
+    const int tiles_dn = (H + 4 * Fmt<F>::RDN - 1) / (4 * Fmt<F>::RDN);
 #define MOE_LAUNCH_DN(G, LP)                                                                                 \
     hipLaunchKernelGGL((k_down<F, G, LP>), dim3(max_active * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, \
                        dv, dn_act, hscale, hbsum,                                                                   \

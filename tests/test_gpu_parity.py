@@ -467,11 +467,13 @@ def test_ffn_slots_matches_oracle(m, cfg, T):
 
 
 @pytest.mark.parametrize("w_type,H,I", [(1, 112, 144), (1, 1040, 784), (0, 80, 48), (2, 1040, 784),
-                                        (2, 2320, 2080), (3, 1056, 544)])
+                                        (2, 2320, 2080), (3, 1056, 544), (3, 224, 256), (3, 160, 1280),
+                                        (2, 144, 48)])
 def test_ffn_ragged_shapes(m, w_type, H, I):
     """Row tiles with a ragged tail and rows whose granules do not fill the waves;
     W8A8 with h rows longer than 2048 (quantised without holding the row in
-    registers)."""
+    registers); 4-bit down rows of 17, 8 and 40 blocks (32-, 16- and 64-lane
+    rows, eight per wave); int8 rows of 9 and 3 granules."""
     E, k, T, S = 12, 3, 11, 7
     rng = np.random.default_rng(H + I)
     x_dtype = 0 if w_type == 0 else 1
