@@ -13,7 +13,9 @@
 //                the list of slots with work; above GROUP_MULTI_P picks the
 //                same sort runs over 1024-pick chunks in two launches
 //                (k_group_hist: per-chunk slot counts; k_group_place: offsets
-//                and ranks, one workgroup per chunk)
+//                and ranks, one workgroup per chunk); one-token batches of
+//                the fp32, bf16 and 4-bit formats skip it (each workgroup of
+//                the next two kernels takes one pick)
 //   k_quant_rows (W8A8) int8 codes + scale per token
 //   k_gu         gate and up rows of a slot against the slot's tokens, SwiGLU
 //                epilogue -> h[pick][I]
@@ -23,9 +25,9 @@
 //
 // Weight streaming: each workgroup owns a tile of rows of one slot; the four
 // waves split the rows, the 64 lanes of a wave read consecutive 16-byte
-// granules of a row (coalesced 1 KiB per wave load), the slot's tokens sit in
-// LDS, and the per-lane partial sums of all rows and tokens are reduced across
-// the wave in one multi-value butterfly.
+// granules of a row (coalesced 1 KiB per wave load), the slot's tokens are
+// read from L2, and the per-lane partial sums of all rows and tokens are
+// reduced across the wave in one multi-value butterfly.
 #include <math.h>
 
 #include <mutex>
@@ -110,8 +112,48 @@ __device__ __forceinline__ float dot2bf(uint32_t a, uint32_t b, float c) {
     return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a), __builtin_bit_cast(bf16x2, b), c, false);
 }
 
+// Sum of the 32 bf16 inputs of one 4-bit block (x0: inputs 0..7, x1: 8..15,
+// x2: 16..23, x3: 24..31) in fp32, through the bf16 pair dot with (1, 1) in
+// a fixed order: the one arithmetic of every block sum (made by the GEMV
+// kernels themselves, or ahead of them by k_block_sums and the sort launch),
+// so a token's bits do not depend on which made it.
+__device__ __forceinline__ float block_sum_bf16(const v4u& x0, const v4u& x1, const v4u& x2, const v4u& x3) {
+    constexpr uint32_t ONES = 0x3F803F80u;  // bf16 1.0 twice
+    const uint32_t xv[16] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w,
+                             x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+    float s = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) s = dot2bf(xv[i], ONES, s);
+    return s;
+}
+
+// 32 nibbles of one 4-bit block against its 32 bf16 inputs (x0 .. x3 as in
+// block_sum_bf16).  Each code q becomes the bf16 value 128 + q (bits 0x4300 |
+// q, exact), so a bf16 dot gives sum (q + 128) x; the block's sum of x
+// (qxsum) removes the offset: sum (q - 8) x = sum (q + 128) x - 136 sum x.
+// Input j of the block is the low nibble of byte j (j < 16) or the high
+// nibble of byte j - 16.
+__device__ __forceinline__ void granule_dot_q4(const v4u& w, const v4u& x0, const v4u& x1, const v4u& x2,
+                                               const v4u& x3, float qscale, float qxsum, float& acc) {
+    const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+    const uint32_t xl[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    const uint32_t xh[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
+    float d = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = wv[i] & 0x0F0F0F0Fu;          // inputs 4i .. 4i+3
+        const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;   // inputs 16+4i .. 16+4i+3
+        d = dot2bf(__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u), xl[2 * i], d);
+        d = dot2bf(__builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u), xl[2 * i + 1], d);
+        d = dot2bf(__builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u), xh[2 * i], d);
+        d = dot2bf(__builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u), xh[2 * i + 1], d);
+    }
+    acc = fmaf(qscale, fmaf(-136.0f, qxsum, d), acc);
+}
+
 // Accumulate one 16-byte weight granule against the matching activation
-// granule `xa` (16 bytes for fp32/bf16/int8; 64 bytes of bf16 for 4-bit).
+// granule `xa` (16 bytes for fp32/bf16/int8; 64 bytes of bf16 for 4-bit,
+// with the block's input sum qxsum).
 template <int F>
 __device__ __forceinline__ void granule_dot(const v4u& w, const unsigned char* xa, float qscale, float qxsum,
                                             typename Fmt<F>::Acc& acc) {
@@ -134,29 +176,8 @@ __device__ __forceinline__ void granule_dot(const v4u& w, const unsigned char* x
         acc = __builtin_amdgcn_sdot4((int)w.z, (int)xv.z, acc, false);
         acc = __builtin_amdgcn_sdot4((int)w.w, (int)xv.w, acc, false);
     } else {
-        // 32 nibbles of one block.  Each code q becomes the bf16 value 128 + q
-        // (bits 0x4300 | q, exact), so a bf16 dot gives sum (q + 128) x; the
-        // block's sum of x (qxsum) removes the offset: sum (q - 8) x =
-        // sum (q + 128) x - 136 sum x.  Input j of the block is the low nibble
-        // of byte j (j < 16) or the high nibble of byte j - 16.
-        const v4u x0 = *reinterpret_cast<const v4u*>(xa);        // inputs 0..7
-        const v4u x1 = *reinterpret_cast<const v4u*>(xa + 16);   // inputs 8..15
-        const v4u x2 = *reinterpret_cast<const v4u*>(xa + 32);   // inputs 16..23
-        const v4u x3 = *reinterpret_cast<const v4u*>(xa + 48);   // inputs 24..31
-        const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-        const uint32_t xl[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        const uint32_t xh[8] = {x2.x, x2.y, x2.z, x2.w, x3.x, x3.y, x3.z, x3.w};
-        float d = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t lo = wv[i] & 0x0F0F0F0Fu;          // inputs 4i .. 4i+3
-            const uint32_t hi = (wv[i] >> 4) & 0x0F0F0F0Fu;   // inputs 16+4i .. 16+4i+3
-            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, lo, 0x04010400u), xl[2 * i], d);
-            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, lo, 0x04030402u), xl[2 * i + 1], d);
-            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, hi, 0x04010400u), xh[2 * i], d);
-            d = dot2bf(__builtin_amdgcn_perm(0x43434343u, hi, 0x04030402u), xh[2 * i + 1], d);
-        }
-        acc = fmaf(qscale, fmaf(-136.0f, qxsum, d), acc);
+        const v4u* xp = reinterpret_cast<const v4u*>(xa);
+        granule_dot_q4(w, xp[0], xp[1], xp[2], xp[3], qscale, qxsum, acc);
     }
 }
 
@@ -290,10 +311,8 @@ __device__ void x_prep_wg(int kind, int wg, const uint16_t* __restrict__ x, int 
         const int nb = H / 32;
         const int64_t i = (int64_t)wg * GROUP_THREADS + tid;
         if (i >= (int64_t)T * nb) return;
-        const uint16_t* p = x + (i / nb) * H + 32 * (i % nb);
-        float sum = 0.0f;
-        for (int e = 0; e < 32; ++e) sum += moe::bf16_to_f32(p[e]);
-        xbs[i] = sum;
+        const v4u* p = reinterpret_cast<const v4u*>(x + (i / nb) * H + 32 * (i % nb));
+        xbs[i] = block_sum_bf16(p[0], p[1], p[2], p[3]);
     }
 }
 
@@ -566,7 +585,8 @@ struct RowPtrs {
 // Activations of one pass: up to NT rows of a row-major [rows][len] array
 // (x for gate/up, h for down), read directly from global memory (they are
 // small and shared by every tile of the slot, so they stay in L2).  4-bit
-// weights also need the per-block sums of those rows.
+// weights also need the per-block sums of those rows (made by gemv_rows
+// itself with INSUM, the one-token kernels).
 struct ActRows {
     const unsigned char* base;  // row r at base + r * row_bytes
     size_t row_bytes;
@@ -581,7 +601,7 @@ struct ActRows {
 // groups of NCHG whose weight loads are all issued before the first is used;
 // granules past the end read a clamped, in-bounds granule with zero weights.
 // acc[i * NT + t] holds the lane's partial sum of its i-th row and token t.
-template <int F, int ROWS, int NT, int NCHG, int LPR>
+template <int F, int ROWS, int NT, int NCHG, int LPR, bool INSUM = false>
 __device__ __forceinline__ void gemv_rows(const RowPtrs<ROWS>& rp, const ActRows& ar, const int (&arow)[NT], int KG,
                                           int lane, typename Fmt<F>::Acc (&acc)[(ROWS * LPR / 64) * NT]) {
     constexpr int XG = Fmt<F>::EPG * Fmt<F>::ABYTES;  // activation bytes per weight granule
@@ -637,10 +657,21 @@ __device__ __forceinline__ void gemv_rows(const RowPtrs<ROWS>& rp, const ActRows
 #pragma unroll
                 for (int t = 0; t < NT; ++t) {
                     const unsigned char* xa = ar.base + (size_t)arow[t] * ar.row_bytes + (size_t)gj[j] * XG;
-                    float xsum = 0.0f;
-                    if constexpr (F == MOE_W_Q4B32) xsum = ar.bsum[(size_t)arow[t] * KG + gj[j]];
+                    if constexpr (F == MOE_W_Q4B32 && INSUM) {
+                        // one-token batches skip the launches that make the block sums: the
+                        // block's inputs held once for all rows, their sum made here
+                        const v4u* xp = reinterpret_cast<const v4u*>(xa);
+                        const v4u x0 = xp[0], x1 = xp[1], x2 = xp[2], x3 = xp[3];
+                        const float xsum = block_sum_bf16(x0, x1, x2, x3);
 #pragma unroll
-                    for (int i = 0; i < RL; ++i) granule_dot<F>(w[j][i], xa, qs[j][i], xsum, acc[i * NT + t]);
+                        for (int i = 0; i < RL; ++i)
+                            granule_dot_q4(w[j][i], x0, x1, x2, x3, qs[j][i], xsum, acc[i * NT + t]);
+                    } else {
+                        float xsum = 0.0f;
+                        if constexpr (F == MOE_W_Q4B32) xsum = ar.bsum[(size_t)arow[t] * KG + gj[j]];
+#pragma unroll
+                        for (int i = 0; i < RL; ++i) granule_dot<F>(w[j][i], xa, qs[j][i], xsum, acc[i * NT + t]);
+                    }
                 }
             }
         } else {
@@ -714,13 +745,14 @@ __host__ __device__ constexpr int down_lpr(int KG, int w_type) {
 
 // Picks of one pass (uniform across the wave): pick[t] for t < nt, the last
 // valid pick repeated above (its results are dropped).
-template <int NT>
+// With DIRECT (one-token batches, no sort) position p is pick p itself.
+template <int NT, bool DIRECT = false>
 __device__ __forceinline__ void pass_picks(const int32_t* __restrict__ pair_list, int p, int nt, int (&pick)[NT]) {
 #pragma unroll
-    for (int t = 0; t < NT; ++t) pick[t] = pair_list[p + min(t, nt - 1)];
+    for (int t = 0; t < NT; ++t) pick[t] = DIRECT ? p + min(t, nt - 1) : pair_list[p + min(t, nt - 1)];
 }
 
-template <int F, int NT, int NCHG>
+template <int F, int NT, int NCHG, bool DIRECT>
 __device__ __forceinline__ void gu_pass(const RowPtrs<2 * Fmt<F>::RGU>& rp, const SlabView& sv, const unsigned char* slab,
                                         const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
                                         int H, int I, int k, int r_base, const float* __restrict__ xscale,
@@ -730,13 +762,13 @@ __device__ __forceinline__ void gu_pass(const RowPtrs<2 * Fmt<F>::RGU>& rp, cons
     constexpr int V = ROWS * NT;
     const int lane = threadIdx.x & 63;
     int pick[NT], tok[NT];
-    pass_picks<NT>(pair_list, p, nt, pick);
+    pass_picks<NT, DIRECT>(pair_list, p, nt, pick);
 #pragma unroll
     for (int t = 0; t < NT; ++t) tok[t] = pick[t] / k;
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    gemv_rows<F, ROWS, NT, NCHG, 64>(rp, ar, tok, H / Fmt<F>::EPG, lane, acc);
+    gemv_rows<F, ROWS, NT, NCHG, 64, DIRECT>(rp, ar, tok, H / Fmt<F>::EPG, lane, acc);
     int idx;
     Acc v = moe::wave_multi_sum<V>(acc, lane, idx);
     const Acc up = __shfl_xor(v, 32, 64);
@@ -777,20 +809,29 @@ constexpr int NT_TOP = NTMAX > 4 ? NTMAX : 4;
 // One workgroup per (slot with work, tile of 4 * RGU gate rows and the
 // same up rows); each wave owns RGU gate and RGU up rows.  Waves are
 // independent: no LDS, no barrier.
-template <int F, int NCHG>
+// DIRECT (one-token batches): no pick sort; workgroup group a takes pick a
+// (slot slot_ids[a]), which needs no list: a token's picks are distinct
+// experts, and a pick taken alone is right in any case.
+template <int F, int NCHG, bool DIRECT>
 __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __restrict__ act,
                                                     const float* __restrict__ xscale, const float* __restrict__ xbsum,
                                                     int H, int I, int k, const int32_t* __restrict__ slot_off,
                                                     const int32_t* __restrict__ pair_list,
                                                     const int32_t* __restrict__ active,
                                                     const int32_t* __restrict__ n_active, void* __restrict__ hbuf,
-                                                    int tiles) {
+                                                    int tiles, const int32_t* __restrict__ slot_ids, int S) {
     constexpr int RPW_GU = Fmt<F>::RGU;
     constexpr int ROWS = 2 * RPW_GU;
     const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
-    if (a >= *n_active) return;
-    const int s = active[a];
+    int s;
+    if constexpr (DIRECT) {
+        s = slot_ids[a];
+        if (s < 0 || s >= S) return;
+    } else {
+        if (a >= *n_active) return;
+        s = active[a];
+    }
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
 #pragma unroll
     for (int rep = 0; rep < Fmt<F>::REP; ++rep) {
@@ -809,18 +850,24 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
         rp.s[RPW_GU + r] = slab + sv.s1 + (size_t)row * KG * 2;
     }
     const ActRows ar{reinterpret_cast<const unsigned char*>(act), (size_t)H * Fmt<F>::ABYTES, xbsum};
-    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
+    const int p0 = DIRECT ? a : slot_off[s], ns = DIRECT ? 1 : slot_off[s + 1] - p0;
+    (void)ns;
     // passes of up to NTMAX tokens (a slot with more tokens re-reads its rows)
-    for (int c0 = 0; c0 < ns; c0 += NTMAX) {
-        const int nt = min(NTMAX, ns - c0);
-#define MOE_GU(N) gu_pass<F, N, NCHG>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, k, r_base, xscale, hbuf)
-        MOE_NT_DISPATCH(nt, MOE_GU);
-#undef MOE_GU
+#define MOE_GU(N) gu_pass<F, N, NCHG, DIRECT>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, k, r_base, xscale, hbuf)
+    if constexpr (DIRECT) {  // one pick
+        const int c0 = 0, nt = 1;
+        MOE_GU(1);
+    } else {
+        for (int c0 = 0; c0 < ns; c0 += NTMAX) {
+            const int nt = min(NTMAX, ns - c0);
+            MOE_NT_DISPATCH(nt, MOE_GU);
+        }
     }
+#undef MOE_GU
     }
 }
 
-template <int F, int NT, int NCHG, int LPR>
+template <int F, int NT, int NCHG, int LPR, bool DIRECT>
 __device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const SlabView& sv, const unsigned char* slab,
                                           const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
                                           int H, int I, int r_base, const float* __restrict__ hscale,
@@ -832,11 +879,11 @@ __device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const 
     static_assert(V <= LPR, "a lane group reduces at most LPR values at once");
     const int lane = threadIdx.x & 63;
     int pick[NT];
-    pass_picks<NT>(pair_list, p, nt, pick);
+    pass_picks<NT, DIRECT>(pair_list, p, nt, pick);
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    gemv_rows<F, RPW_DN, NT, NCHG, LPR>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
+    gemv_rows<F, RPW_DN, NT, NCHG, LPR, DIRECT>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
     // reduce inside each group of LPR lanes (strides LPR/2 .. 1)
     int idx = 0;
     moe::multi_sum_level<V, LPR / 2>(acc, lane, idx);
@@ -856,7 +903,7 @@ __device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const 
     }
 }
 
-template <int F, int NCHG, int LPR>
+template <int F, int NCHG, int LPR, bool DIRECT>
 __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* __restrict__ hact,
                                                       const float* __restrict__ hscale,
                                                       const float* __restrict__ hbsum, const float* __restrict__ wts,
@@ -864,12 +911,18 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
                                                       const int32_t* __restrict__ pair_list,
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, float* __restrict__ part,
-                                                      int tiles) {
+                                                      int tiles, const int32_t* __restrict__ slot_ids, int S) {
     constexpr int RPW_DN = Fmt<F>::RDN;
     const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
-    if (a >= *n_active) return;
-    const int s = active[a];
+    int s;
+    if constexpr (DIRECT) {
+        s = slot_ids[a];
+        if (s < 0 || s >= S) return;
+    } else {
+        if (a >= *n_active) return;
+        s = active[a];
+    }
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
 #pragma unroll
     for (int rep = 0; rep < Fmt<F>::REP; ++rep) {
@@ -886,21 +939,27 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
         rp.s[r] = slab + sv.s0 + (size_t)row * KG * 2;
     }
     const ActRows ar{reinterpret_cast<const unsigned char*>(hact), (size_t)I * Fmt<F>::ABYTES, hbsum};
-    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
-    for (int c0 = 0; c0 < ns; c0 += NTMAX) {
-        const int nt = min(NTMAX, ns - c0);
+    const int p0 = DIRECT ? a : slot_off[s], ns = DIRECT ? 1 : slot_off[s + 1] - p0;
+    (void)ns;
 #define MOE_DN(N) \
-    down_pass<F, N, NCHG, LPR>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
-        MOE_NT_DISPATCH(nt, MOE_DN);
-#undef MOE_DN
+    down_pass<F, N, NCHG, LPR, DIRECT>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
+    if constexpr (DIRECT) {  // one pick
+        const int c0 = 0, nt = 1;
+        MOE_DN(1);
+    } else {
+        for (int c0 = 0; c0 < ns; c0 += NTMAX) {
+            const int nt = min(NTMAX, ns - c0);
+            MOE_NT_DISPATCH(nt, MOE_DN);
+        }
     }
+#undef MOE_DN
     }
 }
 
 // Per-block sums of rows of bf16 activations, for 4-bit weights: out[r][b] =
-// sum of row r's inputs 32b .. 32b+31 (fp32, in input order).  The block is
-// read as four 16-byte loads that do not wait for the row's `valid` entry
-// (in bounds either way; a skipped row's sum is not stored).
+// sum of row r's inputs 32b .. 32b+31 (block_sum_bf16).  The block is read as
+// four 16-byte loads that do not wait for the row's `valid` entry (in bounds
+// either way; a skipped row's sum is not stored).
 __global__ void __launch_bounds__(256) k_block_sums(const uint16_t* __restrict__ src, int rows, int len,
                                                     const int32_t* __restrict__ valid, float* __restrict__ out) {
     const int nb = len / 32;
@@ -909,15 +968,7 @@ __global__ void __launch_bounds__(256) k_block_sums(const uint16_t* __restrict__
     const int r = (int)(i / nb), b = (int)(i % nb);
     const bool ok = !valid || valid[r] >= 0;
     const v4u* p = reinterpret_cast<const v4u*>(src + (int64_t)r * len + 32 * b);
-    v4u g[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) g[c] = p[c];
-    float sum = 0.0f;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) sum += moe::bf16_to_f32((uint16_t)(g[c][e >> 1] >> (16 * (e & 1))));
-    }
+    const float sum = block_sum_bf16(p[0], p[1], p[2], p[3]);
     if (ok) out[i] = sum;
 }
 
@@ -988,14 +1039,19 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     const bool fused_sort = F == MOE_W_BF16 && use_pf && moe_pf_fused_sort(T, k);
     // int8 matrix-core path: per gate/up column tile and pick, the max |h|
     float* hmax = (F == MOE_W_W8A8 && use_pf) ? reinterpret_cast<float*>(ws + L.hmax) : nullptr;
+    // one token on the row-streaming kernels (int8 aside, whose x codes the
+    // sort launch makes): no sort, each gate/up and down workgroup takes one
+    // pick (slot_work), and 4-bit block sums are made by those kernels
+    const bool direct = T == 1 && !use_pf && F != MOE_W_W8A8;
     // quantised batches sorted by one workgroup: x prepared in the same launch
     int xprep = XPREP_NONE;
-    if (P <= GROUP_MULTI_P) {
+    if (P <= GROUP_MULTI_P && !direct) {
         if constexpr (F == MOE_W_W8A8) xprep = XPREP_I8;
         if constexpr (F == MOE_W_Q4B32) xprep = XPREP_BSUM;
     }
-    if (fused_sort) {
+    if (direct || fused_sort) {
         // no sort launch: the gate/up workgroups write the pick and tile lists
+        // (fused sort) or take one pick each (direct)
     } else if (P > GROUP_MULTI_P) {
         const int nch = (P + GROUP_THREADS - 1) / GROUP_THREADS;
         int32_t* gcnt = reinterpret_cast<int32_t*>(ws + L.gcnt);
@@ -1050,25 +1106,31 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
     }
     if constexpr (F == MOE_W_Q4B32) {
         float* xbs = reinterpret_cast<float*>(ws + L.xbs);
-        if (!xprep) {
+        if (!xprep && !direct) {
             const int64_t n = (int64_t)T * (H / 32);
             hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
                                reinterpret_cast<const uint16_t*>(x), T, H, (const int32_t*)nullptr, xbs);
             if ((rc = moe_check_launch("moe_ffn_slots/block_sums_x"))) return rc;
         }
-        xbsum = xbs;
+        xbsum = direct ? nullptr : xbs;
     }
 
     SlabView gv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[0], lay.w[1], lay.s[0], lay.s[1]};
     const int tiles_gu = (I + 4 * Fmt<F>::RGU - 1) / (4 * Fmt<F>::RGU);
     // at most min(S, P) slots have work: workgroups beyond them would only read n_active and leave
     const int max_active = S < P ? S : P;
-#define MOE_LAUNCH_GU(G)                                                                                       \
-    hipLaunchKernelGGL((k_gu<F, G>), dim3(max_active * ((tiles_gu + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, gv,    \
-                       gu_act, xscale, xbsum, H,                                                                    \
-                       I, k, slot_off, pair_list, active, n_active, hbuf, tiles_gu)
+#define MOE_LAUNCH_GU_(G, D)                                                                                  \
+    hipLaunchKernelGGL((k_gu<F, G, D>), dim3(max_active * ((tiles_gu + Fmt<F>::REP - 1) / Fmt<F>::REP)),          \
+                       dim3(FFN_THREADS), 0, st, gv, gu_act, xscale, xbsum, H, I, k, slot_off, pair_list, active,  \
+                       n_active, hbuf, tiles_gu, slot_ids, S)
+#define MOE_LAUNCH_GU(G)                                                    \
+    if (direct) {                                                           \
+        if constexpr (F != MOE_W_W8A8) MOE_LAUNCH_GU_(G, true);             \
+    } else                                                                  \
+        MOE_LAUNCH_GU_(G, false)
     MOE_NCHG_DISPATCH(H / Fmt<F>::EPG, MOE_LAUNCH_GU);
 #undef MOE_LAUNCH_GU
+#undef MOE_LAUNCH_GU_
     if ((rc = moe_check_launch("moe_ffn_slots/gate_up"))) return rc;
 
     const void* dn_act = hbuf;
@@ -1083,21 +1145,29 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hscale = hsc;
     }
     if constexpr (F == MOE_W_Q4B32) {
-        float* hbs = reinterpret_cast<float*>(ws + L.hbs);
-        const int64_t n = (int64_t)P * (I / 32);
-        hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
-                           reinterpret_cast<const uint16_t*>(hbuf), P, I, slot_ids, hbs);
-        if ((rc = moe_check_launch("moe_ffn_slots/block_sums_h"))) return rc;
-        hbsum = hbs;
+        if (!direct) {  // one token: the down kernel sums its blocks itself
+            float* hbs = reinterpret_cast<float*>(ws + L.hbs);
+            const int64_t n = (int64_t)P * (I / 32);
+            hipLaunchKernelGGL(k_block_sums, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, st,
+                               reinterpret_cast<const uint16_t*>(hbuf), P, I, slot_ids, hbs);
+            if ((rc = moe_check_launch("moe_ffn_slots/block_sums_h"))) return rc;
+            hbsum = hbs;
+        }
     }
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
     const int tiles_dn = (H + 4 * Fmt<F>::RDN - 1) / (4 * Fmt<F>::RDN);
-#define MOE_LAUNCH_DN(G, LP)                                                                                 \
-    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(max_active * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)), dim3(FFN_THREADS), 0, st, \
-                       dv, dn_act, hscale, hbsum,                                                                   \
-                       w, H, I, slot_off, pair_list, active, n_active, part, tiles_dn)
+#define MOE_LAUNCH_DN_(G, LP, D)                                                                              \
+    hipLaunchKernelGGL((k_down<F, G, LP, D>), dim3(max_active * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)),     \
+                       dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, w, H, I, slot_off, pair_list, active,  \
+                       n_active, part, tiles_dn, slot_ids, S)
+#define MOE_LAUNCH_DN(G, LP)                                                \
+    if (direct) {                                                           \
+        if constexpr (F != MOE_W_W8A8) MOE_LAUNCH_DN_(G, LP, true);         \
+    } else                                                                  \
+        MOE_LAUNCH_DN_(G, LP, false)
     MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
 #undef MOE_LAUNCH_DN
+#undef MOE_LAUNCH_DN_
     if ((rc = moe_check_launch("moe_ffn_slots/down"))) return rc;
 
     const int64_t n4 = (int64_t)T * (H / 4);

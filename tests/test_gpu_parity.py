@@ -591,6 +591,39 @@ def test_ffn_int8_small_batches(m, T, k, S, H, I, mix):
                                       err_msg=f"token {t} alone")
 
 
+@pytest.mark.parametrize("w_type,H,I", [(0, 64, 128), (1, 2048, 768), (1, 112, 144), (2, 2048, 768), (3, 2048, 512),
+                                        (3, 1056, 544)])
+def test_ffn_one_token(m, w_type, H, I):
+    """One-token batches: fp32, bf16 and 4-bit skip the pick sort (each
+    gate/up and down workgroup takes one pick; 4-bit block sums made by those
+    kernels), int8 keeps it.  Top-8 with some picks resident, a token whose
+    picks share a slot (the same expert twice: each pick is still computed on
+    its own), and a token with no resident pick (+0.0)."""
+    E, k, S = 24, 8, 10
+    rng = np.random.default_rng(H * 3 + I + w_type)
+    x_dtype = 0 if w_type == 0 else 1
+    store = synth.slabs(w_type, 4321 + w_type, 0, 0, E, H, I, 0.05)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    slots = dev(store[resident])
+    cold = np.setdiff1d(np.arange(E), resident)
+    cases = [np.concatenate([resident[:5], cold[:3]]), np.array([resident[0]] * 2 + list(resident[1:3]) + list(cold[:4])),
+             cold[:8]]
+    for n, ids_row in enumerate(cases):
+        ids = ids_row.astype(np.int32)[None, :]
+        x = synth.normal(synth.key(H, 2, n), (1, H), 1.0, x_dtype)
+        w = rng.dirichlet(np.ones(k), 1).astype(np.float32)
+        sl = e2s[ids]
+        li = type("L", (), dict(T=1, k=k, H=H, I=I, E=E, x=x, x_dtype=x_dtype, w_type=w_type, slab=store.shape[1]))
+        _, yg, _ = oracle.layer(w_type, store, E, H, I, x, x_dtype, ids, w, sl)
+        y = run_ffn(m, li, sl, w, slots, S)
+        assert_close(y, yg, w_type, f"w{w_type} one token, case {n}")
+        if n == 2:
+            assert np.all(y == 0) and not np.any(np.signbit(y))
+        np.testing.assert_array_equal(run_ffn(m, li, sl, w, slots, S), y)
+
+
 @pytest.mark.parametrize("T,S", [(64, 24), (128, 40), (129, 40), (70, 1)])
 def test_ffn_decode_sort_in_gemm(m, T, S):
     """bf16 decode batches of 512..1024 picks are grouped by slot inside the
