@@ -69,7 +69,7 @@ MFMA_BF16_PEAK_TFS = 2500.0
 # later ones.
 FFN_SEQS = {64: ((), "k_dec_gemm<0, 4, 2, false>", ("k_dec_gemm<1, 4, 2, false>", "k_reduce")),
             8: (("k_group",), "k_gu<1, 4, false>", ("k_down<1, 3, 32, false>", "k_reduce")),
-            1: ((), "k_gu<1, 4, true>", ("k_down<1, 3, 32, true>", "k_reduce"))}
+            1: ((), "k_gu<1, 4, true>", ("k_down_tok<1, 3, 32>",))}
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
                "expert_vram_slot_amd/csrc/prefill.hpp", "expert_vram_slot_amd/csrc/common.hpp")

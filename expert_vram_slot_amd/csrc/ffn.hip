@@ -867,7 +867,7 @@ __global__ void __launch_bounds__(FFN_THREADS) k_gu(SlabView sv, const void* __r
     }
 }
 
-template <int F, int NT, int NCHG, int LPR, bool DIRECT>
+template <int F, int NT, int NCHG, int LPR>
 __device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const SlabView& sv, const unsigned char* slab,
                                           const ActRows& ar, const int32_t* __restrict__ pair_list, int p, int nt,
                                           int H, int I, int r_base, const float* __restrict__ hscale,
@@ -879,11 +879,11 @@ __device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const 
     static_assert(V <= LPR, "a lane group reduces at most LPR values at once");
     const int lane = threadIdx.x & 63;
     int pick[NT];
-    pass_picks<NT, DIRECT>(pair_list, p, nt, pick);
+    pass_picks<NT>(pair_list, p, nt, pick);
     Acc acc[V];
 #pragma unroll
     for (int i = 0; i < V; ++i) acc[i] = 0;
-    gemv_rows<F, RPW_DN, NT, NCHG, LPR, DIRECT>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
+    gemv_rows<F, RPW_DN, NT, NCHG, LPR>(rp, ar, pick, I / Fmt<F>::EPG, lane, acc);
     // reduce inside each group of LPR lanes (strides LPR/2 .. 1)
     int idx = 0;
     moe::multi_sum_level<V, LPR / 2>(acc, lane, idx);
@@ -903,7 +903,7 @@ __device__ __forceinline__ void down_pass(const RowPtrs<Fmt<F>::RDN>& rp, const 
     }
 }
 
-template <int F, int NCHG, int LPR, bool DIRECT>
+template <int F, int NCHG, int LPR>
 __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* __restrict__ hact,
                                                       const float* __restrict__ hscale,
                                                       const float* __restrict__ hbsum, const float* __restrict__ wts,
@@ -911,18 +911,12 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
                                                       const int32_t* __restrict__ pair_list,
                                                       const int32_t* __restrict__ active,
                                                       const int32_t* __restrict__ n_active, float* __restrict__ part,
-                                                      int tiles, const int32_t* __restrict__ slot_ids, int S) {
+                                                      int tiles) {
     constexpr int RPW_DN = Fmt<F>::RDN;
     const int tiles_l = (tiles + Fmt<F>::REP - 1) / Fmt<F>::REP;  // workgroups per slot
     const int a = blockIdx.x / tiles_l;
-    int s;
-    if constexpr (DIRECT) {
-        s = slot_ids[a];
-        if (s < 0 || s >= S) return;
-    } else {
-        if (a >= *n_active) return;
-        s = active[a];
-    }
+    if (a >= *n_active) return;
+    const int s = active[a];
     const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
 #pragma unroll
     for (int rep = 0; rep < Fmt<F>::REP; ++rep) {
@@ -939,20 +933,67 @@ __global__ void __launch_bounds__(FFN_THREADS) k_down(SlabView sv, const void* _
         rp.s[r] = slab + sv.s0 + (size_t)row * KG * 2;
     }
     const ActRows ar{reinterpret_cast<const unsigned char*>(hact), (size_t)I * Fmt<F>::ABYTES, hbsum};
-    const int p0 = DIRECT ? a : slot_off[s], ns = DIRECT ? 1 : slot_off[s + 1] - p0;
-    (void)ns;
+    const int p0 = slot_off[s], ns = slot_off[s + 1] - p0;
+    for (int c0 = 0; c0 < ns; c0 += NTMAX) {
+        const int nt = min(NTMAX, ns - c0);
 #define MOE_DN(N) \
-    down_pass<F, N, NCHG, LPR, DIRECT>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
-    if constexpr (DIRECT) {  // one pick
-        const int c0 = 0, nt = 1;
-        MOE_DN(1);
-    } else {
-        for (int c0 = 0; c0 < ns; c0 += NTMAX) {
-            const int nt = min(NTMAX, ns - c0);
-            MOE_NT_DISPATCH(nt, MOE_DN);
-        }
-    }
+    down_pass<F, N, NCHG, LPR>(rp, sv, slab, ar, pair_list, p0 + c0, nt, H, I, r_base, hscale, wts, part)
+        MOE_NT_DISPATCH(nt, MOE_DN);
 #undef MOE_DN
+    }
+    }
+}
+
+// One token's down projection and reduction in one launch (fp32, bf16,
+// 4-bit): workgroup b takes output rows [RDN b, RDN b + RDN) for every pick of
+// the token, the four waves splitting the picks (pick j to wave j % 4); each
+// wave's dot products are those of k_down for one pick (same lanes, same
+// order, block sums made here), w_j * o_j is staged in LDS and the rows are
+// summed over the resident picks in pick order from +0.0, as k_reduce does,
+// so y has the bits of k_down followed by k_reduce.
+template <int F, int NCHG, int LPR>
+__global__ void __launch_bounds__(FFN_THREADS) k_down_tok(SlabView sv, const void* __restrict__ hact,
+                                                          const float* __restrict__ wts, int H, int I, int k, int S,
+                                                          const int32_t* __restrict__ slot_ids,
+                                                          float* __restrict__ y) {
+    constexpr int RPW_DN = Fmt<F>::RDN;
+    constexpr int RPI = 64 / LPR;
+    constexpr int V = RPW_DN / RPI;  // values per lane: one token
+    static_assert(F != MOE_W_W8A8, "int8 h needs its codes");
+    __shared__ float cpart[MOE_MAX_K][RPW_DN];
+    const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+    const int r_base = blockIdx.x * RPW_DN;
+    const int KG = I / Fmt<F>::EPG;
+    const size_t row_bytes = (size_t)KG * 16;
+    const ActRows ar{reinterpret_cast<const unsigned char*>(hact), (size_t)I * Fmt<F>::ABYTES, nullptr};
+    for (int j = wid; j < k; j += 4) {
+        const int s = slot_ids[j];
+        if (s < 0 || s >= S) continue;  // the whole wave
+        const unsigned char* slab = sv.slots + (size_t)s * sv.slab_bytes;
+        RowPtrs<RPW_DN> rp;
+#pragma unroll
+        for (int r = 0; r < RPW_DN; ++r) {
+            const int row = min(r_base + r, H - 1);
+            rp.w[r] = slab + sv.w0 + row * row_bytes;
+            rp.s[r] = slab + sv.s0 + (size_t)row * KG * 2;
+        }
+        typename Fmt<F>::Acc acc[V];
+#pragma unroll
+        for (int i = 0; i < V; ++i) acc[i] = 0;
+        const int pick[1] = {j};
+        gemv_rows<F, RPW_DN, 1, NCHG, LPR, true>(rp, ar, pick, KG, lane, acc);
+        int idx = 0;
+        moe::multi_sum_level<V, LPR / 2>(acc, lane, idx);
+        if ((lane & (LPR / V - 1)) == 0) cpart[j][lane / LPR + RPI * idx] = wts[j] * (float)acc[0];
+    }
+    __syncthreads();
+    if (threadIdx.x < RPW_DN && r_base + (int)threadIdx.x < H) {
+        float acc = 0.0f;
+        for (int j = 0; j < k; ++j) {
+            const int s = slot_ids[j];
+            if (s >= 0 && s < S) acc += cpart[j][threadIdx.x];
+        }
+        y[r_base + threadIdx.x] = acc;
     }
 }
 
@@ -1155,19 +1196,23 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         }
     }
     SlabView dv{reinterpret_cast<const unsigned char*>(slot_store), slab_bytes, lay.w[2], 0, lay.s[2], 0};
+    if constexpr (F != MOE_W_W8A8) {
+        if (direct) {  // one token: down projection and reduction in one launch
+#define MOE_LAUNCH_DT(G, LP)                                                                                       \
+    hipLaunchKernelGGL((k_down_tok<F, G, LP>), dim3((H + Fmt<F>::RDN - 1) / Fmt<F>::RDN), dim3(FFN_THREADS), 0, st, \
+                       dv, dn_act, w, H, I, k, S, slot_ids, y)
+            MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DT);
+#undef MOE_LAUNCH_DT
+            return moe_check_launch("moe_ffn_slots/down_token");
+        }
+    }
     const int tiles_dn = (H + 4 * Fmt<F>::RDN - 1) / (4 * Fmt<F>::RDN);
-#define MOE_LAUNCH_DN_(G, LP, D)                                                                              \
-    hipLaunchKernelGGL((k_down<F, G, LP, D>), dim3(max_active * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)),     \
-                       dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, w, H, I, slot_off, pair_list, active,  \
-                       n_active, part, tiles_dn, slot_ids, S)
-#define MOE_LAUNCH_DN(G, LP)                                                \
-    if (direct) {                                                           \
-        if constexpr (F != MOE_W_W8A8) MOE_LAUNCH_DN_(G, LP, true);         \
-    } else                                                                  \
-        MOE_LAUNCH_DN_(G, LP, false)
+#define MOE_LAUNCH_DN(G, LP)                                                                                 \
+    hipLaunchKernelGGL((k_down<F, G, LP>), dim3(max_active * ((tiles_dn + Fmt<F>::REP - 1) / Fmt<F>::REP)),     \
+                       dim3(FFN_THREADS), 0, st, dv, dn_act, hscale, hbsum, w, H, I, slot_off, pair_list, active, \
+                       n_active, part, tiles_dn)
     MOE_DOWN_DISPATCH(I / Fmt<F>::EPG, MOE_LAUNCH_DN);
 #undef MOE_LAUNCH_DN
-#undef MOE_LAUNCH_DN_
     if ((rc = moe_check_launch("moe_ffn_slots/down"))) return rc;
 
     const int64_t n4 = (int64_t)T * (H / 4);
