@@ -81,3 +81,38 @@ def test_noalloc_refuses_sizes_beyond_the_scratch(m):
     with pytest.raises(m.MoeError) as e:
         m.moe_ffn_slots_noalloc(x, 1, sl, w, T, k, slots, slab, E, 1, H, I, y)
     assert e.value.code == m.MOE_E_SHAPE and "static scratch" in str(e.value)
+
+
+@pytest.mark.parametrize("cfg,T,S,other", [("c2", 64, 64, 8), ("c2", 1, 64, 8), ("c3", 16, 32, 3), ("c4", 32, 192, 1)])
+def test_noalloc_replayed_from_a_hip_graph(m, cfg, T, S, other):
+    """The allocation-free call captured once in a HIP graph and replayed
+    three times, with eager calls of another size on the same static scratch
+    between the replays: every replay equals the eager result bit for bit (the
+    kernels clear what they count in, so a replay does not depend on what the
+    scratch held)."""
+    li, x, sl, w, slots, S = case(cfg, T, S, seed=11)
+    lo, xo, slo, wo, slotso, So = case(cfg, other, S, seed=12)
+    _, y_ref = both(m, li, x, sl, w, slots, S)
+
+    def call(L, xx, ss, ww, st, SS, out):
+        m.moe_ffn_slots_noalloc(xx, L.x_dtype, ss, ww, L.T, L.k, st, L.slab, SS, L.w_type, L.H, L.I, out)
+
+    y = torch.full((li.T, li.H), float("nan"), dtype=torch.float32, device="cuda")
+    y_other = torch.empty((lo.T, lo.H), dtype=torch.float32, device="cuda")
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call(li, x, sl, w, slots, S, y)  # warm-up outside the capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call(li, x, sl, w, slots, S, y)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        y.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(y.cpu().numpy(), y_ref, err_msg=f"replay {rep}")
+        call(lo, xo, slo, wo, slotso, So, y_other)  # eager work on the same scratch between replays
+        torch.cuda.synchronize()
