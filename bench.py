@@ -966,11 +966,18 @@ def cpu_baseline(synth, T, n_tok=48, reps=3):
 
 
 def ffn_source_hash():
+    """Hash of the FFN kernels' code: the sources with comments and
+    whitespace taken out, so that only a change of the code itself voids the
+    stored counter readings."""
     import hashlib
+    import re
     h = hashlib.sha256()
     for f in FFN_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, f)) as fh:
+            src = fh.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 

@@ -22,6 +22,8 @@
 //   k_quant_rows (W8A8) int8 codes + scale per pick of h
 //   k_down       down rows against h -> part[pick][H] = w * o
 //   k_reduce     y[t] = sum over resident picks in top-k order
+//   (one token, fp32 / bf16 / 4-bit: k_gu with one pick per workgroup, then
+//   k_down_tok, the down rows of all the token's picks and their sum)
 //
 // Weight streaming: each workgroup owns a tile of rows of one slot; the four
 // waves split the rows, the 64 lanes of a wave read consecutive 16-byte
