@@ -55,7 +55,9 @@ constexpr int GROUP_THREADS = 1024;
 constexpr bool X_PREFETCH = true;  // activation granules one chunk ahead (16-byte activation granules)
 constexpr int GROUP_MULTI_P = 4096;  // larger batches sort with one workgroup per 1024 picks
 // bf16 batches with at least this many picks take the MFMA grouped-GEMM path
-constexpr int PF_MIN_P = 512;
+// (128-expert 2048 x 768 layer, 64 slots: at 32 tokens 96 vs 102 us for the
+// row-streaming kernels; at 16 tokens 82 vs 77, at 8 tokens 58 vs 55)
+constexpr int PF_MIN_P = 256;
 // and W8A8 batches from this many (int8 MFMA tiles; measured on the 128-expert, 2048 x 768 layer with 32
 // slots: at 16 tokens a wash against the row-streaming kernels, 47 vs 49 us with every slot busy and 38 vs 33 us
 // with half of them; from 32 tokens on the tiles win: 49 vs 63 us, 55 vs 99 at 64, 88 vs 341 at 256)

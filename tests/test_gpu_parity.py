@@ -624,11 +624,12 @@ def test_ffn_one_token(m, w_type, H, I):
         np.testing.assert_array_equal(run_ffn(m, li, sl, w, slots, S), y)
 
 
-@pytest.mark.parametrize("T,S", [(64, 24), (128, 40), (129, 40), (70, 1)])
+@pytest.mark.parametrize("T,S", [(64, 24), (128, 40), (129, 40), (70, 1), (32, 24), (40, 12), (31, 24)])
 def test_ffn_decode_sort_in_gemm(m, T, S):
-    """bf16 decode batches of 512..1024 picks are grouped by slot inside the
-    gate/up GEMM (no sort launch); 1032 picks go through the sort kernel.
-    Slots with several 32-row tiles, non-resident picks, a single slot."""
+    """bf16 decode batches of 256..1024 picks are grouped by slot inside the
+    gate/up GEMM (no sort launch); 1032 picks go through the sort kernel, 248
+    picks (31 tokens) through the row-streaming kernels.  Slots with several
+    32-row tiles, non-resident picks, a single slot."""
     E, k, H, I = 40, 8, 256, 128
     rng = np.random.default_rng(T * 7 + S)
     x = synth.normal(synth.key(T, 1, S), (T, H), 1.0, 1)
