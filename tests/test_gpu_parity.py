@@ -671,7 +671,9 @@ def test_ffn_prefill_grouped_gemm(m, T, S, H):
     more picks than one tile, ragged tiles, non-resident experts; from 4096
     picks the 128-row tiles, with four 32-row weight blocks per wave in the
     gate/up GEMM and, in the down GEMM, eight when H is a multiple of 256 (two
-    and four 256-column tiles at H = 512 and 1024) and four otherwise."""
+    and four 256-column tiles at H = 512 and 1024) and four otherwise.  The
+    last tiles of the slots at T = 520 and 700 hold 1-32, 33-64, 65-96 and
+    97-128 picks, so each count of staged 32-row token blocks runs."""
     E, k, I = 24, 8, 384
     rng = np.random.default_rng(T + S)
     x = synth.normal(synth.key(7, 1, T), (T, H), 1.0, 1)
