@@ -68,7 +68,7 @@ MFMA_BF16_PEAK_TFS = 2500.0
 # name anchors a launch; the names before it are the closest earlier dispatches, those after it the closest
 # later ones.
 FFN_SEQS = {64: ((), "k_dec_gemm<0, 4, 2, false>", ("k_dec_gemm<1, 4, 2, false>", "k_reduce")),
-            8: (("k_group",), "k_gu<1, 4, false>", ("k_down<1, 3, 32, false>", "k_reduce")),
+            8: (("k_group_small",), "k_gu<1, 4, false>", ("k_down<1, 3, 32>", "k_reduce")),
             1: ((), "k_gu<1, 4, true>", ("k_down_tok<1, 3, 32>",))}
 # source files whose change invalidates stored HBM counter readings of those kernels
 FFN_SOURCES = ("expert_vram_slot_amd/csrc/ffn.hip", "expert_vram_slot_amd/csrc/prefill.hip",
@@ -1015,7 +1015,7 @@ def _csv_rows(d, suffix):
 
 def _short(name):
     n = name.split("(")[0] if "::" not in name else name
-    for k in ("k_group_hist", "k_group_place", "k_group", "k_gu", "k_down_tok", "k_down", "k_reduce", "k_route",
+    for k in ("k_group_hist", "k_group_place", "k_group_small", "k_group", "k_gu", "k_down_tok", "k_down", "k_reduce", "k_route",
               "k_logits",
               "k_topk", "k_manage", "k_gather", "k_combine", "k_quant_rows", "k_block_sums", "k_pick_static",
               "k_bias_table", "k_cache_init", "k_pf_gemm", "k_pf_wide", "k_dec_gemm", "k_pf_tiles", "k_residual_bf16",

@@ -437,6 +437,57 @@ __global__ void __launch_bounds__(GROUP_THREADS) k_group(const int32_t* __restri
     }
 }
 
+// k_group's lists (slot_off, pair_list, active, n_active) for batches of at
+// most 64 picks that need nothing else (fp32 and bf16 weights): one wave,
+// one pick per lane; ranks within a slot from ballots (wave_slot_rank), the
+// offsets by a wave prefix sum over the slots, 64 at a time.  (The
+// 128-expert bf16 layer, 64 slots: 8 tokens 52.0 -> 50.2 us, 4 tokens
+// 30.9 -> 29.2 us, back to back, against the 1024-thread sort.)
+constexpr int GROUP_SMALL_P = 64;
+__global__ void __launch_bounds__(64) k_group_small(const int32_t* __restrict__ slot_ids, int P, int S,
+                                                    int32_t* __restrict__ slot_off, int32_t* __restrict__ pair_list,
+                                                    int32_t* __restrict__ active, int32_t* __restrict__ n_active) {
+    __shared__ int cnt[MOE_MAX_S];  // per slot: its pick count, then its first position
+    const int lane = threadIdx.x;
+    int nbits = 0;
+    while ((1 << nbits) < S) ++nbits;
+    int s = lane < P ? slot_ids[lane] : -1;
+    if (s >= S) s = -1;
+    const bool valid = s >= 0;
+    for (int i = lane; i < S; i += 64) cnt[i] = 0;
+    int c;
+    const int rank = wave_slot_rank(s, valid, nbits, &c);
+    __syncthreads();
+    if (valid && rank == 0) cnt[s] = c;
+    __syncthreads();
+    const uint64_t lt = (1ull << lane) - 1ull;
+    int carry = 0, acarry = 0;
+    for (int base = 0; base < S; base += 64) {
+        const int sl = base + lane;
+        const int cv = sl < S ? cnt[sl] : 0;
+        int incl = cv;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int t = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += t;
+        }
+        const uint64_t busy = __ballot(cv > 0);
+        if (sl < S) {
+            slot_off[sl] = carry + incl - cv;
+            cnt[sl] = carry + incl - cv;
+        }
+        if (cv > 0) active[acarry + __popcll(busy & lt)] = sl;
+        carry += __shfl(incl, 63, 64);
+        acarry += __popcll(busy);
+    }
+    if (lane == 0) {
+        slot_off[S] = carry;
+        *n_active = acarry;
+    }
+    __syncthreads();
+    if (valid) pair_list[cnt[s] + rank] = lane;
+}
+
 // Per-chunk slot counts: cnt[c][s] = picks of chunk c (1024 picks) with slot s.
 __global__ void __launch_bounds__(GROUP_THREADS) k_group_hist(const int32_t* __restrict__ slot_ids, int P, int S,
                                                               int32_t* __restrict__ cnt) {
@@ -1105,6 +1156,10 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         hipLaunchKernelGGL(k_group_place, dim3(nch), dim3(GROUP_THREADS), 0, st, slot_ids, P, S, gcnt, nch, slot_off,
                            pair_list, active, n_active, pf_tiles, pf_n_tiles, pf_mt);
         if ((rc = moe_check_launch("moe_ffn_slots/group_place"))) return rc;
+    } else if (P <= GROUP_SMALL_P && xprep == XPREP_NONE && !use_pf) {
+        hipLaunchKernelGGL(k_group_small, dim3(1), dim3(64), 0, st, slot_ids, P, S, slot_off, pair_list, active,
+                           n_active);
+        if ((rc = moe_check_launch("moe_ffn_slots/group_small"))) return rc;
     } else {
         hipLaunchKernelGGL(k_group, dim3(1 + x_prep_wgs(xprep, T, H)), dim3(GROUP_THREADS), 0, st, slot_ids, P, S,
                            slot_off, pair_list, active, n_active, pf_tiles, pf_n_tiles, pf_mt, xprep,

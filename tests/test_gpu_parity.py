@@ -591,6 +591,55 @@ def test_ffn_int8_small_batches(m, T, k, S, H, I, mix):
                                       err_msg=f"token {t} alone")
 
 
+@pytest.mark.parametrize("w_type,T,k,S,H,I,mix", [(1, 8, 8, 64, 2048, 768, "zipf"), (1, 8, 8, 6, 2048, 768, "uniform"),
+                                                   (1, 2, 8, 64, 2048, 768, "uniform"), (1, 64, 1, 5, 256, 128, "uniform"),
+                                                   (1, 5, 8, 40, 112, 144, "uniform"), (0, 8, 8, 16, 64, 128, "uniform"),
+                                                   (1, 6, 8, 200, 256, 128, "uniform"), (1, 4, 8, 16, 2048, 768, "cold")])
+def test_ffn_small_batches(m, w_type, T, k, S, H, I, mix):
+    """fp32 and bf16 batches of 2..64 picks, sorted by the one-wave sort: the
+    128-expert layer's 8-token Zipf batch; 8 tokens over 6 slots (two passes
+    of four over some slots); 64 one-pick tokens over 5 slots; ragged 112 x
+    144 rows; fp32; 200 slots (the slot offsets summed 64 at a time); a batch
+    with no resident pick.  Against the oracle, and bit-identical to the same
+    tokens in a batch of more than 64 picks (sorted by k_group), padded with
+    tokens whose picks all miss."""
+    E = max(2 * S, 16, k + 4)
+    rng = np.random.default_rng(T * 37 + S + H + w_type)
+    x = synth.normal(synth.key(T, 12, S), (T, H), 1.0, 0 if w_type == 0 else 1)
+    store = synth.slabs(w_type, 333 + H + I, 0, 0, E, H, I, 0.05)
+    if mix == "zipf":
+        ids = synth.zipf_ids(synth.key(T, 13), synth.key(T, 14), T, E, k, 0.8).astype(np.int32)
+        resident = np.argsort(-np.bincount(ids.reshape(-1), minlength=E), kind="stable")[:S]
+    else:
+        ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+        resident = rng.choice(E, S, replace=False)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    e2s = np.full(E, -1, np.int32)
+    if mix != "cold":
+        e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    assert 1 < T and T * k <= 64
+    slots = dev(store[resident])
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=0 if w_type == 0 else 1, w_type=w_type,
+                            slab=store.shape[1]))
+    _, yg, _ = oracle.layer(w_type, store, E, H, I, x, li.x_dtype, ids, w, sl)
+    y = run_ffn(m, li, sl, w, slots, S)
+    assert_close(y, yg, w_type, f"small T={T} k={k} S={S} H={H} I={I} {mix}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+    # the same tokens followed by tokens whose picks all miss, past 64 picks: the workgroup sort
+    n_pad = (64 - T * k) // k + 1
+    xp = np.concatenate([x, x[:1].repeat(n_pad, axis=0)])
+    slp = np.concatenate([sl, np.full((n_pad, k), -1, np.int32)])
+    wp = np.concatenate([w, w[:1].repeat(n_pad, axis=0)])
+    big = type("L", (), dict(T=T + n_pad, k=k, H=H, I=I, E=E, x=xp, x_dtype=li.x_dtype, w_type=w_type,
+                             slab=store.shape[1]))
+    assert (T + n_pad) * k > 64
+    yp = run_ffn(m, big, slp, wp, slots, S)
+    np.testing.assert_array_equal(yp[:T], y, err_msg="the same tokens sorted by the workgroup sort")
+    assert np.all(yp[T:] == 0)
+
+
 @pytest.mark.parametrize("w_type,H,I", [(0, 64, 128), (1, 2048, 768), (1, 112, 144), (2, 2048, 768), (3, 2048, 512),
                                         (3, 1056, 544)])
 def test_ffn_one_token(m, w_type, H, I):
