@@ -1259,6 +1259,31 @@ def test_ffn_top1_and_top32(m, w_type, k):
     assert_close(y, yg, w_type, f"w{w_type} k={k}")
 
 
+@pytest.mark.parametrize("T", [4, 40, 600])
+def test_ffn_1024_slots(m, T):
+    """The ABI's largest slot count (1,024 slots of 1,200 experts, bf16, H = I
+    = 128) at 32 picks (the one-wave sort, its offsets over 16 groups of 64
+    slots), 320 picks (matrix-core tiles sorted inside the gate/up kernel) and
+    4,800 picks (prefill tiles, the multi-workgroup sort), a sixth of the
+    experts not resident.  Against the oracle."""
+    E, S, k, H, I = 1200, 1024, 8, 128, 128
+    rng = np.random.default_rng(1024 + T)
+    x = synth.normal(synth.key(T, 21, S), (T, H), 1.0, 1)
+    store = synth.slabs(1, 1024, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(1, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 1, f"1024 slots T={T}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+
+
 def test_empty_batch_is_a_no_op(m):
     """T = 0 tokens through every entry point that takes a batch: each returns
     success and leaves its outputs as they were; the native step too."""
