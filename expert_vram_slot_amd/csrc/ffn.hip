@@ -90,9 +90,11 @@ struct Fmt<MOE_W_W8A8> {
     static constexpr int REP = 1;  // row tiles per GEMV workgroup, taken one after the other
     // two gate rows (and two up rows) per wave: a 2 KiB row is two chunks of
     // 64 granules, so one row pair left each lane four loads in flight
-    // (128-expert layer, 16 tokens, 32 busy slots: 51.8 -> 48.4 us)
+    // (128-expert layer, 16 tokens, 32 busy slots: 51.8 -> 48.4 us); eight
+    // down rows per wave on 32 lanes each (45.8 -> 45.0 us; 8 tokens 41.8 ->
+    // 41.0 us, against four rows on 64 lanes)
     static constexpr int RGU = 2;  // gate rows (and as many up rows) per wave
-    static constexpr int RDN = 4;  // down rows per wave
+    static constexpr int RDN = 8;  // down rows per wave
     static constexpr int EPG = 16;
     static constexpr int ABYTES = 1;
     using Acc = int;
@@ -763,13 +765,14 @@ __host__ __device__ constexpr int chunk_group(int KG, int LPR = 64) {
 
 // Lanes per row of the down projection.  Narrower lane groups keep every
 // lane busy on short rows but give each lane fewer rows to share one
-// activation read with; that pays for fp32/bf16 (one activation byte per
-// weight byte), not for int8 weights, whose activations are as large as the
-// weight bytes.  4-bit rows of up to 16 (32) granules take 16 (32) lanes,
-// with eight rows per wave (Fmt<MOE_W_Q4B32>::RDN).
+// activation read with.  fp32/bf16 rows take the widest group that divides
+// them; int8 rows 32 lanes, with eight rows per wave (Fmt<MOE_W_W8A8>::RDN);
+// 4-bit rows of up to 16 (32) granules 16 (32) lanes, with eight rows per
+// wave (Fmt<MOE_W_Q4B32>::RDN).
 __host__ __device__ constexpr int down_lpr(int KG, int w_type) {
     return w_type == MOE_W_Q4B32 ? (KG <= 16 ? 16 : KG <= 32 ? 32 : 64)
-           : (w_type == MOE_W_W8A8 || KG % 64 == 0 || KG >= 128) ? 64
+           : w_type == MOE_W_W8A8                                  ? 32
+           : (KG % 64 == 0 || KG >= 128)                           ? 64
            : KG % 32 == 0                                                              ? 32
            : KG % 16 == 0                                                              ? 16
                                                                                        : 64;
