@@ -114,6 +114,18 @@ def test_route_prefill_shape(m):
     check_route(m, li)
 
 
+@pytest.mark.parametrize("T,E,H,k", [(517, 77, 96, 4), (600, 40, 32, 8), (512, 288, 4096, 8)])
+def test_route_matrix_core_logits_ragged(m, T, E, H, k):
+    """bf16 batches of 512 tokens and more take the fp64 matrix-core logits:
+    token and expert counts off the 16 / 32 tiles (a partial and an empty
+    expert tile), h of three 32-input blocks (halves of two and one) and of
+    one block (one wave pair with nothing to add), and the 288-expert gate."""
+    x = synth.normal(synth.key(T, 31, E), (T, H), 1.0, 1)
+    G = synth.normal(synth.key(T, 32, H), (E, H), 0.05, 1)
+    li = type("L", (), dict(T=T, H=H, E=E, k=k, x=x, x_dtype=1, G=G))
+    check_route(m, li)
+
+
 def test_route_with_graded_bias(m):
     li = synth.LayerInputs("c4", T=32, with_store=False, layer=3)
     b = synth.dirichlet(synth.key(li.base, synth.TAG_B, 3), li.E, 0.3)
