@@ -79,9 +79,7 @@ __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 // The sum over k is then taken in a rotated order, fixed per workgroup.
 // Rows whose length is not a multiple of 4 KiB spread by themselves (and the
 // down GEMM of the decode layer ran slower rotated), so they start at 0.
-#ifndef ROT_BYTES
-#define ROT_BYTES 4096
-#endif
+constexpr int ROT_BYTES = 4096;
 __device__ __forceinline__ int k_rot(int nk) {
     return (nk * PF_ROWB) % ROT_BYTES == 0 ? (int)(blockIdx.x % (unsigned)nk) : 0;
 }
