@@ -11,6 +11,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <stdlib.h>
+
 #include <algorithm>
 #include <atomic>
 #include <chrono>
@@ -142,6 +144,53 @@ Pool& pool() {
 }
 
 void parallel(int threads, int n, const std::function<void(int)>& fn) { pool().run(threads, n, fn); }
+
+// ---------------------------------------------------------- scratch
+
+// Intermediate rows of the pass, kept per calling thread between calls so
+// that a step neither zero-fills nor faults in its buffers again: every
+// element the pass reads it has written in the same call (the rows of the
+// picks it serves).  A buffer above KEEP_BYTES is released when its call
+// ends, so only decode-sized needs stay allocated.
+constexpr size_t KEEP_BYTES = size_t(64) << 20;
+enum ScratchBuf { SB_XF, SB_XQ, SB_XS, SB_XW, SB_XBS, SB_XP, SB_HF, SB_HQ, SB_HS, SB_HW, SB_HB, SB_HBS, SB_HP, SB_PART,
+                  SB_COUNT };
+
+struct Scratch {
+    void* p[SB_COUNT] = {};
+    size_t cap[SB_COUNT] = {};
+    ~Scratch() {
+        for (void* q : p) free(q);
+    }
+};
+thread_local Scratch tl_scratch;
+
+// n elements of buffer b, 64-byte aligned, contents undefined; nullptr when
+// the allocation fails (n == 0 gives a valid pointer too)
+template <class T>
+T* scratch(ScratchBuf b, size_t n) {
+    Scratch& s = tl_scratch;
+    const size_t bytes = (std::max<size_t>(n * sizeof(T), 64) + 63) & ~size_t(63);
+    if (bytes > s.cap[b]) {
+        free(s.p[b]);
+        s.p[b] = aligned_alloc(64, bytes);
+        s.cap[b] = s.p[b] ? bytes : 0;
+    }
+    return static_cast<T*>(s.p[b]);
+}
+
+// releases the call's buffers above KEEP_BYTES on every return path
+struct ScratchTrim {
+    ~ScratchTrim() {
+        Scratch& s = tl_scratch;
+        for (int b = 0; b < SB_COUNT; ++b)
+            if (s.cap[b] > KEEP_BYTES) {
+                free(s.p[b]);
+                s.p[b] = nullptr;
+                s.cap[b] = 0;
+            }
+    }
+};
 
 // ---------------------------------------------------------- formats
 
@@ -490,13 +539,31 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     const bool q4x = q4_fast && H % 128 == 0 && I % 128 == 0;
     const bool i8_fast = w_type == MOE_W_W8A8 && have_avx512bw() && H % 32 == 0 && I % 32 == 0;
     const bool need_xf = w_type == MOE_W_W8A8 || (w_type == MOE_W_Q4B32 && !q4_fast);
-    std::vector<float> xf(need_xf ? (size_t)T * H : 0);
-    const float* xfp = w_type == MOE_W_F32 ? reinterpret_cast<const float*>(x_h) : xf.data();
-    std::vector<int8_t> xq(w_type == MOE_W_W8A8 ? (size_t)T * H : 0);
-    std::vector<float> xs(w_type == MOE_W_W8A8 ? T : 0);
-    std::vector<int16_t> xw(i8_fast ? (size_t)T * H : 0);  // W8A8: int8 activations widened once
-    std::vector<float> xbs(q4_fast ? (size_t)T * (H / 32) : 0);  // 4-bit: per-block sums of x
-    std::vector<uint16_t> xp(q4x ? (size_t)T * H : 0);          // 4-bit: grouped order
+    const bool bf16_fast = w_type == MOE_W_BF16 && have_avx512bf16() && H % 32 == 0 && I % 32 == 0;
+    const bool need_hb = (w_type == MOE_W_BF16 && bf16_fast) || q4_fast;
+    const bool w8 = w_type == MOE_W_W8A8;
+    const ScratchTrim trim;
+    float* xf = scratch<float>(SB_XF, need_xf ? (size_t)T * H : 0);
+    const float* xfp = w_type == MOE_W_F32 ? reinterpret_cast<const float*>(x_h) : xf;
+    int8_t* xq = scratch<int8_t>(SB_XQ, w8 ? (size_t)T * H : 0);
+    float* xs = scratch<float>(SB_XS, w8 ? T : 0);
+    int16_t* xw = scratch<int16_t>(SB_XW, i8_fast ? (size_t)T * H : 0);   // W8A8: int8 activations widened once
+    float* xbs = scratch<float>(SB_XBS, q4_fast ? (size_t)T * (H / 32) : 0);  // 4-bit: per-block sums of x
+    uint16_t* xp = scratch<uint16_t>(SB_XP, q4x ? (size_t)T * H : 0);        // 4-bit: grouped order
+    // per pick: h (fp32; bf16-rounded where the format says so), its int8
+    // codes and scale and the codes widened (W8A8), its bf16 bits (bf16,
+    // 4-bit), block sums and grouped order (4-bit), and w * FFN(x) rows
+    float* hf = scratch<float>(SB_HF, (size_t)P * I);
+    int8_t* hq = scratch<int8_t>(SB_HQ, w8 ? (size_t)P * I : 0);
+    float* hs = scratch<float>(SB_HS, w8 ? P : 0);
+    int16_t* hw = scratch<int16_t>(SB_HW, i8_fast ? (size_t)P * I : 0);
+    uint16_t* hb = scratch<uint16_t>(SB_HB, need_hb ? (size_t)P * I : 0);
+    float* hbs = scratch<float>(SB_HBS, q4_fast ? (size_t)P * (I / 32) : 0);
+    uint16_t* hp = scratch<uint16_t>(SB_HP, q4x ? (size_t)P * I : 0);
+    float* part = scratch<float>(SB_PART, (size_t)P * H);
+    if (!xf || !xq || !xs || !xw || !xbs || !xp || !hf || !hq || !hs || !hw || !hb || !hbs || !hp || !part)
+        return moe_fail(MOE_E_NOMEM, "moe_ffn_host_misses: cannot allocate %zu bytes of host scratch",
+                        (size_t)P * (I * 4 + H * 4));
     const std::function<void(int)> prep_token = [&](int t) {
         const uint16_t* xr = xb + (size_t)t * H;
         if (need_xf)
@@ -518,8 +585,6 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     // phase 1: gate/up rows, blocks of RB rows per work item
     const int RB = 32;
     const int nrb = (I + RB - 1) / RB;
-    std::vector<float> hf((size_t)P * I);  // h per pick (fp32; bf16-rounded where the format says so)
-    const bool bf16_fast = w_type == MOE_W_BF16 && have_avx512bf16() && H % 32 == 0 && I % 32 == 0;
     parallel(n_threads, NE * nrb, [&](int item) {
         const int e = experts[item / nrb], r0 = (item % nrb) * RB, r1 = std::min(I, r0 + RB);
         const unsigned char* slab = store + (size_t)e * slab_bytes;
@@ -647,13 +712,6 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     // per-pick forms of h, one pick per work item: int8 with its scale and
     // widened (W8A8), bf16 bits (bf16, 4-bit), and for 4-bit the block sums
     // and the grouped order
-    const bool need_hb = (w_type == MOE_W_BF16 && bf16_fast) || q4_fast;
-    std::vector<int8_t> hq(w_type == MOE_W_W8A8 ? (size_t)P * I : 0);
-    std::vector<float> hs(w_type == MOE_W_W8A8 ? P : 0);
-    std::vector<int16_t> hw(i8_fast ? (size_t)P * I : 0);  // W8A8: int8 h widened once
-    std::vector<uint16_t> hb(need_hb ? (size_t)P * I : 0);
-    std::vector<float> hbs(q4_fast ? (size_t)P * (I / 32) : 0);  // 4-bit: per-block sums of h
-    std::vector<uint16_t> hp(q4x ? (size_t)P * I : 0);          // 4-bit: grouped order
     const std::function<void(int)> prep_pick = [&](int q) {
         const int p = order[q];
         const float* hr = &hf[(size_t)p * I];
@@ -677,7 +735,6 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     // phase 2: down rows -> part[p][m] = w * o
     const int RD = 64;
     const int nrd = (H + RD - 1) / RD;
-    std::vector<float> part((size_t)P * H);
     parallel(n_threads, NE * nrd, [&](int item) {
         const int e = experts[item / nrd], m0 = (item % nrd) * RD, m1 = std::min(H, m0 + RD);
         const unsigned char* slab = store + (size_t)e * slab_bytes;

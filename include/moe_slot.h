@@ -45,8 +45,9 @@
  *     holds a one-line reason (thread-local).  Nothing aborts or exits.
  *   - "device" pointers are HIP device memory (or device-visible pinned host
  *     memory where stated); "host" pointers are CPU memory.  The caller owns
- *     every buffer.  The library allocates nothing per call and keeps no
- *     pointer between calls.
+ *     every buffer.  The device calls allocate nothing per call and keep no
+ *     pointer to caller memory between calls (the host pass keeps host
+ *     scratch of its own, below).
  *   - Device calls enqueue on the given stream and never synchronise with the
  *     host.  Counts produced on the device (n_miss, n_host) stay there.
  *   - Identical inputs give bit-identical outputs (fixed reduction orders, no
@@ -74,7 +75,7 @@ extern "C" {
 #define MOE_E_DTYPE (-3)  /* unsupported activation / weight format pair */
 #define MOE_E_SHAPE (-4)  /* inconsistent or unsupported shape (k > E, S > E, limits) */
 #define MOE_E_HIP (-5)    /* a HIP runtime call or kernel launch failed */
-#define MOE_E_NOMEM (-6)  /* pinned host allocation failed */
+#define MOE_E_NOMEM (-6)  /* a pinned or host allocation failed */
 
 /* activation formats (x and the router gate G) */
 #define MOE_X_F32 0
@@ -377,7 +378,11 @@ size_t moe_ffn_noalloc_scratch_bytes(void);
  *   y_h                          host float[T][H] out (overwritten):
  *                                sum over j with slot_ids[t][j] < 0 of
  *                                w[t][j] * FFN_ids[t][j](x[t]), in j order
- * Same per-format arithmetic as moe_ffn_slots.  Errors: ARG, DTYPE, SHAPE. */
+ * Same per-format arithmetic as moe_ffn_slots.  Intermediate rows (about
+ * T*k*(4H + 6I) bytes) live in host scratch kept per calling thread between
+ * calls, so repeated steps neither zero-fill nor fault them in again; a
+ * buffer above 64 MiB is released when its call returns.  Errors: ARG,
+ * DTYPE, SHAPE, NOMEM (the scratch cannot be allocated). */
 int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* ids_h, const int32_t* slot_ids_h,
                         const float* w_h, int T, int k, const void* host_store, size_t slab_bytes, int E, int w_type,
                         int H, int I, float* y_h, int n_threads);

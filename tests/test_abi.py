@@ -209,3 +209,22 @@ def test_host_pass_all_miss_is_the_whole_layer(mlib):
     yf, _, _ = oracle.layer(0, li.store, 8, 64, 128, li.x, 0, ids, w)
     y = _run_host(mlib, li, ids, w, np.full_like(ids, -1), 3)
     _assert_close(y, yf, 0)
+
+
+def test_host_pass_scratch_kept_between_calls(mlib):
+    # the pass keeps its intermediate rows between calls on one thread: a
+    # call after larger ones, in other formats and with other residency, must
+    # give the bits it gives first, and a token with no host pick exactly +0.0
+    li, ids, w, sl, yg, yh = _host_case("c2", 4, 32, 1)
+    first = _run_host(mlib, li, ids, w, sl, 3)
+    for cfg, T, S in (("c2", 12, 16), ("c3", 8, 8), ("c4", 6, 96), ("c1", 16, 4)):
+        o = _host_case(cfg, T, S, 3)
+        _run_host(mlib, o[0], o[1], o[2], o[3], 3)
+    np.testing.assert_array_equal(_run_host(mlib, li, ids, w, sl, 3), first)
+    # now every pick of token 0 resident: its row must not pick up rows left
+    # by the calls before
+    sl2 = sl.copy()
+    sl2[0] = np.maximum(sl2[0], 0)
+    y2 = _run_host(mlib, li, ids, w, sl2, 3)
+    assert np.all(y2[0] == 0) and not np.any(np.signbit(y2[0]))
+    np.testing.assert_array_equal(y2[1:], first[1:])
