@@ -778,6 +778,49 @@ def test_ffn_large_groups_256_row_tiles(m, T, S, skew):
     assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
 
 
+
+def test_ffn_large_groups_many_items_per_workgroup(m):
+    """Enough 256 x 256 tiles that each workgroup of the large-group GEMMs
+    takes several (token tile, column tile) items in turn: 129 resident
+    slots of 384 picks each (two tiles per slot, the second half full), a
+    non-resident expert, hidden 512 and intermediate 256.  Every token tile
+    is checked through the tokens of its first and last pick (which make up
+    every column of the tile), plus random tokens, against the oracle."""
+    E, S, k, H, I = 130, 129, 2, 512, 256
+    T = E * 384 // k
+    t = np.arange(T)
+    ids = np.stack([t % E, (t + 1 + (t // E) % (E - 1)) % E], axis=1).astype(np.int32)
+    rng = np.random.default_rng(129)
+    ids = ids[rng.permutation(T)]
+    assert np.all(np.bincount(ids.ravel(), minlength=E) == 384) and np.all(ids[:, 0] != ids[:, 1])
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    x = synth.normal(synth.key(11, 1, T), (T, H), 1.0, 1)
+    store = synth.slabs(1, 557, 0, 0, E, H, I, 0.05)
+    resident = np.setdiff1d(np.arange(E), [77])
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert np.all(np.isfinite(y))
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+    # a slot's picks in pick order, 256 to a tile: the first and last pick of each tile
+    flat = sl.ravel()
+    sample = set(rng.choice(T, 8, replace=False).tolist())
+    for s in range(S):
+        picks = np.flatnonzero(flat == s)
+        for a in range(0, len(picks), 256):
+            tile = picks[a:a + 256]
+            sample.update((int(tile[0]) // k, int(tile[-1]) // k))
+    for tok in sorted(sample):
+        ref = np.zeros(H)
+        for j in range(k):
+            if sl[tok, j] >= 0:
+                ref += w[tok, j] * oracle.expert(1, store[ids[tok, j]], H, I, x[tok], 1)
+        assert_close(y[tok:tok + 1], ref[None, :].astype(np.float32), 1, f"many items token {tok}")
+
+
 @functools.lru_cache(maxsize=1)
 def prefill_inputs():
     """The 288-expert prefill layer's inputs (10.9 GB of slabs), made once per session."""
