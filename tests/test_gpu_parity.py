@@ -779,13 +779,14 @@ def test_ffn_large_groups_256_row_tiles(m, T, S, skew):
 
 
 
-def test_ffn_large_groups_many_items_per_workgroup(m):
-    """Enough 256 x 256 tiles that each workgroup of the large-group GEMMs
-    takes several (token tile, column tile) items in turn: 129 resident
-    slots of 384 picks each (two tiles per slot, the second half full), a
+def test_ffn_large_groups_258_tiles(m):
+    """Many 256 x 256 tiles on the large-group GEMMs: 129 resident slots of
+    384 picks each (two tiles per slot, the second half full: 258 tiles, 33
+    in each XCD's run of the tile list, 66 workgroups per XCD and GEMM), a
     non-resident expert, hidden 512 and intermediate 256.  Every token tile
-    is checked through the tokens of its first and last pick (which make up
-    every column of the tile), plus random tokens, against the oracle."""
+    is checked through the tokens of its first and last pick (their outputs
+    take every column tile of the tile), plus random tokens, against the
+    oracle."""
     E, S, k, H, I = 130, 129, 2, 512, 256
     T = E * 384 // k
     t = np.arange(T)
