@@ -111,6 +111,9 @@ def parse():
     ap.add_argument("--summarize-prefill", nargs=5, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR",
                                                               "COPY_WRITE_DIR"), default=None,
                     help="write the prefill kernels' summary (2048- and 16384-token legs) from the same runs")
+    ap.add_argument("--prefill-mfma", default=None, metavar="MFMA_DIR",
+                    help="with --summarize-prefill: a run of this benchmark with --pmc SQ_VALU_MFMA_BUSY_CYCLES "
+                         "GRBM_GUI_ACTIVE MfmaUtil SQ_INSTS_VALU_MFMA_MOPS_BF16, summarised per prefill kernel")
     ap.add_argument("--out", default=None, help="summary file for --summarize")
     ap.add_argument("--commands", default=None, help="text file with the profiling commands, quoted in the summary")
     return ap.parse_args()
@@ -1252,11 +1255,56 @@ def summarize_prefill(args):
             tfs = f"{flops / us / 1e6:>9.1f}" if flops else f"{'':>9}"
             lines.append(f"  {name:<18}{len(tr_rows):>6}{us:>10.1f}{hbm / 1e9:>9.2f}{alg / 1e9:>9.2f}"
                          f"{hbm / alg:>9.2f}{alg / us / 1e3:>10.0f}{tfs}")
+    if args.prefill_mfma:
+        lines.extend(_prefill_mfma_lines(args.prefill_mfma, trace, legs, pick))
     out = args.out or os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
                                    "moe_ffn_slots_bf16_prefill_c5.txt")
     with open(out, "w") as fh:
         fh.write("\n".join(lines) + "\n")
     print(f"wrote {out}")
+
+
+def _prefill_mfma_lines(d, trace, legs, pick):
+    """MFMA counters of the prefill GEMMs: the matrix cores' busy share
+    (MfmaUtil = SQ_VALU_MFMA_BUSY_CYCLES summed over the SIMDs / (GRBM_GUI_ACTIVE
+    of one XCD x SIMDs)), the shader clock those busy cycles were counted at
+    (GRBM_GUI_ACTIVE of one XCD / kernel time, the XCD's count recovered from
+    MfmaUtil), and the bf16 flops the MFMA instructions did (MOPS x 512)
+    against the algorithmic flops (the difference is the padding of partial
+    tiles)."""
+    rows = _csv_rows(d, "counter_collection.csv")
+    simds = 4 * 256
+
+    def per(name, counter, grid):
+        v = [float(r["Counter_Value"]) for r in pick(rows, name, grid, "Grid_Size") if r["Counter_Name"] == counter]
+        return float(np.mean(v)) if v else None
+
+    out = ["", "MFMA counters (a run of its own: --pmc SQ_VALU_MFMA_BUSY_CYCLES GRBM_GUI_ACTIVE MfmaUtil "
+           "SQ_INSTS_VALU_MFMA_MOPS_BF16), per call. MFMA busy: the matrix cores' busy share of the kernel's cycles "
+           "(rocprofv3's MfmaUtil); clock: those cycles over the kernel time; MFMA TFLOP: the bf16 work the MFMA "
+           "instructions did (tile padding included), alg TFLOP: 2 flops per multiply-add of the picks' rows; "
+           "of peak: alg TFLOP/s over 2.5 PFLOP/s (2.4 GHz), at clock: over the peak at the measured clock:"]
+    for T, ks in legs:
+        out.append(f"  {T} tokens:")
+        out.append(f"    {'kernel':<18}{'MFMA busy':>10}{'clock GHz':>10}{'MFMA TFLOP':>11}{'alg TFLOP':>10}"
+                   f"{'MFMA/alg':>9}{'TFLOP/s':>9}{'of peak':>8}{'at clock':>9}")
+        for name, alg, flops, grid in ks:
+            if not flops:
+                continue
+            busy, gui, util, mops = (per(name, c, grid) for c in ("SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE",
+                                                                   "MfmaUtil", "SQ_INSTS_VALU_MFMA_MOPS_BF16"))
+            tr_rows = pick(trace, name, grid, "Grid_Size_X")
+            if None in (busy, util, mops) or not tr_rows or util <= 0:
+                continue
+            us = float(np.mean([(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in tr_rows]))
+            gui_one = busy * 100.0 / (util * simds)  # GRBM_GUI_ACTIVE of one XCD
+            ghz = gui_one / us / 1e3
+            mf = mops * 512
+            tfs = flops / us / 1e6
+            peak_at_clock = 2500.0 * ghz / 2.4
+            out.append(f"    {name:<18}{util:>9.1f}%{ghz:>10.2f}{mf / 1e12:>11.2f}{flops / 1e12:>10.2f}"
+                       f"{mf / flops:>9.2f}{tfs:>9.1f}{tfs / 2500.0:>8.3f}{tfs / peak_at_clock:>9.3f}")
+    return out
 
 
 if __name__ == "__main__":
