@@ -227,21 +227,27 @@ def main():
     # from Python with HIP events around every moe_ffn_slots launch on the compute stream: the FFN's
     # duration for the roofline, free of gaps from CPU threads competing with the launching thread
     t1 = time.perf_counter()
-    ffn_ms_arr, per_launch, distinct = gpu_ffn_pass(m, torch, layers, n_x, T, args.steps, args.warmup, x_dtype,
-                                                    H, E, k, slab)
+    ffn_ms_arr, per_launch, distinct, b2b_ms = gpu_ffn_pass(m, torch, layers, n_x, T, args.steps, args.warmup,
+                                                            x_dtype, H, E, k, slab)
     elapsed_py = time.perf_counter() - t1
     achieved = float(np.mean(per_launch) / (np.mean(ffn_ms_arr) * 1e-3) / 1e9)
     # the smaller decode batches of the same layer (same layers, same steps, first T rows of x)
     batches = {}
     for Tb in (() if args.no_extra_batches else (1, 8)):
-        ms_b, pl_b, d_b = gpu_ffn_pass(m, torch, layers, n_x, Tb, args.steps, args.warmup, x_dtype, H, E, k, slab)
+        ms_b, pl_b, d_b, b2b_b = gpu_ffn_pass(m, torch, layers, n_x, Tb, args.steps, args.warmup, x_dtype, H, E, k,
+                                              slab)
         gbs = float(np.mean(pl_b) / (np.mean(ms_b) * 1e-3) / 1e9)
+        gbs_b2b = float(np.mean(pl_b) / (b2b_b * 1e-3) / 1e9)
         batches[f"T{Tb}"] = {"ffn_us": round(float(np.mean(ms_b)) * 1e3, 2), "bytes_per_launch": int(np.mean(pl_b)),
                              "distinct_slabs_per_step": round(float(np.mean(d_b)), 2), "gbs": round(gbs, 1),
-                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+                             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                             "ffn_us_back_to_back": round(b2b_b * 1e3, 2),
+                             "hbm_frac_back_to_back": round(gbs_b2b / HBM_PEAK_GBS, 4)}
+    gbs64_b2b = float(np.mean(per_launch) / (b2b_ms * 1e-3) / 1e9)
     batches["T64"] = {"ffn_us": round(float(np.mean(ffn_ms_arr)) * 1e3, 2), "bytes_per_launch": int(np.mean(per_launch)),
                       "distinct_slabs_per_step": round(float(np.mean(distinct)), 2), "gbs": round(achieved, 1),
-                      "hbm_frac": round(achieved / HBM_PEAK_GBS, 4)}
+                      "hbm_frac": round(achieved / HBM_PEAK_GBS, 4), "ffn_us_back_to_back": round(b2b_ms * 1e3, 2),
+                      "hbm_frac_back_to_back": round(gbs64_b2b / HBM_PEAK_GBS, 4)}
 
     out = {
         "metric": "MoE-layer tokens/s; expert-weight HBM GB/s as % of peak; gather GB/s",
@@ -269,7 +275,10 @@ def main():
                      "bytes_per_launch": int(np.mean(per_launch)), "ms_per_launch": round(float(np.mean(ffn_ms_arr)), 5),
                      "distinct_slabs_per_step": round(float(np.mean(distinct)), 2)},
         "decode_batches": dict(batches, workload="the same 128-expert bf16 layer, 64 resident slots, moe_ffn_slots "
-                                                 "alone (HIP events), 4 layer copies rotated"),
+                                                 "alone, 4 layer copies rotated; ffn_us: HIP events around each "
+                                                 "launch; ffn_us_back_to_back: the same launches (each step's picks "
+                                                 "and weights kept) issued back to back, one pair of events around "
+                                                 "them all"),
     }
 
     del layers, specs
@@ -313,10 +322,13 @@ def gpu_ffn_pass(m, torch, layers, n_x, T, steps, warmup, x_dtype, H, E, k, slab
     """route -> manage -> moe_ffn_slots for T tokens over the rotated layers,
     no host pass, HIP events around every moe_ffn_slots launch; returns the
     per-launch times (ms), the algorithmic bytes of each launch (every
-    distinct resident slab the step touched, read once, plus x in and y out)
-    and the distinct slabs per step (from rerunning each step's routing,
-    untimed)."""
+    distinct resident slab the step touched, read once, plus x in and y out),
+    the distinct slabs per step (from rerunning each step's routing, untimed)
+    and the mean time per launch of the same launches issued back to back
+    (each step's picks and weights kept, one pair of events around them all:
+    no event packets between the launches)."""
     ev_pairs = []
+    kept = []
 
     def one_step(i, record):
         L, xs = layers[i % len(layers)]
@@ -328,6 +340,7 @@ def gpu_ffn_pass(m, torch, layers, n_x, T, steps, warmup, x_dtype, H, E, k, slab
         L.step(x, T, host_pass=False)
         if record:
             ev_pairs.append(L.ffn_events)
+            kept.append((L, x, L.slot_ids[:T * k].clone(), L.w[:T * k].clone()))
         L.ffn_events = None
 
     for i in range(warmup):
@@ -337,6 +350,15 @@ def gpu_ffn_pass(m, torch, layers, n_x, T, steps, warmup, x_dtype, H, E, k, slab
         one_step(warmup + i, True)
     torch.cuda.synchronize()
     ms = np.array([a.elapsed_time(b) for a, b in ev_pairs])
+    cur = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(cur)
+    for L, x, sl, w in kept:
+        m.moe_ffn_slots(x, x_dtype, sl, w, T, k, L.slot_store, L.slab, max(L.S, 1), L.w_type, H, L.I, L.y, L.ws,
+                        L.ws_bytes, cur)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    b2b_ms = e0.elapsed_time(e1) / len(kept)
     distinct = []
     for i in range(steps):
         L, xs = layers[(warmup + i) % len(layers)]
@@ -347,7 +369,7 @@ def gpu_ffn_pass(m, torch, layers, n_x, T, steps, warmup, x_dtype, H, E, k, slab
         sl = L.e2s.cpu().numpy()[ids]
         distinct.append(len(set(sl[sl >= 0].tolist())))
     act_bytes = T * H * 2 + T * H * 4  # x (bf16) in, y (fp32) out
-    return ms, [d * slab + act_bytes for d in distinct], distinct
+    return ms, [d * slab + act_bytes for d in distinct], distinct, b2b_ms
 
 
 def bench_prefill(m, torch, synth, SlotLayer, steps=10, warmup=2):
