@@ -62,12 +62,13 @@ namespace {
 constexpr int kBellTimeoutS = 10;  // seconds a layer step waits for its cache step's doorbell
 // Streamed miss pass: a step of T_max >= kStreamMinT tokens gets a ring of 2 * kStreamR staging slots.  It
 // streams its misses instead of running the CPU lane when the host picks reach kStreamPicks per host expert:
-// measured on the 288-expert bf16 layer (144 resident, 16 host threads), the CPU lane took 32 / 49 / 95 / 185 ms
-// at 256 / 512 / 1024 / 2048 tokens (7 / 14 / 28 / 57 picks per host expert) and the streamed pass 100-104 ms
-// (the 144 slabs over the host link), so the two cost the same near 31 picks per expert.
+// measured on the 288-expert bf16 layer (144 resident, 16 host threads), the CPU lane took 24 / 31 / 68 / 90 /
+// 99 / 106 / 125 / 133 ms at 256 / 512 / 1024 / 1280 / 1408 / 1536 / 1792 / 2048 tokens (7 / 14 / 28 / 36 / 39 /
+// 43 / 50 / 57 picks per host expert) and the streamed pass 101-104 ms (the 144 slabs over the host link), so
+// the two cost the same near 41 picks per expert.
 constexpr int kStreamMinT = 128;
 constexpr int kStreamR = 8;
-constexpr int kStreamPicks = 32;
+constexpr int kStreamPicks = 40;
 
 int hip_fail(const char* what, hipError_t e) {
     (void)hipGetLastError();
