@@ -316,8 +316,53 @@ void dot_i8x_rows(int nt, const int8_t* w, const int16_t* const* x, int n, int32
     }
 }
 
+// The same rows with AVX-512 VNNI, the activations held as u8 = x + 128 (n % 64
+// == 0): dpbusd adds four u8 x s8 products into each int32 lane, so the row
+// gives sum (x + 128) w = sum x w + 128 sum w, and one more dpbusd against
+// ones (the row's sum of w, shared by the NT rows) takes the offset out.  All
+// of it is exact modulo 2^32 (unsigned at the end), and the result, at most
+// 127 * 128 * n in magnitude, fits int32, so it is the one the int16 path gives.
+template <int NT>
+__attribute__((target("avx512f,avx512bw,avx512vnni"))) void dot_i8u(const int8_t* w, const uint8_t* const* x, int n,
+                                                                     int32_t* out) {
+    __m512i acc[NT];
+    __m512i sw = _mm512_setzero_si512();
+    const __m512i ones = _mm512_set1_epi8(1);
+    for (int t = 0; t < NT; ++t) acc[t] = _mm512_setzero_si512();
+    for (int i = 0; i < n; i += 64) {
+        const __m512i wv = _mm512_loadu_si512(reinterpret_cast<const void*>(w + i));
+        sw = _mm512_dpbusd_epi32(sw, ones, wv);
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            acc[t] = _mm512_dpbusd_epi32(acc[t], _mm512_loadu_si512(reinterpret_cast<const void*>(x[t] + i)), wv);
+    }
+    const uint32_t s = (uint32_t)_mm512_reduce_add_epi32(sw);
+    for (int t = 0; t < NT; ++t) out[t] = (int32_t)((uint32_t)_mm512_reduce_add_epi32(acc[t]) - 128u * s);
+}
+
+void dot_i8u_rows(int nt, const int8_t* w, const uint8_t* const* x, int n, int32_t* out) {
+    switch (nt) {
+        case 1: dot_i8u<1>(w, x, n, out); break;
+        case 2: dot_i8u<2>(w, x, n, out); break;
+        case 3: dot_i8u<3>(w, x, n, out); break;
+        default: dot_i8u<4>(w, x, n, out); break;
+    }
+}
+
+// one int8 row against nt activation rows in the form the pass keeps them:
+// u8 = x + 128 (vnni) or int16
+void dot_i8_rows(bool vnni, int nt, const int8_t* w, const void* const* x, int n, int32_t* out) {
+    if (vnni) dot_i8u_rows(nt, w, reinterpret_cast<const uint8_t* const*>(x), n, out);
+    else dot_i8x_rows(nt, w, reinterpret_cast<const int16_t* const*>(x), n, out);
+}
+
 bool have_avx512bw() {
     static const bool v = __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw");
+    return v;
+}
+
+bool have_avx512vnni() {
+    static const bool v = have_avx512bw() && __builtin_cpu_supports("avx512vnni");
     return v;
 }
 
@@ -538,6 +583,7 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     const bool q4_fast = w_type == MOE_W_Q4B32 && have_avx512bf16() && have_avx512bw() && have_avx512vl();
     const bool q4x = q4_fast && H % 128 == 0 && I % 128 == 0;
     const bool i8_fast = w_type == MOE_W_W8A8 && have_avx512bw() && H % 32 == 0 && I % 32 == 0;
+    const bool i8_vnni = i8_fast && have_avx512vnni() && H % 64 == 0 && I % 64 == 0;
     const bool need_xf = w_type == MOE_W_W8A8 || (w_type == MOE_W_Q4B32 && !q4_fast);
     const bool bf16_fast = w_type == MOE_W_BF16 && have_avx512bf16() && H % 32 == 0 && I % 32 == 0;
     const bool need_hb = (w_type == MOE_W_BF16 && bf16_fast) || q4_fast;
@@ -547,7 +593,8 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
     const float* xfp = w_type == MOE_W_F32 ? reinterpret_cast<const float*>(x_h) : xf;
     int8_t* xq = scratch<int8_t>(SB_XQ, w8 ? (size_t)T * H : 0);
     float* xs = scratch<float>(SB_XS, w8 ? T : 0);
-    int16_t* xw = scratch<int16_t>(SB_XW, i8_fast ? (size_t)T * H : 0);   // W8A8: int8 activations widened once
+    // W8A8: int8 activations as u8 = x + 128 (VNNI) or widened to int16, once
+    int16_t* xw = scratch<int16_t>(SB_XW, i8_fast ? (size_t)T * H : 0);
     float* xbs = scratch<float>(SB_XBS, q4_fast ? (size_t)T * (H / 32) : 0);  // 4-bit: per-block sums of x
     uint16_t* xp = scratch<uint16_t>(SB_XP, q4x ? (size_t)T * H : 0);        // 4-bit: grouped order
     // per pick: h (fp32; bf16-rounded where the format says so), its int8
@@ -570,8 +617,12 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
             for (int i = 0; i < H; ++i) xf[(size_t)t * H + i] = bf16f(xr[i]);
         if (w_type == MOE_W_W8A8) {
             xs[t] = quant_row(&xf[(size_t)t * H], H, &xq[(size_t)t * H]);
-            if (i8_fast)
+            if (i8_vnni) {
+                uint8_t* xu = reinterpret_cast<uint8_t*>(xw) + (size_t)t * H;
+                for (int i = 0; i < H; ++i) xu[i] = (uint8_t)(xq[(size_t)t * H + i] + 128);
+            } else if (i8_fast) {
                 for (int i = 0; i < H; ++i) xw[(size_t)t * H + i] = xq[(size_t)t * H + i];
+            }
         }
         if (q4_fast) block_sums(xr, H, &xbs[(size_t)t * (H / 32)]);
         if (q4x) q4x_order(xr, H, &xp[(size_t)t * H]);
@@ -621,14 +672,17 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
             const float* su = reinterpret_cast<const float*>(slab + lay.s[1]);
             for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
                 const int nt = std::min(4, cnt[e + 1] - c0);
-                const int16_t* xr[4];
-                for (int i = 0; i < nt; ++i) xr[i] = &xw[(size_t)(order[c0 + i] / k) * H];
+                const void* xr[4];
+                for (int i = 0; i < nt; ++i) {
+                    const size_t o = (size_t)(order[c0 + i] / k) * H;
+                    xr[i] = i8_vnni ? (const void*)(reinterpret_cast<const uint8_t*>(xw) + o) : (const void*)&xw[o];
+                }
                 const RowPrefetch p_g(wg, H, I), p_u(wu, H, I);
                 for (int r = r0; r < r1; ++r) {
                     p_g(r), p_u(r);
                     int32_t dg[4], du[4];
-                    dot_i8x_rows(nt, wg + (size_t)r * H, xr, H, dg);
-                    dot_i8x_rows(nt, wu + (size_t)r * H, xr, H, du);
+                    dot_i8_rows(i8_vnni, nt, wg + (size_t)r * H, xr, H, dg);
+                    dot_i8_rows(i8_vnni, nt, wu + (size_t)r * H, xr, H, du);
                     for (int i = 0; i < nt; ++i) {
                         const int p = order[c0 + i], t = p / k;
                         const float g = ((float)dg[i] * xs[t]) * sg[r];
@@ -717,8 +771,12 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
         const float* hr = &hf[(size_t)p * I];
         if (w_type == MOE_W_W8A8) {
             hs[p] = quant_row(hr, I, &hq[(size_t)p * I]);
-            if (i8_fast)
+            if (i8_vnni) {
+                uint8_t* hu = reinterpret_cast<uint8_t*>(hw) + (size_t)p * I;
+                for (int i = 0; i < I; ++i) hu[i] = (uint8_t)(hq[(size_t)p * I + i] + 128);
+            } else if (i8_fast) {
                 for (int i = 0; i < I; ++i) hw[(size_t)p * I + i] = hq[(size_t)p * I + i];
+            }
         }
         if (need_hb)
             for (int i = 0; i < I; ++i) hb[(size_t)p * I + i] = f2bf(hr[i]);
@@ -767,13 +825,16 @@ extern "C" int moe_ffn_host_misses(const void* x_h, int x_dtype, const int32_t* 
             const float* sd = reinterpret_cast<const float*>(slab + lay.s[2]);
             for (int c0 = cnt[e]; c0 < cnt[e + 1]; c0 += 4) {
                 const int nt = std::min(4, cnt[e + 1] - c0);
-                const int16_t* hr[4];
-                for (int i = 0; i < nt; ++i) hr[i] = &hw[(size_t)order[c0 + i] * I];
+                const void* hr[4];
+                for (int i = 0; i < nt; ++i) {
+                    const size_t o = (size_t)order[c0 + i] * I;
+                    hr[i] = i8_vnni ? (const void*)(reinterpret_cast<const uint8_t*>(hw) + o) : (const void*)&hw[o];
+                }
                 const RowPrefetch pw(wd, I, H);
                 for (int m = m0; m < m1; ++m) {
                     pw(m);
                     int32_t d[4];
-                    dot_i8x_rows(nt, wd + (size_t)m * I, hr, I, d);
+                    dot_i8_rows(i8_vnni, nt, wd + (size_t)m * I, hr, I, d);
                     for (int i = 0; i < nt; ++i) {
                         const int p = order[c0 + i];
                         part[(size_t)p * H + m] = w_h[p] * (((float)d[i] * hs[p]) * sd[m]);
