@@ -1227,6 +1227,46 @@ def test_native_prefill_144_slots_with_host_misses(m, mode):
     torch.cuda.empty_cache()
 
 
+def test_native_switch_at_its_threshold(m):
+    """The big-batch switch compares the step's host picks with the
+    threshold times its host experts: with the threshold at the step's own
+    ratio (rounded down) the misses stream, one above it the CPU lane runs.
+    The 128-expert bf16 layer at 256 tokens (a step with a staging ring), 64
+    experts resident; both lanes' outputs against the oracle on sampled
+    tokens, and a step the default threshold sends to the CPU lane."""
+    from expert_vram_slot_amd.layer import NativeStack
+    T = 256
+    li = synth.LayerInputs("c2", T=T)
+    E, k, H, I, S = li.E, li.k, li.H, li.I, 64
+    z = oracle.logits(li.x, 1, li.G)
+    ids = oracle.topk(z, k)
+    w = oracle.route_weights(z, ids)
+    resident = np.arange(0, E, 2).astype(np.int32)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    host_ids = ids[e2s[ids] < 0]
+    ratio = len(host_ids) / len(set(host_ids.tolist()))
+    assert 8 < ratio < 40  # the default threshold keeps this step on the CPU lane
+    spec = dict(host_store=torch.from_numpy(li.store).pin_memory(), slot_store=dev(li.store[resident]),
+                G=dev(li.G.view(np.int16)), bias=None, resident=dev(resident))
+    nat = NativeStack(E=E, k=k, H=H, I=I, S=S, w_type=1, T_max=T, layers=[spec])
+    x = dev(li.x.view(np.int16))
+    rng = np.random.default_rng(256)
+    sample = np.concatenate([[0, T - 1], rng.choice(np.arange(1, T - 1), 6, replace=False)])
+    for thr, mode in ((None, 1), (int(np.floor(ratio)), 2), (int(np.floor(ratio)) + 1, 1)):
+        if thr is not None:
+            nat.set_stream_threshold(thr)
+        y = host(nat.layer_step(0, x, T))
+        assert nat.last_host_mode() == mode, f"threshold {thr}, {ratio:.2f} host picks per host expert"
+        assert np.all(np.isfinite(y))
+        for t in sample:
+            ref = np.zeros(H)
+            for j in range(k):
+                ref += w[t, j] * oracle.expert(1, li.store[ids[t, j]], H, I, li.x[t], 1)
+            assert_close(y[t:t + 1], ref[None, :].astype(np.float32), 1, f"threshold {thr} token {t}")
+    nat.close()
+
+
 @pytest.mark.parametrize("T", [1, 32])
 def test_native_stack_equals_python_stack(m, T):
     from expert_vram_slot_amd.layer import NativeStack, SlotStack
