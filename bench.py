@@ -1040,7 +1040,7 @@ def _csv_rows(d, suffix):
 
 def _short(name):
     n = name.split("(")[0] if "::" not in name else name
-    for k in ("k_group_hist", "k_group_place", "k_group_small", "k_group", "k_gu", "k_down_tok", "k_down", "k_reduce", "k_route",
+    for k in ("k_group_hist", "k_group_place", "k_group_small", "k_group", "k_gu", "k_down_tok", "k_down", "k_reduce16", "k_reduce", "k_route",
               "k_logits",
               "k_topk", "k_manage", "k_gather", "k_combine", "k_quant_rows", "k_block_sums", "k_pick_static",
               "k_bias_table", "k_cache_init", "k_pf_gemm", "k_pf_wide", "k_dec_gemm", "k_pf_tiles", "k_residual_bf16",
@@ -1232,8 +1232,8 @@ def summarize_prefill(args):
         gu_cols = I // 128 if big else I // 64
         legs.append((T, [
             (gu, w_gu + T * H * 2 + P * I * 2, 2.0 * P * 2 * I * H, 8 * tile_groups * gu_cols * 256),
-            (dn, w_dn + P * I * 2 + P * H * 4, 2.0 * P * H * I, 8 * tile_groups * (H // 256) * 256),
-            ("k_reduce", P * H * 4 + T * H * 4, 0.0, T * H // 4),
+            (dn, w_dn + P * I * 2 + P * H * 2, 2.0 * P * H * I, 8 * tile_groups * (H // 256) * 256),
+            ("k_reduce16", P * H * 2 + T * H * 4, 0.0, T * H // 8),
         ]))
 
     def pick(rows, name, grid, grid_key):
@@ -1254,7 +1254,7 @@ def summarize_prefill(args):
             lines.extend("  " + l.rstrip() for l in fh if l.strip())
         lines.append("")
     lines.append(f"HBM counters scaled by a 1 GiB copy: FETCH_SIZE x {f_fetch:.3f}, WRITE_SIZE x {f_write:.3f}. "
-                 "Algorithmic bytes: weights once, activations in and out once (x, h, fp32 partials, y).")
+                 "Algorithmic bytes: weights once, activations in and out once (x, h, bf16 partials, y).")
     for T, ks in legs:
         # the leg's reductions: those dispatched right after its down GEMMs
         dn_ids = [int(r["Dispatch_Id"]) for r in pick(trace, ks[1][0], ks[1][3], "Grid_Size_X")]
@@ -1266,7 +1266,7 @@ def summarize_prefill(args):
             tr_rows = pick(trace, name, None if grid is None else grid, "Grid_Size_X")
             f_rows = pick(frows, name, grid, "Grid_Size")
             w_rows = pick(wrows, name, grid, "Grid_Size")
-            if name == "k_reduce" and dn_ids:
+            if name.startswith("k_reduce") and dn_ids:
                 tr_rows = [r for r in tr_rows if int(r["Dispatch_Id"]) - 1 in dn_ids]
             if not tr_rows:
                 continue

@@ -1110,6 +1110,44 @@ __global__ void __launch_bounds__(256) k_reduce(const float* __restrict__ part, 
     reinterpret_cast<float4*>(y + (int64_t)t * H)[m4] = acc;
 }
 
+// k_reduce for the bf16 partials of the prefill-shaped kernels: each thread
+// sums eight columns (16 bytes of each pick's row) in fp32, picks in top-k
+// order as k_reduce, and stores them as two float4.
+__global__ void __launch_bounds__(256) k_reduce16(const uint16_t* __restrict__ part,
+                                                  const int32_t* __restrict__ slot_ids, int T, int k, int S, int H,
+                                                  float* __restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;  // index of an 8-column group
+    const int h8 = H / 8;
+    if (i >= (int64_t)T * h8) return;
+    const int t = (int)(i / h8), m8 = (int)(i % h8);
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int j0 = 0; j0 < k; j0 += 8) {
+        v4u v[8];
+        bool ok[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const int j = j0 + u;
+            const int sl = j < k ? slot_ids[t * k + j] : -1;
+            ok[u] = sl >= 0 && sl < S;
+            const int64_t row = (int64_t)t * k + (j < k ? j : 0);
+            v[u] = reinterpret_cast<const v4u*>(part + row * H)[m8];
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            if (ok[u]) {
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    acc[2 * c] += __uint_as_float(v[u][c] << 16);
+                    acc[2 * c + 1] += __uint_as_float(v[u][c] & 0xffff0000u);
+                }
+            }
+        }
+    }
+    float4* yr = reinterpret_cast<float4*>(y + (int64_t)t * H) + 2 * m8;
+    yr[0] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    yr[1] = make_float4(acc[4], acc[5], acc[6], acc[7]);
+}
+
 __global__ void __launch_bounds__(256) k_combine(float* __restrict__ y, const float* __restrict__ y_add, int64_t n) {
     const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
     if (i < n) y[i] = y[i] + y_add[i];
@@ -1190,6 +1228,12 @@ int run_ffn(const void* x, const int32_t* slot_ids, const float* w, int T, int k
         rc = moe_pf_run(act, w, T, k, slot_store, slab_bytes, S, H, I, lay, pair_list, ws + L.pf_tiles, hbuf, part,
                         st, fused_sort ? slot_ids : nullptr, F, xs, hmax);
         if (rc) return rc;
+        if (moe_pf_part_bf16(F, T, k)) {  // prefill-shaped kernels: bf16 partials
+            const int64_t n8 = (int64_t)T * (H / 8);
+            hipLaunchKernelGGL(k_reduce16, dim3((unsigned)((n8 + 255) / 256)), dim3(256), 0, st,
+                               reinterpret_cast<const uint16_t*>(part), slot_ids, T, k, S, H, y);
+            return moe_check_launch("moe_ffn_slots/reduce16");
+        }
         const int64_t n4 = (int64_t)T * (H / 4);
         hipLaunchKernelGGL(k_reduce, dim3((unsigned)((n4 + 255) / 256)), dim3(256), 0, st, part, slot_ids, T, k, S,
                            H, y);

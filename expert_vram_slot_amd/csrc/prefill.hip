@@ -14,11 +14,13 @@
 //   k_pf_gemm<GU>   [g | u] = X_s [W_g; W_u]^T per tile of 64 h columns,
 //                   SwiGLU epilogue, h (bf16, RNE) stored in sorted-pick order
 //   k_pf_gemm<DOWN> O = H_s W_d^T per tile of 128 output columns,
-//                   part[pick] = w * O (fp32)
+//                   part[pick] = w * O (bf16, RNE; the decode-shaped
+//                   kernels keep fp32 partials)
 //   k_dec_gemm<GU|DOWN>  the same two GEMMs on decode-shaped tiles
 //   k_pf_wide<GU|DOWN>   the same two GEMMs on 256 x 256 tiles when slots
 //                        hold hundreds of picks
-//   k_reduce     y[t] = sum over resident picks in top-k order (decode path's)
+//   k_reduce16   y[t] = fp32 sum of the bf16 partials of its resident picks
+//                in top-k order (k_reduce, the decode path's, sums fp32 ones)
 //
 // Prefill-sized batches (4096 picks and more): a workgroup owns PF_MT = 128
 // token rows x NB * 32 weight rows (NB = 8 when H is a multiple of 256, else 4)
@@ -95,7 +97,8 @@ struct PfArgs {
     const float* wts;            // routing weights [P]
     const PfTile* tiles;
     const int32_t* n_tiles;
-    void* out;                   // GU: h [P][I] bf16 (sorted order); DOWN: part [P][H] fp32
+    void* out;                   // GU: h [P][I] bf16 (sorted order); DOWN: part [P][H] (bf16 in the
+                                 // prefill-shaped kernels, fp32 in the decode-shaped one)
     int K;                       // contraction length (GU: H, DOWN: I)
     int N;                       // output columns (GU: I, DOWN: H)
     int k;                       // top-k (GU: token = pick / k)
@@ -277,7 +280,10 @@ __device__ __forceinline__ void pf_gemm_tile(const PfArgs& g, const PfTile& tl, 
             }
         }
     } else {
-        float* part = reinterpret_cast<float*>(g.out);
+        // bf16 partials: half the bytes of the write here and of the
+        // reduction's read (0.27 GB a call at 2048 tokens of the 288-expert
+        // layer), one rounding of each pick's weighted row before the fp32 sum
+        uint16_t* part = reinterpret_cast<uint16_t*>(g.out);
         // the pick and routing weight of each of this lane's 16 rows: all
         // loads of a kind issued together (looked up row by row behind the
         // row test, the dependent pairs serialise)
@@ -292,9 +298,10 @@ __device__ __forceinline__ void pf_gemm_tile(const PfArgs& g, const PfTile& tl, 
         for (int x = 0; x < 16; ++x) {
             const int r = wv * 32 + (x >> 2) * 8 + (lane >> 5) * 4 + (x & 3);
             if (r >= tl.rows) continue;
-            float* prow = part + (size_t)epk[x] * g.N + jn * (NB * 32);
+            uint16_t* prow = part + (size_t)epk[x] * g.N + jn * (NB * 32);
 #pragma unroll
-            for (int nb = 0; nb < NB; ++nb) __builtin_nontemporal_store(ewt[x] * acc[nb][x], &prow[nb * 32 + col]);
+            for (int nb = 0; nb < NB; ++nb)
+                __builtin_nontemporal_store(moe::f32_to_bf16(ewt[x] * acc[nb][x]), &prow[nb * 32 + col]);
         }
     }
 }
@@ -925,12 +932,12 @@ __global__ void __launch_bounds__(PW_THREADS) k_pf_wide(PfArgs g) {
                     h[hrow + half * 32 + col] = moe::f32_to_bf16(sg * uv);
                 }
             } else {
-                float* part = reinterpret_cast<float*>(g.out);
+                uint16_t* part = reinterpret_cast<uint16_t*>(g.out);  // bf16 partials, as k_pf_gemm
                 const int pk = row_pick[r];
                 const float wt = row_wt[r];
-                float* prow = part + (size_t)pk * g.N + jn * 256 + wc * 128;
+                uint16_t* prow = part + (size_t)pk * g.N + jn * 256 + wc * 128;
 #pragma unroll
-                for (int nb = 0; nb < 4; ++nb) prow[nb * 32 + col] = wt * acc[mb][nb][x];
+                for (int nb = 0; nb < 4; ++nb) prow[nb * 32 + col] = moe::f32_to_bf16(wt * acc[mb][nb][x]);
             }
         }
     }
@@ -1074,6 +1081,8 @@ int moe_pf_max_tiles(int T, int k, int S) {
 }
 
 size_t moe_pf_tiles_bytes(int T, int k, int S) { return (size_t)moe_pf_max_tiles(T, k, S) * sizeof(PfTile) + 16; }
+
+bool moe_pf_part_bf16(int w_type, int T, int k) { return w_type == MOE_W_BF16 && T * k >= PF_BIG_P; }
 
 bool moe_pf_fused_sort(int T, int k) {
     const int P = T * k;

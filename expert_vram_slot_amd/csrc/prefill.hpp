@@ -31,8 +31,12 @@ int moe_pf_max_tiles(int T, int k, int S);
 // True when a batch of T*k picks can be sorted by the gate/up workgroups
 // themselves (decode-shaped tiles, at most 1024 picks).
 bool moe_pf_fused_sort(int T, int k);
+// True when moe_pf_run writes the partials as bf16 (the prefill-shaped
+// kernels: bf16 weights, 4096 picks and more); otherwise they are fp32.
+bool moe_pf_part_bf16(int w_type, int T, int k);
 // Gate/up and down grouped GEMMs over the slot-sorted picks; h goes to hbuf
-// in sorted order, w * (W_d h) to part[pick][H].  Enqueued on `st`.  With
+// in sorted order, w * (W_d h) to part[pick][H] (bf16 or fp32, as
+// moe_pf_part_bf16 says).  Enqueued on `st`.  With
 // sort_slots == NULL, pair_list and the tile list in tiles_ws were written by
 // the sorting kernels; otherwise (moe_pf_fused_sort(T, k) must hold) the
 // gate/up kernel sorts the picks by sort_slots (slot per pick) and writes
