@@ -1205,7 +1205,8 @@ def summarize_prefill(args):
     --summarize reads.  A dispatch belongs to a leg by its grid (the 144-slot
     leg runs the same kernels on other grids): the GEMMs' grids are 8 XCDs x
     ceil(max tiles / 8) x column tiles workgroups of 256 threads, max tiles
-    = min(S, P) + P / 32 + 1 as the library sizes its tile list."""
+    = min(S, P) + P / rows + 1 for tiles of 128 rows (2048 tokens) or 256
+    (16384), as the library sizes those grids."""
     tr, fe, wr, cfe, cwr = args.summarize_prefill
     import synth
     c = synth.CONFIGS["c5"]
@@ -1227,7 +1228,7 @@ def summarize_prefill(args):
         P = T * k
         big = T == 16384
         gu, dn = ("k_pf_wide<0>", "k_pf_wide<1>") if big else ("k_pf_gemm<0, 4>", "k_pf_gemm<1, 8>")
-        tile_groups = (min(E, P) + P // 32 + 1 + 7) // 8
+        tile_groups = (min(E, P) + P // (256 if big else 128) + 1 + 7) // 8
         # gate/up column tiles: 128 gate + up rows (wide tiles), 64 (128-row tiles, four 32-row blocks per wave)
         gu_cols = I // 128 if big else I // 64
         legs.append((T, [

@@ -1074,6 +1074,13 @@ int moe_pf_tile_rows_for(int w_type, int T, int k, int S, int H, int I) {
     return w_type == MOE_W_W8A8 ? DEC_MT : moe_pf_tile_rows(T, k, S, H, I);
 }
 
+namespace {
+// Bound on the tiles of `rows` picks the sort writes for P picks over S
+// slots: each of the at most min(S, P) slots with picks adds at most one
+// partial tile to its P_s / rows whole ones.
+int pf_grid_tiles(int P, int S, int rows) { return (S < P ? S : P) + P / rows + 1; }
+}  // namespace
+
 int moe_pf_max_tiles(int T, int k, int S) {
     const int P = T * k;
     // bounds the sum over slots of ceil(n_s / rows) for every tile height in use (32 rows and up)
@@ -1110,16 +1117,21 @@ int moe_pf_run(const void* x, const float* w, int T, int k, const void* slot_sto
     if (P < PF_BIG_P)
         return dec_launch<DEC_NW, false>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
                                          max_tiles, hbuf, part, st, sort_slots, P, S, nullptr, nullptr);
+    // the grids of the prefill-shaped kernels cover the tiles the sort can
+    // write at their own height (workgroups past the tile count only exit,
+    // but each is still dispatched: at 16384 tokens of the 288-expert layer
+    // the 32-row bound launched ~46,000 of them for ~6,900 tiles)
     if (moe_pf_big(T, k, S, H, I))
-        return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
-                         part, st);
+        return pb_launch(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles,
+                         pf_grid_tiles(P, S, PB_MT), hbuf, part, st);
+    const int grid_tiles = pf_grid_tiles(P, S, PF_MT);
     // down: eight 32-row weight blocks per wave where the output columns come
     // in 256s (fewer, longer workgroups: the 2048-token layer 2.06 -> 2.02 ms);
     // gate/up: four (64 KiB of LDS, two workgroups per CU: 2.13 -> 2.08 ms
     // against eight; two blocks: 2.35 ms)
     if (H % 256 == 0)
-        return pf_launch<4, 8>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles,
+        return pf_launch<4, 8>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, grid_tiles,
                                hbuf, part, st);
-    return pf_launch<4, 4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, max_tiles, hbuf,
+    return pf_launch<4, 4>(x, w, k, slot_store, slab_bytes, H, I, lay, pair_list, tiles, n_tiles, grid_tiles, hbuf,
                            part, st);
 }
