@@ -753,6 +753,34 @@ def test_ffn_prefill_grouped_gemm(m, T, S, H):
     assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
 
 
+@pytest.mark.parametrize("T,k,E,S", [(4100, 1, 24, 20), (420, 10, 40, 30), (136, 32, 48, 36)])
+def test_ffn_prefill_bf16_partials_other_k(m, T, k, E, S):
+    """From 4096 picks the prefill-shaped GEMMs keep each pick's weighted
+    row in bf16 and the reduction sums it in fp32 eight picks at a time: top-1
+    (one pick per token), top-10 (a group of eight and a ragged group of two)
+    and top-32 (four groups), with non-resident experts; every output against
+    the oracle, tokens without a resident pick exactly +0."""
+    H, I = 256, 384
+    assert T * k >= 4096
+    rng = np.random.default_rng(T * k)
+    x = synth.normal(synth.key(11, 2, T), (T, H), 1.0, 1)
+    store = synth.slabs(1, 777, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(T)]).astype(np.int32)
+    w = rng.dirichlet(np.ones(k), T).astype(np.float32)
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(1, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 1, f"prefill T={T} k={k}")
+    none = np.all(sl < 0, axis=1)
+    if k == 1:
+        assert none.any()
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+
+
 @pytest.mark.parametrize("T,S,skew", [(1200, 6, False), (1100, 8, True)])
 def test_ffn_large_groups_256_row_tiles(m, T, S, skew):
     """Hundreds of picks per slot run on 256 x 256 tiles of eight waves:
