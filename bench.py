@@ -1040,7 +1040,8 @@ def _csv_rows(d, suffix):
 
 def _short(name):
     n = name.split("(")[0] if "::" not in name else name
-    for k in ("k_group_hist", "k_group_place", "k_group_small", "k_group", "k_gu", "k_down_tok", "k_down", "k_reduce16", "k_reduce", "k_route",
+    for k in ("k_group_hist", "k_group_place", "k_group_small", "k_group", "k_gu", "k_down_tok", "k_down", "k_reduce16", "k_reduce",
+              "k_manage_gather", "k_logits_mfma", "k_stream_chunk", "k_stream_pos", "k_route",
               "k_logits",
               "k_topk", "k_manage", "k_gather", "k_combine", "k_quant_rows", "k_block_sums", "k_pick_static",
               "k_bias_table", "k_cache_init", "k_pf_gemm", "k_pf_wide", "k_dec_gemm", "k_pf_tiles", "k_residual_bf16",
