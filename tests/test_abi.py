@@ -201,6 +201,34 @@ def test_host_pass_q4_rows_not_in_whole_groups(mlib):
     _assert_close(y, yh, synth.W_Q4B32)
 
 
+@pytest.mark.parametrize("w_type,H,I", [(synth.W_W8A8, 96, 160), (synth.W_W8A8, 80, 112), (synth.W_W8A8, 128, 192),
+                                         (synth.W_BF16, 80, 112), (synth.W_BF16, 96, 160)])
+def test_host_pass_row_lengths_of_every_dot_path(mlib, w_type, H, I):
+    # the host pass picks its dot products by row length: W8A8 rows in whole
+    # 64s take the VNNI path (128 / 192), in 32s the int16 path (96 / 160),
+    # others the scalar one (80 / 112); bf16 rows in 32s the AVX-512 BF16 path,
+    # others the scalar one.  Each against the oracle, several picks per
+    # expert so the grouped row passes run, bits independent of the threads.
+    E, k, T = 6, 3, 9
+    base = synth.config_seed("c3")
+    x = synth.normal(synth.key(base, synth.TAG_X, 5, H), (T, H), 1.0, synth.X_BF16)
+    G = synth.normal(synth.key(base, synth.TAG_G, 5, H), (E, H), 0.5, synth.X_BF16)
+    store = synth.slabs(w_type, base, 5, 0, E, H, I, 0.05)
+    z = oracle.logits(x, synth.X_BF16, G)
+    ids = oracle.topk(z, k)
+    w = oracle.route_weights(z, ids)
+    sl = np.where(ids % 3 == 0, 0, -1).astype(np.int32)
+    _, _, yh = oracle.layer(w_type, store, E, H, I, x, synth.X_BF16, ids, w, sl)
+    slab = synth.slab_bytes(w_type, H, I)
+    ys = []
+    for nt in (1, 4):
+        y = np.full((T, H), np.nan, np.float32)
+        mlib.moe_ffn_host_misses(x, synth.X_BF16, ids, sl, w, T, k, store, slab, E, w_type, H, I, y, nt)
+        ys.append(y)
+    _assert_close(ys[0], yh, w_type)
+    np.testing.assert_array_equal(ys[0], ys[1])
+
+
 def test_host_pass_all_miss_is_the_whole_layer(mlib):
     li = synth.LayerInputs("c1")
     z = oracle.logits(li.x, 0, li.G)
