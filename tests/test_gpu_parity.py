@@ -753,6 +753,29 @@ def test_ffn_prefill_grouped_gemm(m, T, S, H):
     assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
 
 
+@pytest.mark.parametrize("T", [511, 512])
+def test_ffn_bf16_at_the_prefill_tile_switch(m, T):
+    """4088 picks run on the decode-shaped tiles with fp32 partials, 4096 on
+    the prefill-shaped tiles with bf16 partials; both against the oracle, on
+    the same layer and the same first 511 tokens' picks."""
+    E, k, H, I, S = 32, 8, 256, 384, 24
+    rng = np.random.default_rng(4096)
+    x = synth.normal(synth.key(13, 3, 512), (512, H), 1.0, 1)[:T]
+    store = synth.slabs(1, 991, 0, 0, E, H, I, 0.05)
+    ids = np.stack([rng.choice(E, k, replace=False) for _ in range(512)]).astype(np.int32)[:T]
+    w = rng.dirichlet(np.ones(k), 512).astype(np.float32)[:T]
+    resident = rng.choice(E, S, replace=False)
+    e2s = np.full(E, -1, np.int32)
+    e2s[resident] = np.arange(S)
+    sl = e2s[ids]
+    li = type("L", (), dict(T=T, k=k, H=H, I=I, E=E, x=x, x_dtype=1, w_type=1, slab=store.shape[1]))
+    _, yg, _ = oracle.layer(1, store, E, H, I, x, 1, ids, w, sl)
+    y = run_ffn(m, li, sl, w, dev(store[resident]), S)
+    assert_close(y, yg, 1, f"bf16 T={T}")
+    none = np.all(sl < 0, axis=1)
+    assert np.all(y[none] == 0) and not np.any(np.signbit(y[none]))
+
+
 @pytest.mark.parametrize("T,k,E,S", [(4100, 1, 24, 20), (420, 10, 40, 30), (136, 32, 48, 36)])
 def test_ffn_prefill_bf16_partials_other_k(m, T, k, E, S):
     """From 4096 picks the prefill-shaped GEMMs keep each pick's weighted
