@@ -260,7 +260,7 @@ __device__ __forceinline__ void pf_gemm_tile(const PfArgs& g, const PfTile& tl, 
 
     if (!active_wave) return;
     // accumulator element x of lane l: column l % 32 of block nb, row (x/4)*8 + (l/32)*4 + x%4.
-    // h and the fp32 partials are stored non-temporally: the next kernel reads them from other XCDs, so
+    // h and the bf16 partials are stored non-temporally: the next kernel reads them from other XCDs, so
     // they gain nothing in this XCD's L2, where they would push out the weight and token lines still in
     // use (2048-token layer: 2.14 -> 2.07-2.10 ms; the same stores in the decode-shaped and the
     // large-group kernels were 1 % slower)

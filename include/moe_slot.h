@@ -339,7 +339,9 @@ size_t moe_ffn_workspace_bytes(int T, int k, int S, int w_type, int H, int I);
  *   slot_store device [S][slab_bytes] (16-byte aligned; slab_bytes >= layout)
  *   y         device float[T][H] out (overwritten):
  *             y[t] = sum over j with slot_ids[t][j] >= 0 of w[t][j] * FFN_slot(x[t]),
- *             summed in j order; +0.0 where token t has no resident pick
+ *             summed in j order in fp32; +0.0 where token t has no resident
+ *             pick.  With bf16 weights and T*k >= 4096 each term is rounded
+ *             once to bf16 before the sum (prefill-sized batches)
  *   ws        device workspace of >= moe_ffn_workspace_bytes(...) bytes
  * Errors: ARG, ALIGN, DTYPE, SHAPE, HIP. */
 int moe_ffn_slots(const void* x, int x_dtype, const int32_t* slot_ids, const float* w, int T, int k,
